@@ -1,0 +1,294 @@
+// Row-wise kernels of the decoder forward and the set-up kernels of qw_create.
+//
+//  embed      token id -> residual row ("augur": full forward pass starts from
+//             the embedding table; "LLM Speedrun: Architecture", harness
+//             listing's Embedding: the table is [vocab, hidden]).
+//  rmsnorm    "LLM Speedrun: Architecture", section "Normalization": each row
+//             divided by sqrt(mean(x^2) + eps), times the norm weight.
+//  rope_cache q/k/v bias ("Introducing bias"), split-half RoPE on q and k
+//             ("Split-half RoPE implementation"), and the write of k and v
+//             into the preallocated cache ("augur": preallocated KV-cache).
+//  argmax     greedy choice: lowest index of the largest logit.
+#include "qw_internal.h"
+
+#include <math.h>
+
+namespace qw {
+
+// ---------------------------------------------------------------- embed
+template <typename T>
+__global__ void __launch_bounds__(256) embed_kernel(const int32_t *__restrict__ ids, const T *__restrict__ emb,
+                                                    float emb_scale, int hidden, int vocab,
+                                                    float *__restrict__ x, int *__restrict__ bad) {
+  const int r = blockIdx.x;
+  int id = ids[r];
+  if (id < 0 || id >= vocab) {
+    if (threadIdx.x == 0) atomicOr(bad, 1);
+    id = 0;
+  }
+  const T *src = emb + (int64_t)id * hidden;
+  float *dst = x + (int64_t)r * hidden;
+  for (int c = threadIdx.x; c < hidden; c += blockDim.x) dst[c] = to_f32(src[c]) * emb_scale;
+}
+
+hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int rows, const void *emb,
+                        float emb_scale, int hidden, int vocab, float *x, int *bad) {
+  if (rows <= 0) return hipSuccess;
+  if (f16_mode)
+    embed_kernel<f16><<<rows, 256, 0, s>>>(ids, (const f16 *)emb, emb_scale, hidden, vocab, x, bad);
+  else
+    embed_kernel<float><<<rows, 256, 0, s>>>(ids, (const float *)emb, emb_scale, hidden, vocab, x, bad);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- rmsnorm
+// One wave per row; fp32 statistics; the product is rounded once to T.
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ x, int rows, int row_stride,
+                                                      int hidden, const float *__restrict__ w, float eps,
+                                                      T *__restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const float4 *xr = reinterpret_cast<const float4 *>(x + (int64_t)r * row_stride);
+  const int n4 = hidden >> 2;
+  float ss = 0.f;
+  for (int c = lane; c < n4; c += 64) {
+    float4 v = xr[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)hidden + eps);
+  const float4 *w4 = reinterpret_cast<const float4 *>(w);
+  T *o = out + (int64_t)r * hidden;
+  for (int c = lane; c < n4; c += 64) {
+    float4 v = xr[c], g = w4[c];
+    o[4 * c + 0] = from_f32<T>(v.x * inv * g.x);
+    o[4 * c + 1] = from_f32<T>(v.y * inv * g.y);
+    o[4 * c + 2] = from_f32<T>(v.z * inv * g.z);
+    o[4 * c + 3] = from_f32<T>(v.w * inv * g.w);
+  }
+}
+
+hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows, int row_stride, int hidden,
+                          const float *w, float eps, void *out) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid((rows + 3) / 4);
+  if (f16_mode)
+    rmsnorm_kernel<f16><<<grid, 256, 0, s>>>(x, rows, row_stride, hidden, w, eps, (f16 *)out);
+  else
+    rmsnorm_kernel<float><<<grid, 256, 0, s>>>(x, rows, row_stride, hidden, w, eps, (float *)out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- bias + RoPE + cache write
+// One block per row.  Work item i enumerates (head, pair) over the q heads,
+// then the k heads (both rotated), then the v heads (copied).
+template <typename T>
+__global__ void __launch_bounds__(256) rope_cache_kernel(RopeCacheArgs a) {
+  const int t = blockIdx.x;
+  const int half = a.head_dim >> 1;
+  const int b = t / a.rows_per_seq;
+  const int pos = (a.pos0_dev ? *a.pos0_dev : a.pos0) + (t % a.rows_per_seq);
+  const int qd = a.n_heads * a.head_dim, kvd = a.n_kv_heads * a.head_dim;
+  const int ncols = qd + 2 * kvd;
+  const float *row = a.qkv + (int64_t)t * ncols;
+  const float2 *cs = a.rope + (int64_t)pos * half;
+  const int n_items = (a.n_heads + 2 * a.n_kv_heads) * half;
+  for (int it = threadIdx.x; it < n_items; it += blockDim.x) {
+    const int head = it / half, i = it % half;
+    const int c0 = head * a.head_dim + i, c1 = c0 + half;   // column in qkv
+    float re = row[c0] + a.bias[c0];
+    float im = row[c1] + a.bias[c1];
+    if (head < a.n_heads + a.n_kv_heads) {                  // q or k: rotate
+      const float2 r = cs[i];
+      const float nre = re * r.x - im * r.y;
+      const float nim = im * r.x + re * r.y;
+      re = nre;
+      im = nim;
+    }
+    if (head < a.n_heads) {
+      T *q = (T *)a.q_out + (int64_t)t * qd;
+      q[c0] = from_f32<T>(re);
+      q[c1] = from_f32<T>(im);
+    } else {
+      const bool is_k = head < a.n_heads + a.n_kv_heads;
+      const int j = is_k ? head - a.n_heads : head - a.n_heads - a.n_kv_heads;
+      T *cache = (T *)(is_k ? a.k_cache : a.v_cache);
+      T *dst = cache + (((int64_t)b * a.n_kv_heads + j) * a.max_seq + pos) * a.head_dim;
+      dst[i] = from_f32<T>(re);
+      dst[i + half] = from_f32<T>(im);
+    }
+  }
+}
+
+hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a) {
+  if (a.T <= 0) return hipSuccess;
+  if (f16_mode)
+    rope_cache_kernel<f16><<<a.T, 256, 0, s>>>(a);
+  else
+    rope_cache_kernel<float><<<a.T, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- argmax
+// One block per row.  Ties go to the lowest index; NaN never wins.
+__global__ void __launch_bounds__(256) argmax_kernel(const float *__restrict__ logits, int vocab, int64_t stride,
+                                                     int32_t *__restrict__ next_ids, int *pos_dev, int pos_add) {
+  const float *row = logits + (int64_t)blockIdx.x * stride;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int v = threadIdx.x; v < vocab; v += blockDim.x) {
+    const float x = row[v];
+    if (x > best) { best = x; bi = v; }      // v increases, so the first max is kept
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+  }
+  __shared__ float sb[4];
+  __shared__ int si[4];
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sb[wv] = best; si[wv] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (sb[w] > best || (sb[w] == best && si[w] < bi)) { best = sb[w]; bi = si[w]; }
+    next_ids[blockIdx.x] = (bi == 0x7fffffff) ? 0 : bi;     // all-NaN row: 0
+    if (pos_dev && blockIdx.x == 0) *pos_dev += pos_add;
+  }
+}
+
+hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
+                         int32_t *next_ids, int *pos_dev, int pos_add) {
+  if (rows <= 0) return hipSuccess;
+  argmax_kernel<<<rows, 256, 0, s>>>(logits, vocab, row_stride, next_ids, pos_dev, pos_add);
+  return hipGetLastError();
+}
+
+__global__ void set_int_kernel(int *p, int v) { *p = v; }
+
+// Copies around the captured decode graph: caller ids into the staging row the
+// graph reads, and the graph's next ids (and logits, when asked) out to the
+// caller's buffers.
+__global__ void __launch_bounds__(256) copy_i32_kernel(int32_t *dst, const int32_t *src, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) dst[i] = src[i];
+}
+
+__global__ void __launch_bounds__(256) stage_out_kernel(int32_t *next_dst, const int32_t *next_src, int b,
+                                                        float *logits_dst, const float *logits_src, int64_t n) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid < b) next_dst[tid] = next_src[tid];
+  for (int64_t i = tid; i < n; i += (int64_t)gridDim.x * blockDim.x) logits_dst[i] = logits_src[i];
+}
+
+hipError_t launch_copy_i32(hipStream_t s, int32_t *dst, const int32_t *src, int n) {
+  copy_i32_kernel<<<(n + 255) / 256, 256, 0, s>>>(dst, src, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_out(hipStream_t s, int32_t *next_dst, const int32_t *next_src, int b, float *logits_dst,
+                            const float *logits_src, int64_t n_logits) {
+  const int64_t n = logits_dst ? n_logits : 0;
+  const int64_t total = n > b ? n : b;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  stage_out_kernel<<<(unsigned)blocks, 256, 0, s>>>(next_dst, next_src, b, logits_dst, logits_src, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_int(hipStream_t s, int *p, int v) {
+  set_int_kernel<<<1, 1, 0, s>>>(p, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- set-up
+__device__ __forceinline__ float load_src(const void *p, int64_t i, bool bf16) {
+  return bf16 ? bf16_bits_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
+}
+
+// Largest |value| of a tensor, as the bit pattern of a non-negative float
+// (ordered like the floats themselves, so an integer max works).
+__global__ void __launch_bounds__(256) absmax_kernel(const void *src, int64_t n, bool bf16, unsigned *out) {
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    m = fmaxf(m, fabsf(load_src(src, i, bf16)));
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(m));
+}
+
+hipError_t launch_absmax(hipStream_t s, bool src_bf16, const void *src, int64_t n, unsigned *out_bits) {
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  absmax_kernel<<<blocks, 256, 0, s>>>(src, n, src_bf16, out_bits);
+  return hipGetLastError();
+}
+
+template <typename D>
+__global__ void __launch_bounds__(256) convert_kernel(const void *src, int64_t n, bool bf16, D *dst, float scale) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = from_f32<D>(load_src(src, i, bf16) * scale);
+}
+
+hipError_t launch_convert(hipStream_t s, bool src_bf16, const void *src, int64_t n, bool dst_f16, void *dst,
+                          int64_t dst_offset, float scale) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 16384) blocks = 16384;
+  if (dst_f16)
+    convert_kernel<f16><<<blocks, 256, 0, s>>>(src, n, src_bf16, (f16 *)dst + dst_offset, scale);
+  else
+    convert_kernel<float><<<blocks, 256, 0, s>>>(src, n, src_bf16, (float *)dst + dst_offset, scale);
+  return hipGetLastError();
+}
+
+template <typename D>
+__global__ void __launch_bounds__(256) convert_gu_kernel(const void *gate, const void *up, int inter, int hidden,
+                                                         bool bf16, D *dst, float scale) {
+  const int64_t n = 2LL * inter * hidden;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t drow = i / hidden;
+    const int c = (int)(i % hidden);
+    const int64_t blk = drow / (2 * GU_BLOCK);
+    const int within = (int)(drow % (2 * GU_BLOCK));
+    const bool is_up = within >= GU_BLOCK;
+    const int64_t f = blk * GU_BLOCK + (is_up ? within - GU_BLOCK : within);
+    dst[i] = from_f32<D>(load_src(is_up ? up : gate, f * hidden + c, bf16) * scale);
+  }
+}
+
+hipError_t launch_convert_gu(hipStream_t s, bool src_bf16, const void *gate, const void *up, int inter, int hidden,
+                             bool dst_f16, void *dst, float scale) {
+  const int64_t n = 2LL * inter * hidden;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 16384) blocks = 16384;
+  if (dst_f16)
+    convert_gu_kernel<f16><<<blocks, 256, 0, s>>>(gate, up, inter, hidden, src_bf16, (f16 *)dst, scale);
+  else
+    convert_gu_kernel<float><<<blocks, 256, 0, s>>>(gate, up, inter, hidden, src_bf16, (float *)dst, scale);
+  return hipGetLastError();
+}
+
+// RoPE table: entry (pos, i) = (cos, sin) of pos * theta^(-2i/hd), evaluated in
+// double and rounded once to float ("Rotary Positional Embeddings RoPE").
+__global__ void __launch_bounds__(256) rope_table_kernel(float2 *table, int max_seq, int head_dim, double theta) {
+  const int half = head_dim / 2;
+  const int64_t n = (int64_t)max_seq * half;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int pos = (int)(e / half), i = (int)(e % half);
+    const double ang = (double)pos * pow(theta, -2.0 * (double)i / (double)head_dim);
+    table[e] = make_float2((float)cos(ang), (float)sin(ang));
+  }
+}
+
+hipError_t launch_rope_table(hipStream_t s, float2 *table, int max_seq, int head_dim, double theta) {
+  const int64_t n = (int64_t)max_seq * (head_dim / 2);
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  rope_table_kernel<<<blocks, 256, 0, s>>>(table, max_seq, head_dim, theta);
+  return hipGetLastError();
+}
+
+}  // namespace qw

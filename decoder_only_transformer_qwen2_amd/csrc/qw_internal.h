@@ -1,0 +1,108 @@
+// Internal declarations shared by the HIP kernels and the host runtime of
+// libqw.so.  Device helpers are header-inline; every kernel family has a host
+// launcher declared here and defined next to its kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qw {
+
+// Packed gate/up projection: rows of W_gate and W_up alternate in blocks of
+// GU_BLOCK rows ([g0..g15, u0..u15, g16..g31, u16..u31, ...]), so a tile of
+// whole block pairs holds the gate and up value of the same features.
+constexpr int GU_BLOCK = 16;
+
+typedef _Float16 f16;
+
+// ------------------------------------------------------------ device helpers
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(f16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float v) { return (f16)v; }  // RNE
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------ launch params
+enum class Epi : int {
+  StoreF32 = 0,   // out_f32[m, n] = acc * scale
+  ResidAdd = 1,   // resid[m, n] += acc * scale
+  SwiGLU = 2,     // act_out[m, f] = silu(gate) * up over GU_BLOCK-interleaved rows
+};
+
+struct GemmArgs {
+  const void *A;        // [M, K] activations (compute type), row stride lda
+  const void *W;        // [N, K] weights (compute type), row stride K
+  int M, N, K, lda;
+  float scale;          // exact power of two undoing the weight scaling
+  Epi epi;
+  float *out_f32;       // StoreF32: [M, ldo]; ResidAdd: residual [M, ldo]
+  void *act_out;        // SwiGLU: [M, ldo] compute type, ldo = N / 2
+  int ldo;
+};
+
+struct RopeCacheArgs {
+  const float *qkv;      // [T, nq*hd + 2*nkv*hd] projections without bias
+  const float *bias;     // [nq*hd + 2*nkv*hd]
+  const float2 *rope;    // [max_seq, hd/2] (cos, sin)
+  void *q_out;           // [T, nq*hd] compute type
+  void *k_cache, *v_cache;  // layer base: [max_batch][nkv][max_seq][hd]
+  int T, rows_per_seq, n_heads, n_kv_heads, head_dim, max_seq;
+  int pos0;              // position of each sequence's first row ...
+  const int *pos0_dev;   // ... or, if non-null, read from the device
+};
+
+struct AttnArgs {
+  const void *q;              // [T, nq*hd]
+  const void *k_cache, *v_cache;  // layer base
+  void *o;                    // [T, nq*hd]
+  int T, rows_per_seq, n_heads, n_kv_heads, head_dim, max_seq;
+  int pos0;
+  const int *pos0_dev;
+  float softmax_scale;
+};
+
+// ------------------------------------------------------------ launchers
+// Each returns the hipError_t of its launch.  `f16_mode` selects the compute
+// type (f16 when true, float when false).
+hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int rows, const void *emb,
+                        float emb_scale, int hidden, int vocab, float *x, int *bad_id_flag);
+hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows, int row_stride,
+                          int hidden, const float *w, float eps, void *out);
+hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a);
+hipError_t launch_attention_generic(hipStream_t s, bool f16_mode, const AttnArgs &a);
+hipError_t launch_gemm_generic(hipStream_t s, bool f16_mode, const GemmArgs &a);
+hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
+                         int32_t *next_ids, int *pos_dev, int pos_add);
+hipError_t launch_set_int(hipStream_t s, int *p, int v);
+hipError_t launch_copy_i32(hipStream_t s, int32_t *dst, const int32_t *src, int n);
+// next_dst[0..b) = next_src; if logits_dst, logits_dst[0..n_logits) = logits_src
+hipError_t launch_stage_out(hipStream_t s, int32_t *next_dst, const int32_t *next_src, int b, float *logits_dst,
+                            const float *logits_src, int64_t n_logits);
+
+// set-up kernels (qw_create)
+hipError_t launch_absmax(hipStream_t s, bool src_bf16, const void *src, int64_t n, unsigned *out_bits);
+// dst[dst_offset + i] = src[i] * scale for i < n (scale: exact power of two)
+hipError_t launch_convert(hipStream_t s, bool src_bf16, const void *src, int64_t n, bool dst_f16, void *dst,
+                          int64_t dst_offset, float scale);
+hipError_t launch_convert_gu(hipStream_t s, bool src_bf16, const void *gate, const void *up, int inter,
+                             int hidden, bool dst_f16, void *dst, float scale);
+hipError_t launch_rope_table(hipStream_t s, float2 *table, int max_seq, int head_dim, double theta);
+
+}  // namespace qw

@@ -1,0 +1,613 @@
+// Host runtime of libqw.so: argument and state validation, the library's own
+// packed weight copies, KV cache and workspace, the per-layer launch sequence
+// of prefill and decode, and the captured HIP graph of a decode step.
+//
+// Launch sequence of one decoder block (pre-norm, "LLM Speedrun:
+// Architecture", section "Why pre-norm over post-norm?"; "augur": decoder
+// blocks are norm, attention, residual, norm, MLP, residual):
+//   rmsnorm(x) -> u;  u.Wqkv^T -> qkv;  bias + RoPE -> q, cache[k, v];
+//   attention(q, cache) -> o;  x += o.Wo^T;  rmsnorm(x) -> u;
+//   silu(u.Wg^T) * (u.Wu^T) -> h;  x += h.Wd^T
+// then, after the last block, the final norm of each sequence's last row, the
+// LM head and the greedy argmax ("augur": full forward pass; greedy
+// generation).  Prefill runs this over every prompt row at once; a decode step
+// over one row per sequence at the next position ("Building a Qwen2.5-1.5B
+// Inference Engine From Scratch", section 1: prefill and decode).
+#include "../../include/qw.h"
+#include "qw_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <utility>
+#include <vector>
+
+using namespace qw;
+
+namespace {
+
+thread_local std::string g_err;
+
+qw_status fail(qw_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                         \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess)                                                                     \
+      return fail(e_ == hipErrorOutOfMemory ? QW_ERR_OUT_OF_MEMORY : QW_ERR_HIP, "%s: %s (%s:%d)", \
+                  #expr, hipGetErrorString(e_), __FILE__, __LINE__);                          \
+  } while (0)
+
+enum Family { F_EMBED, F_RMSNORM, F_GEMM_QKV, F_ROPE_CACHE, F_ATTENTION, F_GEMM_O, F_GEMM_GATE_UP,
+              F_GEMM_DOWN, F_LM_HEAD, F_ARGMAX, F_COUNT };
+const char *const kFamilyNames[F_COUNT] = {"embed", "rmsnorm", "gemm_qkv", "rope_cache", "attention",
+                                           "gemm_o", "gemm_gate_up", "gemm_down", "lm_head", "argmax"};
+const char *const kFamilyList = "embed,rmsnorm,gemm_qkv,rope_cache,attention,gemm_o,gemm_gate_up,gemm_down,lm_head,argmax";
+
+struct LayerBuf {
+  void *w_qkv = nullptr;    // [qd + 2 kvd, H]
+  float *b_qkv = nullptr;   // [qd + 2 kvd]
+  void *w_o = nullptr;      // [H, qd]
+  void *w_gu = nullptr;     // [2I, H], GU_BLOCK-interleaved
+  void *w_down = nullptr;   // [H, I]
+  float *in_norm = nullptr, *post_norm = nullptr;
+  float s_qkv = 1.f, s_o = 1.f, s_gu = 1.f, s_down = 1.f;
+};
+
+}  // namespace
+
+struct qw_model {
+  qw_config cfg{};
+  bool f16 = false;          // compute type: f16 (bf16 weights) or f32
+  size_t esz = 4;
+  int qd = 0, kvd = 0, nqkv = 0;
+  int64_t rows_cap = 0;      // max_batch * max_seq
+  hipStream_t stream = nullptr;
+  hipStream_t cap = nullptr;
+  std::vector<LayerBuf> L;
+  void *emb = nullptr;
+  float emb_scale = 1.f;
+  void *head = nullptr;
+  float head_scale = 1.f;
+  float *final_norm = nullptr;
+  void *k_cache = nullptr, *v_cache = nullptr;
+  int64_t cache_layer_elems = 0;
+  float2 *rope = nullptr;
+  float *x = nullptr, *qkv = nullptr, *logits = nullptr;
+  void *u = nullptr, *q = nullptr, *o = nullptr, *h = nullptr;
+  int *pos_dev = nullptr, *bad_ids = nullptr;
+  int32_t *ids_stage = nullptr, *next_stage = nullptr;   // [max_batch] rows the decode graph reads / writes
+  int batch = 0, pos = 0;
+  // decode graph, captured against the staging rows (so caller pointers may
+  // change from step to step) for the batch of the last prefill
+  bool use_graph = true;
+  bool graph_ok = false;
+  int graph_batch = 0;
+  hipGraphExec_t gexec = nullptr;
+  // kernel timing
+  int timing_family = -1;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev_used, ev_free;
+  double timing_ms = 0;
+  int64_t timing_n = 0;
+  std::vector<void *> allocs;
+
+  hipError_t alloc(void **p, size_t bytes) {
+    *p = nullptr;
+    if (bytes == 0) bytes = 256;
+    hipError_t e = hipMalloc(p, bytes);
+    if (e == hipSuccess) allocs.push_back(*p);
+    return e;
+  }
+};
+
+namespace {
+
+// Bracket a launch of `fam` with events when timing that family.
+template <class F>
+hipError_t timed(qw_model *m, hipStream_t s, Family fam, F &&launch) {
+  if (m->timing_family != fam) return launch();
+  std::pair<hipEvent_t, hipEvent_t> ev;
+  if (!m->ev_free.empty()) {
+    ev = m->ev_free.back();
+    m->ev_free.pop_back();
+  } else {
+    hipError_t e = hipEventCreate(&ev.first);
+    if (e == hipSuccess) e = hipEventCreate(&ev.second);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipEventRecord(ev.first, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(ev.second, s);
+  m->ev_used.push_back(ev);
+  return e;
+}
+
+hipError_t gemm(qw_model *m, hipStream_t s, Family fam, const void *A, int M, int K, int lda, const void *W, int N,
+                float scale, Epi epi, float *out_f32, void *act_out, int ldo) {
+  GemmArgs a;
+  a.A = A;
+  a.W = W;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.lda = lda;
+  a.scale = scale;
+  a.epi = epi;
+  a.out_f32 = out_f32;
+  a.act_out = act_out;
+  a.ldo = ldo;
+  return timed(m, s, fam, [&] { return launch_gemm_generic(s, m->f16, a); });
+}
+
+// The decoder blocks over T rows (rows_per_seq rows per sequence, the first at
+// position pos0, or at *pos_dev when pos_dev is given); x holds the embedded
+// rows on entry and the final residual stream on exit.
+hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int pos0, const int *pos_dev) {
+  const qw_config &c = m->cfg;
+  const int H = c.hidden, I = c.intermediate;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerBuf &Lw = m->L[l];
+    hipError_t e;
+    e = timed(m, s, F_RMSNORM, [&] { return launch_rmsnorm(s, m->f16, m->x, T, H, H, Lw.in_norm, c.rms_eps, m->u); });
+    if (e != hipSuccess) return e;
+    e = gemm(m, s, F_GEMM_QKV, m->u, T, H, H, Lw.w_qkv, m->nqkv, Lw.s_qkv, Epi::StoreF32, m->qkv, nullptr, m->nqkv);
+    if (e != hipSuccess) return e;
+    char *kc = (char *)m->k_cache + (int64_t)l * m->cache_layer_elems * m->esz;
+    char *vc = (char *)m->v_cache + (int64_t)l * m->cache_layer_elems * m->esz;
+    RopeCacheArgs ra;
+    ra.qkv = m->qkv;
+    ra.bias = Lw.b_qkv;
+    ra.rope = m->rope;
+    ra.q_out = m->q;
+    ra.k_cache = kc;
+    ra.v_cache = vc;
+    ra.T = T;
+    ra.rows_per_seq = rows_per_seq;
+    ra.n_heads = c.n_heads;
+    ra.n_kv_heads = c.n_kv_heads;
+    ra.head_dim = c.head_dim;
+    ra.max_seq = c.max_seq;
+    ra.pos0 = pos0;
+    ra.pos0_dev = pos_dev;
+    e = timed(m, s, F_ROPE_CACHE, [&] { return launch_rope_cache(s, m->f16, ra); });
+    if (e != hipSuccess) return e;
+    AttnArgs aa;
+    aa.q = m->q;
+    aa.k_cache = kc;
+    aa.v_cache = vc;
+    aa.o = m->o;
+    aa.T = T;
+    aa.rows_per_seq = rows_per_seq;
+    aa.n_heads = c.n_heads;
+    aa.n_kv_heads = c.n_kv_heads;
+    aa.head_dim = c.head_dim;
+    aa.max_seq = c.max_seq;
+    aa.pos0 = pos0;
+    aa.pos0_dev = pos_dev;
+    aa.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
+    e = timed(m, s, F_ATTENTION, [&] { return launch_attention_generic(s, m->f16, aa); });
+    if (e != hipSuccess) return e;
+    e = gemm(m, s, F_GEMM_O, m->o, T, m->qd, m->qd, Lw.w_o, H, Lw.s_o, Epi::ResidAdd, m->x, nullptr, H);
+    if (e != hipSuccess) return e;
+    e = timed(m, s, F_RMSNORM, [&] { return launch_rmsnorm(s, m->f16, m->x, T, H, H, Lw.post_norm, c.rms_eps, m->u); });
+    if (e != hipSuccess) return e;
+    e = gemm(m, s, F_GEMM_GATE_UP, m->u, T, H, H, Lw.w_gu, 2 * I, Lw.s_gu, Epi::SwiGLU, nullptr, m->h, I);
+    if (e != hipSuccess) return e;
+    e = gemm(m, s, F_GEMM_DOWN, m->h, T, I, I, Lw.w_down, H, Lw.s_down, Epi::ResidAdd, m->x, nullptr, H);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Final norm of `rows` residual rows (row r at x + r * stride floats), LM head
+// into logits [rows, V], and argmax of `arg_rows` rows of those logits.
+hipError_t run_head(qw_model *m, hipStream_t s, const float *x_rows, int rows, int stride, float *logits,
+                    const float *arg_logits, int arg_rows, int64_t arg_stride, int32_t *next, int *pos_dev,
+                    int pos_add) {
+  const qw_config &c = m->cfg;
+  hipError_t e = timed(m, s, F_RMSNORM, [&] {
+    return launch_rmsnorm(s, m->f16, x_rows, rows, stride, c.hidden, m->final_norm, c.rms_eps, m->u);
+  });
+  if (e != hipSuccess) return e;
+  e = gemm(m, s, F_LM_HEAD, m->u, rows, c.hidden, c.hidden, m->head, c.vocab, m->head_scale, Epi::StoreF32, logits,
+           nullptr, c.vocab);
+  if (e != hipSuccess) return e;
+  return timed(m, s, F_ARGMAX,
+               [&] { return launch_argmax(s, arg_logits, arg_rows, c.vocab, arg_stride, next, pos_dev, pos_add); });
+}
+
+hipError_t decode_body(qw_model *m, hipStream_t s, const int32_t *ids, float *logits, int32_t *next) {
+  const qw_config &c = m->cfg;
+  const int B = m->batch;
+  hipError_t e = timed(m, s, F_EMBED, [&] {
+    return launch_embed(s, m->f16, ids, B, m->emb, m->emb_scale, c.hidden, c.vocab, m->x, m->bad_ids);
+  });
+  if (e != hipSuccess) return e;
+  e = run_layers(m, s, B, 1, 0, m->pos_dev);
+  if (e != hipSuccess) return e;
+  float *lg = logits ? logits : m->logits;
+  return run_head(m, s, m->x, B, c.hidden, lg, lg, B, c.vocab, next, m->pos_dev, 1);
+}
+
+void drop_graph(qw_model *m) {
+  if (m->gexec) (void)hipGraphExecDestroy(m->gexec);
+  m->gexec = nullptr;
+  m->graph_ok = false;
+}
+
+qw_status validate_config(const qw_config *c) {
+  if (c->n_layers < 1 || c->hidden < 1 || c->n_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 ||
+      c->intermediate < 1 || c->vocab < 1 || c->max_batch < 1 || c->max_seq < 1)
+    return fail(QW_ERR_INVALID_ARG, "qw_create: every size in qw_config must be >= 1");
+  if (c->n_heads % c->n_kv_heads != 0)
+    return fail(QW_ERR_INVALID_ARG, "qw_create: n_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_heads,
+                c->n_kv_heads);
+  if (c->head_dim % 2 != 0) return fail(QW_ERR_INVALID_ARG, "qw_create: head_dim must be even (split-half RoPE)");
+  if (c->dtype != QW_F32 && c->dtype != QW_BF16) return fail(QW_ERR_INVALID_ARG, "qw_create: unknown dtype");
+  if (c->qkv_bias != 1) return fail(QW_ERR_INVALID_ARG, "qw_create: Qwen2 q/k/v projections carry a bias (qkv_bias=1)");
+  if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps)) return fail(QW_ERR_INVALID_ARG, "qw_create: rms_eps must be finite and >= 0");
+  if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return fail(QW_ERR_INVALID_ARG, "qw_create: rope_theta must be finite and > 0");
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(QW_ERR_UNSUPPORTED, "qw_create: head_dim %d not built (32, 64, 128)", c->head_dim);
+  if (c->hidden % 64 != 0 || c->intermediate % 64 != 0)
+    return fail(QW_ERR_UNSUPPORTED, "qw_create: hidden and intermediate must be multiples of 64");
+  const int64_t rows = (int64_t)c->max_batch * c->max_seq;
+  if (rows > (1LL << 30) || (int64_t)c->n_heads * c->head_dim > (1 << 20) || c->vocab > (1 << 30))
+    return fail(QW_ERR_INVALID_ARG, "qw_create: sizes too large");
+  return QW_OK;
+}
+
+qw_status validate_weights(const qw_config *c, const qw_weights *w) {
+  if (!w->embed || !w->final_norm || !w->layers) return fail(QW_ERR_INVALID_ARG, "qw_create: NULL weight pointer (embed, final_norm or layers)");
+  if (!c->tie_embeddings && !w->lm_head) return fail(QW_ERR_INVALID_ARG, "qw_create: lm_head is NULL but tie_embeddings is 0");
+  for (int l = 0; l < c->n_layers; ++l) {
+    const qw_layer_weights &L = w->layers[l];
+    const void *p[] = {L.input_norm, L.q_w, L.q_b, L.k_w, L.k_b, L.v_w, L.v_b, L.o_w, L.post_norm, L.gate_w, L.up_w, L.down_w};
+    for (const void *q : p)
+      if (!q) return fail(QW_ERR_INVALID_ARG, "qw_create: NULL tensor pointer in layer %d", l);
+  }
+  return QW_OK;
+}
+
+// Power-of-two scale 2^k with max|w| * 2^k < 2^15, so that each bf16 value
+// times the scale is an fp16 normal (or zero) and converts exactly.
+float f16_scale_for(float absmax) {
+  if (!(absmax > 0.f) || !isfinite(absmax)) return 1.f;
+  int e;
+  frexpf(absmax, &e);           // absmax < 2^e
+  int k = 15 - e;
+  if (k > 60) k = 60;
+  if (k < -60) k = -60;
+  return ldexpf(1.f, k);
+}
+
+struct Src {
+  const void *p;
+  int64_t n;
+};
+
+}  // namespace
+
+extern "C" {
+
+const char *qw_last_error(void) { return g_err.c_str(); }
+
+const char *qw_kernel_names(void) { return kFamilyList; }
+
+qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_stream, qw_model **out) {
+  g_err.clear();
+  if (!out) return fail(QW_ERR_INVALID_ARG, "qw_create: out is NULL");
+  *out = nullptr;
+  if (!cfg || !weights) return fail(QW_ERR_INVALID_ARG, "qw_create: cfg or weights is NULL");
+  qw_status st = validate_config(cfg);
+  if (st != QW_OK) return st;
+  st = validate_weights(cfg, weights);
+  if (st != QW_OK) return st;
+
+  qw_model *m = new qw_model();
+  const qw_config &c = *cfg;
+  m->cfg = c;
+  m->f16 = (c.dtype == QW_BF16);
+  m->esz = m->f16 ? 2 : 4;
+  m->qd = c.n_heads * c.head_dim;
+  m->kvd = c.n_kv_heads * c.head_dim;
+  m->nqkv = m->qd + 2 * m->kvd;
+  m->rows_cap = (int64_t)c.max_batch * c.max_seq;
+  m->stream = (hipStream_t)hip_stream;
+  const bool src_bf16 = (c.dtype == QW_BF16);
+  const int H = c.hidden, I = c.intermediate, V = c.vocab;
+  auto cleanup_fail = [&](qw_status s) {
+    qw_destroy(m);
+    return s;
+  };
+#define CREATE_TRY(expr)                                                                          \
+  do {                                                                                            \
+    hipError_t e_ = (expr);                                                                       \
+    if (e_ != hipSuccess)                                                                         \
+      return cleanup_fail(fail(e_ == hipErrorOutOfMemory ? QW_ERR_OUT_OF_MEMORY : QW_ERR_HIP,     \
+                               "qw_create: %s: %s", #expr, hipGetErrorString(e_)));              \
+  } while (0)
+
+  CREATE_TRY(hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking));
+  hipStream_t s = m->stream;
+
+  // --- per-tensor-group absmax (only needed for the exact f16 scaling)
+  // groups: per layer {qkv, o, gu, down}, then embed, then head (if untied)
+  const int n_groups = 4 * c.n_layers + 2;
+  std::vector<float> scale(n_groups, 1.f);
+  if (m->f16) {
+    unsigned *amax_dev = nullptr;
+    CREATE_TRY(m->alloc((void **)&amax_dev, n_groups * sizeof(unsigned)));
+    CREATE_TRY(hipMemsetAsync(amax_dev, 0, n_groups * sizeof(unsigned), s));
+    for (int l = 0; l < c.n_layers; ++l) {
+      const qw_layer_weights &Lw = weights->layers[l];
+      CREATE_TRY(launch_absmax(s, true, Lw.q_w, (int64_t)m->qd * H, amax_dev + 4 * l));
+      CREATE_TRY(launch_absmax(s, true, Lw.k_w, (int64_t)m->kvd * H, amax_dev + 4 * l));
+      CREATE_TRY(launch_absmax(s, true, Lw.v_w, (int64_t)m->kvd * H, amax_dev + 4 * l));
+      CREATE_TRY(launch_absmax(s, true, Lw.o_w, (int64_t)H * m->qd, amax_dev + 4 * l + 1));
+      CREATE_TRY(launch_absmax(s, true, Lw.gate_w, (int64_t)I * H, amax_dev + 4 * l + 2));
+      CREATE_TRY(launch_absmax(s, true, Lw.up_w, (int64_t)I * H, amax_dev + 4 * l + 2));
+      CREATE_TRY(launch_absmax(s, true, Lw.down_w, (int64_t)H * I, amax_dev + 4 * l + 3));
+    }
+    CREATE_TRY(launch_absmax(s, true, weights->embed, (int64_t)V * H, amax_dev + 4 * c.n_layers));
+    if (!c.tie_embeddings)
+      CREATE_TRY(launch_absmax(s, true, weights->lm_head, (int64_t)V * H, amax_dev + 4 * c.n_layers + 1));
+    std::vector<unsigned> bits(n_groups);
+    CREATE_TRY(hipMemcpyAsync(bits.data(), amax_dev, n_groups * sizeof(unsigned), hipMemcpyDeviceToHost, s));
+    CREATE_TRY(hipStreamSynchronize(s));
+    for (int g = 0; g < n_groups; ++g) {
+      float f;
+      memcpy(&f, &bits[g], 4);
+      scale[g] = f16_scale_for(f);
+    }
+  }
+
+  // --- packed weight copies
+  m->L.resize(c.n_layers);
+  const bool dst_f16 = m->f16;
+  const size_t es = m->esz;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const qw_layer_weights &Lw = weights->layers[l];
+    LayerBuf &B = m->L[l];
+    CREATE_TRY(m->alloc(&B.w_qkv, (size_t)m->nqkv * H * es));
+    CREATE_TRY(m->alloc((void **)&B.b_qkv, (size_t)m->nqkv * 4));
+    CREATE_TRY(m->alloc(&B.w_o, (size_t)H * m->qd * es));
+    CREATE_TRY(m->alloc(&B.w_gu, (size_t)2 * I * H * es));
+    CREATE_TRY(m->alloc(&B.w_down, (size_t)H * I * es));
+    CREATE_TRY(m->alloc((void **)&B.in_norm, (size_t)H * 4));
+    CREATE_TRY(m->alloc((void **)&B.post_norm, (size_t)H * 4));
+    const float sq = scale[4 * l], so = scale[4 * l + 1], sg = scale[4 * l + 2], sd = scale[4 * l + 3];
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.q_w, (int64_t)m->qd * H, dst_f16, B.w_qkv, 0, sq));
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.k_w, (int64_t)m->kvd * H, dst_f16, B.w_qkv, (int64_t)m->qd * H, sq));
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.v_w, (int64_t)m->kvd * H, dst_f16, B.w_qkv,
+                              (int64_t)(m->qd + m->kvd) * H, sq));
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.q_b, m->qd, false, B.b_qkv, 0, 1.f));
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.k_b, m->kvd, false, B.b_qkv, m->qd, 1.f));
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.v_b, m->kvd, false, B.b_qkv, m->qd + m->kvd, 1.f));
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.o_w, (int64_t)H * m->qd, dst_f16, B.w_o, 0, so));
+    CREATE_TRY(launch_convert_gu(s, src_bf16, Lw.gate_w, Lw.up_w, I, H, dst_f16, B.w_gu, sg));
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.down_w, (int64_t)H * I, dst_f16, B.w_down, 0, sd));
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.input_norm, H, false, B.in_norm, 0, 1.f));
+    CREATE_TRY(launch_convert(s, src_bf16, Lw.post_norm, H, false, B.post_norm, 0, 1.f));
+    B.s_qkv = 1.f / sq;
+    B.s_o = 1.f / so;
+    B.s_gu = 1.f / sg;
+    B.s_down = 1.f / sd;
+  }
+  {
+    const float se = scale[4 * c.n_layers];
+    CREATE_TRY(m->alloc(&m->emb, (size_t)V * H * es));
+    CREATE_TRY(launch_convert(s, src_bf16, weights->embed, (int64_t)V * H, dst_f16, m->emb, 0, se));
+    m->emb_scale = 1.f / se;
+    if (c.tie_embeddings) {
+      m->head = m->emb;
+      m->head_scale = m->emb_scale;
+    } else {
+      const float sh = scale[4 * c.n_layers + 1];
+      CREATE_TRY(m->alloc(&m->head, (size_t)V * H * es));
+      CREATE_TRY(launch_convert(s, src_bf16, weights->lm_head, (int64_t)V * H, dst_f16, m->head, 0, sh));
+      m->head_scale = 1.f / sh;
+    }
+    CREATE_TRY(m->alloc((void **)&m->final_norm, (size_t)H * 4));
+    CREATE_TRY(launch_convert(s, src_bf16, weights->final_norm, H, false, m->final_norm, 0, 1.f));
+  }
+
+  // --- cache, RoPE table, workspace
+  m->cache_layer_elems = (int64_t)c.max_batch * c.n_kv_heads * c.max_seq * c.head_dim;
+  const size_t cache_bytes = (size_t)c.n_layers * m->cache_layer_elems * es;
+  CREATE_TRY(m->alloc(&m->k_cache, cache_bytes));
+  CREATE_TRY(m->alloc(&m->v_cache, cache_bytes));
+  CREATE_TRY(hipMemsetAsync(m->k_cache, 0, cache_bytes, s));
+  CREATE_TRY(hipMemsetAsync(m->v_cache, 0, cache_bytes, s));
+  CREATE_TRY(m->alloc((void **)&m->rope, (size_t)c.max_seq * (c.head_dim / 2) * sizeof(float2)));
+  CREATE_TRY(launch_rope_table(s, m->rope, c.max_seq, c.head_dim, (double)c.rope_theta));
+  const size_t R = (size_t)m->rows_cap;
+  CREATE_TRY(m->alloc((void **)&m->x, R * H * 4));
+  CREATE_TRY(m->alloc(&m->u, R * H * es));
+  CREATE_TRY(m->alloc((void **)&m->qkv, R * m->nqkv * 4));
+  CREATE_TRY(m->alloc(&m->q, R * m->qd * es));
+  CREATE_TRY(m->alloc(&m->o, R * m->qd * es));
+  CREATE_TRY(m->alloc(&m->h, R * I * es));
+  CREATE_TRY(m->alloc((void **)&m->logits, (size_t)c.max_batch * V * 4));
+  CREATE_TRY(m->alloc((void **)&m->pos_dev, 256));
+  CREATE_TRY(m->alloc((void **)&m->bad_ids, 256));
+  CREATE_TRY(m->alloc((void **)&m->ids_stage, (size_t)c.max_batch * 4));
+  CREATE_TRY(m->alloc((void **)&m->next_stage, (size_t)c.max_batch * 4));
+  CREATE_TRY(hipMemsetAsync(m->pos_dev, 0, 256, s));
+  CREATE_TRY(hipMemsetAsync(m->bad_ids, 0, 256, s));
+  CREATE_TRY(hipStreamSynchronize(s));
+#undef CREATE_TRY
+  *out = m;
+  return QW_OK;
+}
+
+qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t prompt_len, float *logits,
+                     int32_t logits_all, int32_t *next_ids) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_prefill: model is NULL");
+  if (!ids || !next_ids) return fail(QW_ERR_INVALID_ARG, "qw_prefill: ids and next_ids must be non-NULL");
+  const qw_config &c = m->cfg;
+  if (batch < 1 || batch > c.max_batch)
+    return fail(QW_ERR_INVALID_ARG, "qw_prefill: batch %d outside [1, max_batch=%d]", batch, c.max_batch);
+  if (prompt_len < 1) return fail(QW_ERR_INVALID_ARG, "qw_prefill: prompt_len must be >= 1");
+  if (prompt_len > c.max_seq)
+    return fail(QW_ERR_CACHE_FULL, "qw_prefill: prompt_len %d exceeds max_seq %d", prompt_len, c.max_seq);
+  if (logits_all && !logits) return fail(QW_ERR_INVALID_ARG, "qw_prefill: logits_all needs a logits buffer");
+  hipStream_t s = m->stream;
+  const int T = batch * prompt_len, H = c.hidden, V = c.vocab;
+  m->batch = 0;          // invalid until the enqueue succeeds
+  HIP_TRY(timed(m, s, F_EMBED, [&] {
+    return launch_embed(s, m->f16, ids, T, m->emb, m->emb_scale, H, V, m->x, m->bad_ids);
+  }));
+  HIP_TRY(run_layers(m, s, T, prompt_len, 0, nullptr));
+  if (logits_all) {
+    HIP_TRY(run_head(m, s, m->x, T, H, logits, logits + (int64_t)(prompt_len - 1) * V, batch,
+                     (int64_t)prompt_len * V, next_ids, nullptr, 0));
+  } else {
+    float *lg = logits ? logits : m->logits;
+    HIP_TRY(run_head(m, s, m->x + (int64_t)(prompt_len - 1) * H, batch, prompt_len * H, lg, lg, batch, V, next_ids,
+                     nullptr, 0));
+  }
+  HIP_TRY(launch_set_int(s, m->pos_dev, prompt_len));
+  m->batch = batch;
+  m->pos = prompt_len;
+  return QW_OK;
+}
+
+qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t *next_ids) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_decode_step: model is NULL");
+  if (!ids || !next_ids) return fail(QW_ERR_INVALID_ARG, "qw_decode_step: ids and next_ids must be non-NULL");
+  if (m->batch == 0) return fail(QW_ERR_BAD_STATE, "qw_decode_step: no prefill has run");
+  if (m->pos >= m->cfg.max_seq)
+    return fail(QW_ERR_CACHE_FULL, "qw_decode_step: cache holds max_seq=%d positions", m->cfg.max_seq);
+  hipStream_t s = m->stream;
+  const bool graph = m->use_graph && m->timing_family < 0;
+  if (!graph) {
+    HIP_TRY(decode_body(m, s, ids, logits, next_ids));
+  } else {
+    if (!m->graph_ok || m->graph_batch != m->batch) {
+      drop_graph(m);
+      hipGraph_t g = nullptr;
+      HIP_TRY(hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal));
+      hipError_t e = decode_body(m, m->cap, m->ids_stage, nullptr, m->next_stage);
+      hipError_t e2 = hipStreamEndCapture(m->cap, &g);
+      if (e != hipSuccess || e2 != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return fail(QW_ERR_HIP, "qw_decode_step: graph capture failed: %s",
+                    hipGetErrorString(e != hipSuccess ? e : e2));
+      }
+      e = hipGraphInstantiate(&m->gexec, g, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(g);
+      if (e != hipSuccess) {
+        m->gexec = nullptr;
+        return fail(QW_ERR_HIP, "qw_decode_step: graph instantiate failed: %s", hipGetErrorString(e));
+      }
+      m->graph_batch = m->batch;
+      m->graph_ok = true;
+    }
+    HIP_TRY(launch_copy_i32(s, m->ids_stage, ids, m->batch));
+    HIP_TRY(hipGraphLaunch(m->gexec, s));
+    HIP_TRY(launch_stage_out(s, next_ids, m->next_stage, m->batch, logits, m->logits,
+                             (int64_t)m->batch * m->cfg.vocab));
+  }
+  m->pos += 1;
+  return QW_OK;
+}
+
+qw_status qw_destroy(qw_model *m) {
+  g_err.clear();
+  if (!m) return QW_OK;
+  (void)hipStreamSynchronize(m->stream);
+  drop_graph(m);
+  for (auto &e : m->ev_used) {
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
+  }
+  for (auto &e : m->ev_free) {
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
+  }
+  for (void *p : m->allocs) (void)hipFree(p);
+  if (m->cap) (void)hipStreamDestroy(m->cap);
+  delete m;
+  return QW_OK;
+}
+
+qw_status qw_get_state(const qw_model *m, int32_t *batch, int32_t *pos) {
+  g_err.clear();
+  if (!m || !batch || !pos) return fail(QW_ERR_INVALID_ARG, "qw_get_state: NULL argument");
+  *batch = m->batch;
+  *pos = m->batch ? m->pos : 0;
+  return QW_OK;
+}
+
+qw_status qw_check_ids(qw_model *m) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_check_ids: model is NULL");
+  HIP_TRY(hipStreamSynchronize(m->stream));
+  int flag = 0;
+  HIP_TRY(hipMemcpy(&flag, m->bad_ids, sizeof(int), hipMemcpyDeviceToHost));
+  if (flag) {
+    HIP_TRY(hipMemset(m->bad_ids, 0, sizeof(int)));
+    return fail(QW_ERR_INVALID_ARG, "a token id outside [0, %d) was passed; it was read as id 0", m->cfg.vocab);
+  }
+  return QW_OK;
+}
+
+qw_status qw_set_graph(qw_model *m, int32_t enable) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_set_graph: model is NULL");
+  m->use_graph = enable != 0;
+  if (!m->use_graph) drop_graph(m);
+  return QW_OK;
+}
+
+qw_status qw_timing_enable(qw_model *m, const char *name) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_timing_enable: model is NULL");
+  if (!name || !*name) {
+    m->timing_family = -1;
+    return QW_OK;
+  }
+  for (int f = 0; f < F_COUNT; ++f)
+    if (strcmp(name, kFamilyNames[f]) == 0) {
+      m->timing_family = f;
+      return QW_OK;
+    }
+  return fail(QW_ERR_INVALID_ARG, "qw_timing_enable: unknown kernel family '%s' (have: %s)", name, kFamilyList);
+}
+
+qw_status qw_timing_read(qw_model *m, double *total_ms, int64_t *launches, int32_t reset) {
+  g_err.clear();
+  if (!m || !total_ms || !launches) return fail(QW_ERR_INVALID_ARG, "qw_timing_read: NULL argument");
+  HIP_TRY(hipStreamSynchronize(m->stream));
+  for (auto &e : m->ev_used) {
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, e.first, e.second));
+    m->timing_ms += ms;
+    m->timing_n += 1;
+    m->ev_free.push_back(e);
+  }
+  m->ev_used.clear();
+  *total_ms = m->timing_ms;
+  *launches = m->timing_n;
+  if (reset) {
+    m->timing_ms = 0;
+    m->timing_n = 0;
+  }
+  return QW_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+/*
+ * qw.h -- C ABI of libqw.so: the Qwen2 decoder forward pass (prefill and
+ * KV-cached greedy decode) on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the pages describe:
+ *   - "augur" (feature list): RMSNorm before attention, before the MLP and
+ *     after the last layer; RoPE on q and k; grouped-query attention; causal
+ *     masking; SwiGLU MLP; pre-norm decoder blocks; embeddings -> layers ->
+ *     final norm -> LM head; greedy generation; a prefill/decode split; a
+ *     preallocated KV cache.
+ *   - "LLM Speedrun: Architecture": sections "Attention", "Every token with
+ *     every other token", "Grouped Query Attention GQA", "Rotary Positional
+ *     Embeddings RoPE", "Split-half RoPE implementation", "Introducing bias",
+ *     "Decoding"; its harness listing fixes weight layouts ([out, in]) and the
+ *     generation loop (the prompt once, then one token per step).
+ *   - "Building a Qwen2.5-1.5B Inference Engine From Scratch", section 1:
+ *     prefill processes every prompt token at once and fills the KV cache;
+ *     decode then feeds one new token per sequence per step.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors
+ *     on the current device) unless a comment says "host".
+ *   - All work is enqueued on the hipStream_t given to qw_create (0 = the
+ *     legacy default stream).  Outputs are valid once the caller synchronises
+ *     that stream.  No call blocks on the GPU except qw_create (which waits
+ *     for its own set-up work) and qw_destroy.
+ *   - Every call returns a qw_status.  On anything but QW_OK, qw_last_error()
+ *     returns a message for the calling thread; argument and state errors
+ *     are detected on the host before anything is enqueued, so the model is
+ *     unchanged.
+ *   - One qw_model must not be used from two host threads at once.
+ */
+#ifndef QW_H_
+#define QW_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qw_status {
+  QW_OK = 0,
+  QW_ERR_INVALID_ARG = -1,    /* bad pointer, shape, or config value          */
+  QW_ERR_OUT_OF_MEMORY = -2,  /* a device allocation failed                    */
+  QW_ERR_HIP = -3,            /* a HIP runtime call failed (message has it)    */
+  QW_ERR_CACHE_FULL = -4,     /* the step would write past max_seq             */
+  QW_ERR_BAD_STATE = -5,      /* e.g. decode before any prefill                */
+  QW_ERR_UNSUPPORTED = -6     /* valid model, but a shape this build lacks     */
+} qw_status;
+
+/* Storage type of every weight tensor handed to qw_create.
+ *   QW_F32 : float32 weights; the whole forward runs in fp32 arithmetic.
+ *   QW_BF16: bf16 weights.  GEMM operands (weights and activations) are held
+ *            in fp16 with fp32 accumulation; weights are converted exactly
+ *            (per-tensor power-of-two scale, so every bf16 value maps to an
+ *            fp16 value without rounding); the residual stream, softmax,
+ *            norms' statistics and logits are fp32. */
+typedef enum qw_dtype { QW_F32 = 0, QW_BF16 = 1 } qw_dtype;
+
+/* Model and capacity.  Field meanings follow the Qwen2 config names the
+ * "augur" feature list enumerates. */
+typedef struct qw_config {
+  int32_t n_layers;       /* decoder blocks                                   */
+  int32_t hidden;         /* H, model width                                   */
+  int32_t n_heads;        /* query heads nq                                   */
+  int32_t n_kv_heads;     /* KV heads nkv; nq % nkv == 0 (GQA)                */
+  int32_t head_dim;       /* hd; 32, 64 or 128 in this build                  */
+  int32_t intermediate;   /* I, SwiGLU width                                  */
+  int32_t vocab;          /* V                                                */
+  float rms_eps;          /* RMSNorm epsilon (1e-6 for Qwen2.5)               */
+  float rope_theta;       /* RoPE base (1e6 for Qwen2.5)                      */
+  int32_t qkv_bias;       /* must be 1: q/k/v projections carry a bias        */
+  int32_t tie_embeddings; /* 1: LM head = embedding; 0: weights.lm_head used  */
+  qw_dtype dtype;         /* storage type of all weight tensors               */
+  int32_t max_batch;      /* largest batch any later call may use             */
+  int32_t max_seq;        /* KV-cache positions per sequence                  */
+} qw_config;
+
+/* One decoder block's tensors, HF layouts: projection weights are row-major
+ * [out, in]; vectors are [n].  Every pointer is a device pointer of `dtype`. */
+typedef struct qw_layer_weights {
+  const void *input_norm;     /* [H]                                          */
+  const void *q_w, *q_b;      /* [nq*hd, H], [nq*hd]                           */
+  const void *k_w, *k_b;      /* [nkv*hd, H], [nkv*hd]                         */
+  const void *v_w, *v_b;      /* [nkv*hd, H], [nkv*hd]                         */
+  const void *o_w;            /* [H, nq*hd]   (no bias)                        */
+  const void *post_norm;      /* [H]                                          */
+  const void *gate_w, *up_w;  /* [I, H]       (no bias)                        */
+  const void *down_w;         /* [H, I]       (no bias)                        */
+} qw_layer_weights;
+
+typedef struct qw_weights {
+  const void *embed;                /* [V, H] token embedding                  */
+  const void *final_norm;           /* [H]                                     */
+  const void *lm_head;              /* [V, H], or NULL when tie_embeddings     */
+  const qw_layer_weights *layers;   /* HOST array of n_layers entries          */
+} qw_weights;
+
+typedef struct qw_model qw_model;
+
+/* Build a model on the current HIP device.
+ * Reads every weight once to make the library's own packed copies (fused QKV
+ * with fp32 bias, row-interleaved gate/up, fp16 or fp32 compute copies), so
+ * the caller's weight buffers may be freed after this returns.  Allocates the
+ * KV cache (2 * n_layers * max_batch * nkv * max_seq * hd elements of the
+ * compute type), a RoPE cos/sin table for max_seq positions, and workspace for
+ * max_batch * max_seq prefill rows.  `hip_stream` (a hipStream_t) is the
+ * stream all later work is enqueued on.  Waits for its set-up work.
+ * Errors: INVALID_ARG (NULL pointers, non-positive sizes, nq % nkv != 0, odd
+ * head_dim, qkv_bias != 1, lm_head NULL while untied), UNSUPPORTED (head_dim
+ * not in {32, 64, 128}, hidden or intermediate not a multiple of 64),
+ * OUT_OF_MEMORY, HIP.  On error *out is set to NULL. */
+qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_stream,
+                    qw_model **out);
+
+/* Prefill: run `batch` equal-length prompts ids[batch][prompt_len] (int32,
+ * device, each in [0, V)) through the model at positions 0 .. prompt_len-1,
+ * writing their keys and values into the cache.  Every sequence restarts at
+ * position 0 (earlier cache contents are overwritten).
+ * Outputs (device):
+ *   next_ids[batch]    greedy token of each sequence: the lowest index of the
+ *                      largest logit of its last prompt position.
+ *   logits             NULL, or fp32 [batch][V] for each last position, or,
+ *                      when logits_all != 0, fp32 [batch][prompt_len][V] for
+ *                      every position (meant for checks on small models).
+ * Token ids outside [0, V) are read as id 0 (never out of bounds) and make
+ * qw_check_ids report an error.
+ * Errors: INVALID_ARG (NULL ids/next_ids, batch < 1 or > max_batch,
+ * prompt_len < 1), CACHE_FULL (prompt_len > max_seq), HIP. */
+qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t prompt_len,
+                     float *logits, int32_t logits_all, int32_t *next_ids);
+
+/* One greedy decode step for every sequence of the last prefill: feeds
+ * ids[batch] (device; may alias the previous call's next_ids) at the next
+ * position, appends their keys and values to the cache, and writes next_ids
+ * [batch] and, if non-NULL, fp32 logits[batch][V].  The position advances on
+ * the device, so steps may be enqueued back to back without host syncs.
+ * Errors: INVALID_ARG (NULL ids/next_ids), BAD_STATE (no prefill yet),
+ * CACHE_FULL (the cache already holds max_seq positions), HIP. */
+qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t *next_ids);
+
+/* Free everything the model owns.  Synchronises its stream first.  NULL is a
+ * no-op. */
+qw_status qw_destroy(qw_model *m);
+
+/* Message of the calling thread's last error ("" if none).  The pointer stays
+ * valid until that thread's next qw_* call. */
+const char *qw_last_error(void);
+
+/* ---- inspection and measurement helpers (not on the hot path) ----------- */
+
+/* Host view of the state: *batch of the last prefill (0 if none) and *pos,
+ * the number of cache positions each sequence holds. */
+qw_status qw_get_state(const qw_model *m, int32_t *batch, int32_t *pos);
+
+/* Synchronise the stream and report whether any token id handed to prefill or
+ * decode since the last check was outside [0, V): QW_ERR_INVALID_ARG if so
+ * (and the flag is cleared), QW_OK otherwise. */
+qw_status qw_check_ids(qw_model *m);
+
+/* Decode-step execution: 1 (default) replays a captured HIP graph of the whole
+ * step; 0 launches its kernels one by one.  Both run the same kernels on the
+ * same data and give identical results. */
+qw_status qw_set_graph(qw_model *m, int32_t enable);
+
+/* Kernel timing for roofline reports.  While enabled, decode steps run
+ * without the graph and every launch of the kernel family `name` (see
+ * qw_kernel_names) is bracketed by hipEvents on the model's stream; the
+ * elapsed times accumulate.  qw_timing_read synchronises the stream and
+ * returns the total milliseconds and launch count since the last reset. */
+qw_status qw_timing_enable(qw_model *m, const char *name);
+qw_status qw_timing_read(qw_model *m, double *total_ms, int64_t *launches, int32_t reset);
+
+/* Comma-separated names of the kernel families the library launches. */
+const char *qw_kernel_names(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QW_H_ */

@@ -1,0 +1,199 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle.
+
+Every case runs prefill + greedy decode on the GPU, then feeds the GPU's own
+token stream to the oracle (teacher forcing) and compares logits at every
+step and tokens wherever the oracle's top-2 margin is clear.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+from tests.helpers import LOGIT_TOL, compare_row, gpu_generate, with_random_norms
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def Q():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decoder_only_transformer_qwen2_amd as Q
+    Q.load_library()
+    return Q
+
+
+def make(Q, shape, W, max_batch, max_seq):
+    return Q.Model(shape, Q.device_tensors(shape, W), max_batch, max_seq)
+
+
+SMALL = {
+    # several 64-wide tiles with ragged tails (vocab, prompt, intermediate)
+    "bf16-hd32": (S.ModelShape("s32", 3, 256, 8, 2, 32, 640, 1000), 3, 37, 6, 64),
+    "bf16-hd64-mqa": (S.ModelShape("s64", 2, 384, 6, 1, 64, 1024, 777), 2, 70, 5, 96),
+    "bf16-hd128": (S.ModelShape("s128", 2, 512, 4, 2, 128, 1536, 2049), 2, 130, 4, 160),
+    "f32-hd64": (S.ModelShape("f64", 2, 192, 6, 3, 64, 448, 513, dtype="f32"), 2, 21, 5, 32),
+}
+
+
+@pytest.mark.parametrize("graph", [True, False])
+def test_tiny_fp32_full_workload(Q, graph):
+    w = S.WORKLOADS["tiny"]
+    W = with_random_norms(S.make_weights(w.model, 0), w.model)
+    ids = S.make_ids(w)
+    say(f"tiny fp32 B={w.batch} P={w.prompt_len} D={w.decode_steps} graph={graph}")
+    m = make(Q, w.model, W, w.batch, w.max_seq)
+    toks, logits = gpu_generate(m, ids, w.decode_steps, graph=graph)
+    om = O.OracleModel(w.model, W)
+    err, n = compare_row(om, ids[0], toks[0], logits[0], "f32", "tiny")
+    say(f"  max err {err:.2e}, {n} steps with a clear margin")
+    # free-running agreement with the oracle's own generation
+    o_toks, _ = om.generate(ids[0], w.decode_steps)
+    say(f"  oracle tokens {o_toks}, gpu tokens {toks[0]}")
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_small_shapes(Q, case):
+    shape, B, P, D, smax = SMALL[case]
+    W = with_random_norms(S.make_weights(shape, 5), shape)
+    ids = np.random.default_rng(7).integers(0, shape.vocab, (B, P)).astype(np.int32)
+    say(f"{case}: B={B} P={P} D={D}")
+    m = make(Q, shape, W, B, smax)
+    toks, logits = gpu_generate(m, ids, D)
+    om = O.OracleModel(shape, W)
+    for b in range(B):
+        err, n = compare_row(om, ids[b], toks[b], logits[b], shape.dtype, f"{case} row {b}")
+        say(f"  row {b}: max err {err:.2e}")
+
+
+def test_graph_and_eager_bit_identical(Q):
+    shape, B, P, D, smax = SMALL["bf16-hd64-mqa"]
+    W = S.make_weights(shape, 1)
+    ids = np.random.default_rng(3).integers(0, shape.vocab, (B, P)).astype(np.int32)
+    m = make(Q, shape, W, B, smax)
+    t1, l1 = gpu_generate(m, ids, D, graph=True)
+    t2, l2 = gpu_generate(m, ids, D, graph=False)
+    assert np.array_equal(t1, t2) and np.array_equal(l1, l2)
+
+
+def test_logits_all_and_causal_invariance(Q):
+    import torch
+    shape, B, P, D, smax = SMALL["bf16-hd32"]
+    W = S.make_weights(shape, 2)
+    ids = np.random.default_rng(4).integers(0, shape.vocab, (B, P)).astype(np.int32)
+    m = make(Q, shape, W, B, smax)
+
+    def all_logits(ids_np):
+        t = torch.from_numpy(ids_np).cuda()
+        lg = torch.empty((B, P, shape.vocab), dtype=torch.float32, device="cuda")
+        nxt = m.prefill(t, logits=lg, logits_all=True)
+        torch.cuda.synchronize()
+        return lg.cpu().numpy(), nxt.cpu().numpy()
+
+    a, na = all_logits(ids)
+    om = O.OracleModel(shape, W)
+    for b in range(B):
+        ref = om.forward(ids[b], 0, om.new_cache(P), logits_rows=slice(0, P))
+        assert np.abs(a[b] - ref).max() <= LOGIT_TOL["bf16"]
+        assert na[b] == int(np.argmax(a[b, -1]))
+    ids2 = ids.copy()
+    ids2[:, 20:] = (ids2[:, 20:] + 1) % shape.vocab
+    c, _ = all_logits(ids2)
+    assert np.array_equal(a[:, :20], c[:, :20])        # rows before the change: bit-identical
+    assert not np.array_equal(a[:, 20:], c[:, 20:])
+
+
+def test_cached_decode_equals_full_prefill(Q):
+    """Decode-step logits equal the logits_all of one prefill over the prompt
+    plus the emitted tokens (same kernels, different row counts)."""
+    import torch
+    shape, B, P, D, smax = SMALL["bf16-hd128"]
+    W = S.make_weights(shape, 3)
+    ids = np.random.default_rng(5).integers(0, shape.vocab, (B, P)).astype(np.int32)
+    m = make(Q, shape, W, B, smax)
+    toks, logits = gpu_generate(m, ids, D)
+    full = np.concatenate([ids, toks[:, :-1]], axis=1).astype(np.int32)
+    lg = torch.empty((B, P + D, shape.vocab), dtype=torch.float32, device="cuda")
+    m.prefill(torch.from_numpy(full).cuda(), logits=lg, logits_all=True)
+    torch.cuda.synchronize()
+    ref = lg.cpu().numpy()[:, P - 1:]
+    assert np.abs(ref - logits).max() <= LOGIT_TOL["bf16"] / 10
+
+
+def test_batch_rows_are_independent(Q):
+    shape, B, P, D, smax = SMALL["bf16-hd32"]
+    W = S.make_weights(shape, 4)
+    ids = np.random.default_rng(6).integers(0, shape.vocab, (B, P)).astype(np.int32)
+    m = make(Q, shape, W, B, smax)
+    tb, lb = gpu_generate(m, ids, D)
+    for b in range(B):
+        t1, l1 = gpu_generate(m, ids[b:b + 1], D)
+        assert np.array_equal(t1[0], tb[b])
+        assert np.abs(l1[0] - lb[b]).max() <= 1e-3
+
+
+def test_prompt_of_one_and_full_cache(Q):
+    import torch
+    shape = SMALL["bf16-hd64-mqa"][0]
+    W = S.make_weights(shape, 8)
+    smax = 12
+    m = make(Q, shape, W, 2, smax)
+    om = O.OracleModel(shape, W)
+    ids = np.array([[5], [700]], dtype=np.int32)
+    toks, logits = gpu_generate(m, ids, smax - 1)            # positions 0 .. smax-1: cache exactly full
+    for b in range(2):
+        compare_row(om, ids[b], toks[b], logits[b], "bf16", f"P=1 row {b}")
+    assert m.state() == (2, smax)
+    nxt = torch.empty(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(Q.QwError) as e:
+        m.decode_step(torch.from_numpy(toks[:, -1].copy()).cuda(), next_ids=nxt)
+    assert e.value.status == -4                              # QW_ERR_CACHE_FULL
+    assert m.state() == (2, smax)
+
+
+def test_error_paths(Q):
+    import torch
+    shape, B, P, D, smax = SMALL["bf16-hd32"]
+    m = make(Q, shape, S.make_weights(shape, 0), 2, 16)
+    ids = torch.zeros((2, 4), dtype=torch.int32, device="cuda")
+    nxt = torch.empty(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(Q.QwError) as e:
+        m.decode_step(ids[:, 0].contiguous(), next_ids=nxt)
+    assert e.value.status == -5                              # BAD_STATE: no prefill yet
+    with pytest.raises(Q.QwError) as e:
+        m.prefill(torch.zeros((3, 4), dtype=torch.int32, device="cuda"))
+    assert e.value.status == -1                              # batch > max_batch
+    with pytest.raises(Q.QwError) as e:
+        m.prefill(torch.zeros((1, 17), dtype=torch.int32, device="cuda"))
+    assert e.value.status == -4                              # prompt longer than the cache
+    bad = torch.tensor([[1, 2, shape.vocab, 3], [0, -1, 2, 3]], dtype=torch.int32, device="cuda")
+    m.prefill(bad, next_ids=nxt)
+    with pytest.raises(Q.QwError):
+        m.check_ids()
+    m.check_ids()                                            # flag was cleared
+    with pytest.raises(Q.QwError):
+        m.timing_enable("no_such_kernel")
+
+
+@pytest.mark.parametrize("name", ["0.5b", "1.5b"])
+def test_full_workload(Q, name):
+    w = S.WORKLOADS[name]
+    say(f"{name}: generating weights")
+    W = S.make_weights(w.model, w.weight_seed)
+    ids = S.make_ids(w)
+    say(f"{name}: GPU B={w.batch} P={w.prompt_len} D={w.decode_steps}")
+    m = make(Q, w.model, W, w.batch, w.max_seq)
+    toks, logits = gpu_generate(m, ids, w.decode_steps)
+    m.close()
+    say(f"{name}: oracle teacher-forced")
+    om = O.OracleModel(w.model, W)
+    err, n = compare_row(om, ids[0], toks[0], logits[0], "bf16", name)
+    say(f"{name}: max err {err:.3e} over {w.decode_steps + 1} steps; {n} with margin > 0.1")

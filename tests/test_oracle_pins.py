@@ -18,6 +18,7 @@ import oracle as O
 import oracle.qwen2_oracle as OQ
 import synthetic as S
 from tests import bruteforce_ref as BF
+from tests.helpers import with_random_norms
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 TINY = S.WORKLOADS["tiny"]
@@ -196,18 +197,6 @@ def _hf_logits(m, W, seq):
 # HF evaluates RoPE's cos/sin in float32 even in a float64 model (about 1e-7
 # relative here); any of the planted mistakes below moves logits by > 1e-3.
 HF_TOL = 2e-5
-
-
-def with_random_norms(W, m, seed=21):
-    """Norm weights drawn around 1 (the synthetic init sets them to exactly 1,
-    which would hide a dropped norm-weight multiply)."""
-    rng = np.random.default_rng(seed)
-    W = dict(W)
-    for k in W:
-        if k.endswith("layernorm.weight") or k == "model.norm.weight":
-            f = (1.0 + 0.3 * rng.standard_normal(W[k].shape)).astype(np.float32)
-            W[k] = S.f32_to_bf16_bits(f) if W[k].dtype == np.uint16 else f
-    return W
 
 
 @pytest.mark.parametrize("shape,random_norms", [
