@@ -78,6 +78,37 @@ struct AttnArgs {
   float softmax_scale;
 };
 
+// Decode-step projection (B <= 32 rows), see k_decode.hip.  f16 operands.
+struct DecGemvArgs {
+  const void *W;            // [N, K] f16
+  int M, N, K;
+  const void *act;          // [M, lda] f16 activations, or
+  const long long *act_fix; // [M, lda] fixed-point gate/up sums (down projection: silu(g) * up)
+  int lda;
+  float scale;              // exact power of two undoing the weight scaling
+  long long *out_fix;       // fixed-point accumulator [M, ldo] (atomic adds)
+  int ldo;
+  int splits;               // K slices
+  int units_per_split;      // set by the launcher
+  // LM-head mode: logits [M, ldo] (may be NULL) and per-64-row-block argmax
+  int logits_mode;
+  float *logits;
+  float *arg_v;             // [M, ceil(N / 64)]
+  int *arg_i;
+};
+
+// Decode-step attention, see k_decode.hip.
+struct DecAttnArgs {
+  const long long *qkv_fix;          // [batch, nq*hd + 2*nkv*hd] fixed-point projection sums
+  const float *bias;                 // [nq*hd + 2*nkv*hd]
+  const float2 *rope;                // [max_seq, hd/2]
+  void *k_cache, *v_cache;           // layer base [max_batch][nkv][max_seq][hd]
+  void *o;                           // [batch, nq*hd] f16
+  int batch, n_heads, n_kv_heads, head_dim, max_seq;
+  const int *pos_dev;                // position of the new row
+  float softmax_scale;
+};
+
 // ------------------------------------------------------------ launchers
 // Each returns the hipError_t of its launch.  `f16_mode` selects the compute
 // type (f16 when true, float when false).
@@ -88,6 +119,16 @@ hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows
 hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a);
 hipError_t launch_attention_generic(hipStream_t s, bool f16_mode, const AttnArgs &a);
 hipError_t launch_gemm_generic(hipStream_t s, bool f16_mode, const GemmArgs &a);
+bool decode_fast_supported(int head_dim, int group, int hidden, int q_dim, int inter);
+int dec_gemv_splits(int N, int K, int M, int target_groups);
+hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
+                            long long *x_fix, int *bad);
+hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int B, int H, const float *w, float eps, void *u,
+                           long long *zero_buf, int zero_per_row);
+hipError_t launch_dec_end(hipStream_t s, const float *arg_v, const int *arg_i, int nblk, int B, int32_t *next,
+                          int *pos_dev);
+hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &a);
+hipError_t launch_dec_attention(hipStream_t s, const DecAttnArgs &a);
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
                          int32_t *next_ids, int *pos_dev, int pos_add);
 hipError_t launch_set_int(hipStream_t s, int *p, int v);

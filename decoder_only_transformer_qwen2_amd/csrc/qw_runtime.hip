@@ -88,6 +88,14 @@ struct qw_model {
   void *u = nullptr, *q = nullptr, *o = nullptr, *h = nullptr;
   int *pos_dev = nullptr, *bad_ids = nullptr;
   int32_t *ids_stage = nullptr, *next_stage = nullptr;   // [max_batch] rows the decode graph reads / writes
+  // decode-step state (bf16-weight mode): fixed-point residual stream and
+  // projection accumulators, LM-head argmax partials
+  bool fast_decode = false;
+  long long *x_fix = nullptr;        // [max_batch, H]
+  long long *qkv_fix = nullptr;      // [max_batch, nq*hd + 2*nkv*hd]
+  long long *gu_fix = nullptr;       // [max_batch, 2I]
+  float *arg_v = nullptr;            // [max_batch, ceil(V / 64)]
+  int *arg_i = nullptr;
   int batch = 0, pos = 0;
   // decode graph, captured against the staging rows (so caller pointers may
   // change from step to step) for the batch of the last prefill
@@ -112,6 +120,9 @@ struct qw_model {
 };
 
 namespace {
+
+// Workgroups a decode projection aims for (256 CUs, a few workgroups each).
+constexpr int kGemvTargetGroups = 1024;
 
 // Bracket a launch of `fam` with events when timing that family.
 template <class F>
@@ -197,6 +208,7 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
     aa.pos0_dev = pos_dev;
     aa.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
     e = timed(m, s, F_ATTENTION, [&] { return launch_attention_generic(s, m->f16, aa); });
+
     if (e != hipSuccess) return e;
     e = gemm(m, s, F_GEMM_O, m->o, T, m->qd, m->qd, Lw.w_o, H, Lw.s_o, Epi::ResidAdd, m->x, nullptr, H);
     if (e != hipSuccess) return e;
@@ -227,7 +239,8 @@ hipError_t run_head(qw_model *m, hipStream_t s, const float *x_rows, int rows, i
                [&] { return launch_argmax(s, arg_logits, arg_rows, c.vocab, arg_stride, next, pos_dev, pos_add); });
 }
 
-hipError_t decode_body(qw_model *m, hipStream_t s, const int32_t *ids, float *logits, int32_t *next) {
+// Generic decode step (fp32 mode): the prefill kernels on one row per sequence.
+hipError_t decode_generic(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next) {
   const qw_config &c = m->cfg;
   const int B = m->batch;
   hipError_t e = timed(m, s, F_EMBED, [&] {
@@ -236,8 +249,109 @@ hipError_t decode_body(qw_model *m, hipStream_t s, const int32_t *ids, float *lo
   if (e != hipSuccess) return e;
   e = run_layers(m, s, B, 1, 0, m->pos_dev);
   if (e != hipSuccess) return e;
-  float *lg = logits ? logits : m->logits;
-  return run_head(m, s, m->x, B, c.hidden, lg, lg, B, c.vocab, next, m->pos_dev, 1);
+  return run_head(m, s, m->x, B, c.hidden, m->logits, m->logits, B, c.vocab, next, m->pos_dev, 1);
+}
+
+DecGemvArgs dec_args(const void *W, int M, int N, int K, float scale) {
+  DecGemvArgs g{};
+  g.W = W;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.scale = scale;
+  g.splits = dec_gemv_splits(N, K, M, kGemvTargetGroups);
+  return g;
+}
+
+// Decode step of the bf16-weight mode (kernels of k_decode.hip): per layer
+// norm, q/k/v projection, attention (with bias, RoPE and the cache write),
+// o projection, norm, gate/up projection, down projection; then the final
+// norm, the LM head with per-block argmax, and the argmax reduction.
+hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next) {
+  const qw_config &c = m->cfg;
+  const int B = m->batch, H = c.hidden, I = c.intermediate, V = c.vocab;
+  hipError_t e = timed(m, s, F_EMBED, [&] {
+    return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, m->x_fix, m->bad_ids);
+  });
+  if (e != hipSuccess) return e;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerBuf &Lw = m->L[l];
+    char *kc = (char *)m->k_cache + (int64_t)l * m->cache_layer_elems * m->esz;
+    char *vc = (char *)m->v_cache + (int64_t)l * m->cache_layer_elems * m->esz;
+    e = timed(m, s, F_RMSNORM, [&] {
+      return launch_dec_norm(s, m->x_fix, B, H, Lw.in_norm, c.rms_eps, m->u, m->qkv_fix, m->nqkv);
+    });
+    if (e != hipSuccess) return e;
+    DecGemvArgs g = dec_args(Lw.w_qkv, B, m->nqkv, H, Lw.s_qkv);
+    g.act = m->u;
+    g.lda = H;
+    g.out_fix = m->qkv_fix;
+    g.ldo = m->nqkv;
+    e = timed(m, s, F_GEMM_QKV, [&] { return launch_dec_gemv(s, g); });
+    if (e != hipSuccess) return e;
+    DecAttnArgs da{};
+    da.qkv_fix = m->qkv_fix;
+    da.bias = Lw.b_qkv;
+    da.rope = m->rope;
+    da.k_cache = kc;
+    da.v_cache = vc;
+    da.o = m->o;
+    da.batch = B;
+    da.n_heads = c.n_heads;
+    da.n_kv_heads = c.n_kv_heads;
+    da.head_dim = c.head_dim;
+    da.max_seq = c.max_seq;
+    da.pos_dev = m->pos_dev;
+    da.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
+    e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
+    if (e != hipSuccess) return e;
+    g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o);
+    g.act = m->o;
+    g.lda = m->qd;
+    g.out_fix = m->x_fix;
+    g.ldo = H;
+    e = timed(m, s, F_GEMM_O, [&] { return launch_dec_gemv(s, g); });
+    if (e != hipSuccess) return e;
+    e = timed(m, s, F_RMSNORM, [&] {
+      return launch_dec_norm(s, m->x_fix, B, H, Lw.post_norm, c.rms_eps, m->u, m->gu_fix, 2 * I);
+    });
+    if (e != hipSuccess) return e;
+    g = dec_args(Lw.w_gu, B, 2 * I, H, Lw.s_gu);
+    g.act = m->u;
+    g.lda = H;
+    g.out_fix = m->gu_fix;
+    g.ldo = 2 * I;
+    e = timed(m, s, F_GEMM_GATE_UP, [&] { return launch_dec_gemv(s, g); });
+    if (e != hipSuccess) return e;
+    g = dec_args(Lw.w_down, B, H, I, Lw.s_down);
+    g.act_fix = m->gu_fix;
+    g.lda = 2 * I;
+    g.out_fix = m->x_fix;
+    g.ldo = H;
+    e = timed(m, s, F_GEMM_DOWN, [&] { return launch_dec_gemv(s, g); });
+    if (e != hipSuccess) return e;
+  }
+  e = timed(m, s, F_RMSNORM, [&] {
+    return launch_dec_norm(s, m->x_fix, B, H, m->final_norm, c.rms_eps, m->u, nullptr, 0);
+  });
+  if (e != hipSuccess) return e;
+  DecGemvArgs g = dec_args(m->head, B, V, H, m->head_scale);
+  g.act = m->u;
+  g.lda = H;
+  g.ldo = V;
+  g.logits_mode = 1;
+  g.logits = m->logits;
+  g.arg_v = m->arg_v;
+  g.arg_i = m->arg_i;
+  e = timed(m, s, F_LM_HEAD, [&] { return launch_dec_gemv(s, g); });
+  if (e != hipSuccess) return e;
+  return timed(m, s, F_ARGMAX,
+               [&] { return launch_dec_end(s, m->arg_v, m->arg_i, (V + 63) / 64, B, next, m->pos_dev); });
+}
+
+// One decode step writing next ids to `next` and logits to m->logits.
+hipError_t decode_body(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next) {
+  return m->fast_decode ? decode_fast(m, s, ids, next) : decode_generic(m, s, ids, next);
 }
 
 void drop_graph(qw_model *m) {
@@ -443,6 +557,16 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   CREATE_TRY(m->alloc((void **)&m->pos_dev, 256));
   CREATE_TRY(m->alloc((void **)&m->bad_ids, 256));
   CREATE_TRY(m->alloc((void **)&m->ids_stage, (size_t)c.max_batch * 4));
+  m->fast_decode = m->f16 && c.max_batch <= 32 &&
+                   decode_fast_supported(c.head_dim, c.n_heads / c.n_kv_heads, H, m->qd, I);
+  if (m->fast_decode) {
+    const size_t nb = (size_t)c.max_batch;
+    CREATE_TRY(m->alloc((void **)&m->x_fix, nb * H * 8));
+    CREATE_TRY(m->alloc((void **)&m->qkv_fix, nb * m->nqkv * 8));
+    CREATE_TRY(m->alloc((void **)&m->gu_fix, nb * 2 * I * 8));
+    CREATE_TRY(m->alloc((void **)&m->arg_v, nb * ((V + 63) / 64) * 4));
+    CREATE_TRY(m->alloc((void **)&m->arg_i, nb * ((V + 63) / 64) * 4));
+  }
   CREATE_TRY(m->alloc((void **)&m->next_stage, (size_t)c.max_batch * 4));
   CREATE_TRY(hipMemsetAsync(m->pos_dev, 0, 256, s));
   CREATE_TRY(hipMemsetAsync(m->bad_ids, 0, 256, s));
@@ -495,13 +619,13 @@ qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t
   hipStream_t s = m->stream;
   const bool graph = m->use_graph && m->timing_family < 0;
   if (!graph) {
-    HIP_TRY(decode_body(m, s, ids, logits, next_ids));
+    HIP_TRY(decode_body(m, s, ids, m->next_stage));
   } else {
     if (!m->graph_ok || m->graph_batch != m->batch) {
       drop_graph(m);
       hipGraph_t g = nullptr;
       HIP_TRY(hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal));
-      hipError_t e = decode_body(m, m->cap, m->ids_stage, nullptr, m->next_stage);
+      hipError_t e = decode_body(m, m->cap, m->ids_stage, m->next_stage);
       hipError_t e2 = hipStreamEndCapture(m->cap, &g);
       if (e != hipSuccess || e2 != hipSuccess) {
         if (g) (void)hipGraphDestroy(g);
@@ -519,9 +643,8 @@ qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t
     }
     HIP_TRY(launch_copy_i32(s, m->ids_stage, ids, m->batch));
     HIP_TRY(hipGraphLaunch(m->gexec, s));
-    HIP_TRY(launch_stage_out(s, next_ids, m->next_stage, m->batch, logits, m->logits,
-                             (int64_t)m->batch * m->cfg.vocab));
   }
+  HIP_TRY(launch_stage_out(s, next_ids, m->next_stage, m->batch, logits, m->logits, (int64_t)m->batch * m->cfg.vocab));
   m->pos += 1;
   return QW_OK;
 }
