@@ -1,25 +1,29 @@
 // Kernels of one decode step (one new token per sequence, B <= 32 sequences).
 //
 // What a step computes is the decoder block of "LLM Speedrun: Architecture"
-// (sections "Attention", "Grouped Query Attention GQA", "Split-half RoPE
-// implementation", "Introducing bias", "Decoding") for one row per sequence,
-// reading past keys and values from the preallocated cache ("augur").  How it
-// is laid out is specific to this GPU:
+// (sections "Normalization", "Attention", "Grouped Query Attention GQA",
+// "Split-half RoPE implementation", "Introducing bias", "Decoding") for one
+// row per sequence, reading past keys and values from the preallocated cache
+// ("augur").  How it is laid out is specific to this GPU:
 //
 //  * Kernel boundaries are the only cheap device-wide synchronisation here,
-//    and a device-scope fence per workgroup is expensive, so no kernel waits
-//    on another workgroup.  Projections split K over workgroups and add their
+//    and a device-scope fence per workgroup is expensive, so no workgroup
+//    waits on another.  Projections split K over workgroups and add their
 //    partial sums with 64-bit integer atomics on a fixed-point copy of the
 //    value (32 fractional bits).  Integer addition is associative, so the
-//    result does not depend on arrival order (deterministic), and no fence
-//    is needed: the consumer is the next kernel.
-//  * The consumer of each fixed-point sum finishes the step it belongs to:
-//    attention converts the q/k/v sums, adds the bias, applies RoPE and writes
-//    k and v into the cache; the down projection converts the gate/up sums and
-//    applies silu(gate) * up while loading its operand; the RMSNorm kernel
-//    converts the residual stream.
-//  * The residual stream of the decode rows lives in fixed point ([B, H]
+//    result does not depend on arrival order (deterministic), and no fence is
+//    needed: the consumer is the next kernel.
+//  * Each consumer finishes the step its input belongs to while staging its
+//    operand in LDS: the q/k/v sums get bias and RoPE inside attention (which
+//    also writes k and v into the cache), the gate/up sums become
+//    silu(gate) * up inside the down projection, the split-KV attention
+//    partials are merged inside the o projection, and for one or two rows the
+//    RMSNorm is computed inside the projection that follows it.
+//  * The residual stream of the decode rows is kept in fixed point ([B, H]
 //    int64), so o_proj and down_proj add into it atomically.
+//  * Accumulators are cleared by an earlier kernel of the same step (embed
+//    clears both, attention clears gate/up, o_proj clears q/k/v), so the step
+//    needs no memset and replays as a graph.
 #include "qw_internal.h"
 
 #include <math.h>
@@ -31,9 +35,11 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float FIX_ONE = 4294967296.0f;        // 2^32
+constexpr float FIX_ONE = 4294967296.0f;            // 2^32
 constexpr float FIX_INV = 2.3283064365386963e-10f;  // 2^-32
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int CH = 256;                             // k per staged chunk
+constexpr int MERGE_MAX_S = 16;                     // split-KV partials merged per head
 
 __device__ __forceinline__ long long to_fix(float v) {
   v = fminf(fmaxf(v, -1.0e9f), 1.0e9f);
@@ -45,10 +51,20 @@ __device__ __forceinline__ void fix_add(long long *p, float v) {
 }
 __device__ __forceinline__ f16x8 load8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 
+// Clear n int64 values, spread over `parts` cooperating workgroups.
+__device__ __forceinline__ void clear_share(long long *p, int64_t n, int part, int parts) {
+  if (!p) return;
+  const int64_t per = (n + parts - 1) / parts;
+  const int64_t lo = (int64_t)part * per, hi = min(n, lo + per);
+  for (int64_t e = lo + threadIdx.x; e < hi; e += blockDim.x) p[e] = 0;
+}
+
 // ---------------------------------------------------------------- begin / norm / end
-// x_fix[b] = embedding row of ids[b] (exact value, fixed point)
+// x_fix[b] = embedding row of ids[b] (its exact value, in fixed point); clears
+// the q/k/v and gate/up accumulators for the first layer.
 __global__ void __launch_bounds__(256) dec_embed_kernel(const int32_t *ids, const f16 *emb, float emb_scale, int H,
-                                                        int V, long long *x_fix, int *bad) {
+                                                        int V, long long *x_fix, int *bad, long long *clr0,
+                                                        int64_t n0, long long *clr1, int64_t n1) {
   const int b = blockIdx.x;
   int id = ids[b];
   if (id < 0 || id >= V) {
@@ -57,12 +73,14 @@ __global__ void __launch_bounds__(256) dec_embed_kernel(const int32_t *ids, cons
   }
   const f16 *row = emb + (int64_t)id * H;
   for (int c = threadIdx.x; c < H; c += blockDim.x) x_fix[(int64_t)b * H + c] = to_fix((float)row[c] * emb_scale);
+  clear_share(clr0, n0, b, gridDim.x);
+  clear_share(clr1, n1, b, gridDim.x);
 }
 
-// u[b] = f16(x[b] / sqrt(mean(x[b]^2) + eps) * w), and clears `zero_buf`
-// (the fixed-point accumulator the next projection adds into).
-__global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, int H, const float *w, float eps, f16 *u,
-                                                       long long *zero_buf, int zero_per_row) {
+// u[b] = f16(x[b] / sqrt(mean(x[b]^2) + eps) * w): used when the batch is too
+// large for the projections to normalise their own operand.
+__global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, int H, const float *w, float eps,
+                                                       f16 *u) {
   const int b = blockIdx.x;
   __shared__ float red[4];
   const long long *xr = x_fix + (int64_t)b * H;
@@ -77,8 +95,6 @@ __global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, i
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
   for (int c = threadIdx.x; c < H; c += 256) u[(int64_t)b * H + c] = (f16)(from_fix(xr[c]) * inv * w[c]);
-  if (zero_buf)
-    for (int c = threadIdx.x; c < zero_per_row; c += 256) zero_buf[(int64_t)b * zero_per_row + c] = 0;
 }
 
 // Reduce the LM head's per-block (max, index) pairs: lowest index among equal
@@ -113,72 +129,133 @@ __global__ void __launch_bounds__(256) dec_end_kernel(const float *pv, const int
 // ---------------------------------------------------------------- projections
 // out[b, n] (+)= sum_k act[b, k] * W[n, k] * scale for b < M <= 16 * NB.
 // One wave = 16 weight rows x a K slice; a workgroup = 4 waves = 64 rows;
-// gridDim.y = K slices.  See the header comment for the fixed-point output.
-enum class DecAct : int { F16 = 0, SwiGLUFix = 1 };
+// gridDim.y = K slices.  The operand slice is produced once per workgroup
+// into LDS, CH columns at a time, by one of the operand modes below; the
+// weight rows of the next chunk are already in flight while a chunk is
+// staged.  MFMA: weights are the A operand (16 rows), activations the B
+// operand (16 batch rows); unit t of a chunk gives lane group g the 8
+// columns 32t + 8g .. 32t + 8g + 7.
+enum class DecAct : int { F16 = 0, NormFix = 1, SwiGLUFix = 2, AttnMerge = 3 };
 enum class DecOut : int { FixAdd = 0, Logits = 1 };
 
 template <int NB, DecAct AM, DecOut OM>
 __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
+  constexpr int BT = 16 * NB;
+  __shared__ f16 s_act[BT][CH + 8];
+  __shared__ float s_inv[BT];
+  __shared__ float s_c[(AM == DecAct::AttnMerge) ? BT * (CH / 32 + 1) * MERGE_MAX_S : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, g = lane >> 4;
   const int nblk = blockIdx.x, split = blockIdx.y;
   const int row = nblk * 64 + wave * 16 + i;
   const bool row_ok = row < a.N;
   const f16 *W = (const f16 *)a.W + (int64_t)(row_ok ? row : 0) * a.K;
-  const int units = a.K >> 5;
-  const int u0 = split * a.units_per_split;
-  const int u1 = min(units, u0 + a.units_per_split);
+  const int k0 = split * a.units_per_split * 32;
+  const int k1 = min(a.K, k0 + a.units_per_split * 32);
+  const f16x8 zero = {};
+
+  // side job: clear an accumulator of the next layer, shared by all workgroups
+  if (a.clear)
+    clear_share(a.clear, a.clear_n, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+
+  f16x8 w[8];
+  auto load_w = [&](int kc) {
+    const int nu = min(8, (k1 - kc) >> 5);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) w[t] = (row_ok && t < nu) ? load8(W + kc + 32 * t + 8 * g) : zero;
+  };
+  load_w(k0);
+
+  if constexpr (AM == DecAct::NormFix) {
+    // inverse RMS of each batch row over the whole hidden vector
+    for (int b = wave; b < a.M; b += 4) {
+      const long long *xr = a.x_fix + (int64_t)b * a.lda;
+      float ss = 0.f;
+      for (int c = lane; c < a.K; c += 64) {
+        const float v = from_fix(xr[c]);
+        ss += v * v;
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) s_inv[b] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+    }
+    __syncthreads();
+  }
 
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const f16x8 zero = {};
 
-  // 8 consecutive activations of batch row b at column k, as f16
-  auto act8 = [&](int b, int k) -> f16x8 {
-    if constexpr (AM == DecAct::F16) {
-      return load8((const f16 *)a.act + (int64_t)b * a.lda + k);
+  for (int kc = k0; kc < k1; kc += CH) {
+    const int ck = min(CH, k1 - kc);
+    if (kc != k0) __syncthreads();            // the previous chunk's LDS reads are done
+    // ---- stage act[b][kc .. kc + ck) for b < M
+    if constexpr (AM == DecAct::AttnMerge) {
+      // per (b, head) merge weights of the split-KV partials, normalised
+      const int hd = a.head_dim, S = a.attn_splits;
+      const int hfirst = kc / hd, hlast = (kc + ck - 1) / hd;
+      const int nh = hlast - hfirst + 1;
+      for (int p = tid; p < a.M * nh; p += 256) {
+        const int b = p / nh, hh = p % nh, h = hfirst + hh;
+        const float *pm = a.part_m + ((int64_t)b * a.n_heads + h) * S;
+        const float *pl = a.part_l + ((int64_t)b * a.n_heads + h) * S;
+        float M = -INFINITY;
+        for (int s = 0; s < S; ++s) M = fmaxf(M, pm[s]);
+        float L = 0.f;
+        float *c = s_c + (b * (CH / 32 + 1) + hh) * MERGE_MAX_S;
+        for (int s = 0; s < S; ++s) {
+          const float cs = (pm[s] == -INFINITY) ? 0.f : exp2f(pm[s] - M);
+          c[s] = cs;
+          L += cs * pl[s];
+        }
+        const float inv = 1.0f / L;
+        for (int s = 0; s < S; ++s) c[s] *= inv;
+      }
+      __syncthreads();
+      for (int e = tid; e < a.M * ck; e += 256) {
+        const int b = e / ck, kk = e % ck, k = kc + kk;
+        const int h = k / hd, d = k % hd, hh = h - hfirst;
+        const float *c = s_c + (b * (CH / 32 + 1) + hh) * MERGE_MAX_S;
+        const float *po = a.part_o + (((int64_t)b * a.n_heads + h) * S) * hd + d;
+        float v = 0.f;
+        for (int s = 0; s < S; ++s) v = fmaf(c[s], po[(int64_t)s * hd], v);
+        s_act[b][kk] = (f16)v;
+      }
+    } else if constexpr (AM == DecAct::F16) {
+      for (int e = tid; e < a.M * (ck >> 3); e += 256) {
+        const int b = e / (ck >> 3), kk = (e % (ck >> 3)) * 8;
+        *reinterpret_cast<f16x8 *>(&s_act[b][kk]) = load8((const f16 *)a.act + (int64_t)b * a.lda + kc + kk);
+      }
+    } else if constexpr (AM == DecAct::NormFix) {
+      for (int e = tid; e < a.M * ck; e += 256) {
+        const int b = e / ck, kk = e % ck;
+        s_act[b][kk] = (f16)(from_fix(a.x_fix[(int64_t)b * a.lda + kc + kk]) * s_inv[b] * a.norm_w[kc + kk]);
+      }
     } else {
-      // k indexes features; gate/up of feature f sit in GU_BLOCK-interleaved rows
-      const long long *row2 = a.act_fix + (int64_t)b * a.lda;
-      const int blk = k / GU_BLOCK, w = k % GU_BLOCK;
-      const long long *gp = row2 + blk * 2 * GU_BLOCK + w;
-      const long long *up = gp + GU_BLOCK;
-      f16x8 r;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float gt = from_fix(gp[e]), uv = from_fix(up[e]);
-        r[e] = (f16)(silu_f(gt) * uv);
-      }
-      return r;
-    }
-  };
-
-  int u = u0;
-  for (; u + 4 <= u1; u += 4) {
-    const int kb = u * 32 + g * 32;            // lane group g: k = kb .. kb + 31
-    f16x8 w[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) w[c] = row_ok ? load8(W + kb + c * 8) : zero;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int b = nb * 16 + i;
-      const bool b_ok = b < a.M;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f16x8 x = b_ok ? act8(b, kb + c * 8) : zero;
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[c], x, acc[nb], 0, 0, 0);
+      // features kc + kk; gate and up of feature f sit in GU_BLOCK-interleaved rows
+      for (int e = tid; e < a.M * ck; e += 256) {
+        const int b = e / ck, kk = e % ck, f = kc + kk;
+        const long long *r2 = a.act_fix + (int64_t)b * a.lda + (f / GU_BLOCK) * 2 * GU_BLOCK + f % GU_BLOCK;
+        const float gt = from_fix(r2[0]), up = from_fix(r2[GU_BLOCK]);
+        s_act[b][kk] = (f16)(silu_f(gt) * up);
       }
     }
-  }
-  for (; u < u1; ++u) {
-    const int kb = u * 32 + g * 8;
-    const f16x8 w = row_ok ? load8(W + kb) : zero;
+    __syncthreads();
+    // ---- multiply the chunk; fetch the next chunk's weights first
+    f16x8 wc[8];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int b = nb * 16 + i;
-      const f16x8 x = (b < a.M) ? act8(b, kb) : zero;
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w, x, acc[nb], 0, 0, 0);
+    for (int t = 0; t < 8; ++t) wc[t] = w[t];
+    if (kc + CH < k1) load_w(kc + CH);
+    const int nu = ck >> 5;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t < nu) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int b = nb * 16 + i;
+          const f16x8 x = (b < a.M) ? *reinterpret_cast<const f16x8 *>(&s_act[b][32 * t + 8 * g]) : zero;
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wc[t], x, acc[nb], 0, 0, 0);
+        }
+      }
     }
   }
 
@@ -195,8 +272,8 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
     }
   } else {
     // logits (optional copy) and this block's (max, lowest index) per batch row
-    __shared__ float s_v[4][16 * NB];
-    __shared__ int s_i[4][16 * NB];
+    __shared__ float s_v[4][BT];
+    __shared__ int s_i[4][BT];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int b = nb * 16 + i;
@@ -227,8 +304,11 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
     if (tid < a.M) {
       float best = s_v[0][tid];
       int bi = s_i[0][tid];
-      for (int w = 1; w < 4; ++w)
-        if (s_v[w][tid] > best || (s_v[w][tid] == best && s_i[w][tid] < bi)) { best = s_v[w][tid]; bi = s_i[w][tid]; }
+      for (int w2 = 1; w2 < 4; ++w2)
+        if (s_v[w2][tid] > best || (s_v[w2][tid] == best && s_i[w2][tid] < bi)) {
+          best = s_v[w2][tid];
+          bi = s_i[w2][tid];
+        }
       a.arg_v[(int64_t)tid * gridDim.x + nblk] = best;
       a.arg_i[(int64_t)tid * gridDim.x + nblk] = bi;
     }
@@ -237,24 +317,36 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
 
 template <int NB>
 hipError_t launch_gemv_nb(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
+  const DecAct am = (DecAct)a.act_mode;
   if (a.logits_mode) {
-    dec_gemv_kernel<NB, DecAct::F16, DecOut::Logits><<<grid, 256, 0, s>>>(a);
-  } else if (a.act_fix) {
-    dec_gemv_kernel<NB, DecAct::SwiGLUFix, DecOut::FixAdd><<<grid, 256, 0, s>>>(a);
+    if (am == DecAct::NormFix)
+      dec_gemv_kernel<NB, DecAct::NormFix, DecOut::Logits><<<grid, 256, 0, s>>>(a);
+    else
+      dec_gemv_kernel<NB, DecAct::F16, DecOut::Logits><<<grid, 256, 0, s>>>(a);
   } else {
-    dec_gemv_kernel<NB, DecAct::F16, DecOut::FixAdd><<<grid, 256, 0, s>>>(a);
+    switch (am) {
+      case DecAct::F16: dec_gemv_kernel<NB, DecAct::F16, DecOut::FixAdd><<<grid, 256, 0, s>>>(a); break;
+      case DecAct::NormFix: dec_gemv_kernel<NB, DecAct::NormFix, DecOut::FixAdd><<<grid, 256, 0, s>>>(a); break;
+      case DecAct::SwiGLUFix: dec_gemv_kernel<NB, DecAct::SwiGLUFix, DecOut::FixAdd><<<grid, 256, 0, s>>>(a); break;
+      case DecAct::AttnMerge: dec_gemv_kernel<NB, DecAct::AttnMerge, DecOut::FixAdd><<<grid, 256, 0, s>>>(a); break;
+    }
   }
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- attention
-// grid (n_kv_heads, B), 64 * NW threads (NW = 16 waves for g <= 4, else 8 so
-// that the per-lane state of g heads fits in registers).  Prologue: q (the group's g heads), the
-// new k and v from the fixed-point q/k/v sums + bias, RoPE at `pos`; k and v
-// are written to the cache.  Body: keys 0..pos-1 from the cache, key pos from
-// LDS; online softmax in the exp2 domain; merge of all lanes and waves.
-template <int HD, int G, int NW>
-__global__ void __launch_bounds__(64 * NW) dec_attn_kernel(DecAttnArgs a) {
+// grid (split, kv head j, sequence b), 256 threads.  Prologue: the group's g
+// query heads and the new k and v from the fixed-point q/k/v sums + bias,
+// RoPE at `pos` (q rounded to f16 like the prefill path); the split that
+// holds position pos writes k and v into the cache.  Body: the split's cached
+// keys, plus key pos from LDS; HD/8 lanes share one key (16 bytes each);
+// online softmax in the exp2 domain; lanes and waves merged at the end.  With
+// one split the normalised output is written (f16); otherwise the split's
+// (max, sum, unnormalised output) per head go to the partials that the o
+// projection merges.
+template <int HD, int G>
+__global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
+  constexpr int NW = 4;
   constexpr int LPK = HD / 8;        // lanes per key
   constexpr int KPW = 64 / LPK;      // keys per wave per load
   constexpr int KPB = NW * KPW;
@@ -266,8 +358,16 @@ __global__ void __launch_bounds__(64 * NW) dec_attn_kernel(DecAttnArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int slot = lane / LPK, dl = lane % LPK, d0 = dl * 8;
-  const int j = blockIdx.x, b = blockIdx.y;
+  const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int S = gridDim.x;
   const int pos = *a.pos_dev;
+  const int n_keys = pos + 1;
+  int per = (n_keys + S - 1) / S;
+  per = (per + KPB - 1) / KPB * KPB;
+  const int kb0 = split * per;
+  const int kb1 = min(n_keys, kb0 + per);
+  const bool has_new = kb0 <= pos && pos < kb1;
+
   const int nq = a.n_kv_heads * G;
   const int qd = nq * HD, kvd = a.n_kv_heads * HD;
   const int ncols = qd + 2 * kvd;
@@ -275,8 +375,10 @@ __global__ void __launch_bounds__(64 * NW) dec_attn_kernel(DecAttnArgs a) {
   const float2 *cs = a.rope + (int64_t)pos * HALF;
   const float qscale = a.softmax_scale * LOG2E;
 
-  // prologue: (G + 1) rotated heads (q heads of the group, then k) and v
-  for (int e = tid; e < (G + 1) * HALF + HD; e += 64 * NW) {
+  // side job: clear the gate/up accumulator (its last reader finished)
+  clear_share(a.clear, a.clear_n, (b * gridDim.y + j) * S + split, S * gridDim.y * gridDim.z);
+
+  for (int e = tid; e < (G + 1) * HALF + HD; e += 256) {
     if (e < (G + 1) * HALF) {
       const int hh = e / HALF, i = e % HALF;
       const int c0 = (hh < G) ? (j * G + hh) * HD + i : qd + j * HD + i;
@@ -285,7 +387,7 @@ __global__ void __launch_bounds__(64 * NW) dec_attn_kernel(DecAttnArgs a) {
       const float2 r = cs[i];
       const float nre = re * r.x - im * r.y, nim = im * r.x + re * r.y;
       if (hh < G) {
-        s_q[hh][i] = (float)(f16)nre * qscale;       // q is rounded to f16 like the prefill path
+        s_q[hh][i] = (float)(f16)nre * qscale;
         s_q[hh][i + HALF] = (float)(f16)nim * qscale;
       } else {
         s_k[i] = (float)(f16)nre;
@@ -301,7 +403,7 @@ __global__ void __launch_bounds__(64 * NW) dec_attn_kernel(DecAttnArgs a) {
   const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
   f16 *Kc = (f16 *)a.k_cache + head_base;
   f16 *Vc = (f16 *)a.v_cache + head_base;
-  if (tid < HD) {
+  if (has_new && tid < HD) {
     Kc[(int64_t)pos * HD + tid] = (f16)s_k[tid];
     Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
   }
@@ -338,33 +440,32 @@ __global__ void __launch_bounds__(64 * NW) dec_attn_kernel(DecAttnArgs a) {
     }
   };
 
-  // cached keys 0 .. pos-1, two loads in flight per lane
-  for (int kb = wave * KPW; kb < pos; kb += 2 * KPB) {
+  const int kc_end = min(kb1, pos);               // cached keys of this split
+  for (int kb = kb0 + wave * KPW; kb < kc_end; kb += 2 * KPB) {
     const int t0 = kb + slot, t1 = kb + KPB + slot;
-    f16x8 k0 = {}, v0 = {}, k1 = {}, v1 = {};
-    if (t0 < pos) {
+    f16x8 k0 = {}, v0 = {}, k1v = {}, v1 = {};
+    if (t0 < kc_end) {
       k0 = load8(Kc + (int64_t)t0 * HD + d0);
       v0 = load8(Vc + (int64_t)t0 * HD + d0);
     }
-    if (t1 < pos) {
-      k1 = load8(Kc + (int64_t)t1 * HD + d0);
+    if (t1 < kc_end) {
+      k1v = load8(Kc + (int64_t)t1 * HD + d0);
       v1 = load8(Vc + (int64_t)t1 * HD + d0);
     }
-    if (t0 < pos) {
+    if (t0 < kc_end) {
       float kf[8], vf[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) { kf[e] = (float)k0[e]; vf[e] = (float)v0[e]; }
       visit(kf, vf);
     }
-    if (t1 < pos) {
+    if (t1 < kc_end) {
       float kf[8], vf[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { kf[e] = (float)k1[e]; vf[e] = (float)v1[e]; }
+      for (int e = 0; e < 8; ++e) { kf[e] = (float)k1v[e]; vf[e] = (float)v1[e]; }
       visit(kf, vf);
     }
   }
-  // the new key (position pos), handled by slot 0 of wave 0
-  if (wave == 0 && slot == 0) {
+  if (has_new && wave == 0 && slot == 0) {
     float kf[8], vf[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { kf[e] = s_k[d0 + e]; vf[e] = s_v[d0 + e]; }
@@ -402,34 +503,45 @@ __global__ void __launch_bounds__(64 * NW) dec_attn_kernel(DecAttnArgs a) {
     }
   }
   __syncthreads();
-  f16 *out = (f16 *)a.o + (int64_t)b * qd;
-  for (int e = tid; e < G * HD; e += 64 * NW) {
+  for (int e = tid; e < G * HD; e += 256) {
     const int hh = e / HD, d = e % HD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][hh]);
+    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, s_m[w2][hh]);
     float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float c = (s_m[w][hh] == -INFINITY) ? 0.f : exp2f(s_m[w][hh] - M);
-      L += s_l[w][hh] * c;
-      O += s_o[w][hh][d] * c;
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const float c = (s_m[w2][hh] == -INFINITY) ? 0.f : exp2f(s_m[w2][hh] - M);
+        L += s_l[w2][hh] * c;
+        O += s_o[w2][hh][d] * c;
+      }
     }
-    out[(j * G + hh) * HD + d] = (f16)(O / L);
+    const int h = j * G + hh;
+    if (S == 1) {
+      ((f16 *)a.o)[(int64_t)b * qd + h * HD + d] = (f16)(O / L);
+    } else {
+      const int64_t st = ((int64_t)b * nq + h) * S + split;
+      if (d == 0) {
+        a.part_m[st] = M;
+        a.part_l[st] = L;
+      }
+      a.part_o[st * HD + d] = O;
+    }
   }
 }
 
 template <int HD>
 hipError_t launch_attn_hd(hipStream_t s, const DecAttnArgs &a, dim3 grid, int g) {
   switch (g) {
-    case 1: dec_attn_kernel<HD, 1, 16><<<grid, 1024, 0, s>>>(a); break;
-    case 2: dec_attn_kernel<HD, 2, 16><<<grid, 1024, 0, s>>>(a); break;
-    case 3: dec_attn_kernel<HD, 3, 16><<<grid, 1024, 0, s>>>(a); break;
-    case 4: dec_attn_kernel<HD, 4, 16><<<grid, 1024, 0, s>>>(a); break;
-    case 5: dec_attn_kernel<HD, 5, 8><<<grid, 512, 0, s>>>(a); break;
-    case 6: dec_attn_kernel<HD, 6, 8><<<grid, 512, 0, s>>>(a); break;
-    case 7: dec_attn_kernel<HD, 7, 8><<<grid, 512, 0, s>>>(a); break;
-    case 8: dec_attn_kernel<HD, 8, 8><<<grid, 512, 0, s>>>(a); break;
+    case 1: dec_attn_kernel<HD, 1><<<grid, 256, 0, s>>>(a); break;
+    case 2: dec_attn_kernel<HD, 2><<<grid, 256, 0, s>>>(a); break;
+    case 3: dec_attn_kernel<HD, 3><<<grid, 256, 0, s>>>(a); break;
+    case 4: dec_attn_kernel<HD, 4><<<grid, 256, 0, s>>>(a); break;
+    case 5: dec_attn_kernel<HD, 5><<<grid, 256, 0, s>>>(a); break;
+    case 6: dec_attn_kernel<HD, 6><<<grid, 256, 0, s>>>(a); break;
+    case 7: dec_attn_kernel<HD, 7><<<grid, 256, 0, s>>>(a); break;
+    case 8: dec_attn_kernel<HD, 8><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -455,15 +567,23 @@ int dec_gemv_splits(int N, int K, int M, int target_groups) {
   return splits;
 }
 
+int dec_attn_splits(int batch, int n_kv_heads, int max_seq, int target_groups) {
+  int S = (target_groups + batch * n_kv_heads - 1) / (batch * n_kv_heads);
+  const int by_len = (max_seq + 511) / 512;    // splits of a few hundred keys at the cache's capacity
+  if (S > by_len) S = by_len;
+  if (S > MERGE_MAX_S) S = MERGE_MAX_S;
+  if (S < 1) S = 1;
+  return S;
+}
+
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
-                            long long *x_fix, int *bad) {
-  dec_embed_kernel<<<B, 256, 0, s>>>(ids, (const f16 *)emb, emb_scale, H, V, x_fix, bad);
+                            long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1) {
+  dec_embed_kernel<<<B, 256, 0, s>>>(ids, (const f16 *)emb, emb_scale, H, V, x_fix, bad, clr0, n0, clr1, n1);
   return hipGetLastError();
 }
 
-hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int B, int H, const float *w, float eps, void *u,
-                           long long *zero_buf, int zero_per_row) {
-  dec_norm_kernel<<<B, 256, 0, s>>>(x_fix, H, w, eps, (f16 *)u, zero_buf, zero_per_row);
+hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int B, int H, const float *w, float eps, void *u) {
+  dec_norm_kernel<<<B, 256, 0, s>>>(x_fix, H, w, eps, (f16 *)u);
   return hipGetLastError();
 }
 
@@ -477,6 +597,8 @@ hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &in) {
   DecGemvArgs a = in;
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.M > 32 || (a.K & 31) || (a.lda & 7)) return hipErrorInvalidValue;
+  if (a.act_mode == (int)DecAct::AttnMerge && (a.attn_splits < 1 || a.attn_splits > MERGE_MAX_S))
+    return hipErrorInvalidValue;
   const int units = a.K / 32;
   int splits = a.logits_mode ? 1 : (a.splits < 1 ? 1 : a.splits);
   a.units_per_split = (units + splits - 1) / splits;
@@ -487,7 +609,7 @@ hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &in) {
 
 hipError_t launch_dec_attention(hipStream_t s, const DecAttnArgs &a) {
   const int g = a.n_heads / a.n_kv_heads;
-  dim3 grid(a.n_kv_heads, a.batch);
+  dim3 grid(a.splits, a.n_kv_heads, a.batch);
   switch (a.head_dim) {
     case 32: return launch_attn_hd<32>(s, a, grid, g);
     case 64: return launch_attn_hd<64>(s, a, grid, g);

@@ -82,14 +82,23 @@ struct AttnArgs {
 struct DecGemvArgs {
   const void *W;            // [N, K] f16
   int M, N, K;
-  const void *act;          // [M, lda] f16 activations, or
-  const long long *act_fix; // [M, lda] fixed-point gate/up sums (down projection: silu(g) * up)
+  int act_mode;             // 0: f16 act; 1: RMSNorm of x_fix; 2: silu(gate)*up of act_fix;
+                            // 3: merge of split-KV attention partials
+  const void *act;          // mode 0: [M, lda] f16
+  const long long *x_fix;   // mode 1: [M, lda] fixed-point residual rows (lda = K)
+  const float *norm_w;      // mode 1: [K]
+  float eps;                // mode 1
+  const long long *act_fix; // mode 2: [M, lda] fixed-point gate/up sums (lda = 2K)
+  const float *part_m, *part_l, *part_o;  // mode 3: [M][n_heads][S] (+ [head_dim])
+  int attn_splits, n_heads, head_dim;     // mode 3
   int lda;
   float scale;              // exact power of two undoing the weight scaling
   long long *out_fix;       // fixed-point accumulator [M, ldo] (atomic adds)
   int ldo;
   int splits;               // K slices
   int units_per_split;      // set by the launcher
+  long long *clear;         // side job: zero clear[0 .. clear_n) (may be NULL)
+  int64_t clear_n;
   // LM-head mode: logits [M, ldo] (may be NULL) and per-64-row-block argmax
   int logits_mode;
   float *logits;
@@ -103,10 +112,14 @@ struct DecAttnArgs {
   const float *bias;                 // [nq*hd + 2*nkv*hd]
   const float2 *rope;                // [max_seq, hd/2]
   void *k_cache, *v_cache;           // layer base [max_batch][nkv][max_seq][hd]
-  void *o;                           // [batch, nq*hd] f16
+  void *o;                           // splits == 1: [batch, nq*hd] f16
+  float *part_m, *part_l, *part_o;   // splits > 1: [batch][nq][splits] (+ [hd])
+  int splits;
   int batch, n_heads, n_kv_heads, head_dim, max_seq;
   const int *pos_dev;                // position of the new row
   float softmax_scale;
+  long long *clear;                  // side job: zero clear[0 .. clear_n)
+  int64_t clear_n;
 };
 
 // ------------------------------------------------------------ launchers
@@ -121,10 +134,10 @@ hipError_t launch_attention_generic(hipStream_t s, bool f16_mode, const AttnArgs
 hipError_t launch_gemm_generic(hipStream_t s, bool f16_mode, const GemmArgs &a);
 bool decode_fast_supported(int head_dim, int group, int hidden, int q_dim, int inter);
 int dec_gemv_splits(int N, int K, int M, int target_groups);
+int dec_attn_splits(int batch, int n_kv_heads, int max_seq, int target_groups);
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
-                            long long *x_fix, int *bad);
-hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int B, int H, const float *w, float eps, void *u,
-                           long long *zero_buf, int zero_per_row);
+                            long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1);
+hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int B, int H, const float *w, float eps, void *u);
 hipError_t launch_dec_end(hipStream_t s, const float *arg_v, const int *arg_i, int nblk, int B, int32_t *next,
                           int *pos_dev);
 hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &a);

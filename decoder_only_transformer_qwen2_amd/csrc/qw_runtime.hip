@@ -96,6 +96,7 @@ struct qw_model {
   long long *gu_fix = nullptr;       // [max_batch, 2I]
   float *arg_v = nullptr;            // [max_batch, ceil(V / 64)]
   int *arg_i = nullptr;
+  float *att_m = nullptr, *att_l = nullptr, *att_o = nullptr;   // split-KV partials
   int batch = 0, pos = 0;
   // decode graph, captured against the staging rows (so caller pointers may
   // change from step to step) for the batch of the last prefill
@@ -121,8 +122,12 @@ struct qw_model {
 
 namespace {
 
-// Workgroups a decode projection aims for (256 CUs, a few workgroups each).
+// Workgroups a decode projection / attention launch aims for (256 CUs).
 constexpr int kGemvTargetGroups = 1024;
+constexpr int kAttnTargetGroups = 256;
+// Up to this many rows, a projection normalises its own operand (each
+// workgroup reads the whole residual rows); above it a norm kernel runs.
+constexpr int kFusedNormRows = 2;
 
 // Bracket a launch of `fam` with events when timing that family.
 template <class F>
@@ -264,27 +269,46 @@ DecGemvArgs dec_args(const void *W, int M, int N, int K, float scale) {
 }
 
 // Decode step of the bf16-weight mode (kernels of k_decode.hip): per layer
-// norm, q/k/v projection, attention (with bias, RoPE and the cache write),
-// o projection, norm, gate/up projection, down projection; then the final
-// norm, the LM head with per-block argmax, and the argmax reduction.
+// [norm] q/k/v projection, attention (bias, RoPE, cache write, split-KV),
+// o projection (merging the attention splits), [norm] gate/up projection,
+// down projection (silu(gate) * up on its operand); then the LM head with
+// per-block argmax and the argmax reduction.  The bracketed norms are folded
+// into the projection that follows them for batches of up to two rows.
 hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next) {
   const qw_config &c = m->cfg;
   const int B = m->batch, H = c.hidden, I = c.intermediate, V = c.vocab;
+  const bool fused_norm = B <= kFusedNormRows;
+  const int S = dec_attn_splits(B, c.n_kv_heads, c.max_seq, kAttnTargetGroups);
+  const int64_t n_qkv = (int64_t)B * m->nqkv, n_gu = (int64_t)B * 2 * I;
   hipError_t e = timed(m, s, F_EMBED, [&] {
-    return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, m->x_fix, m->bad_ids);
+    return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, m->x_fix, m->bad_ids, m->qkv_fix, n_qkv,
+                            m->gu_fix, n_gu);
   });
   if (e != hipSuccess) return e;
+  // operand of a projection that follows an RMSNorm
+  auto normed = [&](DecGemvArgs &g, const float *w) {
+    g.lda = H;
+    if (fused_norm) {
+      g.act_mode = 1;
+      g.x_fix = m->x_fix;
+      g.norm_w = w;
+      g.eps = c.rms_eps;
+    } else {
+      g.act_mode = 0;
+      g.act = m->u;
+    }
+  };
+  auto norm = [&](const float *w) -> hipError_t {
+    if (fused_norm) return hipSuccess;
+    return timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, m->x_fix, B, H, w, c.rms_eps, m->u); });
+  };
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerBuf &Lw = m->L[l];
     char *kc = (char *)m->k_cache + (int64_t)l * m->cache_layer_elems * m->esz;
     char *vc = (char *)m->v_cache + (int64_t)l * m->cache_layer_elems * m->esz;
-    e = timed(m, s, F_RMSNORM, [&] {
-      return launch_dec_norm(s, m->x_fix, B, H, Lw.in_norm, c.rms_eps, m->u, m->qkv_fix, m->nqkv);
-    });
-    if (e != hipSuccess) return e;
+    if ((e = norm(Lw.in_norm)) != hipSuccess) return e;
     DecGemvArgs g = dec_args(Lw.w_qkv, B, m->nqkv, H, Lw.s_qkv);
-    g.act = m->u;
-    g.lda = H;
+    normed(g, Lw.in_norm);
     g.out_fix = m->qkv_fix;
     g.ldo = m->nqkv;
     e = timed(m, s, F_GEMM_QKV, [&] { return launch_dec_gemv(s, g); });
@@ -296,6 +320,10 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     da.k_cache = kc;
     da.v_cache = vc;
     da.o = m->o;
+    da.part_m = m->att_m;
+    da.part_l = m->att_l;
+    da.part_o = m->att_o;
+    da.splits = S;
     da.batch = B;
     da.n_heads = c.n_heads;
     da.n_kv_heads = c.n_kv_heads;
@@ -303,27 +331,39 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     da.max_seq = c.max_seq;
     da.pos_dev = m->pos_dev;
     da.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
+    da.clear = m->gu_fix;
+    da.clear_n = n_gu;
     e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
     if (e != hipSuccess) return e;
     g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o);
-    g.act = m->o;
+    if (S > 1) {
+      g.act_mode = 3;
+      g.part_m = m->att_m;
+      g.part_l = m->att_l;
+      g.part_o = m->att_o;
+      g.attn_splits = S;
+      g.n_heads = c.n_heads;
+      g.head_dim = c.head_dim;
+    } else {
+      g.act_mode = 0;
+      g.act = m->o;
+    }
     g.lda = m->qd;
     g.out_fix = m->x_fix;
     g.ldo = H;
+    g.clear = m->qkv_fix;
+    g.clear_n = n_qkv;
     e = timed(m, s, F_GEMM_O, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
-    e = timed(m, s, F_RMSNORM, [&] {
-      return launch_dec_norm(s, m->x_fix, B, H, Lw.post_norm, c.rms_eps, m->u, m->gu_fix, 2 * I);
-    });
-    if (e != hipSuccess) return e;
+    if ((e = norm(Lw.post_norm)) != hipSuccess) return e;
     g = dec_args(Lw.w_gu, B, 2 * I, H, Lw.s_gu);
-    g.act = m->u;
-    g.lda = H;
+    normed(g, Lw.post_norm);
     g.out_fix = m->gu_fix;
     g.ldo = 2 * I;
     e = timed(m, s, F_GEMM_GATE_UP, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
     g = dec_args(Lw.w_down, B, H, I, Lw.s_down);
+    g.act_mode = 2;
     g.act_fix = m->gu_fix;
     g.lda = 2 * I;
     g.out_fix = m->x_fix;
@@ -331,13 +371,9 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     e = timed(m, s, F_GEMM_DOWN, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
   }
-  e = timed(m, s, F_RMSNORM, [&] {
-    return launch_dec_norm(s, m->x_fix, B, H, m->final_norm, c.rms_eps, m->u, nullptr, 0);
-  });
-  if (e != hipSuccess) return e;
+  if ((e = norm(m->final_norm)) != hipSuccess) return e;
   DecGemvArgs g = dec_args(m->head, B, V, H, m->head_scale);
-  g.act = m->u;
-  g.lda = H;
+  normed(g, m->final_norm);
   g.ldo = V;
   g.logits_mode = 1;
   g.logits = m->logits;
@@ -566,6 +602,10 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
     CREATE_TRY(m->alloc((void **)&m->gu_fix, nb * 2 * I * 8));
     CREATE_TRY(m->alloc((void **)&m->arg_v, nb * ((V + 63) / 64) * 4));
     CREATE_TRY(m->alloc((void **)&m->arg_i, nb * ((V + 63) / 64) * 4));
+    const size_t ns = nb * c.n_heads * 16;    // at most 16 attention splits
+    CREATE_TRY(m->alloc((void **)&m->att_m, ns * 4));
+    CREATE_TRY(m->alloc((void **)&m->att_l, ns * 4));
+    CREATE_TRY(m->alloc((void **)&m->att_o, ns * c.head_dim * 4));
   }
   CREATE_TRY(m->alloc((void **)&m->next_stage, (size_t)c.max_batch * 4));
   CREATE_TRY(hipMemsetAsync(m->pos_dev, 0, 256, s));
