@@ -63,6 +63,27 @@ def decode_family_bytes(w: S.Workload, family: str, ctx_mean: float) -> float:
     return float("nan")
 
 
+def prefill_family_flops(w: S.Workload, family: str) -> float:
+    """Algorithmic FLOP of ONE prefill launch of a kernel family (T = B*P
+    rows): 2*M*N*K for the projections, causal QK^T + PV for attention."""
+    m, B, P = w.model, w.batch, w.prompt_len
+    T = B * P
+    H, I, V, qd, kvd = m.hidden, m.intermediate, m.vocab, m.q_dim, m.kv_dim
+    if family == "gemm_qkv":
+        return 2.0 * T * (qd + 2 * kvd) * H
+    if family == "gemm_o":
+        return 2.0 * T * H * qd
+    if family == "gemm_gate_up":
+        return 2.0 * T * 2 * I * H
+    if family == "gemm_down":
+        return 2.0 * T * H * I
+    if family == "lm_head":
+        return 2.0 * B * V * H
+    if family == "attention":
+        return 2.0 * B * m.n_heads * m.head_dim * P * (P + 1)
+    return float("nan")
+
+
 def run_step(model, ids, toks, D, torch, ev=None):
     """prefill + D decode steps; ev = (start, after_prefill, end) events."""
     if ev:
@@ -182,6 +203,22 @@ def main():
                            "avg_launch_us": round(avg_s * 1e6, 3), "launches": n,
                            "algorithmic_bytes_per_launch": int(bytes_per)}
         out["decode_family_ms_per_step"] = {f: round(per[f][0] / D, 4) for f in per}
+        # prefill: per-family time over one eager prefill each
+        pper = {}
+        for f in ("gemm_qkv", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "rope_cache", "rmsnorm", "lm_head"):
+            model.timing_enable(f)
+            model.prefill(ids, next_ids=toks[0])
+            ms, n = model.timing_read(reset=True)
+            model.timing_enable(None)
+            pper[f] = (ms, n)
+        pdom = max(("gemm_qkv", "attention", "gemm_o", "gemm_gate_up", "gemm_down"), key=lambda f: pper[f][0])
+        ms, n = pper[pdom]
+        tflops = prefill_family_flops(w, pdom) / (ms / n / 1e3) / 1e12
+        out["prefill_roofline"] = {"bound": "mfma", "kernel": pdom, "achieved": round(tflops, 1),
+                                   "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                                   "avg_launch_us": round(ms / n * 1e3, 3), "launches": n}
+        out["prefill_family_ms"] = {f: round(pper[f][0], 3) for f in pper}
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

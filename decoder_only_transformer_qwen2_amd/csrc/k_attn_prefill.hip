@@ -1,0 +1,231 @@
+// Prefill attention on the matrix cores: causal grouped-query attention of
+// every prompt row against the keys/values already in the cache ("LLM
+// Speedrun: Architecture", sections "Attention", "Every token with every
+// other token, even the future ones?" and "Grouped Query Attention GQA";
+// query head h reads KV head floor(h / g)).
+//
+// Flash-style: keys are visited 64 at a time with an online softmax, so the
+// score matrix is never stored.  The products are taken transposed,
+//   S^T = K . Q^T          (A = K tile rows, B = query rows)
+//   O^T += V^T . P^T       (A = V^T from LDS, B = probabilities)
+// which leaves each lane owning ONE query column of S^T and O^T: the running
+// max / sum / rescale of the online softmax are per-lane scalars, and the
+// probabilities already sit in the B-operand layout of the second product
+// (the key order inside each 32-key step is permuted identically on the V^T
+// side), so P never goes through LDS.  A workgroup is 4 waves x 32 queries of
+// one head; the K tile ([key][d]) and the transposed V tile ([d][key]) are
+// staged in LDS with two buffers.  Work items are ordered heaviest (latest
+// query tile) first and mapped so that the g query heads of a KV head and
+// query tile run on the same XCD, where they share the K/V tiles in L2.
+#include "qw_internal.h"
+
+#include <math.h>
+
+namespace qw {
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BQ = 128;   // queries per workgroup (4 waves x 32)
+constexpr int BKEY = 64;  // keys per step
+
+template <int HD>
+__global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt) {
+  constexpr int KP = HD + 8;          // padded K row
+  constexpr int VP = BKEY + 8;        // padded V^T row
+  constexpr int KS = HD / 32;         // 32-wide d steps for S
+  constexpr int DT = HD / 16;         // 16-wide d tiles of O
+  constexpr int VEC = BKEY * HD / 8;  // 16-byte vectors per K (or V) tile
+  constexpr int VPT = VEC / 256;      // per thread
+  __shared__ f16 sK[2][BKEY][KP];
+  __shared__ f16 sV[2][HD][VP];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int nq = a.n_heads, grp = a.n_heads / a.n_kv_heads;
+  const int P = a.rows_per_seq;
+  // work item: heaviest query tiles first; the g heads of a group adjacent,
+  // and adjacent items on one XCD (workgroups go round-robin over 8 XCDs)
+  const int total = n_qt * nq * (a.T / P);
+  const int L = blockIdx.x;
+  const int per_x = (total + 7) / 8;
+  int w = (L % 8) * per_x + L / 8;
+  if (w >= total) return;
+  const int h = w % nq;
+  const int qt = n_qt - 1 - (w / nq) % n_qt;
+  const int b = w / (nq * n_qt);
+  const int j = h / grp;
+  const int q0 = qt * BQ + wave * 32;                 // this wave's first query
+  const int qd = nq * HD;
+
+  const f16 *Q = (const f16 *)a.q + (int64_t)b * P * qd + h * HD;
+  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
+  const f16 *Kc = (const f16 *)a.k_cache + head_base;
+  const f16 *Vc = (const f16 *)a.v_cache + head_base;
+  const f16x8 zero8 = {};
+
+  // queries as B operands: lane (i, g) holds query q0 + 16t + i, dims 32s + 8g .. +8
+  f16x8 qf[2][KS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int q = q0 + 16 * t + i;
+      qf[t][s] = (q < P) ? *reinterpret_cast<const f16x8 *>(Q + (int64_t)q * qd + 32 * s + 8 * g) : zero8;
+    }
+
+  const float sl2 = a.softmax_scale * 1.4426950408889634f;
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  f32x4 o[DT][2];
+#pragma unroll
+  for (int d = 0; d < DT; ++d)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) o[d][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int q_last = min(P - 1, qt * BQ + BQ - 1);    // last query of the workgroup
+  const int n_kb = q_last / BKEY + 1;                  // key blocks it needs
+  f16x8 rk[VPT], rv[VPT];
+  auto gload = [&](int kb) {
+#pragma unroll
+    for (int t = 0; t < VPT; ++t) {
+      const int v = tid + 256 * t;
+      const int key = kb * BKEY + v / (HD / 8), c = (v % (HD / 8)) * 8;
+      const bool ok = key < P;
+      rk[t] = ok ? *reinterpret_cast<const f16x8 *>(Kc + (int64_t)key * HD + c) : zero8;
+      rv[t] = ok ? *reinterpret_cast<const f16x8 *>(Vc + (int64_t)key * HD + c) : zero8;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < VPT; ++t) {
+      const int v = tid + 256 * t;
+      const int key = v / (HD / 8), c = (v % (HD / 8)) * 8;
+      *reinterpret_cast<f16x8 *>(&sK[buf][key][c]) = rk[t];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sV[buf][c + e][key] = rv[t][e];
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kb = 0; kb < n_kb; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < n_kb) gload(kb + 1);
+    const bool wave_active = kb * BKEY <= q0 + 31;     // any key of the block visible to this wave
+    if (wave_active) {
+      // S^T tiles: y = 16-key tile, t = 16-query tile
+      f32x4 s[4][2];
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) s[y][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const f16x8 kf = *reinterpret_cast<const f16x8 *>(&sK[cur][16 * y + i][32 * ks + 8 * g]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) s[y][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[t][ks], s[y][t], 0, 0, 0);
+        }
+      // online softmax per query column; lane (i, g) holds keys 16y + 4g + r
+      f16x8 pb[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int q = q0 + 16 * t + i;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kb * BKEY + 16 * y + 4 * g + r;
+            const float v = (key <= q) ? s[y][t][r] * sl2 : -INFINITY;
+            s[y][t][r] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m[t], mx);
+        const float corr = (m[t] == -INFINITY) ? 0.f : exp2f(m[t] - mn);
+        float sum = 0.f;
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = (mn == -INFINITY) ? 0.f : exp2f(s[y][t][r] - mn);
+            s[y][t][r] = p;
+            sum += p;
+          }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        l[t] = l[t] * corr + sum;
+        m[t] = mn;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) o[d][t] *= corr;
+        // B operand of step u (keys 32u .. 32u+31): keys 32u + 4g + e (e < 4), 32u + 16 + 4g + e - 4
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pb[t][u][e] = (f16)s[2 * u][t][e];
+            pb[t][u][e + 4] = (f16)s[2 * u + 1][t][e];
+          }
+      }
+      // O^T += V^T . P^T, A operand from the transposed V tile with the same key order
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int d = 0; d < DT; ++d) {
+          const f16x4 lo = *reinterpret_cast<const f16x4 *>(&sV[cur][16 * d + i][32 * u + 4 * g]);
+          const f16x4 hi = *reinterpret_cast<const f16x4 *>(&sV[cur][16 * d + i][32 * u + 16 + 4 * g]);
+          const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int t = 0; t < 2; ++t) o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[t][u], o[d][t], 0, 0, 0);
+        }
+    }
+    if (kb + 1 < n_kb) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // O^T: lane (i, g) holds dims 16d + 4g + r of query q0 + 16t + i
+  f16 *O = (f16 *)a.o + (int64_t)b * P * qd + h * HD;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int q = q0 + 16 * t + i;
+    if (q >= P) continue;
+    const float inv = 1.0f / l[t];
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      f16x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (f16)(o[d][t][r] * inv);
+      *reinterpret_cast<f16x4 *>(O + (int64_t)q * qd + 16 * d + 4 * g) = v;
+    }
+  }
+}
+
+}  // namespace
+
+bool attn_prefill_supported(int head_dim) { return head_dim == 32 || head_dim == 64 || head_dim == 128; }
+
+hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.pos0_dev || a.pos0 != 0 || a.T % a.rows_per_seq) return hipErrorInvalidValue;
+  const int P = a.rows_per_seq, B = a.T / P;
+  const int n_qt = (P + BQ - 1) / BQ;
+  const int total = n_qt * a.n_heads * B;
+  const int per_x = (total + 7) / 8;
+  dim3 grid(per_x * 8);
+  switch (a.head_dim) {
+    case 32: attn_prefill_kernel<32><<<grid, 256, 0, s>>>(a, n_qt); break;
+    case 64: attn_prefill_kernel<64><<<grid, 256, 0, s>>>(a, n_qt); break;
+    case 128: attn_prefill_kernel<128><<<grid, 256, 0, s>>>(a, n_qt); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qw

@@ -1,0 +1,151 @@
+// Prefill projections on the matrix cores: C[M, N] = A[M, K] . W[N, K]^T with
+// f16 operands and fp32 accumulation (v_mfma_f32_16x16x32_f16), for the
+// q/k/v, o, gate/up and down projections and the LM head over all prompt
+// rows at once ("Building a Qwen2.5-1.5B Inference Engine From Scratch",
+// section 1: prefill processes every prompt token in parallel, which makes it
+// compute-bound).  Epilogues as in the generic kernel: store fp32, add into
+// the fp32 residual stream, or silu(gate) * up over the GU_BLOCK-interleaved
+// gate/up rows.
+//
+// Tiling: a workgroup computes a 128 x 128 tile with 4 wavefronts (2 x 2),
+// each a 64 x 64 sub-tile = 4 x 4 MFMA tiles of 16 x 16.  K advances 64 at a
+// time; both operand tiles are staged in LDS (rows padded by 16 bytes so the
+// 16 rows an MFMA operand load touches fall in different banks) with two
+// buffers: the next tile's global loads are in flight while the current
+// tile is multiplied, and one barrier per K step orders the buffers.
+#include "qw_internal.h"
+
+namespace qw {
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LDP = BK + 8;           // padded LDS row (f16 elements)
+
+template <Epi EPI>
+__global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
+  __shared__ f16 sA[2][BM][LDP];
+  __shared__ f16 sB[2][BN][LDP];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;          // wave's 64 x 64 sub-tile
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const f16 *A = (const f16 *)a.A;
+  const f16 *W = (const f16 *)a.W;
+  const f16x8 zero = {};
+
+  // global -> register staging: 1024 16-byte vectors per operand tile, 4 per thread
+  f16x8 ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int v = tid + 256 * t;
+      const int r = v >> 3, c = (v & 7) * 8;
+      const int gm = m0 + r, gn = n0 + r, gk = k0 + c;
+      ra[t] = (gm < a.M && gk < a.K) ? *reinterpret_cast<const f16x8 *>(A + (int64_t)gm * a.lda + gk) : zero;
+      rb[t] = (gn < a.N && gk < a.K) ? *reinterpret_cast<const f16x8 *>(W + (int64_t)gn * a.K + gk) : zero;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int v = tid + 256 * t;
+      const int r = v >> 3, c = (v & 7) * 8;
+      *reinterpret_cast<f16x8 *>(&sA[buf][r][c]) = ra[t];
+      *reinterpret_cast<f16x8 *>(&sB[buf][r][c]) = rb[t];
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = (a.K + BK - 1) / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 32) {
+      f16x8 fa[4], fb[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        fa[x] = *reinterpret_cast<const f16x8 *>(&sA[cur][wm * 64 + x * 16 + i][ks + 8 * g]);
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        fb[y] = *reinterpret_cast<const f16x8 *>(&sB[cur][wn * 64 + y * 16 + i][ks + 8 * g]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+    if (kt + 1 < KT) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // acc[x][y]: lane (i, g) holds rows 4g..4g+3 of column i of MFMA tile (x, y)
+  if constexpr (EPI == Epi::SwiGLU) {
+    // the wave's 64 columns are two (gate block, up block) pairs: y = 0/1 and 2/3
+    f16 *out = (f16 *)a.act_out;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int f = (n0 + wn * 64) / 2 + p * GU_BLOCK + i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 64 + x * 16 + 4 * g + r;
+          if (row < a.M && f < a.N / 2) {
+            const float gt = acc[x][2 * p][r] * a.scale, up = acc[x][2 * p + 1][r] * a.scale;
+            out[(int64_t)row * a.ldo + f] = (f16)(silu_f(gt) * up);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int col = n0 + wn * 64 + y * 16 + i;
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 64 + x * 16 + 4 * g + r;
+          if (row >= a.M) continue;
+          float *o = a.out_f32 + (int64_t)row * a.ldo + col;
+          const float v = acc[x][y][r] * a.scale;
+          if constexpr (EPI == Epi::ResidAdd)
+            *o += v;
+          else
+            *o = v;
+        }
+      }
+  }
+}
+
+}  // namespace
+
+bool gemm_mfma_supported(const GemmArgs &a) {
+  return (a.K % 8) == 0 && (a.lda % 8) == 0 && (a.epi != Epi::SwiGLU || a.N % 128 == 0);
+}
+
+hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (!gemm_mfma_supported(a)) return hipErrorInvalidValue;
+  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
+  switch (a.epi) {
+    case Epi::StoreF32: gemm_mfma_kernel<Epi::StoreF32><<<grid, 256, 0, s>>>(a); break;
+    case Epi::ResidAdd: gemm_mfma_kernel<Epi::ResidAdd><<<grid, 256, 0, s>>>(a); break;
+    case Epi::SwiGLU: gemm_mfma_kernel<Epi::SwiGLU><<<grid, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qw

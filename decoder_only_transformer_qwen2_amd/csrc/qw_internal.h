@@ -131,7 +131,11 @@ hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows
                           int hidden, const float *w, float eps, void *out);
 hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a);
 hipError_t launch_attention_generic(hipStream_t s, bool f16_mode, const AttnArgs &a);
+bool attn_prefill_supported(int head_dim);
+hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a);   // f16, prompt from position 0
 hipError_t launch_gemm_generic(hipStream_t s, bool f16_mode, const GemmArgs &a);
+bool gemm_mfma_supported(const GemmArgs &a);
+hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a);     // f16 operands
 bool decode_fast_supported(int head_dim, int group, int hidden, int q_dim, int inter);
 int dec_gemv_splits(int N, int K, int M, int target_groups);
 int dec_attn_splits(int batch, int n_kv_heads, int max_seq, int target_groups);

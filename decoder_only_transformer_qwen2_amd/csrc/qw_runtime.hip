@@ -163,6 +163,7 @@ hipError_t gemm(qw_model *m, hipStream_t s, Family fam, const void *A, int M, in
   a.out_f32 = out_f32;
   a.act_out = act_out;
   a.ldo = ldo;
+  if (m->f16 && gemm_mfma_supported(a)) return timed(m, s, fam, [&] { return launch_gemm_mfma(s, a); });
   return timed(m, s, fam, [&] { return launch_gemm_generic(s, m->f16, a); });
 }
 
@@ -212,7 +213,10 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
     aa.pos0 = pos0;
     aa.pos0_dev = pos_dev;
     aa.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
-    e = timed(m, s, F_ATTENTION, [&] { return launch_attention_generic(s, m->f16, aa); });
+    if (m->f16 && !pos_dev && pos0 == 0 && attn_prefill_supported(c.head_dim))
+      e = timed(m, s, F_ATTENTION, [&] { return launch_attention_prefill(s, aa); });
+    else
+      e = timed(m, s, F_ATTENTION, [&] { return launch_attention_generic(s, m->f16, aa); });
 
     if (e != hipSuccess) return e;
     e = gemm(m, s, F_GEMM_O, m->o, T, m->qd, m->qd, Lw.w_o, H, Lw.s_o, Epi::ResidAdd, m->x, nullptr, H);
