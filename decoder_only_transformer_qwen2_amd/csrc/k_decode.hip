@@ -85,9 +85,18 @@ __global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, i
   __shared__ float red[4];
   const long long *xr = x_fix + (int64_t)b * H;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < H; c += 256) {
-    const float v = from_fix(xr[c]);
-    ss += v * v;
+  for (int c0 = 0; c0 < H; c0 += 256 * 8) {
+    long long v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int c = c0 + t * 256 + threadIdx.x;
+      v[t] = c < H ? xr[c] : 0;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float f = from_fix(v[t]);
+      ss += f * f;
+    }
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -167,17 +176,31 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
   load_w(k0);
 
   if constexpr (AM == DecAct::NormFix) {
-    // inverse RMS of each batch row over the whole hidden vector
-    for (int b = wave; b < a.M; b += 4) {
+    // inverse RMS of each batch row over the whole hidden vector: every
+    // thread issues its loads up front, then one block reduction per row
+    __shared__ float s_red[4][BT];
+    for (int b = 0; b < a.M; ++b) {
       const long long *xr = a.x_fix + (int64_t)b * a.lda;
+      constexpr int PER = 8;                  // values per thread per pass (K <= 2048 in one pass)
       float ss = 0.f;
-      for (int c = lane; c < a.K; c += 64) {
-        const float v = from_fix(xr[c]);
-        ss += v * v;
+      for (int c0 = 0; c0 < a.K; c0 += 256 * PER) {
+        long long v[PER];
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+          const int c = c0 + t * 256 + tid;
+          v[t] = c < a.K ? xr[c] : 0;
+        }
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+          const float f = from_fix(v[t]);
+          ss += f * f;
+        }
       }
       ss = wave_sum(ss);
-      if (lane == 0) s_inv[b] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+      if (lane == 0) s_red[wave][b] = ss;
     }
+    __syncthreads();
+    if (tid < a.M) s_inv[tid] = 1.0f / sqrtf((s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid]) / (float)a.K + a.eps);
     __syncthreads();
   }
 
@@ -340,21 +363,27 @@ hipError_t launch_gemv_nb(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
 // RoPE at `pos` (q rounded to f16 like the prefill path); the split that
 // holds position pos writes k and v into the cache.  Body: the split's cached
 // keys, plus key pos from LDS; HD/8 lanes share one key (16 bytes each);
-// online softmax in the exp2 domain; lanes and waves merged at the end.  With
-// one split the normalised output is written (f16); otherwise the split's
-// (max, sum, unnormalised output) per head go to the partials that the o
-// projection merges.
-template <int HD, int G>
+// online softmax in the exp2 domain.  Two wave layouts:
+//   WH == G  (key-parallel): every wave carries all g heads over a quarter of
+//            the keys; the four waves are merged in LDS at the end.
+//   WH <  G  (head-parallel): wave w carries heads w*WH .. w*WH+WH-1 over all
+//            keys, so each lane's chain is WH heads long and no cross-wave
+//            merge is needed (short contexts, where latency dominates).
+// With one split the normalised output is written (f16); otherwise the
+// split's (max, sum, unnormalised output) per head go to the partials that
+// the o projection merges.
+template <int HD, int G, int WH>
 __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
   constexpr int NW = 4;
+  constexpr bool KEYPAR = (WH == G);
   constexpr int LPK = HD / 8;        // lanes per key
   constexpr int KPW = 64 / LPK;      // keys per wave per load
-  constexpr int KPB = NW * KPW;
+  constexpr int KSTEP = KEYPAR ? NW * KPW : KPW;   // keys between a wave's consecutive loads
   constexpr int HALF = HD / 2;
   __shared__ float s_q[G][HD];
   __shared__ float s_k[HD], s_v[HD];
-  __shared__ float s_m[NW][G], s_l[NW][G];
-  __shared__ float s_o[NW][G][HD];
+  __shared__ float s_m[KEYPAR ? NW : 1][G], s_l[KEYPAR ? NW : 1][G];
+  __shared__ float s_o[KEYPAR ? NW : 1][G][HD];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int slot = lane / LPK, dl = lane % LPK, d0 = dl * 8;
@@ -363,7 +392,7 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
   const int pos = *a.pos_dev;
   const int n_keys = pos + 1;
   int per = (n_keys + S - 1) / S;
-  per = (per + KPB - 1) / KPB * KPB;
+  per = (per + NW * KPW - 1) / (NW * KPW) * (NW * KPW);
   const int kb0 = split * per;
   const int kb1 = min(n_keys, kb0 + per);
   const bool has_new = kb0 <= pos && pos < kb1;
@@ -408,143 +437,183 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
     Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
   }
 
-  float q[G][8];
+  // the heads this wave carries: h_lo + t for t < nh
+  const int h_lo = KEYPAR ? 0 : wave * WH;
+  const int nh = KEYPAR ? G : max(0, min(WH, G - h_lo));
+  float q[WH][8];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+  for (int t = 0; t < WH; ++t)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[hh][e] = s_q[hh][d0 + e];
-  float m[G], l[G], o[G][8];
+    for (int e = 0; e < 8; ++e) q[t][e] = (t < nh) ? s_q[h_lo + t][d0 + e] : 0.f;
+  float m[WH], l[WH], o[WH][8];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
+  for (int t = 0; t < WH; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+    for (int e = 0; e < 8; ++e) o[t][e] = 0.f;
   }
 
   auto visit = [&](const float *kf, const float *vf) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
+    for (int t = 0; t < WH; ++t) {
       float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s = fmaf(q[hh][e], kf[e], s);
+      for (int e = 0; e < 8; ++e) s = fmaf(q[t][e], kf[e], s);
 #pragma unroll
       for (int off = LPK / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-      const float mn = fmaxf(m[hh], s);
-      const float corr = exp2f(m[hh] - mn);
+      const float mn = fmaxf(m[t], s);
+      const float corr = exp2f(m[t] - mn);
       const float p = exp2f(s - mn);
-      l[hh] = l[hh] * corr + p;
+      l[t] = l[t] * corr + p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(p, vf[e], o[hh][e] * corr);
-      m[hh] = mn;
+      for (int e = 0; e < 8; ++e) o[t][e] = fmaf(p, vf[e], o[t][e] * corr);
+      m[t] = mn;
     }
   };
 
-  const int kc_end = min(kb1, pos);               // cached keys of this split
-  for (int kb = kb0 + wave * KPW; kb < kc_end; kb += 2 * KPB) {
-    const int t0 = kb + slot, t1 = kb + KPB + slot;
-    f16x8 k0 = {}, v0 = {}, k1v = {}, v1 = {};
-    if (t0 < kc_end) {
-      k0 = load8(Kc + (int64_t)t0 * HD + d0);
-      v0 = load8(Vc + (int64_t)t0 * HD + d0);
+  if (nh > 0) {
+    const int kc_end = min(kb1, pos);               // cached keys of this split
+    for (int kb = kb0 + (KEYPAR ? wave * KPW : 0); kb < kc_end; kb += 2 * KSTEP) {
+      const int t0 = kb + slot, t1 = kb + KSTEP + slot;
+      f16x8 k0 = {}, v0 = {}, k1v = {}, v1 = {};
+      if (t0 < kc_end) {
+        k0 = load8(Kc + (int64_t)t0 * HD + d0);
+        v0 = load8(Vc + (int64_t)t0 * HD + d0);
+      }
+      if (t1 < kc_end) {
+        k1v = load8(Kc + (int64_t)t1 * HD + d0);
+        v1 = load8(Vc + (int64_t)t1 * HD + d0);
+      }
+      if (t0 < kc_end) {
+        float kf[8], vf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kf[e] = (float)k0[e]; vf[e] = (float)v0[e]; }
+        visit(kf, vf);
+      }
+      if (t1 < kc_end) {
+        float kf[8], vf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kf[e] = (float)k1v[e]; vf[e] = (float)v1[e]; }
+        visit(kf, vf);
+      }
     }
-    if (t1 < kc_end) {
-      k1v = load8(Kc + (int64_t)t1 * HD + d0);
-      v1 = load8(Vc + (int64_t)t1 * HD + d0);
-    }
-    if (t0 < kc_end) {
+    if (has_new && (KEYPAR ? wave == 0 : true) && slot == 0) {
       float kf[8], vf[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { kf[e] = (float)k0[e]; vf[e] = (float)v0[e]; }
+      for (int e = 0; e < 8; ++e) { kf[e] = s_k[d0 + e]; vf[e] = s_v[d0 + e]; }
       visit(kf, vf);
     }
-    if (t1 < kc_end) {
-      float kf[8], vf[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { kf[e] = (float)k1v[e]; vf[e] = (float)v1[e]; }
-      visit(kf, vf);
-    }
-  }
-  if (has_new && wave == 0 && slot == 0) {
-    float kf[8], vf[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { kf[e] = s_k[d0 + e]; vf[e] = s_v[d0 + e]; }
-    visit(kf, vf);
   }
 
-  // merge the KPW key slots of each wave
+  // merge the KPW key slots of each wave (lanes with equal dl)
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
+  for (int t = 0; t < WH; ++t) {
 #pragma unroll
     for (int off = LPK; off < 64; off <<= 1) {
-      const float mo = __shfl_xor(m[hh], off, 64);
-      const float lo = __shfl_xor(l[hh], off, 64);
-      const float mn = fmaxf(m[hh], mo);
-      const float ca = (m[hh] == -INFINITY) ? 0.f : exp2f(m[hh] - mn);
+      const float mo = __shfl_xor(m[t], off, 64);
+      const float lo = __shfl_xor(l[t], off, 64);
+      const float mn = fmaxf(m[t], mo);
+      const float ca = (m[t] == -INFINITY) ? 0.f : exp2f(m[t] - mn);
       const float cb = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
-      l[hh] = l[hh] * ca + lo * cb;
+      l[t] = l[t] * ca + lo * cb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float oo = __shfl_xor(o[hh][e], off, 64);
-        o[hh][e] = o[hh][e] * ca + oo * cb;
+        const float oo = __shfl_xor(o[t][e], off, 64);
+        o[t][e] = o[t][e] * ca + oo * cb;
       }
-      m[hh] = mn;
+      m[t] = mn;
     }
   }
-  if (slot == 0) {
+
+  if constexpr (!KEYPAR) {
+    // each wave owns its heads: write them directly (lanes of slot 0)
+    if (slot == 0) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      if (dl == 0) {
-        s_m[wave][hh] = m[hh];
-        s_l[wave][hh] = l[hh];
+      for (int t = 0; t < WH; ++t) {
+        if (t >= nh) continue;
+        const int h = j * G + h_lo + t;
+        if (S == 1) {
+          const float inv = 1.0f / l[t];
+          f16 *out = (f16 *)a.o + (int64_t)b * qd + h * HD + d0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) out[e] = (f16)(o[t][e] * inv);
+        } else {
+          const int64_t st = ((int64_t)b * nq + h) * S + split;
+          if (dl == 0) {
+            a.part_m[st] = m[t];
+            a.part_l[st] = l[t];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a.part_o[st * HD + d0 + e] = o[t][e];
+        }
       }
+    }
+    return;
+  } else {
+    if (slot == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[wave][hh][d0 + e] = o[hh][e];
+      for (int t = 0; t < WH; ++t) {
+        if (dl == 0) {
+          s_m[wave][t] = m[t];
+          s_l[wave][t] = l[t];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_o[wave][t][d0 + e] = o[t][e];
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * HD; e += 256) {
+      const int hh = e / HD, d = e % HD;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, s_m[w2][hh]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+          const float c = (s_m[w2][hh] == -INFINITY) ? 0.f : exp2f(s_m[w2][hh] - M);
+          L += s_l[w2][hh] * c;
+          O += s_o[w2][hh][d] * c;
+        }
+      }
+      const int h = j * G + hh;
+      if (S == 1) {
+        ((f16 *)a.o)[(int64_t)b * qd + h * HD + d] = (f16)(O / L);
+      } else {
+        const int64_t st = ((int64_t)b * nq + h) * S + split;
+        if (d == 0) {
+          a.part_m[st] = M;
+          a.part_l[st] = L;
+        }
+        a.part_o[st * HD + d] = O;
+      }
     }
   }
-  __syncthreads();
-  for (int e = tid; e < G * HD; e += 256) {
-    const int hh = e / HD, d = e % HD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, s_m[w2][hh]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
-        const float c = (s_m[w2][hh] == -INFINITY) ? 0.f : exp2f(s_m[w2][hh] - M);
-        L += s_l[w2][hh] * c;
-        O += s_o[w2][hh][d] * c;
-      }
-    }
-    const int h = j * G + hh;
-    if (S == 1) {
-      ((f16 *)a.o)[(int64_t)b * qd + h * HD + d] = (f16)(O / L);
-    } else {
-      const int64_t st = ((int64_t)b * nq + h) * S + split;
-      if (d == 0) {
-        a.part_m[st] = M;
-        a.part_l[st] = L;
-      }
-      a.part_o[st * HD + d] = O;
-    }
-  }
+}
+
+template <int HD, int G>
+hipError_t launch_attn_g(hipStream_t s, const DecAttnArgs &a, dim3 grid) {
+  if (a.head_parallel && G > 1)
+    dec_attn_kernel<HD, G, (G + 3) / 4><<<grid, 256, 0, s>>>(a);
+  else
+    dec_attn_kernel<HD, G, G><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int HD>
 hipError_t launch_attn_hd(hipStream_t s, const DecAttnArgs &a, dim3 grid, int g) {
   switch (g) {
-    case 1: dec_attn_kernel<HD, 1><<<grid, 256, 0, s>>>(a); break;
-    case 2: dec_attn_kernel<HD, 2><<<grid, 256, 0, s>>>(a); break;
-    case 3: dec_attn_kernel<HD, 3><<<grid, 256, 0, s>>>(a); break;
-    case 4: dec_attn_kernel<HD, 4><<<grid, 256, 0, s>>>(a); break;
-    case 5: dec_attn_kernel<HD, 5><<<grid, 256, 0, s>>>(a); break;
-    case 6: dec_attn_kernel<HD, 6><<<grid, 256, 0, s>>>(a); break;
-    case 7: dec_attn_kernel<HD, 7><<<grid, 256, 0, s>>>(a); break;
-    case 8: dec_attn_kernel<HD, 8><<<grid, 256, 0, s>>>(a); break;
+    case 1: return launch_attn_g<HD, 1>(s, a, grid);
+    case 2: return launch_attn_g<HD, 2>(s, a, grid);
+    case 3: return launch_attn_g<HD, 3>(s, a, grid);
+    case 4: return launch_attn_g<HD, 4>(s, a, grid);
+    case 5: return launch_attn_g<HD, 5>(s, a, grid);
+    case 6: return launch_attn_g<HD, 6>(s, a, grid);
+    case 7: return launch_attn_g<HD, 7>(s, a, grid);
+    case 8: return launch_attn_g<HD, 8>(s, a, grid);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -115,6 +115,7 @@ struct DecAttnArgs {
   void *o;                           // splits == 1: [batch, nq*hd] f16
   float *part_m, *part_l, *part_o;   // splits > 1: [batch][nq][splits] (+ [hd])
   int splits;
+  int head_parallel;                 // 1: waves split the heads (short contexts), 0: waves split the keys
   int batch, n_heads, n_kv_heads, head_dim, max_seq;
   const int *pos_dev;                // position of the new row
   float softmax_scale;

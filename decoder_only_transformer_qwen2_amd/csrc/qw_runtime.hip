@@ -328,6 +328,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     da.part_l = m->att_l;
     da.part_o = m->att_o;
     da.splits = S;
+    da.head_parallel = B <= kFusedNormRows;
     da.batch = B;
     da.n_heads = c.n_heads;
     da.n_kv_heads = c.n_kv_heads;

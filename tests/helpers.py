@@ -67,13 +67,20 @@ def compare_row(oracle_model, prompt, gpu_tokens, gpu_logits, dtype, label=""):
 
 
 def assert_same_sequence(t_a, l_a, t_b, l_b, tol=2e-2, label=""):
-    """Two GPU runs of one sequence under different launch shapes (batch
-    sizes pick different split counts and norm placement, so rounding order
-    differs): logits within `tol`, tokens equal where run a's top-2 margin
-    exceeds 2 * tol.  Rows leaking into each other would differ by O(1)."""
-    d = np.abs(l_a.astype(np.float64) - l_b).max()
-    assert d <= tol, f"{label}: max |dlogit| between runs {d:.3e} > {tol}"
-    srt = np.sort(l_a, axis=-1)
-    clear = (srt[..., -1] - srt[..., -2]) > 2 * tol
-    assert np.array_equal(t_a[clear], t_b[clear]), f"{label}: tokens differ at clear-margin steps"
+    """Two free-running GPU generations of one sequence under different launch
+    shapes (batch sizes pick different split counts and norm placement, so
+    rounding order differs).  Up to the first step where their tokens differ
+    the two runs see the same prefix: logits must agree within `tol`.  At that
+    step the choice must have been a near-tie (top-2 margin <= 2 * tol) --
+    after it the runs decode different sequences and are not compared.
+    Rows leaking into each other would differ by O(1) before any divergence."""
+    n = len(t_a)
+    diff_steps = np.nonzero(t_a != t_b)[0]
+    k = int(diff_steps[0]) if diff_steps.size else n - 1
+    d = np.abs(l_a[:k + 1].astype(np.float64) - l_b[:k + 1]).max()
+    assert d <= tol, f"{label}: max |dlogit| between runs over steps 0..{k}: {d:.3e} > {tol}"
+    if diff_steps.size:
+        srt = np.sort(l_a[k])
+        margin = float(srt[-1] - srt[-2])
+        assert margin <= 2 * tol, f"{label}: tokens differ at step {k} with a clear margin {margin:.3e}"
     return d

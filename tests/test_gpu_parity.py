@@ -202,6 +202,8 @@ LONG = {
     # many 128-row query tiles and 64-key blocks, ragged ends
     "long-hd64": (S.ModelShape("l64", 2, 256, 6, 2, 64, 512, 1001), 2, 700, 3, 704),
     "long-hd128-8k": (S.ModelShape("l128", 2, 256, 6, 1, 128, 512, 999), 1, 8190, 4, 8194),
+    # the 1.5B attention geometry (12 q heads over 2 KV heads, hd 128) at 8k
+    "long-1.5b-attn-8k": (S.ModelShape("l15", 2, 512, 12, 2, 128, 512, 999), 1, 8192, 6, 8320),
 }
 
 
