@@ -132,6 +132,11 @@ def main():
     ap.add_argument("--workload", default="0.5b", choices=sorted(S.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch decode kernels one by one instead of replaying the captured graph "
+                         "(same kernels; for counter collection, which does not follow graph launches)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 4 device copies of 256 MiB (the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
@@ -141,6 +146,18 @@ def main():
     import torch
     import decoder_only_transformer_qwen2_amd as Q
 
+    if args.copy_calibration:
+        # a plain copy of known size: the HBM counters of each dispatch read
+        # 256 MiB fetched and 256 MiB written when the counters are exact
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_dispatch": n, "dispatches": 4}), flush=True)
+        return
+
     w = S.WORKLOADS[args.workload]
     m = w.model
     B, P, D = w.batch, w.prompt_len, w.decode_steps
@@ -148,6 +165,8 @@ def main():
     W = S.make_weights(m, w.weight_seed)
     ids_np = S.make_ids(w)
     model = Q.Model(m, Q.device_tensors(m, W), B, w.max_seq)
+    if args.eager:
+        model.set_graph(False)
     ids = torch.from_numpy(ids_np).cuda()
     toks = torch.empty((D + 1, B), dtype=torch.int32, device="cuda")
 

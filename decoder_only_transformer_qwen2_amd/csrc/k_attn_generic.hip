@@ -79,9 +79,9 @@ hipError_t launch_attention_generic(hipStream_t s, bool f16_mode, const AttnArgs
   const int64_t waves = (int64_t)a.T * a.n_heads;
   dim3 grid((unsigned)((waves + 3) / 4));
   if (f16_mode)
-    attn_generic_kernel<f16><<<grid, 256, 0, s>>>(a);
+    QW_LAUNCH((attn_generic_kernel<f16>), dim3(grid), dim3(256), 0, s, a);
   else
-    attn_generic_kernel<float><<<grid, 256, 0, s>>>(a);
+    QW_LAUNCH((attn_generic_kernel<float>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

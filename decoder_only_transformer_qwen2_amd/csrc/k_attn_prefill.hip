@@ -220,9 +220,9 @@ hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a) {
   const int per_x = (total + 7) / 8;
   dim3 grid(per_x * 8);
   switch (a.head_dim) {
-    case 32: attn_prefill_kernel<32><<<grid, 256, 0, s>>>(a, n_qt); break;
-    case 64: attn_prefill_kernel<64><<<grid, 256, 0, s>>>(a, n_qt); break;
-    case 128: attn_prefill_kernel<128><<<grid, 256, 0, s>>>(a, n_qt); break;
+    case 32: QW_LAUNCH((attn_prefill_kernel<32>), dim3(grid), dim3(256), 0, s, a, n_qt); break;
+    case 64: QW_LAUNCH((attn_prefill_kernel<64>), dim3(grid), dim3(256), 0, s, a, n_qt); break;
+    case 128: QW_LAUNCH((attn_prefill_kernel<128>), dim3(grid), dim3(256), 0, s, a, n_qt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

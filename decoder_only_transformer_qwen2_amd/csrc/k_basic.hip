@@ -35,9 +35,9 @@ hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int ro
                         float emb_scale, int hidden, int vocab, float *x, int *bad) {
   if (rows <= 0) return hipSuccess;
   if (f16_mode)
-    embed_kernel<f16><<<rows, 256, 0, s>>>(ids, (const f16 *)emb, emb_scale, hidden, vocab, x, bad);
+    QW_LAUNCH((embed_kernel<f16>), dim3(rows), dim3(256), 0, s, ids, (const f16 *)emb, emb_scale, hidden, vocab, x, bad);
   else
-    embed_kernel<float><<<rows, 256, 0, s>>>(ids, (const float *)emb, emb_scale, hidden, vocab, x, bad);
+    QW_LAUNCH((embed_kernel<float>), dim3(rows), dim3(256), 0, s, ids, (const float *)emb, emb_scale, hidden, vocab, x, bad);
   return hipGetLastError();
 }
 
@@ -75,9 +75,9 @@ hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows
   if (rows <= 0) return hipSuccess;
   dim3 grid((rows + 3) / 4);
   if (f16_mode)
-    rmsnorm_kernel<f16><<<grid, 256, 0, s>>>(x, rows, row_stride, hidden, w, eps, (f16 *)out);
+    QW_LAUNCH((rmsnorm_kernel<f16>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (f16 *)out);
   else
-    rmsnorm_kernel<float><<<grid, 256, 0, s>>>(x, rows, row_stride, hidden, w, eps, (float *)out);
+    QW_LAUNCH((rmsnorm_kernel<float>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (float *)out);
   return hipGetLastError();
 }
 
@@ -125,9 +125,9 @@ __global__ void __launch_bounds__(256) rope_cache_kernel(RopeCacheArgs a) {
 hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a) {
   if (a.T <= 0) return hipSuccess;
   if (f16_mode)
-    rope_cache_kernel<f16><<<a.T, 256, 0, s>>>(a);
+    QW_LAUNCH((rope_cache_kernel<f16>), dim3(a.T), dim3(256), 0, s, a);
   else
-    rope_cache_kernel<float><<<a.T, 256, 0, s>>>(a);
+    QW_LAUNCH((rope_cache_kernel<float>), dim3(a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -163,7 +163,7 @@ __global__ void __launch_bounds__(256) argmax_kernel(const float *__restrict__ l
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
                          int32_t *next_ids, int *pos_dev, int pos_add) {
   if (rows <= 0) return hipSuccess;
-  argmax_kernel<<<rows, 256, 0, s>>>(logits, vocab, row_stride, next_ids, pos_dev, pos_add);
+  QW_LAUNCH((argmax_kernel), dim3(rows), dim3(256), 0, s, logits, vocab, row_stride, next_ids, pos_dev, pos_add);
   return hipGetLastError();
 }
 

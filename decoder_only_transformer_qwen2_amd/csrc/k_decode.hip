@@ -147,12 +147,12 @@ __global__ void __launch_bounds__(256) dec_end_kernel(const float *pv, const int
 enum class DecAct : int { F16 = 0, NormFix = 1, SwiGLUFix = 2, AttnMerge = 3 };
 enum class DecOut : int { FixAdd = 0, Logits = 1 };
 
-template <int NB, DecAct AM, DecOut OM>
+// ROLE only separates launches in profiles (the gate/up projection gets its
+// own symbol); it does not change the code.
+template <int NB, DecAct AM, DecOut OM, int ROLE>
 __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
   constexpr int BT = 16 * NB;
   __shared__ f16 s_act[BT][CH + 8];
-  __shared__ float s_inv[BT];
-  __shared__ float s_c[(AM == DecAct::AttnMerge) ? BT * (CH / 32 + 1) * MERGE_MAX_S : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, g = lane >> 4;
   const int nblk = blockIdx.x, split = blockIdx.y;
@@ -175,32 +175,44 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
   };
   load_w(k0);
 
+  // NormFix: the whole normalised row (1 or 2 rows) is built once in LDS.
+  // Every thread loads its share of the row and of the norm weight up front
+  // (one memory round trip), then one block reduction gives 1/rms.
+  constexpr int NF_ROWS = 2, NF_PER = 16;     // rows, values per thread (K <= 4096)
+  __shared__ f16 s_row[(AM == DecAct::NormFix) ? NF_ROWS : 1][(AM == DecAct::NormFix) ? 256 * NF_PER : 8];
   if constexpr (AM == DecAct::NormFix) {
-    // inverse RMS of each batch row over the whole hidden vector: every
-    // thread issues its loads up front, then one block reduction per row
-    __shared__ float s_red[4][BT];
-    for (int b = 0; b < a.M; ++b) {
-      const long long *xr = a.x_fix + (int64_t)b * a.lda;
-      constexpr int PER = 8;                  // values per thread per pass (K <= 2048 in one pass)
-      float ss = 0.f;
-      for (int c0 = 0; c0 < a.K; c0 += 256 * PER) {
-        long long v[PER];
+    __shared__ float s_red[4][NF_ROWS];
+    float xv[NF_ROWS][NF_PER], wv[NF_PER];
 #pragma unroll
-        for (int t = 0; t < PER; ++t) {
-          const int c = c0 + t * 256 + tid;
-          v[t] = c < a.K ? xr[c] : 0;
-        }
+    for (int t = 0; t < NF_PER; ++t) {
+      const int c = t * 256 + tid;
+      wv[t] = c < a.K ? a.norm_w[c] : 0.f;
+    }
 #pragma unroll
-        for (int t = 0; t < PER; ++t) {
-          const float f = from_fix(v[t]);
-          ss += f * f;
-        }
+    for (int b = 0; b < NF_ROWS; ++b)
+#pragma unroll
+      for (int t = 0; t < NF_PER; ++t) {
+        const int c = t * 256 + tid;
+        xv[b][t] = (b < a.M && c < a.K) ? from_fix(a.x_fix[(int64_t)b * a.lda + c]) : 0.f;
       }
+#pragma unroll
+    for (int b = 0; b < NF_ROWS; ++b) {
+      float ss = 0.f;
+#pragma unroll
+      for (int t = 0; t < NF_PER; ++t) ss += xv[b][t] * xv[b][t];
       ss = wave_sum(ss);
       if (lane == 0) s_red[wave][b] = ss;
     }
     __syncthreads();
-    if (tid < a.M) s_inv[tid] = 1.0f / sqrtf((s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid]) / (float)a.K + a.eps);
+#pragma unroll
+    for (int b = 0; b < NF_ROWS; ++b) {
+      const float inv = 1.0f / sqrtf((s_red[0][b] + s_red[1][b] + s_red[2][b] + s_red[3][b]) / (float)a.K + a.eps);
+#pragma unroll
+      for (int t = 0; t < NF_PER; ++t) {
+        const int c = t * 256 + tid;
+        if (c < a.K) s_row[b][c] = (f16)(xv[b][t] * inv * wv[t]);
+      }
+    }
     __syncthreads();
   }
 
@@ -213,35 +225,37 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
     if (kc != k0) __syncthreads();            // the previous chunk's LDS reads are done
     // ---- stage act[b][kc .. kc + ck) for b < M
     if constexpr (AM == DecAct::AttnMerge) {
-      // per (b, head) merge weights of the split-KV partials, normalised
+      // merge of the split-KV partials: each element loads its head's S
+      // (max, sum) pairs and its S partial outputs together (one round trip)
       const int hd = a.head_dim, S = a.attn_splits;
-      const int hfirst = kc / hd, hlast = (kc + ck - 1) / hd;
-      const int nh = hlast - hfirst + 1;
-      for (int p = tid; p < a.M * nh; p += 256) {
-        const int b = p / nh, hh = p % nh, h = hfirst + hh;
-        const float *pm = a.part_m + ((int64_t)b * a.n_heads + h) * S;
-        const float *pl = a.part_l + ((int64_t)b * a.n_heads + h) * S;
-        float M = -INFINITY;
-        for (int s = 0; s < S; ++s) M = fmaxf(M, pm[s]);
-        float L = 0.f;
-        float *c = s_c + (b * (CH / 32 + 1) + hh) * MERGE_MAX_S;
-        for (int s = 0; s < S; ++s) {
-          const float cs = (pm[s] == -INFINITY) ? 0.f : exp2f(pm[s] - M);
-          c[s] = cs;
-          L += cs * pl[s];
-        }
-        const float inv = 1.0f / L;
-        for (int s = 0; s < S; ++s) c[s] *= inv;
-      }
-      __syncthreads();
+#pragma unroll 2
       for (int e = tid; e < a.M * ck; e += 256) {
         const int b = e / ck, kk = e % ck, k = kc + kk;
-        const int h = k / hd, d = k % hd, hh = h - hfirst;
-        const float *c = s_c + (b * (CH / 32 + 1) + hh) * MERGE_MAX_S;
-        const float *po = a.part_o + (((int64_t)b * a.n_heads + h) * S) * hd + d;
-        float v = 0.f;
-        for (int s = 0; s < S; ++s) v = fmaf(c[s], po[(int64_t)s * hd], v);
-        s_act[b][kk] = (f16)v;
+        const int h = k / hd, d = k % hd;
+        const int64_t st0 = ((int64_t)b * a.n_heads + h) * S;
+        float pm[MERGE_MAX_S], pl[MERGE_MAX_S], po[MERGE_MAX_S];
+#pragma unroll
+        for (int sp = 0; sp < MERGE_MAX_S; ++sp) {
+          if (sp < S) {
+            pm[sp] = a.part_m[st0 + sp];
+            pl[sp] = a.part_l[st0 + sp];
+            po[sp] = a.part_o[(st0 + sp) * hd + d];
+          }
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int sp = 0; sp < MERGE_MAX_S; ++sp)
+          if (sp < S) M = fmaxf(M, pm[sp]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < MERGE_MAX_S; ++sp) {
+          if (sp < S) {
+            const float c = (pm[sp] == -INFINITY) ? 0.f : exp2f(pm[sp] - M);
+            L = fmaf(c, pl[sp], L);
+            O = fmaf(c, po[sp], O);
+          }
+        }
+        s_act[b][kk] = (f16)(O / L);
       }
     } else if constexpr (AM == DecAct::F16) {
       for (int e = tid; e < a.M * (ck >> 3); e += 256) {
@@ -249,10 +263,7 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
         *reinterpret_cast<f16x8 *>(&s_act[b][kk]) = load8((const f16 *)a.act + (int64_t)b * a.lda + kc + kk);
       }
     } else if constexpr (AM == DecAct::NormFix) {
-      for (int e = tid; e < a.M * ck; e += 256) {
-        const int b = e / ck, kk = e % ck;
-        s_act[b][kk] = (f16)(from_fix(a.x_fix[(int64_t)b * a.lda + kc + kk]) * s_inv[b] * a.norm_w[kc + kk]);
-      }
+      // operand already in s_row
     } else {
       // features kc + kk; gate and up of feature f sit in GU_BLOCK-interleaved rows
       for (int e = tid; e < a.M * ck; e += 256) {
@@ -275,7 +286,9 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int b = nb * 16 + i;
-          const f16x8 x = (b < a.M) ? *reinterpret_cast<const f16x8 *>(&s_act[b][32 * t + 8 * g]) : zero;
+          const f16 *src = (AM == DecAct::NormFix) ? &s_row[b < NF_ROWS ? b : 0][kc + 32 * t + 8 * g]
+                                                   : &s_act[b][32 * t + 8 * g];
+          const f16x8 x = (b < a.M) ? *reinterpret_cast<const f16x8 *>(src) : zero;
           acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wc[t], x, acc[nb], 0, 0, 0);
         }
       }
@@ -338,23 +351,28 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
   }
 }
 
-template <int NB>
-hipError_t launch_gemv_nb(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
+template <int NB, int ROLE>
+hipError_t launch_gemv_role(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
   const DecAct am = (DecAct)a.act_mode;
   if (a.logits_mode) {
     if (am == DecAct::NormFix)
-      dec_gemv_kernel<NB, DecAct::NormFix, DecOut::Logits><<<grid, 256, 0, s>>>(a);
+      QW_LAUNCH((dec_gemv_kernel<NB, DecAct::NormFix, DecOut::Logits, ROLE>), dim3(grid), dim3(256), 0, s, a);
     else
-      dec_gemv_kernel<NB, DecAct::F16, DecOut::Logits><<<grid, 256, 0, s>>>(a);
+      QW_LAUNCH((dec_gemv_kernel<NB, DecAct::F16, DecOut::Logits, ROLE>), dim3(grid), dim3(256), 0, s, a);
   } else {
     switch (am) {
-      case DecAct::F16: dec_gemv_kernel<NB, DecAct::F16, DecOut::FixAdd><<<grid, 256, 0, s>>>(a); break;
-      case DecAct::NormFix: dec_gemv_kernel<NB, DecAct::NormFix, DecOut::FixAdd><<<grid, 256, 0, s>>>(a); break;
-      case DecAct::SwiGLUFix: dec_gemv_kernel<NB, DecAct::SwiGLUFix, DecOut::FixAdd><<<grid, 256, 0, s>>>(a); break;
-      case DecAct::AttnMerge: dec_gemv_kernel<NB, DecAct::AttnMerge, DecOut::FixAdd><<<grid, 256, 0, s>>>(a); break;
+      case DecAct::F16: QW_LAUNCH((dec_gemv_kernel<NB, DecAct::F16, DecOut::FixAdd, ROLE>), dim3(grid), dim3(256), 0, s, a); break;
+      case DecAct::NormFix: QW_LAUNCH((dec_gemv_kernel<NB, DecAct::NormFix, DecOut::FixAdd, ROLE>), dim3(grid), dim3(256), 0, s, a); break;
+      case DecAct::SwiGLUFix: QW_LAUNCH((dec_gemv_kernel<NB, DecAct::SwiGLUFix, DecOut::FixAdd, ROLE>), dim3(grid), dim3(256), 0, s, a); break;
+      case DecAct::AttnMerge: QW_LAUNCH((dec_gemv_kernel<NB, DecAct::AttnMerge, DecOut::FixAdd, ROLE>), dim3(grid), dim3(256), 0, s, a); break;
     }
   }
   return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_gemv_nb(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
+  return a.role_gate_up ? launch_gemv_role<NB, 1>(s, a, grid) : launch_gemv_role<NB, 0>(s, a, grid);
 }
 
 // ---------------------------------------------------------------- attention
@@ -473,29 +491,70 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
   };
 
   if (nh > 0) {
-    const int kc_end = min(kb1, pos);               // cached keys of this split
-    for (int kb = kb0 + (KEYPAR ? wave * KPW : 0); kb < kc_end; kb += 2 * KSTEP) {
-      const int t0 = kb + slot, t1 = kb + KSTEP + slot;
-      f16x8 k0 = {}, v0 = {}, k1v = {}, v1 = {};
-      if (t0 < kc_end) {
-        k0 = load8(Kc + (int64_t)t0 * HD + d0);
-        v0 = load8(Vc + (int64_t)t0 * HD + d0);
-      }
-      if (t1 < kc_end) {
-        k1v = load8(Kc + (int64_t)t1 * HD + d0);
-        v1 = load8(Vc + (int64_t)t1 * HD + d0);
-      }
-      if (t0 < kc_end) {
-        float kf[8], vf[8];
+    // cached keys of this split, U loads per lane in flight: the next batch
+    // is issued before the current one is consumed
+    constexpr int U = 4;
+    const int kc_end = min(kb1, pos);
+    const int kstart = kb0 + (KEYPAR ? wave * KPW : 0);
+    f16x8 kr[U], vr[U];
+    auto issue = [&](int kb) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { kf[e] = (float)k0[e]; vf[e] = (float)v0[e]; }
-        visit(kf, vf);
+      for (int u = 0; u < U; ++u) {
+        const int t = kb + u * KSTEP + slot;
+        if (t < kc_end) {
+          kr[u] = load8(Kc + (int64_t)t * HD + d0);
+          vr[u] = load8(Vc + (int64_t)t * HD + d0);
+        } else {
+          // out-of-range keys get weight 0; their values must be finite
+          kr[u] = f16x8{};
+          vr[u] = f16x8{};
+        }
       }
-      if (t1 < kc_end) {
-        float kf[8], vf[8];
+    };
+    if (kstart < kc_end) issue(kstart);
+    for (int kb = kstart; kb < kc_end; kb += U * KSTEP) {
+      f16x8 kc[U], vc[U];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { kf[e] = (float)k1v[e]; vf[e] = (float)v1[e]; }
-        visit(kf, vf);
+      for (int u = 0; u < U; ++u) {
+        kc[u] = kr[u];
+        vc[u] = vr[u];
+      }
+      if (kb + U * KSTEP < kc_end) issue(kb + U * KSTEP);
+      // the U keys of this lane at once: one running-max update and one
+      // rescale per batch instead of per key
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) ok[u] = kb + u * KSTEP + slot < kc_end;
+#pragma unroll
+      for (int t = 0; t < WH; ++t) {
+        float sc[U];
+        float mx = m[t];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d = fmaf(q[t][e], (float)kc[u][e], d);
+#pragma unroll
+          for (int off = LPK / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+          sc[u] = ok[u] ? d : -INFINITY;
+          mx = fmaxf(mx, sc[u]);
+        }
+        const float corr = (m[t] == -INFINITY) ? 0.f : exp2f(m[t] - mx);
+        float lsum = 0.f;
+        float acc8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc8[e] = o[t][e] * corr;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float p = (mx == -INFINITY) ? 0.f : exp2f(sc[u] - mx);
+          lsum += p;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc8[e] = fmaf(p, (float)vc[u][e], acc8[e]);
+        }
+        l[t] = l[t] * corr + lsum;
+        m[t] = mx;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[t][e] = acc8[e];
       }
     }
     if (has_new && (KEYPAR ? wave == 0 : true) && slot == 0) {
@@ -595,9 +654,9 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
 template <int HD, int G>
 hipError_t launch_attn_g(hipStream_t s, const DecAttnArgs &a, dim3 grid) {
   if (a.head_parallel && G > 1)
-    dec_attn_kernel<HD, G, (G + 3) / 4><<<grid, 256, 0, s>>>(a);
+    QW_LAUNCH((dec_attn_kernel<HD, G, (G + 3) / 4>), dim3(grid), dim3(256), 0, s, a);
   else
-    dec_attn_kernel<HD, G, G><<<grid, 256, 0, s>>>(a);
+    QW_LAUNCH((dec_attn_kernel<HD, G, G>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -628,8 +687,8 @@ int dec_gemv_splits(int N, int K, int M, int target_groups) {
   const int units = K / 32;
   int splits = (target_groups + nblk - 1) / nblk;
   int max_splits = (units + 3) / 4;            // at least 128 k per slice
-  // keep the atomic traffic (8 bytes per output per slice) under ~1/8 of the weight bytes
-  const int atomic_cap = (K * 2) / (8 * 8 * (M < 1 ? 1 : M));
+  // keep the atomic traffic (8 bytes per output per slice) under the weight bytes
+  const int atomic_cap = (K * 2) / (8 * (M < 1 ? 1 : M));
   if (atomic_cap >= 1 && max_splits > atomic_cap) max_splits = atomic_cap;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -647,18 +706,18 @@ int dec_attn_splits(int batch, int n_kv_heads, int max_seq, int target_groups) {
 
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
                             long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1) {
-  dec_embed_kernel<<<B, 256, 0, s>>>(ids, (const f16 *)emb, emb_scale, H, V, x_fix, bad, clr0, n0, clr1, n1);
+  QW_LAUNCH((dec_embed_kernel), dim3(B), dim3(256), 0, s, ids, (const f16 *)emb, emb_scale, H, V, x_fix, bad, clr0, n0, clr1, n1);
   return hipGetLastError();
 }
 
 hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int B, int H, const float *w, float eps, void *u) {
-  dec_norm_kernel<<<B, 256, 0, s>>>(x_fix, H, w, eps, (f16 *)u);
+  QW_LAUNCH((dec_norm_kernel), dim3(B), dim3(256), 0, s, x_fix, H, w, eps, (f16 *)u);
   return hipGetLastError();
 }
 
 hipError_t launch_dec_end(hipStream_t s, const float *arg_v, const int *arg_i, int nblk, int B, int32_t *next,
                           int *pos_dev) {
-  dec_end_kernel<<<B, 256, 0, s>>>(arg_v, arg_i, nblk, next, pos_dev);
+  QW_LAUNCH((dec_end_kernel), dim3(B), dim3(256), 0, s, arg_v, arg_i, nblk, next, pos_dev);
   return hipGetLastError();
 }
 

@@ -90,9 +90,9 @@ hipError_t launch_gemm_generic(hipStream_t s, bool f16_mode, const GemmArgs &a) 
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   dim3 grid((a.N + TN - 1) / TN, (a.M + TM - 1) / TM);
   if (f16_mode)
-    gemm_generic_kernel<f16><<<grid, 256, 0, s>>>(a);
+    QW_LAUNCH((gemm_generic_kernel<f16>), dim3(grid), dim3(256), 0, s, a);
   else
-    gemm_generic_kernel<float><<<grid, 256, 0, s>>>(a);
+    QW_LAUNCH((gemm_generic_kernel<float>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

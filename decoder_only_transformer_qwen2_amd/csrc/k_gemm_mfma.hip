@@ -7,6 +7,11 @@
 // the fp32 residual stream, or silu(gate) * up over the GU_BLOCK-interleaved
 // gate/up rows.
 //
+// Few output tiles (short prompts) leave most of the chip idle, so K can be
+// split over gridDim.z: each slice stores its raw fp32 tile in a workspace and
+// a second kernel adds the slices in slice order (deterministic) and applies
+// the epilogue.
+//
 // Tiling: a workgroup computes a 128 x 128 tile with 4 wavefronts (2 x 2),
 // each a 64 x 64 sub-tile = 4 x 4 MFMA tiles of 16 x 16.  K advances 64 at a
 // time; both operand tiles are staged in LDS (rows padded by 16 bytes so the
@@ -65,13 +70,18 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = (a.K + BK - 1) / BK;
-  gload(0);
+  // K range of this slice (whole BK tiles)
+  const int KT_all = (a.K + BK - 1) / BK;
+  const int kt_per = (KT_all + gridDim.z - 1) / gridDim.z;
+  const int kt0 = blockIdx.z * kt_per;
+  const int KT = max(0, min(KT_all, kt0 + kt_per) - kt0);
+  const int kbase = kt0 * BK;
+  gload(kbase);
   lstore(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
+    if (kt + 1 < KT) gload(kbase + (kt + 1) * BK);
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 32) {
       f16x8 fa[4], fb[4];
@@ -91,6 +101,22 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
   }
 
   // acc[x][y]: lane (i, g) holds rows 4g..4g+3 of column i of MFMA tile (x, y)
+  if (gridDim.z > 1) {
+    float *ws = a.ws + (int64_t)blockIdx.z * a.M * a.N;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int col = n0 + wn * 64 + y * 16 + i;
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + wm * 64 + x * 16 + 4 * g + r;
+          if (row < a.M) ws[(int64_t)row * a.N + col] = acc[x][y][r];
+        }
+      }
+    return;
+  }
   if constexpr (EPI == Epi::SwiGLU) {
     // the wave's 64 columns are two (gate block, up block) pairs: y = 0/1 and 2/3
     f16 *out = (f16 *)a.act_out;
@@ -130,7 +156,46 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
   }
 }
 
+// out = epilogue(sum over slices of ws[slice]), one thread per output value
+template <Epi EPI>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a, int S) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t slice = (int64_t)a.M * a.N;
+  if constexpr (EPI == Epi::SwiGLU) {
+    const int F = a.N / 2;
+    if (idx >= (int64_t)a.M * F) return;
+    const int row = (int)(idx / F), f = (int)(idx % F);
+    const int cg = (f / GU_BLOCK) * 2 * GU_BLOCK + f % GU_BLOCK;
+    float gt = 0.f, up = 0.f;
+    for (int z = 0; z < S; ++z) {
+      gt += a.ws[z * slice + (int64_t)row * a.N + cg];
+      up += a.ws[z * slice + (int64_t)row * a.N + cg + GU_BLOCK];
+    }
+    ((f16 *)a.act_out)[(int64_t)row * a.ldo + f] = (f16)(silu_f(gt * a.scale) * (up * a.scale));
+  } else {
+    if (idx >= slice) return;
+    const int row = (int)(idx / a.N), col = (int)(idx % a.N);
+    float v = 0.f;
+    for (int z = 0; z < S; ++z) v += a.ws[z * slice + idx];
+    float *o = a.out_f32 + (int64_t)row * a.ldo + col;
+    if constexpr (EPI == Epi::ResidAdd)
+      *o += v * a.scale;
+    else
+      *o = v * a.scale;
+  }
+}
+
 }  // namespace
+
+int gemm_mfma_splits(int M, int N, int K) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles >= 128) return 1;
+  int S = (256 + tiles - 1) / tiles;
+  const int max_s = ((K + BK - 1) / BK) / 2;     // at least two K tiles per slice
+  if (S > max_s) S = max_s;
+  if (S > 16) S = 16;
+  return S < 1 ? 1 : S;
+}
 
 bool gemm_mfma_supported(const GemmArgs &a) {
   return (a.K % 8) == 0 && (a.lda % 8) == 0 && (a.epi != Epi::SwiGLU || a.N % 128 == 0);
@@ -139,11 +204,21 @@ bool gemm_mfma_supported(const GemmArgs &a) {
 hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (!gemm_mfma_supported(a)) return hipErrorInvalidValue;
-  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
+  const int S = (a.splits > 1 && a.ws) ? a.splits : 1;
+  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, S);
   switch (a.epi) {
-    case Epi::StoreF32: gemm_mfma_kernel<Epi::StoreF32><<<grid, 256, 0, s>>>(a); break;
-    case Epi::ResidAdd: gemm_mfma_kernel<Epi::ResidAdd><<<grid, 256, 0, s>>>(a); break;
-    case Epi::SwiGLU: gemm_mfma_kernel<Epi::SwiGLU><<<grid, 256, 0, s>>>(a); break;
+    case Epi::StoreF32: QW_LAUNCH((gemm_mfma_kernel<Epi::StoreF32>), dim3(grid), dim3(256), 0, s, a); break;
+    case Epi::ResidAdd: QW_LAUNCH((gemm_mfma_kernel<Epi::ResidAdd>), dim3(grid), dim3(256), 0, s, a); break;
+    case Epi::SwiGLU: QW_LAUNCH((gemm_mfma_kernel<Epi::SwiGLU>), dim3(grid), dim3(256), 0, s, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t n = (a.epi == Epi::SwiGLU) ? (int64_t)a.M * (a.N / 2) : (int64_t)a.M * a.N;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  switch (a.epi) {
+    case Epi::StoreF32: splitk_reduce_kernel<Epi::StoreF32><<<blocks, 256, 0, s>>>(a, S); break;
+    case Epi::ResidAdd: splitk_reduce_kernel<Epi::ResidAdd><<<blocks, 256, 0, s>>>(a, S); break;
+    case Epi::SwiGLU: splitk_reduce_kernel<Epi::SwiGLU><<<blocks, 256, 0, s>>>(a, S); break;
   }
   return hipGetLastError();
 }

@@ -3,10 +3,29 @@
 // launcher declared here and defined next to its kernel.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qw {
+
+// Kernel-duration timing.  While `launch_timing` holds an event pair, the
+// launches of the timed kernel families pass it to hipExtLaunchKernelGGL,
+// which records the events at the start and at the end of the kernel itself
+// (no dispatch gap inside the interval), on the kernel's own stream.
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchTiming launch_timing;
+
+#define QW_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                                   \
+  do {                                                                                                     \
+    if (::qw::launch_timing.start)                                                                         \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, ::qw::launch_timing.start,                  \
+                            ::qw::launch_timing.stop, 0, __VA_ARGS__);                                     \
+    else                                                                                                   \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                                 \
+  } while (0)
 
 // Packed gate/up projection: rows of W_gate and W_up alternate in blocks of
 // GU_BLOCK rows ([g0..g15, u0..u15, g16..g31, u16..u31, ...]), so a tile of
@@ -55,6 +74,8 @@ struct GemmArgs {
   float *out_f32;       // StoreF32: [M, ldo]; ResidAdd: residual [M, ldo]
   void *act_out;        // SwiGLU: [M, ldo] compute type, ldo = N / 2
   int ldo;
+  int splits = 1;       // MFMA path: K slices (> 1 needs ws)
+  float *ws = nullptr;  // [splits, M, N] fp32 slice tiles
 };
 
 struct RopeCacheArgs {
@@ -99,6 +120,7 @@ struct DecGemvArgs {
   int units_per_split;      // set by the launcher
   long long *clear;         // side job: zero clear[0 .. clear_n) (may be NULL)
   int64_t clear_n;
+  int role_gate_up;          // 1 for the gate/up projection (separate kernel symbol in profiles)
   // LM-head mode: logits [M, ldo] (may be NULL) and per-64-row-block argmax
   int logits_mode;
   float *logits;
@@ -136,6 +158,7 @@ bool attn_prefill_supported(int head_dim);
 hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a);   // f16, prompt from position 0
 hipError_t launch_gemm_generic(hipStream_t s, bool f16_mode, const GemmArgs &a);
 bool gemm_mfma_supported(const GemmArgs &a);
+int gemm_mfma_splits(int M, int N, int K);
 hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a);     // f16 operands
 bool decode_fast_supported(int head_dim, int group, int hidden, int q_dim, int inter);
 int dec_gemv_splits(int N, int K, int M, int target_groups);

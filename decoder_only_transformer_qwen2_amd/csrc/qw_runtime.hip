@@ -27,6 +27,10 @@
 
 using namespace qw;
 
+namespace qw {
+thread_local LaunchTiming launch_timing;
+}
+
 namespace {
 
 thread_local std::string g_err;
@@ -97,6 +101,8 @@ struct qw_model {
   float *arg_v = nullptr;            // [max_batch, ceil(V / 64)]
   int *arg_i = nullptr;
   float *att_m = nullptr, *att_l = nullptr, *att_o = nullptr;   // split-KV partials
+  float *splitk_ws = nullptr;        // prefill split-K slices (grown on demand)
+  size_t splitk_bytes = 0;
   int batch = 0, pos = 0;
   // decode graph, captured against the staging rows (so caller pointers may
   // change from step to step) for the batch of the last prefill
@@ -129,9 +135,12 @@ constexpr int kAttnTargetGroups = 256;
 // workgroup reads the whole residual rows); above it a norm kernel runs.
 constexpr int kFusedNormRows = 2;
 
-// Bracket a launch of `fam` with events when timing that family.
+// While timing family `fam`, its kernel launches record an event pair at the
+// kernel's own start and end (see QW_LAUNCH); the pairs are read back by
+// qw_timing_read.
 template <class F>
 hipError_t timed(qw_model *m, hipStream_t s, Family fam, F &&launch) {
+  (void)s;
   if (m->timing_family != fam) return launch();
   std::pair<hipEvent_t, hipEvent_t> ev;
   if (!m->ev_free.empty()) {
@@ -142,9 +151,10 @@ hipError_t timed(qw_model *m, hipStream_t s, Family fam, F &&launch) {
     if (e == hipSuccess) e = hipEventCreate(&ev.second);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = hipEventRecord(ev.first, s);
-  if (e == hipSuccess) e = launch();
-  if (e == hipSuccess) e = hipEventRecord(ev.second, s);
+  launch_timing.start = ev.first;
+  launch_timing.stop = ev.second;
+  hipError_t e = launch();
+  launch_timing = LaunchTiming();
   m->ev_used.push_back(ev);
   return e;
 }
@@ -163,7 +173,27 @@ hipError_t gemm(qw_model *m, hipStream_t s, Family fam, const void *A, int M, in
   a.out_f32 = out_f32;
   a.act_out = act_out;
   a.ldo = ldo;
-  if (m->f16 && gemm_mfma_supported(a)) return timed(m, s, fam, [&] { return launch_gemm_mfma(s, a); });
+  if (m->f16 && gemm_mfma_supported(a)) {
+    const int S = gemm_mfma_splits(M, N, K);
+    if (S > 1) {
+      const size_t need = (size_t)S * M * N * 4;
+      if (need > m->splitk_bytes) {          // grow-only; the stream is synchronised before a free
+        if (m->splitk_ws) {
+          hipError_t e = hipStreamSynchronize(s);
+          if (e != hipSuccess) return e;
+          (void)hipFree(m->splitk_ws);
+        }
+        m->splitk_ws = nullptr;
+        m->splitk_bytes = 0;
+        hipError_t e = hipMalloc((void **)&m->splitk_ws, need);
+        if (e != hipSuccess) return e;
+        m->splitk_bytes = need;
+      }
+      a.splits = S;
+      a.ws = m->splitk_ws;
+    }
+    return timed(m, s, fam, [&] { return launch_gemm_mfma(s, a); });
+  }
   return timed(m, s, fam, [&] { return launch_gemm_generic(s, m->f16, a); });
 }
 
@@ -261,14 +291,14 @@ hipError_t decode_generic(qw_model *m, hipStream_t s, const int32_t *ids, int32_
   return run_head(m, s, m->x, B, c.hidden, m->logits, m->logits, B, c.vocab, next, m->pos_dev, 1);
 }
 
-DecGemvArgs dec_args(const void *W, int M, int N, int K, float scale) {
+DecGemvArgs dec_args(const void *W, int M, int N, int K, float scale, int target = kGemvTargetGroups) {
   DecGemvArgs g{};
   g.W = W;
   g.M = M;
   g.N = N;
   g.K = K;
   g.scale = scale;
-  g.splits = dec_gemv_splits(N, K, M, kGemvTargetGroups);
+  g.splits = dec_gemv_splits(N, K, M, target);
   return g;
 }
 
@@ -281,7 +311,7 @@ DecGemvArgs dec_args(const void *W, int M, int N, int K, float scale) {
 hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next) {
   const qw_config &c = m->cfg;
   const int B = m->batch, H = c.hidden, I = c.intermediate, V = c.vocab;
-  const bool fused_norm = B <= kFusedNormRows;
+  const bool fused_norm = B <= kFusedNormRows && H <= 4096;
   const int S = dec_attn_splits(B, c.n_kv_heads, c.max_seq, kAttnTargetGroups);
   const int64_t n_qkv = (int64_t)B * m->nqkv, n_gu = (int64_t)B * 2 * I;
   hipError_t e = timed(m, s, F_EMBED, [&] {
@@ -328,7 +358,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     da.part_l = m->att_l;
     da.part_o = m->att_o;
     da.splits = S;
-    da.head_parallel = B <= kFusedNormRows;
+    da.head_parallel = B <= kFusedNormRows;      // latency-bound: split the heads over the waves
     da.batch = B;
     da.n_heads = c.n_heads;
     da.n_kv_heads = c.n_kv_heads;
@@ -361,8 +391,11 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     e = timed(m, s, F_GEMM_O, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
     if ((e = norm(Lw.post_norm)) != hipSuccess) return e;
-    g = dec_args(Lw.w_gu, B, 2 * I, H, Lw.s_gu);
+    // every workgroup of a norm-fused projection re-reads the residual rows,
+    // so fewer, larger K slices pay off when there are many row blocks
+    g = dec_args(Lw.w_gu, B, 2 * I, H, Lw.s_gu, fused_norm ? kGemvTargetGroups / 2 : kGemvTargetGroups);
     normed(g, Lw.post_norm);
+    g.role_gate_up = 1;
     g.out_fix = m->gu_fix;
     g.ldo = 2 * I;
     e = timed(m, s, F_GEMM_GATE_UP, [&] { return launch_dec_gemv(s, g); });
@@ -708,6 +741,7 @@ qw_status qw_destroy(qw_model *m) {
     (void)hipEventDestroy(e.second);
   }
   for (void *p : m->allocs) (void)hipFree(p);
+  if (m->splitk_ws) (void)hipFree(m->splitk_ws);
   if (m->cap) (void)hipStreamDestroy(m->cap);
   delete m;
   return QW_OK;
