@@ -56,11 +56,26 @@ def decode_family_bytes(w: S.Workload, family: str, ctx_mean: float) -> float:
         return 2 * I * H * e + B * H * e + B * I * e
     if family == "gemm_down":
         return H * I * e + B * I * e + 2 * B * H * 4
+    if family == "mlp":   # norm + gate/up + SwiGLU + down in one launch (1-2 rows)
+        return 3 * I * H * e + B * H * 8 * 2
     if family == "lm_head":
         return V * H * e + B * H * e + B * V * 4
     if family == "attention":
         return B * m.n_kv_heads * ctx_mean * m.head_dim * e * 2 + 2 * B * qd * e
     return float("nan")
+
+
+def decode_step_bytes(w: S.Workload, ctx_mean: float) -> float:
+    """Algorithmic HBM bytes of one whole decode step: every weight once (all
+    layers and the LM head), the live K/V context of every sequence read, and
+    the new K/V rows written."""
+    m, B = w.model, w.batch
+    e = 2 if m.dtype == "bf16" else 4
+    H, I, V, qd, kvd = m.hidden, m.intermediate, m.vocab, m.q_dim, m.kv_dim
+    per_layer = H * (qd + 2 * kvd) + qd * H + 3 * H * I
+    weights = e * (m.n_layers * per_layer + V * H)
+    kv = B * m.n_layers * 2 * kvd * e * (ctx_mean + 1)
+    return weights + kv
 
 
 def prefill_family_flops(w: S.Workload, family: str) -> float:
@@ -199,8 +214,8 @@ def main():
 
     if not args.no_roofline:
         # per-family decode time, each family timed over one eager pass
-        fams = ["gemm_qkv", "rope_cache", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "lm_head", "argmax",
-                "rmsnorm", "embed"]
+        fams = ["gemm_qkv", "rope_cache", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "mlp", "lm_head",
+                "argmax", "rmsnorm", "embed"]
         per = {}
         for f in fams:
             model.prefill(ids, next_ids=toks[0])
@@ -210,7 +225,8 @@ def main():
             ms, n = model.timing_read(reset=True)
             model.timing_enable(None)
             per[f] = (ms, n)
-        dom = max((f for f in per if f in ("gemm_qkv", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "lm_head")),
+        dom = max((f for f in per if per[f][1] > 0 and f in ("gemm_qkv", "attention", "gemm_o", "gemm_gate_up",
+                                                               "gemm_down", "mlp", "lm_head")),
                   key=lambda f: per[f][0])
         ms, n = per[dom]
         avg_s = ms / n / 1e3
@@ -222,6 +238,10 @@ def main():
                            "avg_launch_us": round(avg_s * 1e6, 3), "launches": n,
                            "algorithmic_bytes_per_launch": int(bytes_per)}
         out["decode_family_ms_per_step"] = {f: round(per[f][0] / D, 4) for f in per}
+        step_gbs = decode_step_bytes(w, ctx_mean) / (decode_ms / D / 1e3) / 1e9
+        out["decode_step_roofline"] = {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                                       "bytes_per_step": int(decode_step_bytes(w, ctx_mean))}
         # prefill: per-family time over one eager prefill each
         pper = {}
         for f in ("gemm_qkv", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "rope_cache", "rmsnorm", "lm_head"):

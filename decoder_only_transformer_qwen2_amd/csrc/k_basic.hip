@@ -271,6 +271,33 @@ hipError_t launch_convert_gu(hipStream_t s, bool src_bf16, const void *gate, con
   return hipGetLastError();
 }
 
+// dst[c][r] = src[r][c] * scale for a [rows, cols] source (f16 destination):
+// the down projection's [I, H] copy that the decode MLP reads row by row.
+// 32 x 32 tiles through LDS so both sides are read and written along rows.
+__global__ void __launch_bounds__(256) convert_t_kernel(const void *src, int rows, int cols, bool bf16, f16 *dst,
+                                                        float scale) {
+  __shared__ float t[32][33];
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int y = ty; y < 32; y += 8) {
+    const int r = r0 + y, c = c0 + tx;
+    t[y][tx] = (r < rows && c < cols) ? load_src(src, (int64_t)r * cols + c, bf16) * scale : 0.f;
+  }
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8) {
+    const int c = c0 + y, r = r0 + tx;
+    if (c < cols && r < rows) dst[(int64_t)c * rows + r] = (f16)t[tx][y];
+  }
+}
+
+hipError_t launch_convert_t(hipStream_t s, bool src_bf16, const void *src, int rows, int cols, void *dst,
+                            float scale) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  dim3 grid((cols + 31) / 32, (rows + 31) / 32);
+  convert_t_kernel<<<grid, 256, 0, s>>>(src, rows, cols, src_bf16, (f16 *)dst, scale);
+  return hipGetLastError();
+}
+
 // RoPE table: entry (pos, i) = (cos, sin) of pos * theta^(-2i/hd), evaluated in
 // double and rounded once to float ("Rotary Positional Embeddings RoPE").
 __global__ void __launch_bounds__(256) rope_table_kernel(float2 *table, int max_seq, int head_dim, double theta) {

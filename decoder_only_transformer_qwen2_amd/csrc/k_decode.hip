@@ -79,8 +79,8 @@ __global__ void __launch_bounds__(256) dec_embed_kernel(const int32_t *ids, cons
 
 // u[b] = f16(x[b] / sqrt(mean(x[b]^2) + eps) * w): used when the batch is too
 // large for the projections to normalise their own operand.
-__global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, int H, const float *w, float eps,
-                                                       f16 *u) {
+__global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, int reps, int64_t rep_stride, int H,
+                                                       const float *w, float eps, f16 *u) {
   const int b = blockIdx.x;
   __shared__ float red[4];
   const long long *xr = x_fix + (int64_t)b * H;
@@ -92,6 +92,12 @@ __global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, i
       const int c = c0 + t * 256 + threadIdx.x;
       v[t] = c < H ? xr[c] : 0;
     }
+    for (int r = 1; r < reps; ++r)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int c = c0 + t * 256 + threadIdx.x;
+        if (c < H) v[t] += xr[r * rep_stride + c];
+      }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float f = from_fix(v[t]);
@@ -103,7 +109,11 @@ __global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, i
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int c = threadIdx.x; c < H; c += 256) u[(int64_t)b * H + c] = (f16)(from_fix(xr[c]) * inv * w[c]);
+  for (int c = threadIdx.x; c < H; c += 256) {
+    long long q = xr[c];
+    for (int r = 1; r < reps; ++r) q += xr[r * rep_stride + c];
+    u[(int64_t)b * H + c] = (f16)(from_fix(q) * inv * w[c]);
+  }
 }
 
 // Reduce the LM head's per-block (max, index) pairs: lowest index among equal
@@ -188,13 +198,26 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
       const int c = t * 256 + tid;
       wv[t] = c < a.K ? a.norm_w[c] : 0.f;
     }
+    long long q[NF_ROWS][NF_PER];
 #pragma unroll
     for (int b = 0; b < NF_ROWS; ++b)
 #pragma unroll
       for (int t = 0; t < NF_PER; ++t) {
         const int c = t * 256 + tid;
-        xv[b][t] = (b < a.M && c < a.K) ? from_fix(a.x_fix[(int64_t)b * a.lda + c]) : 0.f;
+        q[b][t] = (b < a.M && c < a.K) ? a.x_fix[(int64_t)b * a.lda + c] : 0;
       }
+    for (int r = 1; r < a.x_reps; ++r)
+#pragma unroll
+      for (int b = 0; b < NF_ROWS; ++b)
+#pragma unroll
+        for (int t = 0; t < NF_PER; ++t) {
+          const int c = t * 256 + tid;
+          if (b < a.M && c < a.K) q[b][t] += a.x_fix[r * a.x_rep_stride + (int64_t)b * a.lda + c];
+        }
+#pragma unroll
+    for (int b = 0; b < NF_ROWS; ++b)
+#pragma unroll
+      for (int t = 0; t < NF_PER; ++t) xv[b][t] = from_fix(q[b][t]);
 #pragma unroll
     for (int b = 0; b < NF_ROWS; ++b) {
       float ss = 0.f;
@@ -375,6 +398,169 @@ hipError_t launch_gemv_nb(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
   return a.role_gate_up ? launch_gemv_role<NB, 1>(s, a, grid) : launch_gemv_role<NB, 0>(s, a, grid);
 }
 
+// ---------------------------------------------------------------- fused MLP
+// For one or two rows the MLP of a layer ("LLM Speedrun: Architecture",
+// "But how does it remember things?": gated SiLU MLP) is a single kernel:
+//   x_out = x_in + W_down (silu(W_gate u) * (W_up u)),  u = RMSNorm(x_in) * w.
+// Workgroup p owns the GU_BLOCK intermediate features f0 = 16p .. 16p + 15.
+// It forms their gate and up values over the whole hidden width (MFMA, the
+// four waves split K and meet in LDS), applies SwiGLU, and multiplies the 16
+// values into rows f0 .. f0 + 15 of the transposed down weight, adding the H
+// results per row into x_out.  The down projection is thus split over its K
+// (= I) across the workgroups and needs neither a launch nor a buffer of its
+// own.  x_in and x_out are different buffers, so no workgroup reads a value
+// that another one is adding to; workgroup 0 also adds x_in itself (exactly,
+// in fixed point), so x_out must be zero on entry.  Every weight load of the
+// workgroup is issued before the norm prologue.
+constexpr int MLP_F = GU_BLOCK;
+
+template <int NR, int KU>
+__global__ void __launch_bounds__(256) dec_mlp_kernel(DecMlpArgs a) {
+  constexpr int NPER = 8;                       // residual values per thread (H <= 2048)
+  // normalised rows (f16) during gate/up, then the down results (fp32)
+  __shared__ float s_buf[NR * 256 * NPER];
+  f16 (*s_row)[256 * NPER] = reinterpret_cast<f16 (*)[256 * NPER]>(s_buf);
+  __shared__ float s_red[4][NR];
+  __shared__ float s_gu[4][2][NR][MLP_F];
+  __shared__ float s_h[NR][MLP_F];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int p = blockIdx.x, f0 = p * MLP_F;
+  const int H = a.H;
+  const f16x8 zero = {};
+
+  // gate row f0 + i and up row f0 + i (packed rows 2 f0 + i and 2 f0 + 16 + i);
+  // wave w covers k in [w H / 4, (w + 1) H / 4)
+  const f16 *Wg = (const f16 *)a.w_gu + (int64_t)(2 * f0 + i) * H;
+  const f16 *Wu = Wg + (int64_t)GU_BLOCK * H;
+  const int ku = H / 128;
+  const int kw0 = wave * ku * 32;
+  f16x8 wg[KU], wu[KU];
+#pragma unroll
+  for (int t = 0; t < KU; ++t) {
+    const bool ok = t < ku;
+    const int k = kw0 + 32 * t + 8 * g;
+    wg[t] = ok ? load8(Wg + k) : zero;
+    wu[t] = ok ? load8(Wu + k) : zero;
+  }
+  // down weights: rows f0 .. f0 + 15 of W_down^T, columns n .. n + 7
+  const int n = 8 * tid;
+  const bool n_ok = n < H;
+  const f16 *Wd = (const f16 *)a.w_down_t + (int64_t)f0 * H + (n_ok ? n : 0);
+  f16x8 wd[MLP_F];
+#pragma unroll
+  for (int f = 0; f < MLP_F; ++f) wd[f] = n_ok ? load8(Wd + (int64_t)f * H) : zero;
+
+  // u = RMSNorm(x_in) * w into LDS (one round trip, one block reduction);
+  // x_in is the sum of its replicas (exact, in fixed point)
+  long long xq[NR][NPER];
+  {
+    float xv[NR][NPER], wv[NPER];
+#pragma unroll
+    for (int t = 0; t < NPER; ++t) {
+      const int c = t * 256 + tid;
+      wv[t] = c < H ? a.norm_w[c] : 0.f;
+#pragma unroll
+      for (int b = 0; b < NR; ++b) xq[b][t] = c < H ? a.x_in[(int64_t)b * H + c] : 0;
+    }
+    for (int r = 1; r < a.reps; ++r)
+#pragma unroll
+      for (int t = 0; t < NPER; ++t) {
+        const int c = t * 256 + tid;
+#pragma unroll
+        for (int b = 0; b < NR; ++b)
+          if (c < H) xq[b][t] += a.x_in[r * a.rep_stride + (int64_t)b * H + c];
+      }
+#pragma unroll
+    for (int t = 0; t < NPER; ++t)
+#pragma unroll
+      for (int b = 0; b < NR; ++b) xv[b][t] = from_fix(xq[b][t]);
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      float ss = 0.f;
+#pragma unroll
+      for (int t = 0; t < NPER; ++t) ss += xv[b][t] * xv[b][t];
+      ss = wave_sum(ss);
+      if (lane == 0) s_red[wave][b] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      const float inv = 1.0f / sqrtf((s_red[0][b] + s_red[1][b] + s_red[2][b] + s_red[3][b]) / (float)H + a.eps);
+#pragma unroll
+      for (int t = 0; t < NPER; ++t) {
+        const int c = t * 256 + tid;
+        if (c < H) s_row[b][c] = (f16)(xv[b][t] * inv * wv[t]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // gate and up sums of this wave's K quarter: lane (i, g) gets features
+  // f0 + 4g .. f0 + 4g + 3 of row i
+  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < KU; ++t) {
+    if (t < ku) {
+      const f16x8 x = (i < NR) ? *reinterpret_cast<const f16x8 *>(&s_row[i < NR ? i : 0][kw0 + 32 * t + 8 * g]) : zero;
+      ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wg[t], x, ag, 0, 0, 0);
+      au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wu[t], x, au, 0, 0, 0);
+    }
+  }
+  if (i < NR) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s_gu[wave][0][i][4 * g + r] = ag[r];
+      s_gu[wave][1][i][4 * g + r] = au[r];
+    }
+  }
+  __syncthreads();
+  if (tid < NR * MLP_F) {
+    const int b = tid / MLP_F, f = tid % MLP_F;
+    const float gt = (s_gu[0][0][b][f] + s_gu[1][0][b][f] + s_gu[2][0][b][f] + s_gu[3][0][b][f]) * a.gu_scale;
+    const float up = (s_gu[0][1][b][f] + s_gu[1][1][b][f] + s_gu[2][1][b][f] + s_gu[3][1][b][f]) * a.gu_scale;
+    s_h[b][f] = silu_f(gt) * up;
+  }
+  __syncthreads();
+
+  // down: y[b][n .. n + 7] = sum_f h[b][f] * W_down^T[f0 + f][n .. n + 7] into
+  // LDS (reusing the normalised rows' space), then one atomic per value with
+  // consecutive lanes on consecutive addresses
+  float *s_y = s_buf;                                       // [NR][H], H <= 2048
+  __syncthreads();                                          // the MFMA reads of s_row are done
+  if (n_ok) {
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < MLP_F; ++f) {
+        const float hf = s_h[b][f];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = fmaf(hf, (float)wd[f][e], y[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_y[b * H + n + e] = y[e] * a.down_scale;
+    }
+  }
+  __syncthreads();
+  // workgroups start their adds at different 64-column blocks (rotating by
+  // p), so the atomics arriving at one address at a time come from few
+  // workgroups; workgroup 0 starts at column 0, where its xq values line up
+  long long *xo = a.x_out + (p % a.reps) * a.rep_stride;
+  const int rot = 64 * (p % (H / 64));
+#pragma unroll
+  for (int b = 0; b < NR; ++b)
+#pragma unroll
+    for (int t = 0; t < NPER; ++t) {
+      const int cl = t * 256 + tid;
+      if (cl < H) {
+        const int c = (cl + rot) % H;
+        const long long v = to_fix(s_y[b * H + c]) + (p == 0 ? xq[b][t] : 0);
+        atomicAdd(reinterpret_cast<unsigned long long *>(xo + (int64_t)b * H + c), (unsigned long long)v);
+      }
+    }
+}
+
 // ---------------------------------------------------------------- attention
 // grid (split, kv head j, sequence b), 256 threads.  Prologue: the group's g
 // query heads and the new k and v from the fixed-point q/k/v sums + bias,
@@ -415,6 +601,36 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
   const int kb1 = min(n_keys, kb0 + per);
   const bool has_new = kb0 <= pos && pos < kb1;
 
+  // the heads this wave carries: h_lo + t for t < nh
+  const int h_lo = KEYPAR ? 0 : wave * WH;
+  const int nh = KEYPAR ? G : max(0, min(WH, G - h_lo));
+  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
+  f16 *Kc = (f16 *)a.k_cache + head_base;
+  f16 *Vc = (f16 *)a.v_cache + head_base;
+
+  // cached keys of this split, U loads per lane in flight: the first batch
+  // goes out before the prologue (it does not depend on it), each next batch
+  // before the current one is consumed
+  constexpr int U = 4;
+  const int kc_end = min(kb1, pos);
+  const int kstart = kb0 + (KEYPAR ? wave * KPW : 0);
+  f16x8 kr[U], vr[U];
+  auto issue = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = kb + u * KSTEP + slot;
+      if (t < kc_end) {
+        kr[u] = load8(Kc + (int64_t)t * HD + d0);
+        vr[u] = load8(Vc + (int64_t)t * HD + d0);
+      } else {
+        // out-of-range keys get weight 0; their values must be finite
+        kr[u] = f16x8{};
+        vr[u] = f16x8{};
+      }
+    }
+  };
+  if (nh > 0 && kstart < kc_end) issue(kstart);
+
   const int nq = a.n_kv_heads * G;
   const int qd = nq * HD, kvd = a.n_kv_heads * HD;
   const int ncols = qd + 2 * kvd;
@@ -447,17 +663,11 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
     }
   }
   __syncthreads();
-  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
-  f16 *Kc = (f16 *)a.k_cache + head_base;
-  f16 *Vc = (f16 *)a.v_cache + head_base;
   if (has_new && tid < HD) {
     Kc[(int64_t)pos * HD + tid] = (f16)s_k[tid];
     Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
   }
 
-  // the heads this wave carries: h_lo + t for t < nh
-  const int h_lo = KEYPAR ? 0 : wave * WH;
-  const int nh = KEYPAR ? G : max(0, min(WH, G - h_lo));
   float q[WH][8];
 #pragma unroll
   for (int t = 0; t < WH; ++t)
@@ -491,27 +701,6 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
   };
 
   if (nh > 0) {
-    // cached keys of this split, U loads per lane in flight: the next batch
-    // is issued before the current one is consumed
-    constexpr int U = 4;
-    const int kc_end = min(kb1, pos);
-    const int kstart = kb0 + (KEYPAR ? wave * KPW : 0);
-    f16x8 kr[U], vr[U];
-    auto issue = [&](int kb) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = kb + u * KSTEP + slot;
-        if (t < kc_end) {
-          kr[u] = load8(Kc + (int64_t)t * HD + d0);
-          vr[u] = load8(Vc + (int64_t)t * HD + d0);
-        } else {
-          // out-of-range keys get weight 0; their values must be finite
-          kr[u] = f16x8{};
-          vr[u] = f16x8{};
-        }
-      }
-    };
-    if (kstart < kc_end) issue(kstart);
     for (int kb = kstart; kb < kc_end; kb += U * KSTEP) {
       f16x8 kc[U], vc[U];
 #pragma unroll
@@ -677,6 +866,29 @@ hipError_t launch_attn_hd(hipStream_t s, const DecAttnArgs &a, dim3 grid, int g)
 
 }  // namespace
 
+bool dec_mlp_supported(int hidden, int inter) {
+  return hidden % 128 == 0 && hidden <= 2048 && inter % MLP_F == 0;
+}
+
+hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a) {
+  if (!dec_mlp_supported(a.H, a.I) || a.M < 1 || a.M > 2 || a.reps < 1 || a.reps > kMaxXReps)
+    return hipErrorInvalidValue;
+  const dim3 grid(a.I / MLP_F);
+  const bool small = a.H <= 1024;
+  if (a.M == 1) {
+    if (small)
+      QW_LAUNCH((dec_mlp_kernel<1, 8>), dim3(grid), dim3(256), 0, s, a);
+    else
+      QW_LAUNCH((dec_mlp_kernel<1, 16>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (small)
+      QW_LAUNCH((dec_mlp_kernel<2, 8>), dim3(grid), dim3(256), 0, s, a);
+    else
+      QW_LAUNCH((dec_mlp_kernel<2, 16>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 bool decode_fast_supported(int head_dim, int group, int hidden, int q_dim, int inter) {
   return (head_dim == 32 || head_dim == 64 || head_dim == 128) && group >= 1 && group <= 8 && hidden % 32 == 0 &&
          q_dim % 32 == 0 && inter % GU_BLOCK == 0;
@@ -710,8 +922,9 @@ hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void
   return hipGetLastError();
 }
 
-hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int B, int H, const float *w, float eps, void *u) {
-  QW_LAUNCH((dec_norm_kernel), dim3(B), dim3(256), 0, s, x_fix, H, w, eps, (f16 *)u);
+hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int reps, int64_t rep_stride, int B, int H,
+                           const float *w, float eps, void *u) {
+  QW_LAUNCH((dec_norm_kernel), dim3(B), dim3(256), 0, s, x_fix, reps, rep_stride, H, w, eps, (f16 *)u);
   return hipGetLastError();
 }
 

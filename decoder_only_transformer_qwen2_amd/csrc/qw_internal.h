@@ -106,7 +106,9 @@ struct DecGemvArgs {
   int act_mode;             // 0: f16 act; 1: RMSNorm of x_fix; 2: silu(gate)*up of act_fix;
                             // 3: merge of split-KV attention partials
   const void *act;          // mode 0: [M, lda] f16
-  const long long *x_fix;   // mode 1: [M, lda] fixed-point residual rows (lda = K)
+  const long long *x_fix;   // mode 1: [M, lda] fixed-point residual rows (lda = K), stored as
+  int x_reps;               //   x_reps replicas x_rep_stride apart whose sum is the value
+  int64_t x_rep_stride;     //   (x_reps <= kMaxXReps; 0 is taken as 1)
   const float *norm_w;      // mode 1: [K]
   float eps;                // mode 1
   const long long *act_fix; // mode 2: [M, lda] fixed-point gate/up sums (lda = 2K)
@@ -145,6 +147,29 @@ struct DecAttnArgs {
   int64_t clear_n;
 };
 
+// The decode residual stream may be kept as up to this many fixed-point
+// replicas whose sum is the value: writers that would otherwise all add into
+// the same addresses spread their atomics over the replicas.
+constexpr int kMaxXReps = 8;
+
+// Decode-step MLP for one or two rows, see k_decode.hip:
+//   x_out = x_in + W_down . (silu(W_gate u) * (W_up u)),  u = RMSNorm(x_in) * norm_w
+// x_out must be zero on entry (workgroup 0 adds x_in itself).
+struct DecMlpArgs {
+  const long long *x_in;             // [reps][M, H] fixed-point residual (read; value = sum of replicas)
+  long long *x_out;                  // [reps][M, H] fixed-point residual (accumulated)
+  int reps;                          // 1 .. kMaxXReps; workgroup p adds into replica p % reps
+  int64_t rep_stride;                // elements between replicas
+  const float *norm_w;               // [H] post-attention norm weight
+  float eps;
+  const void *w_gu;                  // [2I, H] f16, GU_BLOCK-interleaved gate/up rows
+  float gu_scale;
+  const void *w_down_t;              // [I, H] f16, W_down transposed
+  float down_scale;
+  int M, H, I;
+};
+bool dec_mlp_supported(int hidden, int inter);
+
 // ------------------------------------------------------------ launchers
 // Each returns the hipError_t of its launch.  `f16_mode` selects the compute
 // type (f16 when true, float when false).
@@ -165,11 +190,13 @@ int dec_gemv_splits(int N, int K, int M, int target_groups);
 int dec_attn_splits(int batch, int n_kv_heads, int max_seq, int target_groups);
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
                             long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1);
-hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int B, int H, const float *w, float eps, void *u);
+hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int reps, int64_t rep_stride, int B, int H,
+                           const float *w, float eps, void *u);
 hipError_t launch_dec_end(hipStream_t s, const float *arg_v, const int *arg_i, int nblk, int B, int32_t *next,
                           int *pos_dev);
 hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &a);
 hipError_t launch_dec_attention(hipStream_t s, const DecAttnArgs &a);
+hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a);
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
                          int32_t *next_ids, int *pos_dev, int pos_add);
 hipError_t launch_set_int(hipStream_t s, int *p, int v);
@@ -185,6 +212,8 @@ hipError_t launch_convert(hipStream_t s, bool src_bf16, const void *src, int64_t
                           int64_t dst_offset, float scale);
 hipError_t launch_convert_gu(hipStream_t s, bool src_bf16, const void *gate, const void *up, int inter,
                              int hidden, bool dst_f16, void *dst, float scale);
+hipError_t launch_convert_t(hipStream_t s, bool src_bf16, const void *src, int rows, int cols, void *dst,
+                            float scale);   // f16 dst[cols][rows]
 hipError_t launch_rope_table(hipStream_t s, float2 *table, int max_seq, int head_dim, double theta);
 
 }  // namespace qw

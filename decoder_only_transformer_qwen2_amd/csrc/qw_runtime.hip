@@ -54,10 +54,12 @@ qw_status fail(qw_status st, const char *fmt, ...) {
   } while (0)
 
 enum Family { F_EMBED, F_RMSNORM, F_GEMM_QKV, F_ROPE_CACHE, F_ATTENTION, F_GEMM_O, F_GEMM_GATE_UP,
-              F_GEMM_DOWN, F_LM_HEAD, F_ARGMAX, F_COUNT };
-const char *const kFamilyNames[F_COUNT] = {"embed", "rmsnorm", "gemm_qkv", "rope_cache", "attention",
-                                           "gemm_o", "gemm_gate_up", "gemm_down", "lm_head", "argmax"};
-const char *const kFamilyList = "embed,rmsnorm,gemm_qkv,rope_cache,attention,gemm_o,gemm_gate_up,gemm_down,lm_head,argmax";
+              F_GEMM_DOWN, F_LM_HEAD, F_ARGMAX, F_MLP, F_COUNT };
+const char *const kFamilyNames[] = {"embed",  "rmsnorm",      "gemm_qkv",  "rope_cache", "attention", "gemm_o",
+                                    "gemm_gate_up", "gemm_down", "lm_head", "argmax", "mlp"};
+static_assert(sizeof(kFamilyNames) / sizeof(kFamilyNames[0]) == F_COUNT, "one name per kernel family");
+const char *const kFamilyList =
+    "embed,rmsnorm,gemm_qkv,rope_cache,attention,gemm_o,gemm_gate_up,gemm_down,lm_head,argmax,mlp";
 
 struct LayerBuf {
   void *w_qkv = nullptr;    // [qd + 2 kvd, H]
@@ -65,6 +67,7 @@ struct LayerBuf {
   void *w_o = nullptr;      // [H, qd]
   void *w_gu = nullptr;     // [2I, H], GU_BLOCK-interleaved
   void *w_down = nullptr;   // [H, I]
+  void *w_down_t = nullptr; // [I, H] copy read by the fused decode MLP (f16 mode)
   float *in_norm = nullptr, *post_norm = nullptr;
   float s_qkv = 1.f, s_o = 1.f, s_gu = 1.f, s_down = 1.f;
 };
@@ -96,6 +99,7 @@ struct qw_model {
   // projection accumulators, LM-head argmax partials
   bool fast_decode = false;
   long long *x_fix = nullptr;        // [max_batch, H]
+  long long *x_fix2 = nullptr;       // [max_batch, H] second residual buffer (fused MLP, ping-pong)
   long long *qkv_fix = nullptr;      // [max_batch, nq*hd + 2*nkv*hd]
   long long *gu_fix = nullptr;       // [max_batch, 2I]
   float *arg_v = nullptr;            // [max_batch, ceil(V / 64)]
@@ -134,6 +138,9 @@ constexpr int kAttnTargetGroups = 256;
 // Up to this many rows, a projection normalises its own operand (each
 // workgroup reads the whole residual rows); above it a norm kernel runs.
 constexpr int kFusedNormRows = 2;
+constexpr bool kHeadNormKernel = true;
+// Residual replicas written by the fused MLP (<= kMaxXReps).
+constexpr int kMlpReps = 2;
 
 // While timing family `fam`, its kernel launches record an event pair at the
 // kernel's own start and end (see QW_LAUNCH); the pairs are read back by
@@ -304,19 +311,33 @@ DecGemvArgs dec_args(const void *W, int M, int N, int K, float scale, int target
 
 // Decode step of the bf16-weight mode (kernels of k_decode.hip): per layer
 // [norm] q/k/v projection, attention (bias, RoPE, cache write, split-KV),
-// o projection (merging the attention splits), [norm] gate/up projection,
-// down projection (silu(gate) * up on its operand); then the LM head with
-// per-block argmax and the argmax reduction.  The bracketed norms are folded
-// into the projection that follows them for batches of up to two rows.
+// o projection (merging the attention splits), then the MLP; then the LM head
+// with per-block argmax and the argmax reduction.  For batches of up to two
+// rows the norms are folded into the projection that follows them and the
+// MLP is one kernel (norm, gate/up, SwiGLU, down) that reads the residual
+// from one buffer and accumulates into the other; for larger batches a norm
+// kernel, the gate/up projection and the down projection (SwiGLU on its
+// operand) run separately on one residual buffer.
 hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next) {
   const qw_config &c = m->cfg;
   const int B = m->batch, H = c.hidden, I = c.intermediate, V = c.vocab;
   const bool fused_norm = B <= kFusedNormRows && H <= 4096;
+  // one-kernel MLP: reads the residual from xr and accumulates xr + MLP into
+  // xo, then the two swap
+  const bool fused_mlp = fused_norm && m->L[0].w_down_t != nullptr;
+  long long *xr = m->x_fix, *xo = m->x_fix2;
+  // every MLP workgroup adds into all H values of a row; spreading them over
+  // replicas of the residual halves the atomics per address (every reader
+  // then sums the replicas, which costs more with each one added)
+  const int R = fused_mlp ? kMlpReps : 1;
+  const int64_t xs = (int64_t)B * H;       // replica stride
   const int S = dec_attn_splits(B, c.n_kv_heads, c.max_seq, kAttnTargetGroups);
   const int64_t n_qkv = (int64_t)B * m->nqkv, n_gu = (int64_t)B * 2 * I;
   hipError_t e = timed(m, s, F_EMBED, [&] {
+    // the embedding goes to replica 0; the other replicas (fused MLP) or the
+    // gate/up accumulator are cleared
     return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, m->x_fix, m->bad_ids, m->qkv_fix, n_qkv,
-                            m->gu_fix, n_gu);
+                            fused_mlp ? m->x_fix + xs : m->gu_fix, fused_mlp ? (R - 1) * xs : n_gu);
   });
   if (e != hipSuccess) return e;
   // operand of a projection that follows an RMSNorm
@@ -324,7 +345,9 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     g.lda = H;
     if (fused_norm) {
       g.act_mode = 1;
-      g.x_fix = m->x_fix;
+      g.x_fix = xr;
+      g.x_reps = R;
+      g.x_rep_stride = xs;
       g.norm_w = w;
       g.eps = c.rms_eps;
     } else {
@@ -334,7 +357,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   };
   auto norm = [&](const float *w) -> hipError_t {
     if (fused_norm) return hipSuccess;
-    return timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, m->x_fix, B, H, w, c.rms_eps, m->u); });
+    return timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, R, xs, B, H, w, c.rms_eps, m->u); });
   };
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerBuf &Lw = m->L[l];
@@ -366,8 +389,8 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     da.max_seq = c.max_seq;
     da.pos_dev = m->pos_dev;
     da.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
-    da.clear = m->gu_fix;
-    da.clear_n = n_gu;
+    da.clear = fused_mlp ? xo : m->gu_fix;
+    da.clear_n = fused_mlp ? R * xs : n_gu;
     e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
     if (e != hipSuccess) return e;
     g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o);
@@ -384,12 +407,32 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       g.act = m->o;
     }
     g.lda = m->qd;
-    g.out_fix = m->x_fix;
+    g.out_fix = xr;
     g.ldo = H;
     g.clear = m->qkv_fix;
     g.clear_n = n_qkv;
     e = timed(m, s, F_GEMM_O, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
+    if (fused_mlp) {
+      DecMlpArgs ma{};
+      ma.x_in = xr;
+      ma.x_out = xo;
+      ma.reps = R;
+      ma.rep_stride = xs;
+      ma.norm_w = Lw.post_norm;
+      ma.eps = c.rms_eps;
+      ma.w_gu = Lw.w_gu;
+      ma.gu_scale = Lw.s_gu;
+      ma.w_down_t = Lw.w_down_t;
+      ma.down_scale = Lw.s_down;
+      ma.M = B;
+      ma.H = H;
+      ma.I = I;
+      e = timed(m, s, F_MLP, [&] { return launch_dec_mlp(s, ma); });
+      if (e != hipSuccess) return e;
+      std::swap(xr, xo);
+      continue;
+    }
     if ((e = norm(Lw.post_norm)) != hipSuccess) return e;
     // every workgroup of a norm-fused projection re-reads the residual rows,
     // so fewer, larger K slices pay off when there are many row blocks
@@ -404,14 +447,23 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     g.act_mode = 2;
     g.act_fix = m->gu_fix;
     g.lda = 2 * I;
-    g.out_fix = m->x_fix;
+    g.out_fix = xr;
     g.ldo = H;
     e = timed(m, s, F_GEMM_DOWN, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
   }
-  if ((e = norm(m->final_norm)) != hipSuccess) return e;
+  // the LM head has thousands of workgroups: the final row is normalised once
+  // by a kernel of its own rather than in every workgroup's prologue
   DecGemvArgs g = dec_args(m->head, B, V, H, m->head_scale);
-  normed(g, m->final_norm);
+  if (kHeadNormKernel || !fused_norm) {
+    e = timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, R, xs, B, H, m->final_norm, c.rms_eps, m->u); });
+    if (e != hipSuccess) return e;
+    g.act_mode = 0;
+    g.act = m->u;
+    g.lda = H;
+  } else {
+    normed(g, m->final_norm);
+  }
   g.ldo = V;
   g.logits_mode = 1;
   g.logits = m->logits;
@@ -487,6 +539,8 @@ struct Src {
 
 }  // namespace
 
+static void release_model(qw_model *m);
+
 extern "C" {
 
 const char *qw_last_error(void) { return g_err.c_str(); }
@@ -516,7 +570,7 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   const bool src_bf16 = (c.dtype == QW_BF16);
   const int H = c.hidden, I = c.intermediate, V = c.vocab;
   auto cleanup_fail = [&](qw_status s) {
-    qw_destroy(m);
+    release_model(m);     // keeps the error message
     return s;
   };
 #define CREATE_TRY(expr)                                                                          \
@@ -564,6 +618,10 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   // --- packed weight copies
   m->L.resize(c.n_layers);
   const bool dst_f16 = m->f16;
+  m->fast_decode = m->f16 && c.max_batch <= 32 &&
+                   decode_fast_supported(c.head_dim, c.n_heads / c.n_kv_heads, H, m->qd, I);
+  // the fused decode MLP (batches of up to two rows) reads W_down transposed
+  const bool with_down_t = m->fast_decode && dec_mlp_supported(H, I);
   const size_t es = m->esz;
   for (int l = 0; l < c.n_layers; ++l) {
     const qw_layer_weights &Lw = weights->layers[l];
@@ -586,6 +644,10 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
     CREATE_TRY(launch_convert(s, src_bf16, Lw.o_w, (int64_t)H * m->qd, dst_f16, B.w_o, 0, so));
     CREATE_TRY(launch_convert_gu(s, src_bf16, Lw.gate_w, Lw.up_w, I, H, dst_f16, B.w_gu, sg));
     CREATE_TRY(launch_convert(s, src_bf16, Lw.down_w, (int64_t)H * I, dst_f16, B.w_down, 0, sd));
+    if (with_down_t) {
+      CREATE_TRY(m->alloc(&B.w_down_t, (size_t)I * H * es));
+      CREATE_TRY(launch_convert_t(s, src_bf16, Lw.down_w, H, I, B.w_down_t, sd));
+    }
     CREATE_TRY(launch_convert(s, src_bf16, Lw.input_norm, H, false, B.in_norm, 0, 1.f));
     CREATE_TRY(launch_convert(s, src_bf16, Lw.post_norm, H, false, B.post_norm, 0, 1.f));
     B.s_qkv = 1.f / sq;
@@ -631,11 +693,10 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   CREATE_TRY(m->alloc((void **)&m->pos_dev, 256));
   CREATE_TRY(m->alloc((void **)&m->bad_ids, 256));
   CREATE_TRY(m->alloc((void **)&m->ids_stage, (size_t)c.max_batch * 4));
-  m->fast_decode = m->f16 && c.max_batch <= 32 &&
-                   decode_fast_supported(c.head_dim, c.n_heads / c.n_kv_heads, H, m->qd, I);
   if (m->fast_decode) {
     const size_t nb = (size_t)c.max_batch;
-    CREATE_TRY(m->alloc((void **)&m->x_fix, nb * H * 8));
+    CREATE_TRY(m->alloc((void **)&m->x_fix, kMaxXReps * nb * H * 8));
+    CREATE_TRY(m->alloc((void **)&m->x_fix2, kMaxXReps * nb * H * 8));
     CREATE_TRY(m->alloc((void **)&m->qkv_fix, nb * m->nqkv * 8));
     CREATE_TRY(m->alloc((void **)&m->gu_fix, nb * 2 * I * 8));
     CREATE_TRY(m->alloc((void **)&m->arg_v, nb * ((V + 63) / 64) * 4));
@@ -729,7 +790,16 @@ qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t
 
 qw_status qw_destroy(qw_model *m) {
   g_err.clear();
-  if (!m) return QW_OK;
+  release_model(m);
+  return QW_OK;
+}
+
+}  // extern "C"
+
+// Frees everything a handle owns (also for a half-built handle); leaves the
+// thread's last error as it is.
+static void release_model(qw_model *m) {
+  if (!m) return;
   (void)hipStreamSynchronize(m->stream);
   drop_graph(m);
   for (auto &e : m->ev_used) {
@@ -744,8 +814,9 @@ qw_status qw_destroy(qw_model *m) {
   if (m->splitk_ws) (void)hipFree(m->splitk_ws);
   if (m->cap) (void)hipStreamDestroy(m->cap);
   delete m;
-  return QW_OK;
 }
+
+extern "C" {
 
 qw_status qw_get_state(const qw_model *m, int32_t *batch, int32_t *pos) {
   g_err.clear();

@@ -61,6 +61,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -m decoder_only_transformer_qwen2_amd.build`")
+    # torch ships its own HIP runtime; loading it first makes libqw.so bind to
+    # that same runtime (one HIP runtime per process, shared streams)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sig = {

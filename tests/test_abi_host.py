@@ -39,7 +39,9 @@ def test_library_exports_every_declared_symbol(Q):
 
 
 def test_kernel_family_names(Q):
-    assert "gemm_gate_up" in Q.qw_kernel_names() and "attention" in Q.qw_kernel_names()
+    names = Q.qw_kernel_names()
+    assert "gemm_gate_up" in names and "attention" in names and "mlp" in names
+    assert len(names) == len(set(names))
 
 
 def _cfg(Q, **kw):
@@ -98,3 +100,18 @@ def test_calls_on_null_model(Q):
     assert lib.qw_prefill(None, None, 1, 1, None, 0, None) == -1
     assert lib.qw_decode_step(None, None, None, None) == -1
     assert lib.qw_destroy(None) == 0
+
+
+def test_create_without_a_device_reports_the_hip_call(Q):
+    """With no GPU the first HIP call of qw_create fails; the status is
+    QW_ERR_HIP and the message still names the call after the half-built
+    handle has been released."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the fake weight pointers must not reach a kernel")
+    w, _keep = _weights(Q)
+    with pytest.raises(Q.QwError) as e:
+        Q.qw_create(_cfg(Q), w, 0)
+    assert e.value.status == -3
+    assert "hipStreamCreateWithFlags" in str(e.value)
+    assert "hipStreamCreateWithFlags" in Q.qw_last_error()
