@@ -56,6 +56,9 @@ def decode_family_bytes(w: S.Workload, family: str, ctx_mean: float) -> float:
         return 2 * I * H * e + B * H * e + B * I * e
     if family == "gemm_down":
         return H * I * e + B * I * e + 2 * B * H * 4
+    if family == "attn_o":   # attention + o projection in one launch (1-2 rows, short context)
+        return (B * m.n_kv_heads * ctx_mean * m.head_dim * e * 2 + H * qd * e + B * nqkv * 8
+                + 2 * B * H * 8)
     if family == "mlp":   # norm + gate/up + SwiGLU + down in one launch (1-2 rows)
         return 3 * I * H * e + B * H * 8 * 2
     if family == "lm_head":
@@ -214,7 +217,7 @@ def main():
 
     if not args.no_roofline:
         # per-family decode time, each family timed over one eager pass
-        fams = ["gemm_qkv", "rope_cache", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "mlp", "lm_head",
+        fams = ["gemm_qkv", "rope_cache", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "mlp", "attn_o", "lm_head",
                 "argmax", "rmsnorm", "embed"]
         per = {}
         for f in fams:
@@ -226,7 +229,7 @@ def main():
             model.timing_enable(None)
             per[f] = (ms, n)
         dom = max((f for f in per if per[f][1] > 0 and f in ("gemm_qkv", "attention", "gemm_o", "gemm_gate_up",
-                                                               "gemm_down", "mlp", "lm_head")),
+                                                               "gemm_down", "mlp", "attn_o", "lm_head")),
                   key=lambda f: per[f][0])
         ms, n = per[dom]
         avg_s = ms / n / 1e3

@@ -428,6 +428,7 @@ __global__ void __launch_bounds__(256) dec_mlp_kernel(DecMlpArgs a) {
   const int p = blockIdx.x, f0 = p * MLP_F;
   const int H = a.H;
   const f16x8 zero = {};
+  clear_share(a.clear, a.clear_n, p, gridDim.x);
 
   // gate row f0 + i and up row f0 + i (packed rows 2 f0 + i and 2 f0 + 16 + i);
   // wave w covers k in [w H / 4, (w + 1) H / 4)
@@ -865,6 +866,236 @@ hipError_t launch_attn_hd(hipStream_t s, const DecAttnArgs &a, dim3 grid, int g)
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------- attention + o projection
+// One or two rows with a short context: attention and the o projection in one
+// kernel.  The o projection is a sum over heads, o . W_o^T = sum_h o_h .
+// W_o[:, h]^T, so workgroup (row block r, query head h, sequence b) computes
+// head h's attention over the whole context (the g heads of a KV group read
+// the same keys and values, which stay in L2), then multiplies o_h into the
+// RB x hd block of W_o and adds the RB results into the residual.  The
+// prologue is the split-KV kernel's (bias, RoPE, q rounded to f16; the new
+// key and value come from LDS and one workgroup per KV head writes them into
+// the cache); the four waves split the keys and meet in LDS.
+template <int HD, int TPW>
+__global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
+  constexpr int NW = 4, LPK = HD / 8, KPW = 64 / LPK, KSTEP = NW * KPW, HALF = HD / 2, U = 4;
+  constexpr int RB = 64 * TPW;                 // W_o rows per workgroup
+  __shared__ float s_q[HD], s_k[HD], s_v[HD];
+  __shared__ float s_m[NW], s_l[NW];
+  __shared__ float s_o[NW][HD];
+  __shared__ f16 s_oh[HD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int slot = lane / LPK, dl = lane % LPK, d0 = dl * 8;
+  const int i = lane & 15, g = lane >> 4;
+  const int rb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int grp = a.n_heads / a.n_kv_heads, j = h / grp;
+  const int pos = *a.pos_dev;
+  const int H = a.H;
+  const int qd = a.n_heads * HD, kvd = a.n_kv_heads * HD, ncols = qd + 2 * kvd;
+  const f16x8 zero = {};
+
+  // W_o block: lane (i, g) holds row r0 + 16 tt + i, columns h hd + 32 s + 8 g
+  const int r0 = rb * RB + wave * 16 * TPW;
+  f16x8 wf[TPW][HD / 32];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int row = r0 + 16 * tt + i;
+#pragma unroll
+    for (int s2 = 0; s2 < HD / 32; ++s2)
+      wf[tt][s2] = row < H ? load8((const f16 *)a.w_o + (int64_t)row * qd + h * HD + 32 * s2 + 8 * g) : zero;
+  }
+  // cached keys 0 .. pos - 1: first batch before the prologue
+  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
+  f16 *Kc = (f16 *)a.k_cache + head_base;
+  f16 *Vc = (f16 *)a.v_cache + head_base;
+  const int kc_end = pos;
+  const int kstart = wave * KPW;
+  f16x8 kr[U], vr[U];
+  auto issue = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = kb + u * KSTEP + slot;
+      if (t < kc_end) {
+        kr[u] = load8(Kc + (int64_t)t * HD + d0);
+        vr[u] = load8(Vc + (int64_t)t * HD + d0);
+      } else {
+        kr[u] = zero;      // weight 0; values must be finite
+        vr[u] = zero;
+      }
+    }
+  };
+  if (kstart < kc_end) issue(kstart);
+
+  clear_share(a.clear, a.clear_n, (b * gridDim.y + h) * gridDim.x + rb, gridDim.x * gridDim.y * gridDim.z);
+
+  // prologue: q of head h, new k and v of KV head j (bias + RoPE at pos)
+  const long long *acc = a.qkv_fix + (int64_t)b * ncols;
+  const float2 *cs = a.rope + (int64_t)pos * HALF;
+  const float qscale = a.softmax_scale * LOG2E;
+  for (int e = tid; e < 2 * HALF + HD; e += 256) {
+    if (e < 2 * HALF) {
+      const bool is_q = e < HALF;
+      const int ii = is_q ? e : e - HALF;
+      const int c0 = is_q ? h * HD + ii : qd + j * HD + ii;
+      const float re = from_fix(acc[c0]) + a.bias[c0];
+      const float im = from_fix(acc[c0 + HALF]) + a.bias[c0 + HALF];
+      const float2 r = cs[ii];
+      const float nre = re * r.x - im * r.y, nim = im * r.x + re * r.y;
+      if (is_q) {
+        s_q[ii] = (float)(f16)nre * qscale;
+        s_q[ii + HALF] = (float)(f16)nim * qscale;
+      } else {
+        s_k[ii] = (float)(f16)nre;
+        s_k[ii + HALF] = (float)(f16)nim;
+      }
+    } else {
+      const int d = e - 2 * HALF;
+      const int c = qd + kvd + j * HD + d;
+      s_v[d] = (float)(f16)(from_fix(acc[c]) + a.bias[c]);
+    }
+  }
+  __syncthreads();
+  if (rb == 0 && h % grp == 0 && tid < HD) {
+    Kc[(int64_t)pos * HD + tid] = (f16)s_k[tid];
+    Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
+  }
+
+  float q[8], o[8], m = -INFINITY, l = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    q[e] = s_q[d0 + e];
+    o[e] = 0.f;
+  }
+  for (int kb = kstart; kb < kc_end; kb += U * KSTEP) {
+    f16x8 kc[U], vc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      kc[u] = kr[u];
+      vc[u] = vr[u];
+    }
+    if (kb + U * KSTEP < kc_end) issue(kb + U * KSTEP);
+    float sc[U];
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(q[e], (float)kc[u][e], d);
+#pragma unroll
+      for (int off = LPK / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+      sc[u] = (kb + u * KSTEP + slot < kc_end) ? d : -INFINITY;
+      mx = fmaxf(mx, sc[u]);
+    }
+    const float corr = (m == -INFINITY) ? 0.f : exp2f(m - mx);
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= corr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = (mx == -INFINITY) ? 0.f : exp2f(sc[u] - mx);
+      lsum += p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(p, (float)vc[u][e], o[e]);
+    }
+    l = l * corr + lsum;
+    m = mx;
+  }
+  if (wave == 0 && slot == 0) {
+    // the new key, from LDS
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d = fmaf(q[e], s_k[d0 + e], d);
+#pragma unroll
+    for (int off = LPK / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+    const float mn = fmaxf(m, d);
+    const float corr = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+    const float p = exp2f(d - mn);
+    l = l * corr + p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = fmaf(p, s_v[d0 + e], o[e] * corr);
+    m = mn;
+  }
+  // merge the key slots of the wave, then the four waves
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    const float mo = __shfl_xor(m, off, 64);
+    const float lo = __shfl_xor(l, off, 64);
+    const float mn = fmaxf(m, mo);
+    const float ca = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+    const float cb = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
+    l = l * ca + lo * cb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float oo = __shfl_xor(o[e], off, 64);
+      o[e] = o[e] * ca + oo * cb;
+    }
+    m = mn;
+  }
+  if (slot == 0) {
+    if (dl == 0) {
+      s_m[wave] = m;
+      s_l[wave] = l;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_o[wave][d0 + e] = o[e];
+  }
+  __syncthreads();
+  if (tid < HD) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float c = (s_m[w] == -INFINITY) ? 0.f : exp2f(s_m[w] - M);
+      L = fmaf(c, s_l[w], L);
+      O = fmaf(c, s_o[w][tid], O);
+    }
+    s_oh[tid] = (f16)(O / L);
+  }
+  __syncthreads();
+
+  // o projection of this block: column 0 of the B operand is o_h
+  f32x4 pacc[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) pacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < HD / 32; ++s2) {
+    const f16x8 x = (i == 0) ? *reinterpret_cast<const f16x8 *>(&s_oh[32 * s2 + 8 * g]) : zero;
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) pacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[tt][s2], x, pacc[tt], 0, 0, 0);
+  }
+  if (i == 0) {
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 16 * tt + 4 * g + r;
+        if (row < H) fix_add(a.x_out + (int64_t)b * H + row, pacc[tt][r] * a.o_scale);
+      }
+  }
+}
+
+bool dec_attn_o_supported(int head_dim, int hidden) {
+  return (head_dim == 64 || head_dim == 128) && hidden % 64 == 0;
+}
+
+hipError_t launch_dec_attn_o(hipStream_t s, const DecAttnOArgs &a) {
+  if (!dec_attn_o_supported(a.head_dim, a.H) || a.batch < 1 || a.n_heads % a.n_kv_heads) return hipErrorInvalidValue;
+  // 128-row blocks for the larger models: half the workgroups re-read the context
+  const bool wide = a.H >= 1024;
+  const int RB = wide ? 128 : 64;
+  const dim3 grid((a.H + RB - 1) / RB, a.n_heads, a.batch);
+  if (a.head_dim == 64) {
+    if (wide) QW_LAUNCH((dec_attn_o_kernel<64, 2>), dim3(grid), dim3(256), 0, s, a);
+    else QW_LAUNCH((dec_attn_o_kernel<64, 1>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (wide) QW_LAUNCH((dec_attn_o_kernel<128, 2>), dim3(grid), dim3(256), 0, s, a);
+    else QW_LAUNCH((dec_attn_o_kernel<128, 1>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
 
 bool dec_mlp_supported(int hidden, int inter) {
   return hidden % 128 == 0 && hidden <= 2048 && inter % MLP_F == 0;

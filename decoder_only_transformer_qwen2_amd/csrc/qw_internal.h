@@ -147,6 +147,25 @@ struct DecAttnArgs {
   int64_t clear_n;
 };
 
+// Decode-step attention merged with the o projection, for one or two rows and
+// short contexts, see k_decode.hip.  Adds o . W_o^T (scaled) into x_out.
+struct DecAttnOArgs {
+  const long long *qkv_fix;          // [batch, nq*hd + 2*nkv*hd] fixed-point projection sums
+  const float *bias;                 // [nq*hd + 2*nkv*hd]
+  const float2 *rope;                // [max_seq, hd/2]
+  void *k_cache, *v_cache;           // layer base [max_batch][nkv][max_seq][hd]
+  int batch, n_heads, n_kv_heads, head_dim, max_seq;
+  const int *pos_dev;                // position of the new row
+  float softmax_scale;
+  const void *w_o;                   // [H, nq*hd] f16
+  float o_scale;
+  int H;
+  long long *x_out;                  // [batch, H] fixed-point residual (atomic adds)
+  long long *clear;                  // side job: zero clear[0 .. clear_n)
+  int64_t clear_n;
+};
+bool dec_attn_o_supported(int head_dim, int hidden);
+
 // The decode residual stream may be kept as up to this many fixed-point
 // replicas whose sum is the value: writers that would otherwise all add into
 // the same addresses spread their atomics over the replicas.
@@ -167,6 +186,8 @@ struct DecMlpArgs {
   const void *w_down_t;              // [I, H] f16, W_down transposed
   float down_scale;
   int M, H, I;
+  long long *clear;                  // side job: zero clear[0 .. clear_n) (may be NULL)
+  int64_t clear_n;
 };
 bool dec_mlp_supported(int hidden, int inter);
 
@@ -197,6 +218,7 @@ hipError_t launch_dec_end(hipStream_t s, const float *arg_v, const int *arg_i, i
 hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &a);
 hipError_t launch_dec_attention(hipStream_t s, const DecAttnArgs &a);
 hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a);
+hipError_t launch_dec_attn_o(hipStream_t s, const DecAttnOArgs &a);
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
                          int32_t *next_ids, int *pos_dev, int pos_add);
 hipError_t launch_set_int(hipStream_t s, int *p, int v);

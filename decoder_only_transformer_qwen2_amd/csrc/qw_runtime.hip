@@ -54,12 +54,12 @@ qw_status fail(qw_status st, const char *fmt, ...) {
   } while (0)
 
 enum Family { F_EMBED, F_RMSNORM, F_GEMM_QKV, F_ROPE_CACHE, F_ATTENTION, F_GEMM_O, F_GEMM_GATE_UP,
-              F_GEMM_DOWN, F_LM_HEAD, F_ARGMAX, F_MLP, F_COUNT };
+              F_GEMM_DOWN, F_LM_HEAD, F_ARGMAX, F_MLP, F_ATTN_O, F_COUNT };
 const char *const kFamilyNames[] = {"embed",  "rmsnorm",      "gemm_qkv",  "rope_cache", "attention", "gemm_o",
-                                    "gemm_gate_up", "gemm_down", "lm_head", "argmax", "mlp"};
+                                    "gemm_gate_up", "gemm_down", "lm_head", "argmax", "mlp", "attn_o"};
 static_assert(sizeof(kFamilyNames) / sizeof(kFamilyNames[0]) == F_COUNT, "one name per kernel family");
 const char *const kFamilyList =
-    "embed,rmsnorm,gemm_qkv,rope_cache,attention,gemm_o,gemm_gate_up,gemm_down,lm_head,argmax,mlp";
+    "embed,rmsnorm,gemm_qkv,rope_cache,attention,gemm_o,gemm_gate_up,gemm_down,lm_head,argmax,mlp,attn_o";
 
 struct LayerBuf {
   void *w_qkv = nullptr;    // [qd + 2 kvd, H]
@@ -113,6 +113,7 @@ struct qw_model {
   bool use_graph = true;
   bool graph_ok = false;
   int graph_batch = 0;
+  int graph_variant = -1;
   hipGraphExec_t gexec = nullptr;
   // kernel timing
   int timing_family = -1;
@@ -141,6 +142,20 @@ constexpr int kFusedNormRows = 2;
 constexpr bool kHeadNormKernel = true;
 // Residual replicas written by the fused MLP (<= kMaxXReps).
 constexpr int kMlpReps = 2;
+// Up to this context length (and two rows), attention and the o projection
+// are one kernel in which every workgroup reads its head's whole context.
+constexpr int kAttnOMaxCtx = 1024;
+
+// Which decode step the next decode call runs: 1 = attention merged with the
+// o projection (short context), 0 = split-KV attention, then o projection.
+// A captured graph is only replayed for the variant it was captured with.
+int decode_variant(const qw_model *m) {
+  const qw_config &c = m->cfg;
+  return (m->fast_decode && m->batch <= kFusedNormRows && m->pos + 1 <= kAttnOMaxCtx &&
+          dec_attn_o_supported(c.head_dim, c.hidden))
+             ? 1
+             : 0;
+}
 
 // While timing family `fam`, its kernel launches record an event pair at the
 // kernel's own start and end (see QW_LAUNCH); the pairs are read back by
@@ -330,6 +345,9 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   // replicas of the residual halves the atomics per address (every reader
   // then sums the replicas, which costs more with each one added)
   const int R = fused_mlp ? kMlpReps : 1;
+  // attention merged with the o projection: the q/k/v sums are still being
+  // read in that kernel, so the next projection clears them instead
+  const bool attn_o = decode_variant(m) == 1;
   const int64_t xs = (int64_t)B * H;       // replica stride
   const int S = dec_attn_splits(B, c.n_kv_heads, c.max_seq, kAttnTargetGroups);
   const int64_t n_qkv = (int64_t)B * m->nqkv, n_gu = (int64_t)B * 2 * I;
@@ -370,49 +388,73 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     g.ldo = m->nqkv;
     e = timed(m, s, F_GEMM_QKV, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
-    DecAttnArgs da{};
-    da.qkv_fix = m->qkv_fix;
-    da.bias = Lw.b_qkv;
-    da.rope = m->rope;
-    da.k_cache = kc;
-    da.v_cache = vc;
-    da.o = m->o;
-    da.part_m = m->att_m;
-    da.part_l = m->att_l;
-    da.part_o = m->att_o;
-    da.splits = S;
-    da.head_parallel = B <= kFusedNormRows;      // latency-bound: split the heads over the waves
-    da.batch = B;
-    da.n_heads = c.n_heads;
-    da.n_kv_heads = c.n_kv_heads;
-    da.head_dim = c.head_dim;
-    da.max_seq = c.max_seq;
-    da.pos_dev = m->pos_dev;
-    da.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
-    da.clear = fused_mlp ? xo : m->gu_fix;
-    da.clear_n = fused_mlp ? R * xs : n_gu;
-    e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
-    if (e != hipSuccess) return e;
-    g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o);
-    if (S > 1) {
-      g.act_mode = 3;
-      g.part_m = m->att_m;
-      g.part_l = m->att_l;
-      g.part_o = m->att_o;
-      g.attn_splits = S;
-      g.n_heads = c.n_heads;
-      g.head_dim = c.head_dim;
+    if (attn_o) {
+      DecAttnOArgs ao{};
+      ao.qkv_fix = m->qkv_fix;
+      ao.bias = Lw.b_qkv;
+      ao.rope = m->rope;
+      ao.k_cache = kc;
+      ao.v_cache = vc;
+      ao.batch = B;
+      ao.n_heads = c.n_heads;
+      ao.n_kv_heads = c.n_kv_heads;
+      ao.head_dim = c.head_dim;
+      ao.max_seq = c.max_seq;
+      ao.pos_dev = m->pos_dev;
+      ao.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
+      ao.w_o = Lw.w_o;
+      ao.o_scale = Lw.s_o;
+      ao.H = H;
+      ao.x_out = xr;
+      ao.clear = fused_mlp ? xo : m->gu_fix;
+      ao.clear_n = fused_mlp ? R * xs : n_gu;
+      e = timed(m, s, F_ATTN_O, [&] { return launch_dec_attn_o(s, ao); });
+      if (e != hipSuccess) return e;
     } else {
-      g.act_mode = 0;
-      g.act = m->o;
+      DecAttnArgs da{};
+      da.qkv_fix = m->qkv_fix;
+      da.bias = Lw.b_qkv;
+      da.rope = m->rope;
+      da.k_cache = kc;
+      da.v_cache = vc;
+      da.o = m->o;
+      da.part_m = m->att_m;
+      da.part_l = m->att_l;
+      da.part_o = m->att_o;
+      da.splits = S;
+      da.head_parallel = B <= kFusedNormRows;      // latency-bound: split the heads over the waves
+      da.batch = B;
+      da.n_heads = c.n_heads;
+      da.n_kv_heads = c.n_kv_heads;
+      da.head_dim = c.head_dim;
+      da.max_seq = c.max_seq;
+      da.pos_dev = m->pos_dev;
+      da.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
+      da.clear = fused_mlp ? xo : m->gu_fix;
+      da.clear_n = fused_mlp ? R * xs : n_gu;
+      e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
+      if (e != hipSuccess) return e;
+      g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o);
+      if (S > 1) {
+        g.act_mode = 3;
+        g.part_m = m->att_m;
+        g.part_l = m->att_l;
+        g.part_o = m->att_o;
+        g.attn_splits = S;
+        g.n_heads = c.n_heads;
+        g.head_dim = c.head_dim;
+      } else {
+        g.act_mode = 0;
+        g.act = m->o;
+      }
+      g.lda = m->qd;
+      g.out_fix = xr;
+      g.ldo = H;
+      g.clear = m->qkv_fix;
+      g.clear_n = n_qkv;
+      e = timed(m, s, F_GEMM_O, [&] { return launch_dec_gemv(s, g); });
+      if (e != hipSuccess) return e;
     }
-    g.lda = m->qd;
-    g.out_fix = xr;
-    g.ldo = H;
-    g.clear = m->qkv_fix;
-    g.clear_n = n_qkv;
-    e = timed(m, s, F_GEMM_O, [&] { return launch_dec_gemv(s, g); });
-    if (e != hipSuccess) return e;
     if (fused_mlp) {
       DecMlpArgs ma{};
       ma.x_in = xr;
@@ -428,6 +470,8 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       ma.M = B;
       ma.H = H;
       ma.I = I;
+      ma.clear = attn_o ? m->qkv_fix : nullptr;
+      ma.clear_n = n_qkv;
       e = timed(m, s, F_MLP, [&] { return launch_dec_mlp(s, ma); });
       if (e != hipSuccess) return e;
       std::swap(xr, xo);
@@ -440,6 +484,10 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     normed(g, Lw.post_norm);
     g.role_gate_up = 1;
     g.out_fix = m->gu_fix;
+    if (attn_o) {
+      g.clear = m->qkv_fix;
+      g.clear_n = n_qkv;
+    }
     g.ldo = 2 * I;
     e = timed(m, s, F_GEMM_GATE_UP, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
@@ -760,7 +808,8 @@ qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t
   if (!graph) {
     HIP_TRY(decode_body(m, s, ids, m->next_stage));
   } else {
-    if (!m->graph_ok || m->graph_batch != m->batch) {
+    const int variant = decode_variant(m);
+    if (!m->graph_ok || m->graph_batch != m->batch || m->graph_variant != variant) {
       drop_graph(m);
       hipGraph_t g = nullptr;
       HIP_TRY(hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal));
@@ -778,6 +827,7 @@ qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t
         return fail(QW_ERR_HIP, "qw_decode_step: graph instantiate failed: %s", hipGetErrorString(e));
       }
       m->graph_batch = m->batch;
+      m->graph_variant = variant;
       m->graph_ok = true;
     }
     HIP_TRY(launch_copy_i32(s, m->ids_stage, ids, m->batch));
