@@ -50,6 +50,11 @@ __device__ __forceinline__ void fix_add(long long *p, float v) {
   atomicAdd(reinterpret_cast<unsigned long long *>(p), (unsigned long long)to_fix(v));
 }
 __device__ __forceinline__ f16x8 load8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+// Loads in these kernels are issued unconditionally from an address clamped
+// into range, and a lane outside the range then selects zero (or its result
+// is never stored).  A per-lane condition around the load itself becomes an
+// exec-mask branch per load, which keeps the compiler from issuing a wave's
+// loads back to back.
 
 // Clear n int64 values, spread over `parts` cooperating workgroups.
 __device__ __forceinline__ void clear_share(long long *p, int64_t n, int part, int parts) {
@@ -79,7 +84,7 @@ __global__ void __launch_bounds__(256) dec_embed_kernel(const int32_t *ids, cons
 
 // u[b] = f16(x[b] / sqrt(mean(x[b]^2) + eps) * w): used when the batch is too
 // large for the projections to normalise their own operand.
-__global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, int reps, int64_t rep_stride, int H,
+__global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, int64_t rep_stride, int H,
                                                        const float *w, float eps, f16 *u) {
   const int b = blockIdx.x;
   __shared__ float red[4];
@@ -87,17 +92,21 @@ __global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, i
   float ss = 0.f;
   for (int c0 = 0; c0 < H; c0 += 256 * 8) {
     long long v[8];
+    long long vr[kXReps][8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int c = c0 + t * 256 + threadIdx.x;
-      v[t] = c < H ? xr[c] : 0;
-    }
-    for (int r = 1; r < reps; ++r)
+    for (int r = 0; r < kXReps; ++r)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int c = c0 + t * 256 + threadIdx.x;
-        if (c < H) v[t] += xr[r * rep_stride + c];
+        const long long q = xr[r * rep_stride + min(c, H - 1)];
+        vr[r][t] = c < H ? q : 0;
       }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      v[t] = vr[0][t];
+#pragma unroll
+      for (int r = 1; r < kXReps; ++r) v[t] += vr[r][t];
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float f = from_fix(v[t]);
@@ -111,7 +120,8 @@ __global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, i
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
   for (int c = threadIdx.x; c < H; c += 256) {
     long long q = xr[c];
-    for (int r = 1; r < reps; ++r) q += xr[r * rep_stride + c];
+#pragma unroll
+    for (int r = 1; r < kXReps; ++r) q += xr[r * rep_stride + c];
     u[(int64_t)b * H + c] = (f16)(from_fix(q) * inv * w[c]);
   }
 }
@@ -159,7 +169,7 @@ enum class DecOut : int { FixAdd = 0, Logits = 1 };
 
 // ROLE only separates launches in profiles (the gate/up projection gets its
 // own symbol); it does not change the code.
-template <int NB, DecAct AM, DecOut OM, int ROLE>
+template <int NB, DecAct AM, DecOut OM, int ROLE, int NFP = 1>
 __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
   constexpr int BT = 16 * NB;
   __shared__ f16 s_act[BT][CH + 8];
@@ -181,14 +191,14 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
   auto load_w = [&](int kc) {
     const int nu = min(8, (k1 - kc) >> 5);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) w[t] = (row_ok && t < nu) ? load8(W + kc + 32 * t + 8 * g) : zero;
+    for (int t = 0; t < 8; ++t) w[t] = (t < nu) ? load8(W + kc + 32 * t + 8 * g) : zero;   // rows >= N: never stored
   };
   load_w(k0);
 
   // NormFix: the whole normalised row (1 or 2 rows) is built once in LDS.
   // Every thread loads its share of the row and of the norm weight up front
   // (one memory round trip), then one block reduction gives 1/rms.
-  constexpr int NF_ROWS = 2, NF_PER = 16;     // rows, values per thread (K <= 4096)
+  constexpr int NF_ROWS = 2, NF_PER = NFP;    // rows, values per thread (K <= 256 NFP)
   __shared__ f16 s_row[(AM == DecAct::NormFix) ? NF_ROWS : 1][(AM == DecAct::NormFix) ? 256 * NF_PER : 8];
   if constexpr (AM == DecAct::NormFix) {
     __shared__ float s_red[4][NF_ROWS];
@@ -196,24 +206,32 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
 #pragma unroll
     for (int t = 0; t < NF_PER; ++t) {
       const int c = t * 256 + tid;
-      wv[t] = c < a.K ? a.norm_w[c] : 0.f;
+      const float w = a.norm_w[min(c, a.K - 1)];
+      wv[t] = c < a.K ? w : 0.f;
     }
-    long long q[NF_ROWS][NF_PER];
+    // all replicas of the rows in one batch of loads (clamped addresses)
+    long long qr[kXReps][NF_ROWS][NF_PER];
 #pragma unroll
-    for (int b = 0; b < NF_ROWS; ++b)
-#pragma unroll
-      for (int t = 0; t < NF_PER; ++t) {
-        const int c = t * 256 + tid;
-        q[b][t] = (b < a.M && c < a.K) ? a.x_fix[(int64_t)b * a.lda + c] : 0;
-      }
-    for (int r = 1; r < a.x_reps; ++r)
+    for (int r = 0; r < kXReps; ++r)
 #pragma unroll
       for (int b = 0; b < NF_ROWS; ++b)
 #pragma unroll
         for (int t = 0; t < NF_PER; ++t) {
           const int c = t * 256 + tid;
-          if (b < a.M && c < a.K) q[b][t] += a.x_fix[r * a.x_rep_stride + (int64_t)b * a.lda + c];
+          const long long v = a.x_fix[r * a.x_rep_stride + (int64_t)min(b, a.M - 1) * a.lda + min(c, a.K - 1)];
+          // masked arithmetically: a select on the (uniform) row test becomes
+          // a branch per load, and the loads are then serialised
+          qr[r][b][t] = v & -(long long)((b < a.M) & (c < a.K));
         }
+    long long q[NF_ROWS][NF_PER];
+#pragma unroll
+    for (int b = 0; b < NF_ROWS; ++b)
+#pragma unroll
+      for (int t = 0; t < NF_PER; ++t) {
+        q[b][t] = qr[0][b][t];
+#pragma unroll
+        for (int r = 1; r < kXReps; ++r) q[b][t] += qr[r][b][t];
+      }
 #pragma unroll
     for (int b = 0; b < NF_ROWS; ++b)
 #pragma unroll
@@ -311,7 +329,8 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
           const int b = nb * 16 + i;
           const f16 *src = (AM == DecAct::NormFix) ? &s_row[b < NF_ROWS ? b : 0][kc + 32 * t + 8 * g]
                                                    : &s_act[b][32 * t + 8 * g];
-          const f16x8 x = (b < a.M) ? *reinterpret_cast<const f16x8 *>(src) : zero;
+          const f16x8 xl = *reinterpret_cast<const f16x8 *>(src);
+          const f16x8 x = (b < a.M) ? xl : zero;
           acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wc[t], x, acc[nb], 0, 0, 0);
         }
       }
@@ -374,18 +393,31 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
   }
 }
 
+// NormFix: one or two rows, the prologue sized to K (values per thread)
+template <int ROLE, int NFP>
+hipError_t launch_gemv_normfix(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
+  if (a.logits_mode)
+    QW_LAUNCH((dec_gemv_kernel<1, DecAct::NormFix, DecOut::Logits, ROLE, NFP>), dim3(grid), dim3(256), 0, s, a);
+  else
+    QW_LAUNCH((dec_gemv_kernel<1, DecAct::NormFix, DecOut::FixAdd, ROLE, NFP>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int NB, int ROLE>
 hipError_t launch_gemv_role(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
   const DecAct am = (DecAct)a.act_mode;
+  if (am == DecAct::NormFix) {
+    if (a.M > 2 || a.K > 4096) return hipErrorInvalidValue;
+    if (a.K <= 1024) return launch_gemv_normfix<ROLE, 4>(s, a, grid);
+    if (a.K <= 2048) return launch_gemv_normfix<ROLE, 8>(s, a, grid);
+    return launch_gemv_normfix<ROLE, 16>(s, a, grid);
+  }
   if (a.logits_mode) {
-    if (am == DecAct::NormFix)
-      QW_LAUNCH((dec_gemv_kernel<NB, DecAct::NormFix, DecOut::Logits, ROLE>), dim3(grid), dim3(256), 0, s, a);
-    else
-      QW_LAUNCH((dec_gemv_kernel<NB, DecAct::F16, DecOut::Logits, ROLE>), dim3(grid), dim3(256), 0, s, a);
+    QW_LAUNCH((dec_gemv_kernel<NB, DecAct::F16, DecOut::Logits, ROLE>), dim3(grid), dim3(256), 0, s, a);
   } else {
     switch (am) {
       case DecAct::F16: QW_LAUNCH((dec_gemv_kernel<NB, DecAct::F16, DecOut::FixAdd, ROLE>), dim3(grid), dim3(256), 0, s, a); break;
-      case DecAct::NormFix: QW_LAUNCH((dec_gemv_kernel<NB, DecAct::NormFix, DecOut::FixAdd, ROLE>), dim3(grid), dim3(256), 0, s, a); break;
+      case DecAct::NormFix: break;
       case DecAct::SwiGLUFix: QW_LAUNCH((dec_gemv_kernel<NB, DecAct::SwiGLUFix, DecOut::FixAdd, ROLE>), dim3(grid), dim3(256), 0, s, a); break;
       case DecAct::AttnMerge: QW_LAUNCH((dec_gemv_kernel<NB, DecAct::AttnMerge, DecOut::FixAdd, ROLE>), dim3(grid), dim3(256), 0, s, a); break;
     }
@@ -416,7 +448,7 @@ constexpr int MLP_F = GU_BLOCK;
 
 template <int NR, int KU>
 __global__ void __launch_bounds__(256) dec_mlp_kernel(DecMlpArgs a) {
-  constexpr int NPER = 8;                       // residual values per thread (H <= 2048)
+  constexpr int NPER = KU / 2;                  // residual values per thread (H <= 256 NPER = 128 KU)
   // normalised rows (f16) during gate/up, then the down results (fp32)
   __shared__ float s_buf[NR * 256 * NPER];
   f16 (*s_row)[256 * NPER] = reinterpret_cast<f16 (*)[256 * NPER]>(s_buf);
@@ -450,27 +482,34 @@ __global__ void __launch_bounds__(256) dec_mlp_kernel(DecMlpArgs a) {
   const f16 *Wd = (const f16 *)a.w_down_t + (int64_t)f0 * H + (n_ok ? n : 0);
   f16x8 wd[MLP_F];
 #pragma unroll
-  for (int f = 0; f < MLP_F; ++f) wd[f] = n_ok ? load8(Wd + (int64_t)f * H) : zero;
+  for (int f = 0; f < MLP_F; ++f) wd[f] = load8(Wd + (int64_t)f * H);     // lanes past H: never stored
 
   // u = RMSNorm(x_in) * w into LDS (one round trip, one block reduction);
   // x_in is the sum of its replicas (exact, in fixed point)
   long long xq[NR][NPER];
   {
     float xv[NR][NPER], wv[NPER];
+    long long qr[kXReps][NR][NPER];
 #pragma unroll
     for (int t = 0; t < NPER; ++t) {
-      const int c = t * 256 + tid;
-      wv[t] = c < H ? a.norm_w[c] : 0.f;
+      const int c = t * 256 + tid, cc = min(c, H - 1);
+      const float w = a.norm_w[cc];
+      wv[t] = c < H ? w : 0.f;
 #pragma unroll
-      for (int b = 0; b < NR; ++b) xq[b][t] = c < H ? a.x_in[(int64_t)b * H + c] : 0;
+      for (int r = 0; r < kXReps; ++r)
+#pragma unroll
+        for (int b = 0; b < NR; ++b) {
+          const long long v = a.x_in[r * a.rep_stride + (int64_t)b * H + cc];
+          qr[r][b][t] = c < H ? v : 0;
+        }
     }
-    for (int r = 1; r < a.reps; ++r)
 #pragma unroll
-      for (int t = 0; t < NPER; ++t) {
-        const int c = t * 256 + tid;
+    for (int t = 0; t < NPER; ++t)
 #pragma unroll
-        for (int b = 0; b < NR; ++b)
-          if (c < H) xq[b][t] += a.x_in[r * a.rep_stride + (int64_t)b * H + c];
+      for (int b = 0; b < NR; ++b) {
+        xq[b][t] = qr[0][b][t];
+#pragma unroll
+        for (int r = 1; r < kXReps; ++r) xq[b][t] += qr[r][b][t];
       }
 #pragma unroll
     for (int t = 0; t < NPER; ++t)
@@ -503,7 +542,8 @@ __global__ void __launch_bounds__(256) dec_mlp_kernel(DecMlpArgs a) {
 #pragma unroll
   for (int t = 0; t < KU; ++t) {
     if (t < ku) {
-      const f16x8 x = (i < NR) ? *reinterpret_cast<const f16x8 *>(&s_row[i < NR ? i : 0][kw0 + 32 * t + 8 * g]) : zero;
+      const f16x8 xl = *reinterpret_cast<const f16x8 *>(&s_row[i < NR ? i : 0][kw0 + 32 * t + 8 * g]);
+      const f16x8 x = (i < NR) ? xl : zero;
       ag = __builtin_amdgcn_mfma_f32_16x16x32_f16(wg[t], x, ag, 0, 0, 0);
       au = __builtin_amdgcn_mfma_f32_16x16x32_f16(wu[t], x, au, 0, 0, 0);
     }
@@ -547,7 +587,7 @@ __global__ void __launch_bounds__(256) dec_mlp_kernel(DecMlpArgs a) {
   // workgroups start their adds at different 64-column blocks (rotating by
   // p), so the atomics arriving at one address at a time come from few
   // workgroups; workgroup 0 starts at column 0, where its xq values line up
-  long long *xo = a.x_out + (p % a.reps) * a.rep_stride;
+  long long *xo = a.x_out + (p % kXReps) * a.rep_stride;
   const int rot = 64 * (p % (H / 64));
 #pragma unroll
   for (int b = 0; b < NR; ++b)
@@ -620,14 +660,11 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = kb + u * KSTEP + slot;
-      if (t < kc_end) {
-        kr[u] = load8(Kc + (int64_t)t * HD + d0);
-        vr[u] = load8(Vc + (int64_t)t * HD + d0);
-      } else {
-        // out-of-range keys get weight 0; their values must be finite
-        kr[u] = f16x8{};
-        vr[u] = f16x8{};
-      }
+      // out-of-range keys get weight 0; their values must be finite
+      const int tc = min(t, max(kc_end - 1, 0));
+      const f16x8 kv = load8(Kc + (int64_t)tc * HD + d0), vv = load8(Vc + (int64_t)tc * HD + d0);
+      kr[u] = t < kc_end ? kv : f16x8{};
+      vr[u] = t < kc_end ? vv : f16x8{};
     }
   };
   if (nh > 0 && kstart < kc_end) issue(kstart);
@@ -903,7 +940,7 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
     const int row = r0 + 16 * tt + i;
 #pragma unroll
     for (int s2 = 0; s2 < HD / 32; ++s2)
-      wf[tt][s2] = row < H ? load8((const f16 *)a.w_o + (int64_t)row * qd + h * HD + 32 * s2 + 8 * g) : zero;
+      wf[tt][s2] = load8((const f16 *)a.w_o + (int64_t)min(row, H - 1) * qd + h * HD + 32 * s2 + 8 * g);  // rows >= H: never stored
   }
   // cached keys 0 .. pos - 1: first batch before the prologue
   const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
@@ -916,13 +953,11 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = kb + u * KSTEP + slot;
-      if (t < kc_end) {
-        kr[u] = load8(Kc + (int64_t)t * HD + d0);
-        vr[u] = load8(Vc + (int64_t)t * HD + d0);
-      } else {
-        kr[u] = zero;      // weight 0; values must be finite
-        vr[u] = zero;
-      }
+      // out-of-range keys get weight 0; their values must be finite
+      const int tc = min(t, max(kc_end - 1, 0));
+      const f16x8 kv = load8(Kc + (int64_t)tc * HD + d0), vv = load8(Vc + (int64_t)tc * HD + d0);
+      kr[u] = t < kc_end ? kv : zero;
+      vr[u] = t < kc_end ? vv : zero;
     }
   };
   if (kstart < kc_end) issue(kstart);
@@ -1102,8 +1137,7 @@ bool dec_mlp_supported(int hidden, int inter) {
 }
 
 hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a) {
-  if (!dec_mlp_supported(a.H, a.I) || a.M < 1 || a.M > 2 || a.reps < 1 || a.reps > kMaxXReps)
-    return hipErrorInvalidValue;
+  if (!dec_mlp_supported(a.H, a.I) || a.M < 1 || a.M > 2) return hipErrorInvalidValue;
   const dim3 grid(a.I / MLP_F);
   const bool small = a.H <= 1024;
   if (a.M == 1) {
@@ -1153,9 +1187,9 @@ hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void
   return hipGetLastError();
 }
 
-hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int reps, int64_t rep_stride, int B, int H,
+hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int64_t rep_stride, int B, int H,
                            const float *w, float eps, void *u) {
-  QW_LAUNCH((dec_norm_kernel), dim3(B), dim3(256), 0, s, x_fix, reps, rep_stride, H, w, eps, (f16 *)u);
+  QW_LAUNCH((dec_norm_kernel), dim3(B), dim3(256), 0, s, x_fix, rep_stride, H, w, eps, (f16 *)u);
   return hipGetLastError();
 }
 

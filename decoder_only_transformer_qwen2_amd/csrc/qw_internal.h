@@ -107,8 +107,7 @@ struct DecGemvArgs {
                             // 3: merge of split-KV attention partials
   const void *act;          // mode 0: [M, lda] f16
   const long long *x_fix;   // mode 1: [M, lda] fixed-point residual rows (lda = K), stored as
-  int x_reps;               //   x_reps replicas x_rep_stride apart whose sum is the value
-  int64_t x_rep_stride;     //   (x_reps <= kMaxXReps; 0 is taken as 1)
+  int64_t x_rep_stride;     //   kXReps replicas x_rep_stride apart whose sum is the value
   const float *norm_w;      // mode 1: [K]
   float eps;                // mode 1
   const long long *act_fix; // mode 2: [M, lda] fixed-point gate/up sums (lda = 2K)
@@ -166,19 +165,19 @@ struct DecAttnOArgs {
 };
 bool dec_attn_o_supported(int head_dim, int hidden);
 
-// The decode residual stream may be kept as up to this many fixed-point
-// replicas whose sum is the value: writers that would otherwise all add into
-// the same addresses spread their atomics over the replicas.
-constexpr int kMaxXReps = 8;
+// The decode residual stream is kept as this many fixed-point replicas whose
+// sum is the value: the fused MLP, whose workgroups would otherwise all add
+// into the same addresses, spreads its atomics over them; every reader loads
+// all replicas in one batch.
+constexpr int kXReps = 2;
 
 // Decode-step MLP for one or two rows, see k_decode.hip:
 //   x_out = x_in + W_down . (silu(W_gate u) * (W_up u)),  u = RMSNorm(x_in) * norm_w
 // x_out must be zero on entry (workgroup 0 adds x_in itself).
 struct DecMlpArgs {
-  const long long *x_in;             // [reps][M, H] fixed-point residual (read; value = sum of replicas)
-  long long *x_out;                  // [reps][M, H] fixed-point residual (accumulated)
-  int reps;                          // 1 .. kMaxXReps; workgroup p adds into replica p % reps
-  int64_t rep_stride;                // elements between replicas
+  const long long *x_in;             // [kXReps][M, H] fixed-point residual (read; value = sum of replicas)
+  long long *x_out;                  // [kXReps][M, H] fixed-point residual (accumulated)
+  int64_t rep_stride;                // elements between replicas; workgroup p adds into replica p % kXReps
   const float *norm_w;               // [H] post-attention norm weight
   float eps;
   const void *w_gu;                  // [2I, H] f16, GU_BLOCK-interleaved gate/up rows
@@ -211,7 +210,7 @@ int dec_gemv_splits(int N, int K, int M, int target_groups);
 int dec_attn_splits(int batch, int n_kv_heads, int max_seq, int target_groups);
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
                             long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1);
-hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int reps, int64_t rep_stride, int B, int H,
+hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int64_t rep_stride, int B, int H,
                            const float *w, float eps, void *u);
 hipError_t launch_dec_end(hipStream_t s, const float *arg_v, const int *arg_i, int nblk, int B, int32_t *next,
                           int *pos_dev);

@@ -140,8 +140,6 @@ constexpr int kAttnTargetGroups = 256;
 // workgroup reads the whole residual rows); above it a norm kernel runs.
 constexpr int kFusedNormRows = 2;
 constexpr bool kHeadNormKernel = true;
-// Residual replicas written by the fused MLP (<= kMaxXReps).
-constexpr int kMlpReps = 2;
 // Up to this context length (and two rows), attention and the o projection
 // are one kernel in which every workgroup reads its head's whole context.
 constexpr int kAttnOMaxCtx = 1024;
@@ -341,21 +339,18 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   // xo, then the two swap
   const bool fused_mlp = fused_norm && m->L[0].w_down_t != nullptr;
   long long *xr = m->x_fix, *xo = m->x_fix2;
-  // every MLP workgroup adds into all H values of a row; spreading them over
-  // replicas of the residual halves the atomics per address (every reader
-  // then sums the replicas, which costs more with each one added)
-  const int R = fused_mlp ? kMlpReps : 1;
   // attention merged with the o projection: the q/k/v sums are still being
   // read in that kernel, so the next projection clears them instead
   const bool attn_o = decode_variant(m) == 1;
-  const int64_t xs = (int64_t)B * H;       // replica stride
+  // the residual is kXReps fixed-point replicas xs apart (value = their sum)
+  const int64_t xs = (int64_t)B * H;
   const int S = dec_attn_splits(B, c.n_kv_heads, c.max_seq, kAttnTargetGroups);
   const int64_t n_qkv = (int64_t)B * m->nqkv, n_gu = (int64_t)B * 2 * I;
   hipError_t e = timed(m, s, F_EMBED, [&] {
-    // the embedding goes to replica 0; the other replicas (fused MLP) or the
-    // gate/up accumulator are cleared
+    // the embedding goes to replica 0; the other replicas and the q/k/v
+    // accumulator are cleared (attention clears the gate/up accumulator)
     return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, m->x_fix, m->bad_ids, m->qkv_fix, n_qkv,
-                            fused_mlp ? m->x_fix + xs : m->gu_fix, fused_mlp ? (R - 1) * xs : n_gu);
+                            m->x_fix + xs, (kXReps - 1) * xs);
   });
   if (e != hipSuccess) return e;
   // operand of a projection that follows an RMSNorm
@@ -364,7 +359,6 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     if (fused_norm) {
       g.act_mode = 1;
       g.x_fix = xr;
-      g.x_reps = R;
       g.x_rep_stride = xs;
       g.norm_w = w;
       g.eps = c.rms_eps;
@@ -375,7 +369,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   };
   auto norm = [&](const float *w) -> hipError_t {
     if (fused_norm) return hipSuccess;
-    return timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, R, xs, B, H, w, c.rms_eps, m->u); });
+    return timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, w, c.rms_eps, m->u); });
   };
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerBuf &Lw = m->L[l];
@@ -407,7 +401,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       ao.H = H;
       ao.x_out = xr;
       ao.clear = fused_mlp ? xo : m->gu_fix;
-      ao.clear_n = fused_mlp ? R * xs : n_gu;
+      ao.clear_n = fused_mlp ? kXReps * xs : n_gu;
       e = timed(m, s, F_ATTN_O, [&] { return launch_dec_attn_o(s, ao); });
       if (e != hipSuccess) return e;
     } else {
@@ -431,7 +425,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       da.pos_dev = m->pos_dev;
       da.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
       da.clear = fused_mlp ? xo : m->gu_fix;
-      da.clear_n = fused_mlp ? R * xs : n_gu;
+      da.clear_n = fused_mlp ? kXReps * xs : n_gu;
       e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
       if (e != hipSuccess) return e;
       g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o);
@@ -459,7 +453,6 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       DecMlpArgs ma{};
       ma.x_in = xr;
       ma.x_out = xo;
-      ma.reps = R;
       ma.rep_stride = xs;
       ma.norm_w = Lw.post_norm;
       ma.eps = c.rms_eps;
@@ -504,7 +497,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   // by a kernel of its own rather than in every workgroup's prologue
   DecGemvArgs g = dec_args(m->head, B, V, H, m->head_scale);
   if (kHeadNormKernel || !fused_norm) {
-    e = timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, R, xs, B, H, m->final_norm, c.rms_eps, m->u); });
+    e = timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, m->final_norm, c.rms_eps, m->u); });
     if (e != hipSuccess) return e;
     g.act_mode = 0;
     g.act = m->u;
@@ -743,8 +736,8 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   CREATE_TRY(m->alloc((void **)&m->ids_stage, (size_t)c.max_batch * 4));
   if (m->fast_decode) {
     const size_t nb = (size_t)c.max_batch;
-    CREATE_TRY(m->alloc((void **)&m->x_fix, kMaxXReps * nb * H * 8));
-    CREATE_TRY(m->alloc((void **)&m->x_fix2, kMaxXReps * nb * H * 8));
+    CREATE_TRY(m->alloc((void **)&m->x_fix, kXReps * nb * H * 8));
+    CREATE_TRY(m->alloc((void **)&m->x_fix2, kXReps * nb * H * 8));
     CREATE_TRY(m->alloc((void **)&m->qkv_fix, nb * m->nqkv * 8));
     CREATE_TRY(m->alloc((void **)&m->gu_fix, nb * 2 * I * 8));
     CREATE_TRY(m->alloc((void **)&m->arg_v, nb * ((V + 63) / 64) * 4));
