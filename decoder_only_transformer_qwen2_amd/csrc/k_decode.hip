@@ -155,6 +155,47 @@ __global__ void __launch_bounds__(256) dec_end_kernel(const float *pv, const int
   }
 }
 
+// For more than two rows the projections take f16 operands that are formed
+// once, rather than in every row-block workgroup's prologue:
+//  * o[b, h] = merge of the S split-KV partials of head h (one workgroup per
+//    (head, row), one thread per dimension);
+//  * h[b, f] = silu(gate) * up from the fixed-point gate/up sums.
+__global__ void __launch_bounds__(128) dec_merge_kernel(const float *pm, const float *pl, const float *po, int S, int nq,
+                                                        int hd, f16 *o) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  if (d >= hd) return;
+  const int64_t st0 = ((int64_t)b * nq + h) * S;
+  float m[MERGE_MAX_S], l[MERGE_MAX_S], v[MERGE_MAX_S];
+#pragma unroll
+  for (int sp = 0; sp < MERGE_MAX_S; ++sp) {
+    const int64_t st = st0 + min(sp, S - 1);
+    m[sp] = pm[st];
+    l[sp] = pl[st];
+    v[sp] = po[st * hd + d];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < MERGE_MAX_S; ++sp)
+    if (sp < S) M = fmaxf(M, m[sp]);
+  float L = 0.f, O = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < MERGE_MAX_S; ++sp) {
+    const float c = (sp < S && m[sp] != -INFINITY) ? exp2f(m[sp] - M) : 0.f;
+    L = fmaf(c, l[sp], L);
+    O = fmaf(c, v[sp], O);
+  }
+  o[(int64_t)b * nq * hd + (int64_t)h * hd + d] = (f16)(O / L);
+}
+
+__global__ void __launch_bounds__(256) dec_swiglu_kernel(const long long *gu_fix, int B, int I, f16 *h) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)B * I) return;
+  const int b = (int)(idx / I), f = (int)(idx % I);
+  const long long *r2 = gu_fix + (int64_t)b * 2 * I + (f / GU_BLOCK) * 2 * GU_BLOCK + f % GU_BLOCK;
+  const float gt = from_fix(r2[0]), up = from_fix(r2[GU_BLOCK]);
+  h[idx] = (f16)(silu_f(gt) * up);
+}
+
 // ---------------------------------------------------------------- projections
 // out[b, n] (+)= sum_k act[b, k] * W[n, k] * scale for b < M <= 16 * NB.
 // One wave = 16 weight rows x a K slice; a workgroup = 4 waves = 64 rows;
@@ -904,6 +945,149 @@ hipError_t launch_attn_hd(hipStream_t s, const DecAttnArgs &a, dim3 grid, int g)
 
 }  // namespace
 
+// The same MLP with 32 features per workgroup and 8 waves: half the
+// workgroups, so half the atomics, and workgroups light enough to all be
+// resident.  Wave w multiplies tile w % 4 of the 64 packed rows (gate 0..15,
+// up 0..15, gate 16..31, up 16..31) over K half w / 4; the down product is
+// split over RG row groups of DR rows that meet in LDS.
+template <int NR, int KU, int DR>
+__global__ void __launch_bounds__(512) dec_mlp32_kernel(DecMlpArgs a) {
+  constexpr int F = 2 * GU_BLOCK;               // features per workgroup
+  constexpr int RG = F / DR;                    // row groups of the down product
+  constexpr int NPER = 4;                       // residual values per thread (H <= 2048)
+  constexpr int YH = 4096 / RG;                 // s_y columns per (group, row) slot: RG * YH = 4096
+  __shared__ float s_buf[NR * 1024];            // normalised rows (f16, H <= 2048)
+  f16 (*s_row)[2048] = reinterpret_cast<f16 (*)[2048]>(s_buf);
+  __shared__ float s_red[8][NR];
+  __shared__ float s_gu[8][NR][16];
+  __shared__ float s_h[NR][F];
+  __shared__ float s_y[RG][NR][YH];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int p = blockIdx.x, f0 = p * F;
+  const int H = a.H;
+  const f16x8 zero = {};
+  clear_share(a.clear, a.clear_n, p, gridDim.x);
+
+  const int tau = wave & 3, kh = wave >> 2;
+  const f16 *Wt = (const f16 *)a.w_gu + (int64_t)(2 * f0 + 16 * tau + i) * H;
+  const int ku = H / 64;
+  const int kw0 = kh * ku * 32;
+  f16x8 wt[KU];
+#pragma unroll
+  for (int t = 0; t < KU; ++t) wt[t] = (t < ku) ? load8(Wt + kw0 + 32 * t + 8 * g) : zero;
+  const int CB = H / 8;
+  const int rg = tid / CB, cb = tid % CB;
+  const bool d_ok = rg < RG;
+  const f16 *Wd = (const f16 *)a.w_down_t + (int64_t)(f0 + (d_ok ? rg : 0) * DR) * H + 8 * cb;
+  f16x8 wd[DR];
+#pragma unroll
+  for (int f = 0; f < DR; ++f) wd[f] = load8(Wd + (int64_t)f * H);     // threads past RG: unused
+
+  long long xq[NR][NPER];
+  {
+    float xv[NR][NPER], wv[NPER];
+    long long qr[kXReps][NR][NPER];
+#pragma unroll
+    for (int t = 0; t < NPER; ++t) {
+      const int c = t * 512 + tid, cc = min(c, H - 1);
+      const float w = a.norm_w[cc];
+      wv[t] = c < H ? w : 0.f;
+#pragma unroll
+      for (int r = 0; r < kXReps; ++r)
+#pragma unroll
+        for (int b = 0; b < NR; ++b) {
+          const long long v = a.x_in[r * a.rep_stride + (int64_t)b * H + cc];
+          qr[r][b][t] = c < H ? v : 0;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NPER; ++t)
+#pragma unroll
+      for (int b = 0; b < NR; ++b) {
+        xq[b][t] = qr[0][b][t];
+#pragma unroll
+        for (int r = 1; r < kXReps; ++r) xq[b][t] += qr[r][b][t];
+        xv[b][t] = from_fix(xq[b][t]);
+      }
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      float ss = 0.f;
+#pragma unroll
+      for (int t = 0; t < NPER; ++t) ss += xv[b][t] * xv[b][t];
+      ss = wave_sum(ss);
+      if (lane == 0) s_red[wave][b] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) tot += s_red[w][b];
+      const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
+#pragma unroll
+      for (int t = 0; t < NPER; ++t) {
+        const int c = t * 512 + tid;
+        if (c < H) s_row[b][c] = (f16)(xv[b][t] * inv * wv[t]);
+      }
+    }
+    __syncthreads();
+  }
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < KU; ++t) {
+    if (t < ku) {
+      const f16x8 xl = *reinterpret_cast<const f16x8 *>(&s_row[i < NR ? i : 0][kw0 + 32 * t + 8 * g]);
+      const f16x8 x = (i < NR) ? xl : zero;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wt[t], x, acc, 0, 0, 0);
+    }
+  }
+  if (i < NR) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_gu[wave][i][4 * g + r] = acc[r];
+  }
+  __syncthreads();
+  if (tid < NR * F) {
+    const int b = tid / F, f = tid % F, hf = f / 16, w16 = f % 16;
+    const float gt = (s_gu[2 * hf][b][w16] + s_gu[4 + 2 * hf][b][w16]) * a.gu_scale;
+    const float up = (s_gu[2 * hf + 1][b][w16] + s_gu[5 + 2 * hf][b][w16]) * a.gu_scale;
+    s_h[b][f] = silu_f(gt) * up;
+  }
+  __syncthreads();
+  if (d_ok) {
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < DR; ++f) {
+        const float hf = s_h[b][rg * DR + f];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = fmaf(hf, (float)wd[f][e], y[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_y[rg][b][8 * cb + e] = y[e];
+    }
+  }
+  __syncthreads();
+  long long *xo = a.x_out + (p % kXReps) * a.rep_stride;
+  const int rot = 64 * (p % (H / 64));
+#pragma unroll
+  for (int b = 0; b < NR; ++b)
+#pragma unroll
+    for (int t = 0; t < NPER; ++t) {
+      const int cl = t * 512 + tid;
+      if (cl < H) {
+        const int c = (cl + rot) % H;
+        float v = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) v += s_y[r][b][c];
+        const long long q = to_fix(v * a.down_scale) + (p == 0 ? xq[b][t] : 0);
+        atomicAdd(reinterpret_cast<unsigned long long *>(xo + (int64_t)b * H + c), (unsigned long long)q);
+      }
+    }
+}
+
 // ---------------------------------------------------------------- attention + o projection
 // One or two rows with a short context: attention and the o projection in one
 // kernel.  The o projection is a sum over heads, o . W_o^T = sum_h o_h .
@@ -916,7 +1100,7 @@ hipError_t launch_attn_hd(hipStream_t s, const DecAttnArgs &a, dim3 grid, int g)
 // the cache); the four waves split the keys and meet in LDS.
 template <int HD, int TPW>
 __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
-  constexpr int NW = 4, LPK = HD / 8, KPW = 64 / LPK, KSTEP = NW * KPW, HALF = HD / 2, U = 4;
+  constexpr int NW = 4, LPK = HD / 8, KPW = 64 / LPK, KSTEP = NW * KPW, HALF = HD / 2, U = 8;
   constexpr int RB = 64 * TPW;                 // W_o rows per workgroup
   __shared__ float s_q[HD], s_k[HD], s_v[HD];
   __shared__ float s_m[NW], s_l[NW];
@@ -1136,8 +1320,24 @@ bool dec_mlp_supported(int hidden, int inter) {
   return hidden % 128 == 0 && hidden <= 2048 && inter % MLP_F == 0;
 }
 
+template <int NR>
+hipError_t launch_dec_mlp32(hipStream_t s, const DecMlpArgs &a) {
+  const dim3 grid(a.I / (2 * GU_BLOCK));
+  if (a.H <= 1024)
+    QW_LAUNCH((dec_mlp32_kernel<NR, 16, 8>), dim3(grid), dim3(512), 0, s, a);
+  else if (a.H <= 1536)
+    QW_LAUNCH((dec_mlp32_kernel<NR, 24, 16>), dim3(grid), dim3(512), 0, s, a);
+  else
+    QW_LAUNCH((dec_mlp32_kernel<NR, 32, 16>), dim3(grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+constexpr bool kMlp32 = true;
+
 hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a) {
   if (!dec_mlp_supported(a.H, a.I) || a.M < 1 || a.M > 2) return hipErrorInvalidValue;
+  if (kMlp32 && a.I % (2 * GU_BLOCK) == 0 && a.H >= 512)
+    return a.M == 1 ? launch_dec_mlp32<1>(s, a) : launch_dec_mlp32<2>(s, a);
   const dim3 grid(a.I / MLP_F);
   const bool small = a.H <= 1024;
   if (a.M == 1) {
@@ -1172,9 +1372,9 @@ int dec_gemv_splits(int N, int K, int M, int target_groups) {
   return splits;
 }
 
-int dec_attn_splits(int batch, int n_kv_heads, int max_seq, int target_groups) {
+int dec_attn_splits(int batch, int n_kv_heads, int ctx, int target_groups) {
   int S = (target_groups + batch * n_kv_heads - 1) / (batch * n_kv_heads);
-  const int by_len = (max_seq + 511) / 512;    // splits of a few hundred keys at the cache's capacity
+  const int by_len = (ctx + 63) / 64;          // at least 64 keys per split
   if (S > by_len) S = by_len;
   if (S > MERGE_MAX_S) S = MERGE_MAX_S;
   if (S < 1) S = 1;
@@ -1184,6 +1384,19 @@ int dec_attn_splits(int batch, int n_kv_heads, int max_seq, int target_groups) {
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
                             long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1) {
   QW_LAUNCH((dec_embed_kernel), dim3(B), dim3(256), 0, s, ids, (const f16 *)emb, emb_scale, H, V, x_fix, bad, clr0, n0, clr1, n1);
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_merge(hipStream_t s, const float *pm, const float *pl, const float *po, int S, int B, int nq,
+                            int hd, void *o) {
+  if (S < 1 || S > MERGE_MAX_S || hd > 128) return hipErrorInvalidValue;
+  QW_LAUNCH((dec_merge_kernel), dim3(nq, B), dim3(128), 0, s, pm, pl, po, S, nq, hd, (f16 *)o);
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_swiglu(hipStream_t s, const long long *gu_fix, int B, int I, void *h) {
+  const int64_t n = (int64_t)B * I;
+  QW_LAUNCH((dec_swiglu_kernel), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu_fix, B, I, (f16 *)h);
   return hipGetLastError();
 }
 

@@ -207,7 +207,7 @@ int gemm_mfma_splits(int M, int N, int K);
 hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a);     // f16 operands
 bool decode_fast_supported(int head_dim, int group, int hidden, int q_dim, int inter);
 int dec_gemv_splits(int N, int K, int M, int target_groups);
-int dec_attn_splits(int batch, int n_kv_heads, int max_seq, int target_groups);
+int dec_attn_splits(int batch, int n_kv_heads, int ctx, int target_groups);
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
                             long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1);
 hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int64_t rep_stride, int B, int H,
@@ -217,6 +217,11 @@ hipError_t launch_dec_end(hipStream_t s, const float *arg_v, const int *arg_i, i
 hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &a);
 hipError_t launch_dec_attention(hipStream_t s, const DecAttnArgs &a);
 hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a);
+// f16 operands formed once for batches of more than two rows: the merged
+// split-KV attention output o [B, nq*hd] and silu(gate) * up h [B, I]
+hipError_t launch_dec_merge(hipStream_t s, const float *pm, const float *pl, const float *po, int S, int B, int nq,
+                            int hd, void *o);
+hipError_t launch_dec_swiglu(hipStream_t s, const long long *gu_fix, int B, int I, void *h);
 hipError_t launch_dec_attn_o(hipStream_t s, const DecAttnOArgs &a);
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
                          int32_t *next_ids, int *pos_dev, int pos_add);

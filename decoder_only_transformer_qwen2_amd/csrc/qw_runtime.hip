@@ -54,12 +54,14 @@ qw_status fail(qw_status st, const char *fmt, ...) {
   } while (0)
 
 enum Family { F_EMBED, F_RMSNORM, F_GEMM_QKV, F_ROPE_CACHE, F_ATTENTION, F_GEMM_O, F_GEMM_GATE_UP,
-              F_GEMM_DOWN, F_LM_HEAD, F_ARGMAX, F_MLP, F_ATTN_O, F_COUNT };
+              F_GEMM_DOWN, F_LM_HEAD, F_ARGMAX, F_MLP, F_ATTN_O, F_ATTN_MERGE, F_SWIGLU, F_COUNT };
 const char *const kFamilyNames[] = {"embed",  "rmsnorm",      "gemm_qkv",  "rope_cache", "attention", "gemm_o",
-                                    "gemm_gate_up", "gemm_down", "lm_head", "argmax", "mlp", "attn_o"};
+                                    "gemm_gate_up", "gemm_down", "lm_head", "argmax", "mlp", "attn_o",
+                                    "attn_merge", "swiglu"};
 static_assert(sizeof(kFamilyNames) / sizeof(kFamilyNames[0]) == F_COUNT, "one name per kernel family");
 const char *const kFamilyList =
-    "embed,rmsnorm,gemm_qkv,rope_cache,attention,gemm_o,gemm_gate_up,gemm_down,lm_head,argmax,mlp,attn_o";
+    "embed,rmsnorm,gemm_qkv,rope_cache,attention,gemm_o,gemm_gate_up,gemm_down,lm_head,argmax,mlp,attn_o,"
+    "attn_merge,swiglu";
 
 struct LayerBuf {
   void *w_qkv = nullptr;    // [qd + 2 kvd, H]
@@ -135,7 +137,7 @@ namespace {
 
 // Workgroups a decode projection / attention launch aims for (256 CUs).
 constexpr int kGemvTargetGroups = 1024;
-constexpr int kAttnTargetGroups = 256;
+constexpr int kAttnTargetGroups = 1024;
 // Up to this many rows, a projection normalises its own operand (each
 // workgroup reads the whole residual rows); above it a norm kernel runs.
 constexpr int kFusedNormRows = 2;
@@ -145,14 +147,16 @@ constexpr bool kHeadNormKernel = true;
 constexpr int kAttnOMaxCtx = 1024;
 
 // Which decode step the next decode call runs: 1 = attention merged with the
-// o projection (short context), 0 = split-KV attention, then o projection.
-// A captured graph is only replayed for the variant it was captured with.
+// o projection (short context), 2 + S = split-KV attention over S splits,
+// then the o projection (S follows the context length, so it grows as the
+// sequence does), 0 = the generic (fp32) step.  A captured graph is only
+// replayed for the variant it was captured with.
 int decode_variant(const qw_model *m) {
   const qw_config &c = m->cfg;
-  return (m->fast_decode && m->batch <= kFusedNormRows && m->pos + 1 <= kAttnOMaxCtx &&
-          dec_attn_o_supported(c.head_dim, c.hidden))
-             ? 1
-             : 0;
+  if (!m->fast_decode) return 0;
+  if (m->batch <= kFusedNormRows && m->pos + 1 <= kAttnOMaxCtx && dec_attn_o_supported(c.head_dim, c.hidden))
+    return 1;
+  return 2 + dec_attn_splits(m->batch, c.n_kv_heads, m->pos + 1, kAttnTargetGroups);
 }
 
 // While timing family `fam`, its kernel launches record an event pair at the
@@ -341,10 +345,11 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   long long *xr = m->x_fix, *xo = m->x_fix2;
   // attention merged with the o projection: the q/k/v sums are still being
   // read in that kernel, so the next projection clears them instead
-  const bool attn_o = decode_variant(m) == 1;
+  const int variant = decode_variant(m);
+  const bool attn_o = variant == 1;
+  const int S = variant >= 2 ? variant - 2 : 1;
   // the residual is kXReps fixed-point replicas xs apart (value = their sum)
   const int64_t xs = (int64_t)B * H;
-  const int S = dec_attn_splits(B, c.n_kv_heads, c.max_seq, kAttnTargetGroups);
   const int64_t n_qkv = (int64_t)B * m->nqkv, n_gu = (int64_t)B * 2 * I;
   hipError_t e = timed(m, s, F_EMBED, [&] {
     // the embedding goes to replica 0; the other replicas and the q/k/v
@@ -429,7 +434,15 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
       if (e != hipSuccess) return e;
       g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o);
-      if (S > 1) {
+      if (S > 1 && !fused_norm) {
+        // many rows: merge once, then an f16 operand
+        e = timed(m, s, F_ATTN_MERGE, [&] {
+          return launch_dec_merge(s, m->att_m, m->att_l, m->att_o, S, B, c.n_heads, c.head_dim, m->o);
+        });
+        if (e != hipSuccess) return e;
+        g.act_mode = 0;
+        g.act = m->o;
+      } else if (S > 1) {
         g.act_mode = 3;
         g.part_m = m->att_m;
         g.part_l = m->att_l;
@@ -485,9 +498,18 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     e = timed(m, s, F_GEMM_GATE_UP, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
     g = dec_args(Lw.w_down, B, H, I, Lw.s_down);
-    g.act_mode = 2;
-    g.act_fix = m->gu_fix;
-    g.lda = 2 * I;
+    if (fused_norm) {
+      g.act_mode = 2;
+      g.act_fix = m->gu_fix;
+      g.lda = 2 * I;
+    } else {
+      // many rows: silu(gate) * up once, then an f16 operand
+      e = timed(m, s, F_SWIGLU, [&] { return launch_dec_swiglu(s, m->gu_fix, B, I, m->h); });
+      if (e != hipSuccess) return e;
+      g.act_mode = 0;
+      g.act = m->h;
+      g.lda = I;
+    }
     g.out_fix = xr;
     g.ldo = H;
     e = timed(m, s, F_GEMM_DOWN, [&] { return launch_dec_gemv(s, g); });
