@@ -37,7 +37,19 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, g = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;          // wave's 64 x 64 sub-tile
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // Tile order: workgroups are dealt round-robin to the 8 XCDs, each with its
+  // own L2.  Workgroup L therefore takes tile t = (L % 8) * per_x + L / 8, so
+  // each XCD works through a contiguous range of t; t runs over groups of
+  // GM row tiles, column by column, so the tiles in flight on one XCD share
+  // their A rows and B columns in that XCD's L2.
+  constexpr int GM = 4;
+  const int TM = (a.M + BM - 1) / BM, TN = (a.N + BN - 1) / BN;
+  const int per_x = (TM * TN + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per_x + (int)(blockIdx.x / 8);
+  if (t >= TM * TN) return;
+  const int grp = t / (GM * TN), within = t % (GM * TN);
+  const int gsz = min(GM, TM - grp * GM);
+  const int m0 = (grp * GM + within % gsz) * BM, n0 = (within / gsz) * BN;
   const f16 *A = (const f16 *)a.A;
   const f16 *W = (const f16 *)a.W;
   const f16x8 zero = {};
@@ -205,7 +217,8 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (!gemm_mfma_supported(a)) return hipErrorInvalidValue;
   const int S = (a.splits > 1 && a.ws) ? a.splits : 1;
-  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM, S);
+  const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
+  dim3 grid(8 * ((tiles + 7) / 8), 1, S);
   switch (a.epi) {
     case Epi::StoreF32: QW_LAUNCH((gemm_mfma_kernel<Epi::StoreF32>), dim3(grid), dim3(256), 0, s, a); break;
     case Epi::ResidAdd: QW_LAUNCH((gemm_mfma_kernel<Epi::ResidAdd>), dim3(grid), dim3(256), 0, s, a); break;
