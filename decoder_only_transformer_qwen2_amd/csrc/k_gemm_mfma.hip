@@ -12,12 +12,16 @@
 // a second kernel adds the slices in slice order (deterministic) and applies
 // the epilogue.
 //
-// Tiling: a workgroup computes a 128 x 128 tile with 4 wavefronts (2 x 2),
-// each a 64 x 64 sub-tile = 4 x 4 MFMA tiles of 16 x 16.  K advances 64 at a
-// time; both operand tiles are staged in LDS (rows padded by 16 bytes so the
-// 16 rows an MFMA operand load touches fall in different banks) with two
-// buffers: the next tile's global loads are in flight while the current
-// tile is multiplied, and one barrier per K step orders the buffers.
+// Two kernels share the epilogues:
+//  * gemm_lds_kernel (K % 32 == 0, the model's shapes): operands go straight
+//    from memory into LDS (16 bytes per lane) through a ring of BK = 32
+//    stages, with no staging registers; 256 x 256 tiles on 8 waves when there
+//    are enough of them (a quarter of the operand bytes per FLOP of 128 x 128:
+//    the 128 x 128 version is bound by operand traffic from L2, not by MFMA),
+//    128 x 128 on 4 waves otherwise.
+//  * gemm_mfma_kernel (any K % 8 == 0): 128 x 128 x 64 tiles, both operands
+//    staged through registers into two LDS buffers (rows padded by 16 bytes).
+// Both order their tiles per XCD (see the kernels).
 #include "qw_internal.h"
 
 namespace qw {
@@ -168,6 +172,179 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
   }
 }
 
+// The same tile with the operands loaded straight into LDS
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base
+// + 16 * lane) through a ring of four BK = 32 stages, three of them in flight
+// while one is multiplied, and no staging registers.  A stage holds 128 rows x
+// 4 chunks of 16 bytes per operand, chunk c of row r stored at position
+// c ^ ((r >> 1) & 3), so the 16 rows an MFMA operand read touches spread over
+// the banks.  Rows past M or N load a clamped row and are never stored;
+// K % 32 == 0.
+constexpr int LK = 32, NSTG = 4;
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 3; }
+
+// One 16-byte-per-lane load straight into LDS at the wave-uniform address
+// `lds` (+ 16 * lane).  Issued as assembly so that the compiler does not
+// drain every load in flight before each LDS read it cannot prove disjoint
+// from it; completion is awaited explicitly (s_waitcnt vmcnt) before the
+// barrier that publishes a stage.
+__device__ __forceinline__ void dma16(const void *src, const void *lds) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);   // wave-uniform
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0v) : "memory");
+}
+// s_barrier without the release/acquire fences __syncthreads carries (the
+// waits they imply are issued explicitly); the empty asm keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <Epi EPI, int TBM, int TBN, int WVM, int WVN, int NS>
+__global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
+  constexpr int NWV = WVM * WVN;                  // waves
+  constexpr int XT = TBM / WVM / 16, YT = TBN / WVN / 16;   // MFMA tiles per wave
+  constexpr int QA = TBM / 16 / NWV, QB = TBN / 16 / NWV;   // load instructions per wave and stage
+  static_assert(TBN / WVN == 64, "a wave's 64 columns hold two gate/up pairs");
+  __shared__ f16x8 sA[NS][TBM * 4];
+  __shared__ f16x8 sB[NS][TBN * 4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int wm = wave / WVN, wn = wave % WVN;
+  constexpr int GM = 4;
+  const int TM = (a.M + TBM - 1) / TBM, TN = (a.N + TBN - 1) / TBN;
+  const int per_x = (TM * TN + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per_x + (int)(blockIdx.x / 8);
+  if (t >= TM * TN) return;
+  const int grp = t / (GM * TN), within = t % (GM * TN);
+  const int gsz = min(GM, TM - grp * GM);
+  const int m0 = (grp * GM + within % gsz) * TBM, n0 = (within / gsz) * TBN;
+  const f16 *A = (const f16 *)a.A;
+  const f16 *W = (const f16 *)a.W;
+
+  // wave w, instruction q covers stage positions 64 (QA w + q) .. + 63, i.e.
+  // rows 16 (QA w + q) + lane / 4 (likewise for B)
+  const int KT_all = a.K / LK;
+  const int kt_per = (KT_all + gridDim.z - 1) / gridDim.z;
+  const int kt0 = blockIdx.z * kt_per;
+  const int KT = max(0, min(KT_all, kt0 + kt_per) - kt0);
+  const f16 *srcA[QA], *srcB[QB];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int row = 16 * (QA * wave + q) + (lane >> 2);
+    const int c = (lane & 3) ^ lds_swz(row);
+    srcA[q] = A + (int64_t)min(m0 + row, a.M - 1) * a.lda + (int64_t)kt0 * LK + 8 * c;
+  }
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    const int row = 16 * (QB * wave + q) + (lane >> 2);
+    const int c = (lane & 3) ^ lds_swz(row);
+    srcB[q] = W + (int64_t)min(n0 + row, a.N - 1) * a.K + (int64_t)kt0 * LK + 8 * c;
+  }
+  auto issue = [&](int kt) {
+    const int st = kt % NS;
+#pragma unroll
+    for (int q = 0; q < QA; ++q) dma16(srcA[q] + kt * LK, &sA[st][64 * (QA * wave + q)]);
+#pragma unroll
+    for (int q = 0; q < QB; ++q) dma16(srcB[q] + kt * LK, &sB[st][64 * (QB * wave + q)]);
+  };
+  constexpr int PER_STAGE = QA + QB;              // vmcnt per stage and wave
+
+  f32x4 acc[XT][YT];
+#pragma unroll
+  for (int x = 0; x < XT; ++x)
+#pragma unroll
+    for (int y = 0; y < YT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k)
+    if (k < KT) issue(k);
+  for (int kt = 0; kt < KT; ++kt) {
+    // stage kt done (this wave's loads; later stages may stay in flight)
+    const int ahead = min(NS - 2, KT - 1 - kt);
+    if (ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(((2 * PER_STAGE) & 15) | (7 << 4) | (15 << 8));
+    else if (ahead == 1)
+      __builtin_amdgcn_s_waitcnt((PER_STAGE & 15) | (7 << 4) | (15 << 8));
+    else
+      __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+    stage_barrier();                     // every wave's share of stage kt is in; stage kt - 1 is consumed
+    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+    const int st = kt % NS;
+    f16x8 fa[XT], fb[YT];
+#pragma unroll
+    for (int x = 0; x < XT; ++x) {
+      const int row = wm * (TBM / WVM) + x * 16 + i;
+      fa[x] = sA[st][row * 4 + (g ^ lds_swz(row))];
+    }
+#pragma unroll
+    for (int y = 0; y < YT; ++y) {
+      const int row = wn * 64 + y * 16 + i;
+      fb[y] = sB[st][row * 4 + (g ^ lds_swz(row))];
+    }
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+#pragma unroll
+      for (int y = 0; y < YT; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+  }
+
+  // acc[x][y]: lane (i, g) holds rows 4g..4g+3 of column i of MFMA tile (x, y)
+  const int rw0 = m0 + wm * (TBM / WVM), cw0 = n0 + wn * 64;
+  if (gridDim.z > 1) {
+    float *ws = a.ws + (int64_t)blockIdx.z * a.M * a.N;
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+#pragma unroll
+      for (int y = 0; y < YT; ++y) {
+        const int col = cw0 + y * 16 + i;
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rw0 + x * 16 + 4 * g + r;
+          if (row < a.M) ws[(int64_t)row * a.N + col] = acc[x][y][r];
+        }
+      }
+    return;
+  }
+  if constexpr (EPI == Epi::SwiGLU) {
+    f16 *out = (f16 *)a.act_out;
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int f = cw0 / 2 + p * GU_BLOCK + i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rw0 + x * 16 + 4 * g + r;
+          if (row < a.M && f < a.N / 2) {
+            const float gt = acc[x][2 * p][r] * a.scale, up = acc[x][2 * p + 1][r] * a.scale;
+            out[(int64_t)row * a.ldo + f] = (f16)(silu_f(gt) * up);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+#pragma unroll
+      for (int y = 0; y < YT; ++y) {
+        const int col = cw0 + y * 16 + i;
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rw0 + x * 16 + 4 * g + r;
+          if (row >= a.M) continue;
+          float *o = a.out_f32 + (int64_t)row * a.ldo + col;
+          const float v = acc[x][y][r] * a.scale;
+          if constexpr (EPI == Epi::ResidAdd)
+            *o += v;
+          else
+            *o = v;
+        }
+      }
+  }
+}
+
 // out = epilogue(sum over slices of ws[slice]), one thread per output value
 template <Epi EPI>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a, int S) {
@@ -199,6 +376,11 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a, int S) {
 
 }  // namespace
 
+constexpr bool kLdsPipeline = true;
+// 256 x 256 tiles halve the operand bytes per FLOP; they pay once there are
+// enough of them to fill the chip a few times over.
+static bool use_big_tile(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256) >= 512; }
+
 int gemm_mfma_splits(int M, int N, int K) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (tiles >= 128) return 1;
@@ -219,7 +401,21 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
   const int S = (a.splits > 1 && a.ws) ? a.splits : 1;
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   dim3 grid(8 * ((tiles + 7) / 8), 1, S);
-  switch (a.epi) {
+  if (kLdsPipeline && a.K % LK == 0 && use_big_tile(a.M, a.N) && S == 1) {
+    const int big = ((a.N + 255) / 256) * ((a.M + 255) / 256);
+    dim3 g2(8 * ((big + 7) / 8), 1, 1);
+    switch (a.epi) {
+      case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, 3>), dim3(g2), dim3(512), 0, s, a); break;
+      case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, 3>), dim3(g2), dim3(512), 0, s, a); break;
+      case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 256, 256, 2, 4, 3>), dim3(g2), dim3(512), 0, s, a); break;
+    }
+  } else if (kLdsPipeline && a.K % LK == 0) {
+    switch (a.epi) {
+      case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a); break;
+      case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a); break;
+      case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a); break;
+    }
+  } else switch (a.epi) {
     case Epi::StoreF32: QW_LAUNCH((gemm_mfma_kernel<Epi::StoreF32>), dim3(grid), dim3(256), 0, s, a); break;
     case Epi::ResidAdd: QW_LAUNCH((gemm_mfma_kernel<Epi::ResidAdd>), dim3(grid), dim3(256), 0, s, a); break;
     case Epi::SwiGLU: QW_LAUNCH((gemm_mfma_kernel<Epi::SwiGLU>), dim3(grid), dim3(256), 0, s, a); break;
