@@ -13,8 +13,11 @@
 // probabilities already sit in the B-operand layout of the second product
 // (the key order inside each 32-key step is permuted identically on the V^T
 // side), so P never goes through LDS.  A workgroup is 4 waves x 32 queries of
-// one head; the K tile ([key][d]) and the transposed V tile ([d][key]) are
-// staged in LDS with two buffers.  Work items are ordered heaviest (latest
+// one head; the K tile ([key][d]) and the V^T tile ([d][key]) are staged in
+// LDS with two buffers, both as 16-byte vectors: V^T comes from a transposed
+// copy of the prompt's V written once per layer (transpose_v_kernel), since
+// transposing inside the kernel took 2-byte LDS stores with 16-way bank
+// conflicts.  Work items are ordered heaviest (latest
 // query tile) first and mapped so that the g query heads of a KV head and
 // query tile run on the same XCD, where they share the K/V tiles in L2.
 #include "qw_internal.h"
@@ -88,14 +91,18 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
   const int q_last = min(P - 1, qt * BQ + BQ - 1);    // last query of the workgroup
   const int n_kb = q_last / BKEY + 1;                  // key blocks it needs
   f16x8 rk[VPT], rv[VPT];
+  // K rows [key][d] from the cache, V^T rows [d][key] from the transposed
+  // copy (rows of round_up(P, 64) keys, zero past P): both as 16-byte vectors
+  const int PP = (P + BKEY - 1) / BKEY * BKEY;
+  const f16 *Vt = (const f16 *)a.v_t + ((int64_t)b * a.n_kv_heads + j) * HD * PP;
   auto gload = [&](int kb) {
 #pragma unroll
     for (int t = 0; t < VPT; ++t) {
       const int v = tid + 256 * t;
       const int key = kb * BKEY + v / (HD / 8), c = (v % (HD / 8)) * 8;
-      const bool ok = key < P;
-      rk[t] = ok ? *reinterpret_cast<const f16x8 *>(Kc + (int64_t)key * HD + c) : zero8;
-      rv[t] = ok ? *reinterpret_cast<const f16x8 *>(Vc + (int64_t)key * HD + c) : zero8;
+      rk[t] = key < P ? *reinterpret_cast<const f16x8 *>(Kc + (int64_t)key * HD + c) : zero8;
+      const int d = v / (BKEY / 8), kc = (v % (BKEY / 8)) * 8;
+      rv[t] = *reinterpret_cast<const f16x8 *>(Vt + (int64_t)d * PP + kb * BKEY + kc);
     }
   };
   auto lstore = [&](int buf) {
@@ -104,8 +111,8 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
       const int v = tid + 256 * t;
       const int key = v / (HD / 8), c = (v % (HD / 8)) * 8;
       *reinterpret_cast<f16x8 *>(&sK[buf][key][c]) = rk[t];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sV[buf][c + e][key] = rv[t][e];
+      const int d = v / (BKEY / 8), kc = (v % (BKEY / 8)) * 8;
+      *reinterpret_cast<f16x8 *>(&sV[buf][d][kc]) = rv[t];
     }
   };
 
@@ -210,6 +217,37 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
 }  // namespace
 
 bool attn_prefill_supported(int head_dim) { return head_dim == 32 || head_dim == 64 || head_dim == 128; }
+
+// 64 keys x 64 dims per workgroup through LDS, so that both the reads (rows
+// of the cache) and the writes (rows of V^T) are contiguous.
+__global__ void __launch_bounds__(256) transpose_v_kernel(const f16 *v_cache, int n_kv_heads, int max_seq, int hd,
+                                                          int P, int PP, f16 *v_t) {
+  __shared__ f16 tile[64][66];
+  const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64, bj = blockIdx.z;
+  const f16 *src = v_cache + (int64_t)bj * max_seq * hd;
+  f16 *dst = v_t + (int64_t)bj * hd * PP;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int r = e / 64, c = e % 64;            // key r, dim c
+    const int key = t0 + r, d = d0 + c;
+    tile[r][c] = (key < P && d < hd) ? src[(int64_t)key * hd + d] : (f16)0.f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int r = e / 64, c = e % 64;            // dim r, key c
+    const int d = d0 + r, key = t0 + c;
+    if (d < hd && key < PP) dst[(int64_t)d * PP + key] = tile[c][r];
+  }
+}
+
+hipError_t launch_transpose_v(hipStream_t s, const void *v_cache, int B, int n_kv_heads, int max_seq, int head_dim,
+                              int P, void *v_t) {
+  if (P <= 0) return hipSuccess;
+  const int PP = (P + BKEY - 1) / BKEY * BKEY;
+  dim3 grid(PP / 64, (head_dim + 63) / 64, B * n_kv_heads);
+  QW_LAUNCH((transpose_v_kernel), dim3(grid), dim3(256), 0, s, (const f16 *)v_cache, n_kv_heads, max_seq, head_dim,
+            P, PP, (f16 *)v_t);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a) {
   if (a.T <= 0) return hipSuccess;

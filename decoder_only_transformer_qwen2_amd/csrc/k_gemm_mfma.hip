@@ -16,7 +16,7 @@
 //  * gemm_lds_kernel (K % 32 == 0, the model's shapes): operands go straight
 //    from memory into LDS (16 bytes per lane) through a ring of BK = 32
 //    stages, with no staging registers; 256 x 256 tiles on 8 waves when there
-//    are enough of them (a quarter of the operand bytes per FLOP of 128 x 128:
+//    are enough of them (half the operand bytes per FLOP of 128 x 128:
 //    the 128 x 128 version is bound by operand traffic from L2, not by MFMA),
 //    128 x 128 on 4 waves otherwise.
 //  * gemm_mfma_kernel (any K % 8 == 0): 128 x 128 x 64 tiles, both operands

@@ -92,6 +92,7 @@ struct RopeCacheArgs {
 struct AttnArgs {
   const void *q;              // [T, nq*hd]
   const void *k_cache, *v_cache;  // layer base
+  const void *v_t;            // prefill (f16): V of the prompt transposed, [B][nkv][hd][round_up(P, 64)]
   void *o;                    // [T, nq*hd]
   int T, rows_per_seq, n_heads, n_kv_heads, head_dim, max_seq;
   int pos0;
@@ -201,6 +202,9 @@ hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &
 hipError_t launch_attention_generic(hipStream_t s, bool f16_mode, const AttnArgs &a);
 bool attn_prefill_supported(int head_dim);
 hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a);   // f16, prompt from position 0
+// v_t[b][j][d][t] = V cache[b][j][t][d] for t < P, 0 for P <= t < round_up(P, 64)
+hipError_t launch_transpose_v(hipStream_t s, const void *v_cache, int B, int n_kv_heads, int max_seq, int head_dim,
+                              int P, void *v_t);
 hipError_t launch_gemm_generic(hipStream_t s, bool f16_mode, const GemmArgs &a);
 bool gemm_mfma_supported(const GemmArgs &a);
 int gemm_mfma_splits(int M, int N, int K);

@@ -107,6 +107,7 @@ struct qw_model {
   float *arg_v = nullptr;            // [max_batch, ceil(V / 64)]
   int *arg_i = nullptr;
   float *att_m = nullptr, *att_l = nullptr, *att_o = nullptr;   // split-KV partials
+  void *v_t = nullptr;               // prefill: V of the prompt transposed (f16 mode)
   float *splitk_ws = nullptr;        // prefill split-K slices (grown on demand)
   size_t splitk_bytes = 0;
   int batch = 0, pos = 0;
@@ -267,9 +268,15 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
     aa.pos0 = pos0;
     aa.pos0_dev = pos_dev;
     aa.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
-    if (m->f16 && !pos_dev && pos0 == 0 && attn_prefill_supported(c.head_dim))
+    aa.v_t = m->v_t;
+    if (m->f16 && !pos_dev && pos0 == 0 && attn_prefill_supported(c.head_dim)) {
+      const int B = T / rows_per_seq;
+      e = timed(m, s, F_ROPE_CACHE, [&] {
+        return launch_transpose_v(s, vc, B, c.n_kv_heads, c.max_seq, c.head_dim, rows_per_seq, m->v_t);
+      });
+      if (e != hipSuccess) return e;
       e = timed(m, s, F_ATTENTION, [&] { return launch_attention_prefill(s, aa); });
-    else
+    } else
       e = timed(m, s, F_ATTENTION, [&] { return launch_attention_generic(s, m->f16, aa); });
 
     if (e != hipSuccess) return e;
@@ -753,6 +760,8 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   CREATE_TRY(m->alloc(&m->o, R * m->qd * es));
   CREATE_TRY(m->alloc(&m->h, R * I * es));
   CREATE_TRY(m->alloc((void **)&m->logits, (size_t)c.max_batch * V * 4));
+  if (m->f16)
+    CREATE_TRY(m->alloc(&m->v_t, (size_t)c.max_batch * c.n_kv_heads * c.head_dim * ((c.max_seq + 63) / 64 * 64) * 2));
   CREATE_TRY(m->alloc((void **)&m->pos_dev, 256));
   CREATE_TRY(m->alloc((void **)&m->bad_ids, 256));
   CREATE_TRY(m->alloc((void **)&m->ids_stage, (size_t)c.max_batch * 4));
