@@ -138,31 +138,44 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
 #pragma unroll
           for (int t = 0; t < 2; ++t) s[y][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[t][ks], s[y][t], 0, 0, 0);
         }
-      // online softmax per query column; lane (i, g) holds keys 16y + 4g + r
+      // online softmax per query column; lane (i, g) holds keys 16y + 4g + r.
+      // Scores stay unscaled: the scale goes into the exponent's FMA, and
+      // only blocks that reach past the wave's first query are masked.  The
+      // running max is finite from block 0 on (key 0 is visible to every
+      // query), and masked scores are -inf, so exp2 needs no guards.
+      const bool diag = kb * BKEY + BKEY - 1 > q0;
       f16x8 pb[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int q = q0 + 16 * t + i;
         float mx = -INFINITY;
+        if (diag) {
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
+          for (int y = 0; y < 4; ++y)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kb * BKEY + 16 * y + 4 * g + r;
-            const float v = (key <= q) ? s[y][t][r] * sl2 : -INFINITY;
-            s[y][t][r] = v;
-            mx = fmaxf(mx, v);
-          }
+            for (int r = 0; r < 4; ++r) {
+              const int key = kb * BKEY + 16 * y + 4 * g + r;
+              const float v = (key <= q) ? s[y][t][r] : -INFINITY;
+              s[y][t][r] = v;
+              mx = fmaxf(mx, v);
+            }
+        } else {
+#pragma unroll
+          for (int y = 0; y < 4; ++y)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[y][t][r]);
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mn = fmaxf(m[t], mx);
-        const float corr = (m[t] == -INFINITY) ? 0.f : exp2f(m[t] - mn);
+        const float corr = exp2f((m[t] - mn) * sl2);
+        const float nb = -mn * sl2;
         float sum = 0.f;
 #pragma unroll
         for (int y = 0; y < 4; ++y)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = (mn == -INFINITY) ? 0.f : exp2f(s[y][t][r] - mn);
+            const float p = exp2f(fmaf(s[y][t][r], sl2, nb));
             s[y][t][r] = p;
             sum += p;
           }
