@@ -377,11 +377,22 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a, int S) {
 }  // namespace
 
 constexpr bool kLdsPipeline = true;
-// 256 x 256 tiles halve the operand bytes per FLOP; they pay once there are
-// enough of them to fill the chip a few times over.
-static bool use_big_tile(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256) >= 512; }
+// 256 x 256 tiles halve the operand bytes per FLOP.  One workgroup runs per
+// CU, so they pay once there are enough of them to fill the chip a few times
+// over: with at least 512 tiles K is not split; with 192 .. 511 tiles (the
+// N = H projections of a long prefill) K is split in two (three rounds of 256
+// instead of one and a half), as long as each slice keeps 24 K tiles.
+// Returns the K slices for the 256 x 256 kernel, or 0 where it is not used.
+static int big_tile_splits(int M, int N, int K) {
+  if (!kLdsPipeline || K % LK) return 0;
+  const int big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= 512) return 1;
+  if (big >= 192 && K / LK >= 48) return 2;
+  return 0;
+}
 
 int gemm_mfma_splits(int M, int N, int K) {
+  if (const int bs = big_tile_splits(M, N, K)) return bs;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (tiles >= 128) return 1;
   int S = (256 + tiles - 1) / tiles;
@@ -401,9 +412,9 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
   const int S = (a.splits > 1 && a.ws) ? a.splits : 1;
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   dim3 grid(8 * ((tiles + 7) / 8), 1, S);
-  if (kLdsPipeline && a.K % LK == 0 && use_big_tile(a.M, a.N) && S == 1) {
+  if (big_tile_splits(a.M, a.N, a.K) > 0) {
     const int big = ((a.N + 255) / 256) * ((a.M + 255) / 256);
-    dim3 g2(8 * ((big + 7) / 8), 1, 1);
+    dim3 g2(8 * ((big + 7) / 8), 1, S);
     switch (a.epi) {
       case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, 3>), dim3(g2), dim3(512), 0, s, a); break;
       case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, 3>), dim3(g2), dim3(512), 0, s, a); break;
