@@ -16,6 +16,7 @@ the CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,8 @@ import synthetic as S  # noqa: E402
 
 METRIC = "decode tokens/s + prefill tokens/s (TTFT) at 1 MI355X; % HBM / MFMA roofline"
 HBM_PEAK_GBS = 8000.0
+# committed rocprofv3 counter summary for the dominant decode kernel
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_mlp_0.5b_hbm_traffic.json")
 MFMA_F16_PEAK_TFLOPS = 2500.0
 DESCRIPTIONS = {
     "tiny": "tiny Qwen2-style decoder, fp32 (2 layers, hidden 128), batch 1, prompt 16, 8 greedy decode steps",
@@ -66,6 +69,23 @@ def decode_family_bytes(w: S.Workload, family: str, ctx_mean: float) -> float:
     if family == "attention":
         return B * m.n_kv_heads * ctx_mean * m.head_dim * e * 2 + 2 * B * qd * e
     return float("nan")
+
+
+def measured_traffic(workload: str, family: str):
+    """HBM bytes per launch of a kernel family from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for
+    a copy of known size), or None when the summary is for another workload or
+    family, or the kernel's source file has changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+        with open(os.path.join(ROOT, d["kernel_source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError, KeyError):
+        return None
+    if sha != d.get("kernel_source_sha256") or d.get("workload") != workload or d.get("family") != family:
+        return None
+    return int(d["fetch_bytes_per_launch"] + d["write_bytes_per_launch"])
 
 
 def decode_step_bytes(w: S.Workload, ctx_mean: float) -> float:
@@ -237,7 +257,8 @@ def main():
         bytes_per = decode_family_bytes(w, dom, ctx_mean)
         achieved = bytes_per / avg_s / 1e9
         out["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic(args.workload, dom),
                            "avg_launch_us": round(avg_s * 1e6, 3), "launches": n,
                            "algorithmic_bytes_per_launch": int(bytes_per)}
         out["decode_family_ms_per_step"] = {f: round(per[f][0] / D, 4) for f in per}

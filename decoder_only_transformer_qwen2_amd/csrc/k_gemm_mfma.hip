@@ -362,15 +362,28 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a, int S) {
     }
     ((f16 *)a.act_out)[(int64_t)row * a.ldo + f] = (f16)(silu_f(gt * a.scale) * (up * a.scale));
   } else {
-    if (idx >= slice) return;
-    const int row = (int)(idx / a.N), col = (int)(idx % a.N);
-    float v = 0.f;
-    for (int z = 0; z < S; ++z) v += a.ws[z * slice + idx];
-    float *o = a.out_f32 + (int64_t)row * a.ldo + col;
-    if constexpr (EPI == Epi::ResidAdd)
-      *o += v * a.scale;
-    else
-      *o = v * a.scale;
+    // four consecutive columns per thread (N and ldo are multiples of 4)
+    const int64_t i4 = idx * 4;
+    if (i4 >= slice) return;
+    const int row = (int)(i4 / a.N), col = (int)(i4 % a.N);
+    float4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < S; ++z) {
+      const float4 w = *reinterpret_cast<const float4 *>(a.ws + z * slice + i4);
+      v.x += w.x;
+      v.y += w.y;
+      v.z += w.z;
+      v.w += w.w;
+    }
+    float4 *o = reinterpret_cast<float4 *>(a.out_f32 + (int64_t)row * a.ldo + col);
+    float4 r = {v.x * a.scale, v.y * a.scale, v.z * a.scale, v.w * a.scale};
+    if constexpr (EPI == Epi::ResidAdd) {
+      const float4 x = *o;
+      r.x += x.x;
+      r.y += x.y;
+      r.z += x.z;
+      r.w += x.w;
+    }
+    *o = r;
   }
 }
 
@@ -392,6 +405,7 @@ static int big_tile_splits(int M, int N, int K) {
 }
 
 int gemm_mfma_splits(int M, int N, int K) {
+  if (N % 4) return 1;                           // the reduce takes four columns per thread
   if (const int bs = big_tile_splits(M, N, K)) return bs;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (tiles >= 128) return 1;
@@ -409,7 +423,7 @@ bool gemm_mfma_supported(const GemmArgs &a) {
 hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (!gemm_mfma_supported(a)) return hipErrorInvalidValue;
-  const int S = (a.splits > 1 && a.ws) ? a.splits : 1;
+  const int S = (a.splits > 1 && a.ws && a.N % 4 == 0 && a.ldo % 4 == 0) ? a.splits : 1;
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   dim3 grid(8 * ((tiles + 7) / 8), 1, S);
   if (big_tile_splits(a.M, a.N, a.K) > 0) {
@@ -433,7 +447,7 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  const int64_t n = (a.epi == Epi::SwiGLU) ? (int64_t)a.M * (a.N / 2) : (int64_t)a.M * a.N;
+  const int64_t n = (a.epi == Epi::SwiGLU) ? (int64_t)a.M * (a.N / 2) : (int64_t)a.M * a.N / 4;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   switch (a.epi) {
     case Epi::StoreF32: splitk_reduce_kernel<Epi::StoreF32><<<blocks, 256, 0, s>>>(a, S); break;
