@@ -237,7 +237,7 @@ def main():
 
     if not args.no_roofline:
         # per-family decode time, each family timed over one eager pass
-        fams = ["gemm_qkv", "rope_cache", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "mlp", "attn_o", "attn_merge", "swiglu", "lm_head",
+        fams = ["gemm_qkv", "rope_cache", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "mlp", "attn_o", "attn_merge", "lm_head",
                 "argmax", "rmsnorm", "embed"]
         per = {}
         for f in fams:

@@ -155,11 +155,10 @@ __global__ void __launch_bounds__(256) dec_end_kernel(const float *pv, const int
   }
 }
 
-// For more than two rows the projections take f16 operands that are formed
-// once, rather than in every row-block workgroup's prologue:
-//  * o[b, h] = merge of the S split-KV partials of head h (one workgroup per
-//    (head, row), one thread per dimension);
-//  * h[b, f] = silu(gate) * up from the fixed-point gate/up sums.
+// For more than two rows the o projection takes an f16 operand formed once,
+// rather than in every row-block workgroup's prologue: o[b, h] = merge of the
+// S split-KV partials of head h (one workgroup per (head, row), one thread
+// per dimension).  (The gate/up projection writes silu(gate) * up itself.)
 __global__ void __launch_bounds__(128) dec_merge_kernel(const float *pm, const float *pl, const float *po, int S, int nq,
                                                         int hd, f16 *o) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
@@ -187,15 +186,6 @@ __global__ void __launch_bounds__(128) dec_merge_kernel(const float *pm, const f
   o[(int64_t)b * nq * hd + (int64_t)h * hd + d] = (f16)(O / L);
 }
 
-__global__ void __launch_bounds__(256) dec_swiglu_kernel(const long long *gu_fix, int B, int I, f16 *h) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)B * I) return;
-  const int b = (int)(idx / I), f = (int)(idx % I);
-  const long long *r2 = gu_fix + (int64_t)b * 2 * I + (f / GU_BLOCK) * 2 * GU_BLOCK + f % GU_BLOCK;
-  const float gt = from_fix(r2[0]), up = from_fix(r2[GU_BLOCK]);
-  h[idx] = (f16)(silu_f(gt) * up);
-}
-
 // ---------------------------------------------------------------- projections
 // out[b, n] (+)= sum_k act[b, k] * W[n, k] * scale for b < M <= 16 * NB.
 // One wave = 16 weight rows x a K slice; a workgroup = 4 waves = 64 rows;
@@ -206,7 +196,7 @@ __global__ void __launch_bounds__(256) dec_swiglu_kernel(const long long *gu_fix
 // operand (16 batch rows); unit t of a chunk gives lane group g the 8
 // columns 32t + 8g .. 32t + 8g + 7.
 enum class DecAct : int { F16 = 0, NormFix = 1, SwiGLUFix = 2, AttnMerge = 3 };
-enum class DecOut : int { FixAdd = 0, Logits = 1 };
+enum class DecOut : int { FixAdd = 0, Logits = 1, SwiGLUOut = 2 };
 
 // ROLE only separates launches in profiles (the gate/up projection gets its
 // own symbol); it does not change the code.
@@ -389,6 +379,21 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
       for (int r = 0; r < 4; ++r)
         if (nw + r < a.N) fix_add(a.out_fix + (int64_t)b * a.ldo + nw + r, acc[nb][r] * a.scale);
     }
+  } else if constexpr (OM == DecOut::SwiGLUOut) {
+    // full K in this workgroup: waves 0/1 hold the gate/up rows of feature
+    // block 2 nblk, waves 2/3 those of block 2 nblk + 1; they meet in LDS
+    __shared__ float s_gu[4][16][BT];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_gu[wave][4 * g + r][nb * 16 + i] = acc[nb][r] * a.scale;
+    __syncthreads();
+    f16 *h = (f16 *)a.h_out;
+    for (int e = tid; e < 2 * 16 * BT; e += 256) {
+      const int pp = e / (16 * BT), rr = (e / BT) % 16, b = e % BT;
+      const int f = nblk * 32 + pp * 16 + rr;
+      if (b < a.M && f < a.N / 2) h[(int64_t)b * a.ldh + f] = (f16)(silu_f(s_gu[2 * pp][rr][b]) * s_gu[2 * pp + 1][rr][b]);
+    }
   } else {
     // logits (optional copy) and this block's (max, lowest index) per batch row
     __shared__ float s_v[4][BT];
@@ -455,6 +460,9 @@ hipError_t launch_gemv_role(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
   }
   if (a.logits_mode) {
     QW_LAUNCH((dec_gemv_kernel<NB, DecAct::F16, DecOut::Logits, ROLE>), dim3(grid), dim3(256), 0, s, a);
+  } else if (a.swiglu_out) {
+    if (am != DecAct::F16 || grid.y != 1) return hipErrorInvalidValue;
+    QW_LAUNCH((dec_gemv_kernel<NB, DecAct::F16, DecOut::SwiGLUOut, ROLE>), dim3(grid), dim3(256), 0, s, a);
   } else {
     switch (am) {
       case DecAct::F16: QW_LAUNCH((dec_gemv_kernel<NB, DecAct::F16, DecOut::FixAdd, ROLE>), dim3(grid), dim3(256), 0, s, a); break;
@@ -1394,12 +1402,6 @@ hipError_t launch_dec_merge(hipStream_t s, const float *pm, const float *pl, con
   return hipGetLastError();
 }
 
-hipError_t launch_dec_swiglu(hipStream_t s, const long long *gu_fix, int B, int I, void *h) {
-  const int64_t n = (int64_t)B * I;
-  QW_LAUNCH((dec_swiglu_kernel), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu_fix, B, I, (f16 *)h);
-  return hipGetLastError();
-}
-
 hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int64_t rep_stride, int B, int H,
                            const float *w, float eps, void *u) {
   QW_LAUNCH((dec_norm_kernel), dim3(B), dim3(256), 0, s, x_fix, rep_stride, H, w, eps, (f16 *)u);
@@ -1419,7 +1421,7 @@ hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &in) {
   if (a.act_mode == (int)DecAct::AttnMerge && (a.attn_splits < 1 || a.attn_splits > MERGE_MAX_S))
     return hipErrorInvalidValue;
   const int units = a.K / 32;
-  int splits = a.logits_mode ? 1 : (a.splits < 1 ? 1 : a.splits);
+  int splits = (a.logits_mode || a.swiglu_out) ? 1 : (a.splits < 1 ? 1 : a.splits);
   a.units_per_split = (units + splits - 1) / splits;
   splits = (units + a.units_per_split - 1) / a.units_per_split;
   dim3 grid((a.N + 63) / 64, splits);

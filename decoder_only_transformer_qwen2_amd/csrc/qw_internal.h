@@ -123,6 +123,11 @@ struct DecGemvArgs {
   long long *clear;         // side job: zero clear[0 .. clear_n) (may be NULL)
   int64_t clear_n;
   int role_gate_up;          // 1 for the gate/up projection (separate kernel symbol in profiles)
+  // gate/up without a K split: silu(gate) * up of the GU_BLOCK-interleaved rows
+  // written as f16 h [M, ldh] (no fixed-point output)
+  int swiglu_out;
+  void *h_out;
+  int ldh;
   // LM-head mode: logits [M, ldo] (may be NULL) and per-64-row-block argmax
   int logits_mode;
   float *logits;
@@ -221,11 +226,10 @@ hipError_t launch_dec_end(hipStream_t s, const float *arg_v, const int *arg_i, i
 hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &a);
 hipError_t launch_dec_attention(hipStream_t s, const DecAttnArgs &a);
 hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a);
-// f16 operands formed once for batches of more than two rows: the merged
-// split-KV attention output o [B, nq*hd] and silu(gate) * up h [B, I]
+// the merged split-KV attention output o [B, nq*hd] as f16, formed once for
+// batches of more than two rows
 hipError_t launch_dec_merge(hipStream_t s, const float *pm, const float *pl, const float *po, int S, int B, int nq,
                             int hd, void *o);
-hipError_t launch_dec_swiglu(hipStream_t s, const long long *gu_fix, int B, int I, void *h);
 hipError_t launch_dec_attn_o(hipStream_t s, const DecAttnOArgs &a);
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
                          int32_t *next_ids, int *pos_dev, int pos_add);

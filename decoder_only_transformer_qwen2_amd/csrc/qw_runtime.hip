@@ -54,14 +54,14 @@ qw_status fail(qw_status st, const char *fmt, ...) {
   } while (0)
 
 enum Family { F_EMBED, F_RMSNORM, F_GEMM_QKV, F_ROPE_CACHE, F_ATTENTION, F_GEMM_O, F_GEMM_GATE_UP,
-              F_GEMM_DOWN, F_LM_HEAD, F_ARGMAX, F_MLP, F_ATTN_O, F_ATTN_MERGE, F_SWIGLU, F_COUNT };
+              F_GEMM_DOWN, F_LM_HEAD, F_ARGMAX, F_MLP, F_ATTN_O, F_ATTN_MERGE, F_COUNT };
 const char *const kFamilyNames[] = {"embed",  "rmsnorm",      "gemm_qkv",  "rope_cache", "attention", "gemm_o",
                                     "gemm_gate_up", "gemm_down", "lm_head", "argmax", "mlp", "attn_o",
-                                    "attn_merge", "swiglu"};
+                                    "attn_merge"};
 static_assert(sizeof(kFamilyNames) / sizeof(kFamilyNames[0]) == F_COUNT, "one name per kernel family");
 const char *const kFamilyList =
     "embed,rmsnorm,gemm_qkv,rope_cache,attention,gemm_o,gemm_gate_up,gemm_down,lm_head,argmax,mlp,attn_o,"
-    "attn_merge,swiglu";
+    "attn_merge";
 
 struct LayerBuf {
   void *w_qkv = nullptr;    // [qd + 2 kvd, H]
@@ -497,6 +497,13 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     normed(g, Lw.post_norm);
     g.role_gate_up = 1;
     g.out_fix = m->gu_fix;
+    if (!fused_norm) {
+      // many rows: full K per workgroup, SwiGLU in the epilogue, f16 h out
+      g.splits = 1;
+      g.swiglu_out = 1;
+      g.h_out = m->h;
+      g.ldh = I;
+    }
     if (attn_o) {
       g.clear = m->qkv_fix;
       g.clear_n = n_qkv;
@@ -510,9 +517,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       g.act_fix = m->gu_fix;
       g.lda = 2 * I;
     } else {
-      // many rows: silu(gate) * up once, then an f16 operand
-      e = timed(m, s, F_SWIGLU, [&] { return launch_dec_swiglu(s, m->gu_fix, B, I, m->h); });
-      if (e != hipSuccess) return e;
+      // many rows: h was written by the gate/up epilogue
       g.act_mode = 0;
       g.act = m->h;
       g.lda = I;
