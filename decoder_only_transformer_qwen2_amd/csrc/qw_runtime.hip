@@ -138,6 +138,9 @@ namespace {
 
 // Workgroups a decode projection / attention launch aims for (256 CUs).
 constexpr int kGemvTargetGroups = 1024;
+// With more than two rows every K slice also adds B fixed-point sums per row
+// with atomics, so fewer, longer slices pay off.
+constexpr int kGemvTargetGroupsBatched = 256;
 constexpr int kAttnTargetGroups = 1024;
 // Up to this many rows, a projection normalises its own operand (each
 // workgroup reads the whole residual rows); above it a norm kernel runs.
@@ -388,7 +391,8 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     char *kc = (char *)m->k_cache + (int64_t)l * m->cache_layer_elems * m->esz;
     char *vc = (char *)m->v_cache + (int64_t)l * m->cache_layer_elems * m->esz;
     if ((e = norm(Lw.in_norm)) != hipSuccess) return e;
-    DecGemvArgs g = dec_args(Lw.w_qkv, B, m->nqkv, H, Lw.s_qkv);
+    const int gemv_target = fused_norm ? kGemvTargetGroups : kGemvTargetGroupsBatched;
+    DecGemvArgs g = dec_args(Lw.w_qkv, B, m->nqkv, H, Lw.s_qkv, gemv_target);
     normed(g, Lw.in_norm);
     g.out_fix = m->qkv_fix;
     g.ldo = m->nqkv;
@@ -440,7 +444,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       da.clear_n = fused_mlp ? kXReps * xs : n_gu;
       e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
       if (e != hipSuccess) return e;
-      g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o);
+      g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o, gemv_target);
       if (S > 1 && !fused_norm) {
         // many rows: merge once, then an f16 operand
         e = timed(m, s, F_ATTN_MERGE, [&] {
@@ -511,7 +515,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     g.ldo = 2 * I;
     e = timed(m, s, F_GEMM_GATE_UP, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
-    g = dec_args(Lw.w_down, B, H, I, Lw.s_down);
+    g = dec_args(Lw.w_down, B, H, I, Lw.s_down, gemv_target);
     if (fused_norm) {
       g.act_mode = 2;
       g.act_fix = m->gu_fix;
