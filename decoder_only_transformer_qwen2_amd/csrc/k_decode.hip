@@ -50,6 +50,29 @@ __device__ __forceinline__ void fix_add(long long *p, float v) {
   atomicAdd(reinterpret_cast<unsigned long long *>(p), (unsigned long long)to_fix(v));
 }
 __device__ __forceinline__ f16x8 load8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+
+// Sum over aligned groups of N lanes (N = 1, 2, 4, 8 or 16; a group never
+// crosses a 16-lane row), every lane ending with its group's sum.  DPP moves
+// (VALU operands read from another lane of the row): swap neighbours, swap
+// pairs, mirror each half-row, mirror the row.  A shuffle would go through the
+// LDS crossbar (ds_bpermute) once per step.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+  auto mv = [](float x, int ctrl) -> float {
+    switch (ctrl) {
+      case 0xB1: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+      case 0x4E: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+      case 0x141: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+      default: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+    }
+  };
+  if constexpr (N >= 2) v += mv(v, 0xB1);    // quad_perm [1, 0, 3, 2]
+  if constexpr (N >= 4) v += mv(v, 0x4E);    // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) v += mv(v, 0x141);   // row_half_mirror
+  if constexpr (N >= 16) v += mv(v, 0x140);  // row_mirror
+  return v;
+}
 // Loads in these kernels are issued unconditionally from an address clamped
 // into range, and a lane outside the range then selects zero (or its result
 // is never stored).  A per-lane condition around the load itself becomes an
@@ -775,8 +798,7 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s = fmaf(q[t][e], kf[e], s);
-#pragma unroll
-      for (int off = LPK / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      s = group_sum<LPK>(s);
       const float mn = fmaxf(m[t], s);
       const float corr = exp2f(m[t] - mn);
       const float p = exp2f(s - mn);
@@ -810,8 +832,7 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
           float d = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) d = fmaf(q[t][e], (float)kc[u][e], d);
-#pragma unroll
-          for (int off = LPK / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+          d = group_sum<LPK>(d);
           sc[u] = ok[u] ? d : -INFINITY;
           mx = fmaxf(mx, sc[u]);
         }
@@ -1209,8 +1230,7 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = fmaf(q[e], (float)kc[u][e], d);
-#pragma unroll
-      for (int off = LPK / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+      d = group_sum<LPK>(d);
       sc[u] = (kb + u * KSTEP + slot < kc_end) ? d : -INFINITY;
       mx = fmaxf(mx, sc[u]);
     }
@@ -1233,8 +1253,7 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
     float d = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) d = fmaf(q[e], s_k[d0 + e], d);
-#pragma unroll
-    for (int off = LPK / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+    d = group_sum<LPK>(d);
     const float mn = fmaxf(m, d);
     const float corr = (m == -INFINITY) ? 0.f : exp2f(m - mn);
     const float p = exp2f(d - mn);
