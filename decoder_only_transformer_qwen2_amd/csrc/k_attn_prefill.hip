@@ -10,9 +10,11 @@
 //   O^T += V^T . P^T       (A = V^T from LDS, B = probabilities)
 // which leaves each lane owning ONE query column of S^T and O^T: the running
 // max / sum / rescale of the online softmax are per-lane scalars, and the
-// probabilities already sit in the B-operand layout of the second product
-// (the key order inside each 32-key step is permuted identically on the V^T
-// side), so P never goes through LDS.  A workgroup is 4 waves x 32 queries of
+// probabilities already sit in the B-operand layout of the second product, so
+// P never goes through LDS.  The K rows of each 32-key step are stored in a
+// permuted order so that the 8 probabilities a lane holds for a step are 8
+// consecutive keys, which its V^T operand reads in one 16-byte load.  A
+// workgroup is 4 waves x 32 queries of
 // one head; the K tile ([key][d]) and the V^T tile ([d][key]) are staged in
 // LDS with two buffers, both as 16-byte vectors: V^T comes from a transposed
 // copy of the prompt's V written once per layer (transpose_v_kernel), since
@@ -110,7 +112,11 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
     for (int t = 0; t < VPT; ++t) {
       const int v = tid + 256 * t;
       const int key = v / (HD / 8), c = (v % (HD / 8)) * 8;
-      *reinterpret_cast<f16x8 *>(&sK[buf][key][c]) = rk[t];
+      // LDS row 32u + 16h + 4q + r holds key 32u + 8q + 4h + r (u, h < 2, q,
+      // r < 4): the S^T rows a lane owns (4q .. 4q+3 of tiles 2u and 2u+1)
+      // are then 8 consecutive keys, read from V^T in one 16-byte load
+      const int krow = (key & ~31) | (((key >> 2) & 1) << 4) | (((key >> 3) & 3) << 2) | (key & 3);
+      *reinterpret_cast<f16x8 *>(&sK[buf][krow][c]) = rk[t];
       const int d = v / (BKEY / 8), kc = (v % (BKEY / 8)) * 8;
       *reinterpret_cast<f16x8 *>(&sV[buf][d][kc]) = rv[t];
     }
@@ -138,7 +144,8 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
 #pragma unroll
           for (int t = 0; t < 2; ++t) s[y][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[t][ks], s[y][t], 0, 0, 0);
         }
-      // online softmax per query column; lane (i, g) holds keys 16y + 4g + r.
+      // online softmax per query column; lane (i, g) holds, for S^T tile y,
+      // keys 32 (y / 2) + 8g + 4 (y % 2) + r (the permuted K rows).
       // Scores stay unscaled: the scale goes into the exponent's FMA, and
       // only blocks that reach past the wave's first query are masked.  The
       // running max is finite from block 0 on (key 0 is visible to every
@@ -154,7 +161,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
           for (int y = 0; y < 4; ++y)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int key = kb * BKEY + 16 * y + 4 * g + r;
+              const int key = kb * BKEY + 32 * (y >> 1) + 8 * g + 4 * (y & 1) + r;
               const float v = (key <= q) ? s[y][t][r] : -INFINITY;
               s[y][t][r] = v;
               mx = fmaxf(mx, v);
@@ -185,7 +192,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
         m[t] = mn;
 #pragma unroll
         for (int d = 0; d < DT; ++d) o[d][t] *= corr;
-        // B operand of step u (keys 32u .. 32u+31): keys 32u + 4g + e (e < 4), 32u + 16 + 4g + e - 4
+        // B operand of step u: keys 32u + 8g + e (tile 2u gives e < 4, tile 2u + 1 the rest)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -199,9 +206,7 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
-          const f16x4 lo = *reinterpret_cast<const f16x4 *>(&sV[cur][16 * d + i][32 * u + 4 * g]);
-          const f16x4 hi = *reinterpret_cast<const f16x4 *>(&sV[cur][16 * d + i][32 * u + 16 + 4 * g]);
-          const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const f16x8 vf = *reinterpret_cast<const f16x8 *>(&sV[cur][16 * d + i][32 * u + 8 * g]);
 #pragma unroll
           for (int t = 0; t < 2; ++t) o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[t][u], o[d][t], 0, 0, 0);
         }
