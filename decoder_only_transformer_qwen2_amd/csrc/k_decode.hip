@@ -948,12 +948,215 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
   }
 }
 
+// Split-KV decode attention on the matrix cores, for batches of more than two
+// rows (grid: split x KV head x row).  The g query heads of the KV group are
+// the columns of the MFMA B operand (g <= 8 of 16 used):
+//   S^T  = K . Q^T    A = 16 keys x 32 dims, 16-byte loads from the cache rows
+//   O^T += V^T . P^T  A = 16 dims x 32 keys, gathered 2 bytes at a time from
+//                     the cache rows (each element is still read once)
+// Within a 32-key chunk the key rows are visited in the order that makes the
+// 8 probabilities a lane holds 8 consecutive keys, which is the B operand of
+// the second product as it stands.  Wave w takes chunks w, w + 4, ...; the
+// four waves' (max, sum, output) meet in LDS.  Prologue, cache write, the new
+// key (from LDS) and the partials are those of dec_attn_kernel.
+template <int HD, int G>
+__global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
+  constexpr int NW = 4, HALF = HD / 2, KS = HD / 32, DT = HD / 16;
+  static_assert(G <= 16, "heads of a group fit the 16 MFMA columns");
+  __shared__ float s_q[G][HD];
+  __shared__ float s_k[HD], s_v[HD];
+  __shared__ float s_m[NW][G], s_l[NW][G];
+  __shared__ float s_o[NW][G][HD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int S = gridDim.x;
+  const int pos = *a.pos_dev;
+  const int n_keys = pos + 1;
+  int per = (n_keys + S - 1) / S;
+  per = (per + 31) / 32 * 32;
+  const int kb0 = split * per;
+  const int kb1 = min(n_keys, kb0 + per);
+  const bool has_new = kb0 <= pos && pos < kb1;
+  const int nq = a.n_kv_heads * G;
+  const int qd = nq * HD, kvd = a.n_kv_heads * HD;
+  const int ncols = qd + 2 * kvd;
+  const long long *acc = a.qkv_fix + (int64_t)b * ncols;
+  const float2 *cs = a.rope + (int64_t)pos * HALF;
+  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
+  f16 *Kc = (f16 *)a.k_cache + head_base;
+  f16 *Vc = (f16 *)a.v_cache + head_base;
+
+  clear_share(a.clear, a.clear_n, (b * gridDim.y + j) * S + split, S * gridDim.y * gridDim.z);
+
+  // q of the group's heads (rounded to f16, unscaled), new k and v
+  for (int e = tid; e < (G + 1) * HALF + HD; e += 256) {
+    if (e < (G + 1) * HALF) {
+      const int hh = e / HALF, ii = e % HALF;
+      const int c0 = (hh < G) ? (j * G + hh) * HD + ii : qd + j * HD + ii;
+      const float re = from_fix(acc[c0]) + a.bias[c0];
+      const float im = from_fix(acc[c0 + HALF]) + a.bias[c0 + HALF];
+      const float2 r = cs[ii];
+      const float nre = re * r.x - im * r.y, nim = im * r.x + re * r.y;
+      if (hh < G) {
+        s_q[hh][ii] = (float)(f16)nre;
+        s_q[hh][ii + HALF] = (float)(f16)nim;
+      } else {
+        s_k[ii] = (float)(f16)nre;
+        s_k[ii + HALF] = (float)(f16)nim;
+      }
+    } else {
+      const int d = e - (G + 1) * HALF;
+      const int c = qd + kvd + j * HD + d;
+      s_v[d] = (float)(f16)(from_fix(acc[c]) + a.bias[c]);
+    }
+  }
+  __syncthreads();
+  if (has_new && tid < HD) {
+    Kc[(int64_t)pos * HD + tid] = (f16)s_k[tid];
+    Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
+  }
+
+  const f16x8 zero = {};
+  f16x8 qf[KS];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[s2][e] = (i < G) ? (f16)s_q[i < G ? i : 0][32 * s2 + 8 * g + e] : (f16)0.f;
+  const float sl2 = a.softmax_scale * LOG2E;
+  float m = -INFINITY, l = 0.f;                 // head i
+  f32x4 o[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kc_end = min(kb1, pos);             // cached keys of this split
+  for (int k0 = kb0 + 32 * wave; k0 < kc_end; k0 += 32 * NW) {
+    const int klast = kc_end - 1;
+    // K rows of the two 16-key tiles: tile y, row i is key k0 + 8 (i / 4) + 4y + i % 4
+    f16x8 kf[2][KS];
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int key = min(k0 + 8 * (i >> 2) + 4 * y + (i & 3), klast);
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) kf[y][s2] = load8(Kc + (int64_t)key * HD + 32 * s2 + 8 * g);
+    }
+    // V^T operand: lane (i, g) holds dim 16d + i of keys k0 + 8g .. k0 + 8g + 7
+    f16x8 vf[DT];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f16 *vrow = Vc + (int64_t)min(k0 + 8 * g + e, klast) * HD + i;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) vf[d][e] = vrow[16 * d];
+    }
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) sacc[y] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[y][s2], qf[s2], sacc[y], 0, 0, 0);
+    // lane (i, g) now holds head i's scores of keys k0 + 8g + 4y + r
+    float sc[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = (k0 + 8 * g + 4 * y + r < kc_end) ? sacc[y][r] * sl2 : -INFINITY;
+        sc[4 * y + r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);             // finite: key k0 is in range
+    const float corr = exp2f(m - mn);
+    float sum = 0.f;
+    f16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = exp2f(sc[e] - mn);
+      sum += p;
+      pb[e] = (f16)p;
+    }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    l = l * corr + sum;
+    m = mn;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      o[d] *= corr;
+      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[d], pb, o[d], 0, 0, 0);
+    }
+  }
+  if (has_new && wave == 0) {
+    // the new key, from LDS: head i's score, then its share of dims 16d + 4g + r
+    float dsum = 0.f;
+#pragma unroll 8
+    for (int e = 0; e < HD; ++e) dsum = fmaf(s_q[i < G ? i : 0][e], s_k[e], dsum);
+    const float sc = dsum * sl2;
+    const float mn = fmaxf(m, sc);
+    const float corr = exp2f(m - mn);
+    const float p = exp2f(sc - mn);
+    l = l * corr + p;
+    m = mn;
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[d][r] = o[d][r] * corr + p * s_v[16 * d + 4 * g + r];
+  }
+
+  if (i < G) {
+    if (g == 0) {
+      s_m[wave][i] = m;
+      s_l[wave][i] = l;
+    }
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_o[wave][i][16 * d + 4 * g + r] = o[d][r];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * HD; e += 256) {
+    const int hh = e / HD, d = e % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, s_m[w2][hh]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const float c = (s_m[w2][hh] == -INFINITY) ? 0.f : exp2f(s_m[w2][hh] - M);
+        L += s_l[w2][hh] * c;
+        O += s_o[w2][hh][d] * c;
+      }
+    }
+    const int h = j * G + hh;
+    if (S == 1) {
+      ((f16 *)a.o)[(int64_t)b * qd + h * HD + d] = (f16)(O / L);
+    } else {
+      const int64_t st = ((int64_t)b * nq + h) * S + split;
+      if (d == 0) {
+        a.part_m[st] = M;
+        a.part_l[st] = L;
+      }
+      a.part_o[st * HD + d] = O;
+    }
+  }
+}
+
+constexpr bool kMfmaDecodeAttn = true;
+
 template <int HD, int G>
 hipError_t launch_attn_g(hipStream_t s, const DecAttnArgs &a, dim3 grid) {
-  if (a.head_parallel && G > 1)
+  if (a.head_parallel && G > 1) {
     QW_LAUNCH((dec_attn_kernel<HD, G, (G + 3) / 4>), dim3(grid), dim3(256), 0, s, a);
-  else
-    QW_LAUNCH((dec_attn_kernel<HD, G, G>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if constexpr (HD >= 64) {
+    if (kMfmaDecodeAttn) {
+      QW_LAUNCH((dec_attn_mfma_kernel<HD, G>), dim3(grid), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  QW_LAUNCH((dec_attn_kernel<HD, G, G>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

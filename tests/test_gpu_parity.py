@@ -41,6 +41,9 @@ SMALL = {
     "bf16-hd64-mqa": (S.ModelShape("s64", 2, 384, 6, 1, 64, 1024, 777), 2, 70, 5, 96),
     "bf16-hd128": (S.ModelShape("s128", 2, 512, 4, 2, 128, 1536, 2049), 2, 130, 4, 160),
     "f32-hd64": (S.ModelShape("f64", 2, 192, 6, 3, 64, 448, 513, dtype="f32"), 2, 21, 5, 32),
+    # more than two rows: the batched decode path (split-KV attention on the
+    # matrix cores, g = 7 as in the 0.5B model; unsplit gate/up with SwiGLU)
+    "bf16-hd64-g7-b5": (S.ModelShape("s64g7", 2, 448, 14, 2, 64, 896, 1100), 5, 53, 6, 96),
 }
 
 
