@@ -1146,15 +1146,15 @@ constexpr bool kMfmaDecodeAttn = true;
 
 template <int HD, int G>
 hipError_t launch_attn_g(hipStream_t s, const DecAttnArgs &a, dim3 grid) {
-  if (a.head_parallel && G > 1) {
-    QW_LAUNCH((dec_attn_kernel<HD, G, (G + 3) / 4>), dim3(grid), dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
   if constexpr (HD >= 64) {
     if (kMfmaDecodeAttn) {
       QW_LAUNCH((dec_attn_mfma_kernel<HD, G>), dim3(grid), dim3(256), 0, s, a);
       return hipGetLastError();
     }
+  }
+  if (a.head_parallel && G > 1) {
+    QW_LAUNCH((dec_attn_kernel<HD, G, (G + 3) / 4>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
   }
   QW_LAUNCH((dec_attn_kernel<HD, G, G>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
