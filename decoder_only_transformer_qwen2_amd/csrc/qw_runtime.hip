@@ -147,8 +147,10 @@ constexpr int kAttnTargetGroups = 1024;
 constexpr int kFusedNormRows = 2;
 constexpr bool kHeadNormKernel = true;
 // Up to this context length (and two rows), attention and the o projection
-// are one kernel in which every workgroup reads its head's whole context.
-constexpr int kAttnOMaxCtx = 1024;
+// are one kernel in which every workgroup reads its head's whole context;
+// past it the split-KV kernel and the o projection (measured: the merged
+// kernel wins at 0.5B / 256 keys, the split pair at 1.5B / 513-768 keys).
+constexpr int kAttnOMaxCtx = 256;
 
 // Which decode step the next decode call runs: 1 = attention merged with the
 // o projection (short context), 2 + S = split-KV attention over S splits,

@@ -207,10 +207,10 @@ LONG = {
     "long-hd128-8k": (S.ModelShape("l128", 2, 256, 6, 1, 128, 512, 999), 1, 8190, 4, 8194),
     # the 1.5B attention geometry (12 q heads over 2 KV heads, hd 128) at 8k
     "long-1.5b-attn-8k": (S.ModelShape("l15", 2, 512, 12, 2, 128, 512, 999), 1, 8192, 6, 8320),
-    # two rows decoding across a context of 1024 keys: the merged attention +
+    # two rows decoding across a context of 256 keys: the merged attention +
     # o projection kernel runs up to there, the split-KV pair after it (the
     # decode graph is captured again at the switch)
-    "cross-1024-hd64": (S.ModelShape("c64", 2, 256, 6, 2, 64, 512, 1003), 2, 1020, 8, 1100),
+    "cross-256-hd64": (S.ModelShape("c64", 2, 256, 6, 2, 64, 512, 1003), 2, 252, 8, 300),
 }
 
 
