@@ -14,16 +14,23 @@
 //    result does not depend on arrival order (deterministic), and no fence is
 //    needed: the consumer is the next kernel.
 //  * Each consumer finishes the step its input belongs to while staging its
-//    operand in LDS: the q/k/v sums get bias and RoPE inside attention (which
-//    also writes k and v into the cache), the gate/up sums become
-//    silu(gate) * up inside the down projection, the split-KV attention
-//    partials are merged inside the o projection, and for one or two rows the
-//    RMSNorm is computed inside the projection that follows it.
-//  * The residual stream of the decode rows is kept in fixed point ([B, H]
-//    int64), so o_proj and down_proj add into it atomically.
-//  * Accumulators are cleared by an earlier kernel of the same step (embed
-//    clears both, attention clears gate/up, o_proj clears q/k/v), so the step
-//    needs no memset and replays as a graph.
+//    operand: attention applies bias and RoPE to the q/k/v sums (and writes
+//    k and v into the cache), the o projection merges split-KV partials (one
+//    or two rows), and for one or two rows every projection computes the
+//    RMSNorm of its own operand.
+//  * One or two rows: per layer three kernels, the q/k/v projection, attention
+//    merged with the o projection (short contexts; split-KV attention + o
+//    projection past them) and the whole MLP (dec_mlp32_kernel).  The
+//    residual is two fixed-point replicas (value = their sum) so that the
+//    MLP's workgroups, which all add into every value of a row, spread their
+//    atomics; it ping-pongs between two buffers around the MLP.
+//  * More than two rows: a norm kernel, the projections (gate/up without a K
+//    split, SwiGLU in its epilogue), split-KV attention on the matrix cores
+//    (dec_attn_mfma_kernel) and a merge kernel.
+//  * Every load of a kernel's first phase is issued before any is consumed
+//    (clamped addresses and selects rather than per-lane branches).
+//  * Accumulators are cleared by an earlier kernel of the same step, so the
+//    step needs no memset and replays as a graph.
 #include "qw_internal.h"
 
 #include <math.h>
