@@ -29,6 +29,15 @@ CFLAGS = [
 ]
 
 
+# Per-source device-code options.  The prefill attention keeps its output
+# accumulators in ordinary VGPRs (the VGPR form of the MFMA instructions):
+# with the accumulation registers the compiler copied every accumulator out
+# and back in once per key block.
+EXTRA = {
+    "k_attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if c and os.path.exists(c):
@@ -38,7 +47,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

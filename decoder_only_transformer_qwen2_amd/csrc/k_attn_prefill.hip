@@ -36,9 +36,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BQ = 128;   // queries per workgroup (4 waves x 32)
 constexpr int BKEY = 64;  // keys per step
+constexpr float RESCALE_LOG2 = 8.0f;  // largest exponent (log2) a probability may reach before a rescale
+
+// 2^x with the hardware instruction alone: results below the smallest normal
+// float flush to zero, which a probability can afford (it is rounded to f16)
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int HD>
-__global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) attn_prefill_kernel(AttnArgs a, int n_qt) {
   constexpr int KP = HD + 8;          // padded K row
   constexpr int VP = BKEY + 8;        // padded V^T row
   constexpr int KS = HD / 32;         // 32-wide d steps for S
@@ -152,6 +157,8 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
       // query), and masked scores are -inf, so exp2 needs no guards.
       const bool diag = kb * BKEY + BKEY - 1 > q0;
       f16x8 pb[2][2];
+      float corr[2];
+      bool any_move = false;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int q = q0 + 16 * t + i;
@@ -174,24 +181,29 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // The reference point of the exponent only moves when the block's
+        // max exceeds it by more than RESCALE_LOG2 (in log2 units): softmax
+        // is invariant to the reference, and a stale one keeps every p below
+        // 2^RESCALE_LOG2.  Block 0 always moves it off -inf.
         const float mn = fmaxf(m[t], mx);
-        const float corr = exp2f((m[t] - mn) * sl2);
-        const float nb = -mn * sl2;
+        const bool move = (mn - m[t]) * sl2 > RESCALE_LOG2;
+        const float mref = move ? mn : m[t];
+        corr[t] = move ? exp2_raw((m[t] - mn) * sl2) : 1.0f;
+        any_move |= move;
+        const float nb = -mref * sl2;
         float sum = 0.f;
 #pragma unroll
         for (int y = 0; y < 4; ++y)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float p = exp2f(fmaf(s[y][t][r], sl2, nb));
+            const float p = exp2_raw(fmaf(s[y][t][r], sl2, nb));
             s[y][t][r] = p;
             sum += p;
           }
         sum += __shfl_xor(sum, 16, 64);
         sum += __shfl_xor(sum, 32, 64);
-        l[t] = l[t] * corr + sum;
-        m[t] = mn;
-#pragma unroll
-        for (int d = 0; d < DT; ++d) o[d][t] *= corr;
+        l[t] = l[t] * corr[t] + sum;
+        m[t] = mref;
         // B operand of step u: keys 32u + 8g + e (tile 2u gives e < 4, tile 2u + 1 the rest)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -200,6 +212,13 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a, int n_qt)
             pb[t][u][e] = (f16)s[2 * u][t][e];
             pb[t][u][e + 4] = (f16)s[2 * u + 1][t][e];
           }
+      }
+      // rescale the accumulators only when some query of the wave moved its reference
+      if (__builtin_amdgcn_ballot_w64(any_move) != 0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int d = 0; d < DT; ++d) o[d][t] *= corr[t];
       }
       // O^T += V^T . P^T, A operand from the transposed V tile with the same key order
 #pragma unroll
