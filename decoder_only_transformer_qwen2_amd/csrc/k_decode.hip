@@ -509,6 +509,178 @@ hipError_t launch_gemv_nb(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
   return a.role_gate_up ? launch_gemv_role<NB, 1>(s, a, grid) : launch_gemv_role<NB, 0>(s, a, grid);
 }
 
+// ---------------------------------------------------------------- batched projections
+// More than two rows (the batch-8 and batch-32 workloads): out[b, n] =
+// sum_k act[b, k] W[n, k] for b < M <= 32, act f16.  A workgroup owns
+// RB = 16 RT weight rows over one K slice; its four waves split the slice
+// into contiguous runs of 32-k units and meet in LDS once, at the end.  Both
+// operands go straight from memory into registers (the activations are at
+// most 32 rows and stay in L2): a wave issues the loads of up to MAXU units
+// at once, then multiplies them, so its whole share is one memory round trip
+// (the launcher sizes the slices for that) and nothing waits on a barrier
+// while the weights stream.  Without a K split a workgroup is the only writer
+// of its outputs: q/k/v sums are stored, residual rows read-modify-written,
+// and no atomics are needed.  With one, the slices add fixed-point values
+// atomically (deterministic, as above).
+template <int RT, int NB, int MAXU, DecOut OM, bool ATOMIC>
+__global__ void __launch_bounds__(256) dec_rows_kernel(DecGemvArgs a) {
+  constexpr int RB = 16 * RT, BT = 16 * NB;
+  __shared__ float s_acc[4][RB][BT + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: unit bounds stay scalar
+  const int i = lane & 15, g = lane >> 4;
+  const int nblk = blockIdx.x, split = blockIdx.y;
+  const int n0 = nblk * RB;
+  const int units = a.K >> 5;
+  const int us0 = split * a.units_per_split, us1 = min(units, us0 + a.units_per_split);
+  const int per_w = (max(0, us1 - us0) + 3) >> 2;
+  const int u0 = us0 + wave * per_w, u1 = min(us1, u0 + per_w);
+
+  if (a.clear)
+    clear_share(a.clear, a.clear_n, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+
+  // lane (i, g): weight row n0 + 16 r + i and batch row 16 nb + i, k offset 8 g
+  // of each unit; rows past N or M are clamped and their results never stored
+  const f16 *wp[RT];
+  const f16 *xp[NB];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) wp[r] = (const f16 *)a.W + (int64_t)min(n0 + 16 * r + i, a.N - 1) * a.K + 8 * g;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) xp[nb] = (const f16 *)a.act + (int64_t)min(16 * nb + i, a.M - 1) * a.lda + 8 * g;
+
+  f32x4 acc[RT][NB];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int ub = u0; ub < u1; ub += MAXU) {
+    f16x8 w[MAXU][RT], x[MAXU][NB];
+#pragma unroll
+    for (int t = 0; t < MAXU; ++t) {
+      if (ub + t < u1) {        // uniform (scalar) condition: no load past the share
+        const int k = 32 * (ub + t);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) w[t][r] = load8(wp[r] + k);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) x[t][nb] = load8(xp[nb] + k);
+      }
+    }
+    // keep every load of the batch ahead of the first multiply (the
+    // scheduler would otherwise wait for the first unit mid-batch)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < MAXU; ++t) {
+      if (ub + t < u1) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[r][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[t][r], x[t][nb], acc[r][nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // lane (i, g) holds rows 4g .. 4g + 3 of tile r, batch column 16 nb + i
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s_acc[wave][16 * r + 4 * g + q][16 * nb + i] = acc[r][nb][q];
+  __syncthreads();
+  auto total = [&](int nl, int b) {
+    return (s_acc[0][nl][b] + s_acc[1][nl][b] + s_acc[2][nl][b] + s_acc[3][nl][b]) * a.scale;
+  };
+
+  if constexpr (OM == DecOut::FixAdd) {
+    for (int e = tid; e < RB * BT; e += 256) {
+      const int nl = e % RB, b = e / RB, n = n0 + nl;
+      if (n >= a.N || b >= a.M) continue;
+      long long *p = a.out_fix + (int64_t)b * a.ldo + n;
+      if constexpr (ATOMIC) {
+        fix_add(p, total(nl, b));
+      } else {
+        // sole writer: a residual row adds to its value, a projection sum
+        // (cleared beforehand) is simply its value
+        *p += to_fix(total(nl, b));
+      }
+    }
+  } else if constexpr (OM == DecOut::SwiGLUOut) {
+    static_assert(RT % 2 == 0, "gate/up rows come in GU_BLOCK pairs");
+    f16 *h = (f16 *)a.h_out;
+    for (int e = tid; e < (RB / 2) * BT; e += 256) {
+      const int fl = e % (RB / 2), b = e / (RB / 2);
+      const int p = fl / GU_BLOCK, j = fl % GU_BLOCK;
+      const int f = nblk * (RB / 2) + fl;
+      if (b >= a.M || f >= a.N / 2) continue;
+      const float gt = total(2 * GU_BLOCK * p + j, b), up = total(2 * GU_BLOCK * p + GU_BLOCK + j, b);
+      h[(int64_t)b * a.ldh + f] = (f16)(silu_f(gt) * up);
+    }
+  } else {
+    // logits (optional copy) and this block's (max, lowest index) per batch row
+    static_assert(RB == 64, "the argmax partials are laid out per 64 vocabulary rows");
+    constexpr int TPB = 256 / BT;               // threads per batch row
+    const int b = tid / TPB, sub = tid % TPB;
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < RB / TPB; ++j) {
+      const int nl = sub + TPB * j, n = n0 + nl;
+      const float v = total(nl, b);
+      if (n < a.N && b < a.M) {
+        if (a.logits) a.logits[(int64_t)b * a.ldo + n] = v;
+        if (v > best) { best = v; bi = n; }      // n increases with j
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < TPB; off <<= 1) {
+      const float ob = __shfl_xor(best, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    }
+    if (sub == 0 && b < a.M) {
+      a.arg_v[(int64_t)b * gridDim.x + nblk] = best;
+      a.arg_i[(int64_t)b * gridDim.x + nblk] = bi;
+    }
+  }
+}
+
+// units a wave loads at once: at most about 200 registers of operands
+template <int RT, int NB>
+constexpr int rows_maxu() { return (RT + NB) * 4 * 16 <= 200 ? 16 : (RT + NB) * 4 * 12 <= 200 ? 12 : 8; }
+
+template <int NB>
+hipError_t launch_rows_nb(hipStream_t s, const DecGemvArgs &a, int splits) {
+  if (a.logits_mode) {
+    const dim3 grid((a.N + 63) / 64, 1);
+    QW_LAUNCH((dec_rows_kernel<4, NB, rows_maxu<4, NB>(), DecOut::Logits, false>), dim3(grid), dim3(256), 0, s, a);
+  } else if (a.swiglu_out) {
+    const dim3 grid((a.N + 31) / 32, 1);
+    QW_LAUNCH((dec_rows_kernel<2, NB, rows_maxu<2, NB>(), DecOut::SwiGLUOut, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    const dim3 grid((a.N + 15) / 16, splits);
+    if (splits > 1)
+      QW_LAUNCH((dec_rows_kernel<1, NB, rows_maxu<1, NB>(), DecOut::FixAdd, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      QW_LAUNCH((dec_rows_kernel<1, NB, rows_maxu<1, NB>(), DecOut::FixAdd, false>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// K slices of a batched FixAdd projection: about `target` workgroups of 16
+// rows, and no more slices than keep a wave's share within one batch of loads
+// ... unless the row blocks alone are fewer than half the target
+// about two workgroups per CU for the split projections (measured: 256 -> 512
+// took the 32-row decode step from 3.92 to 3.76 ms, 1024 was slower again)
+constexpr int kRowsTargetGroups = 512;
+int rows_splits(int N, int units, int maxu, int target) {
+  const int nb16 = (N + 15) / 16;
+  int rs = (target + nb16 / 2) / nb16;
+  rs = max(rs, (units + 4 * maxu - 1) / (4 * maxu));   // one batch of loads per wave
+  return max(1, min(rs, units / 8));                    // at least 2 units per wave
+}
+
 // ---------------------------------------------------------------- fused MLP
 // For one or two rows the MLP of a layer ("LLM Speedrun: Architecture",
 // "But how does it remember things?": gated SiLU MLP) is a single kernel:
@@ -1653,6 +1825,16 @@ hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &in) {
   int splits = (a.logits_mode || a.swiglu_out) ? 1 : (a.splits < 1 ? 1 : a.splits);
   a.units_per_split = (units + splits - 1) / splits;
   splits = (units + a.units_per_split - 1) / a.units_per_split;
+  // (the LM head stays on dec_gemv_kernel: 0.099 vs 0.110 ms per step at 8 rows)
+  if (a.M > 2 && a.act_mode == (int)DecAct::F16 && !a.logits_mode) {
+    // batched rows: K split only for FixAdd outputs
+    int rs = 1;
+    if (!a.logits_mode && !a.swiglu_out)
+      rs = rows_splits(a.N, units, a.M <= 16 ? rows_maxu<1, 1>() : rows_maxu<1, 2>(), kRowsTargetGroups);
+    a.units_per_split = (units + rs - 1) / rs;
+    rs = (units + a.units_per_split - 1) / a.units_per_split;
+    return a.M <= 16 ? launch_rows_nb<1>(s, a, rs) : launch_rows_nb<2>(s, a, rs);
+  }
   dim3 grid((a.N + 63) / 64, splits);
   return a.M <= 16 ? launch_gemv_nb<1>(s, a, grid) : launch_gemv_nb<2>(s, a, grid);
 }

@@ -263,7 +263,10 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   for (int kt = 0; kt < KT; ++kt) {
     // stage kt done (this wave's loads; later stages may stay in flight)
     const int ahead = min(NS - 2, KT - 1 - kt);
-    if (ahead >= 2)
+    static_assert((NS - 2) * PER_STAGE <= 15, "vmcnt field");
+    if (ahead >= 3)
+      __builtin_amdgcn_s_waitcnt(((3 * PER_STAGE) & 15) | (7 << 4) | (15 << 8));
+    else if (ahead == 2)
       __builtin_amdgcn_s_waitcnt(((2 * PER_STAGE) & 15) | (7 << 4) | (15 << 8));
     else if (ahead == 1)
       __builtin_amdgcn_s_waitcnt((PER_STAGE & 15) | (7 << 4) | (15 << 8));

