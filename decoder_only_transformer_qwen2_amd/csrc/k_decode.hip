@@ -58,6 +58,17 @@ __device__ __forceinline__ void fix_add(long long *p, float v) {
 }
 __device__ __forceinline__ f16x8 load8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 
+// Workgroup barrier that publishes LDS writes only: waits for this wave's LDS
+// operations (lgkmcnt 0) but leaves its global loads in flight, where
+// __syncthreads would first wait for every outstanding load (vmcnt 0).  The
+// empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Sum over aligned groups of N lanes (N = 1, 2, 4, 8 or 16; a group never
 // crosses a 16-lane row), every lane ending with its group's sum.  DPP moves
 // (VALU operands read from another lane of the row): swap neighbours, swap
@@ -250,11 +261,16 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
 
   f16x8 w[8];
   auto load_w = [&](int kc) {
+    // units past the chunk load a clamped address and are never multiplied
+    // (a condition around the load would become a branch per load); rows >= N
+    // are never stored
     const int nu = min(8, (k1 - kc) >> 5);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) w[t] = (t < nu) ? load8(W + kc + 32 * t + 8 * g) : zero;   // rows >= N: never stored
+    for (int t = 0; t < 8; ++t) w[t] = load8(W + kc + 32 * min(t, nu - 1) + 8 * g);
   };
-  load_w(k0);
+  // with the norm in the prologue the residual rows are loaded first (the
+  // norm then runs while the weights arrive)
+  if constexpr (AM != DecAct::NormFix) load_w(k0);
 
   // NormFix: the whole normalised row (1 or 2 rows) is built once in LDS.
   // Every thread loads its share of the row and of the norm weight up front
@@ -284,6 +300,9 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
           // a branch per load, and the loads are then serialised
           qr[r][b][t] = v & -(long long)((b < a.M) & (c < a.K));
         }
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(k0);
+    __builtin_amdgcn_sched_barrier(0);
     long long q[NF_ROWS][NF_PER];
 #pragma unroll
     for (int b = 0; b < NF_ROWS; ++b)
@@ -305,7 +324,7 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
       ss = wave_sum(ss);
       if (lane == 0) s_red[wave][b] = ss;
     }
-    __syncthreads();
+    lds_barrier();                 // the weights stay in flight
 #pragma unroll
     for (int b = 0; b < NF_ROWS; ++b) {
       const float inv = 1.0f / sqrtf((s_red[0][b] + s_red[1][b] + s_red[2][b] + s_red[3][b]) / (float)a.K + a.eps);
@@ -315,7 +334,7 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
         if (c < a.K) s_row[b][c] = (f16)(xv[b][t] * inv * wv[t]);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   f32x4 acc[NB];
@@ -324,7 +343,9 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
 
   for (int kc = k0; kc < k1; kc += CH) {
     const int ck = min(CH, k1 - kc);
-    if (kc != k0) __syncthreads();            // the previous chunk's LDS reads are done
+    // the previous chunk's LDS reads are done (NormFix reads only s_row, which
+    // stays as the prologue published it)
+    if (AM != DecAct::NormFix && kc != k0) __syncthreads();
     // ---- stage act[b][kc .. kc + ck) for b < M
     if constexpr (AM == DecAct::AttnMerge) {
       // merge of the split-KV partials: each element loads its head's S
@@ -375,7 +396,7 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
         s_act[b][kk] = (f16)(silu_f(gt) * up);
       }
     }
-    __syncthreads();
+    if constexpr (AM != DecAct::NormFix) __syncthreads();
     // ---- multiply the chunk; fetch the next chunk's weights first
     f16x8 wc[8];
 #pragma unroll
@@ -1380,13 +1401,33 @@ __global__ void __launch_bounds__(512) dec_mlp32_kernel(DecMlpArgs a) {
   const f16x8 zero = {};
   clear_share(a.clear, a.clear_n, p, gridDim.x);
 
+  // the residual rows and the norm weight first, so that the norm can run
+  // while the weights are still arriving; then every weight of the workgroup
+  float wv[NPER];
+  long long qr[kXReps][NR][NPER];
+#pragma unroll
+  for (int t = 0; t < NPER; ++t) {
+    const int c = t * 512 + tid, cc = min(c, H - 1);
+    const float w = a.norm_w[cc];
+    wv[t] = c < H ? w : 0.f;
+#pragma unroll
+    for (int r = 0; r < kXReps; ++r)
+#pragma unroll
+      for (int b = 0; b < NR; ++b) {
+        const long long v = a.x_in[r * a.rep_stride + (int64_t)b * H + cc];
+        qr[r][b][t] = c < H ? v : 0;
+      }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   const int tau = wave & 3, kh = wave >> 2;
   const f16 *Wt = (const f16 *)a.w_gu + (int64_t)(2 * f0 + 16 * tau + i) * H;
   const int ku = H / 64;
   const int kw0 = kh * ku * 32;
   f16x8 wt[KU];
+  // units past ku load a clamped (in-range) address and are never multiplied:
+  // a condition around the load would become a branch per load
 #pragma unroll
-  for (int t = 0; t < KU; ++t) wt[t] = (t < ku) ? load8(Wt + kw0 + 32 * t + 8 * g) : zero;
+  for (int t = 0; t < KU; ++t) wt[t] = load8(Wt + kw0 + 32 * min(t, ku - 1) + 8 * g);
   const int CB = H / 8;
   const int rg = tid / CB, cb = tid % CB;
   const bool d_ok = rg < RG;
@@ -1394,24 +1435,11 @@ __global__ void __launch_bounds__(512) dec_mlp32_kernel(DecMlpArgs a) {
   f16x8 wd[DR];
 #pragma unroll
   for (int f = 0; f < DR; ++f) wd[f] = load8(Wd + (int64_t)f * H);     // threads past RG: unused
+  __builtin_amdgcn_sched_barrier(0);
 
   long long xq[NR][NPER];
   {
-    float xv[NR][NPER], wv[NPER];
-    long long qr[kXReps][NR][NPER];
-#pragma unroll
-    for (int t = 0; t < NPER; ++t) {
-      const int c = t * 512 + tid, cc = min(c, H - 1);
-      const float w = a.norm_w[cc];
-      wv[t] = c < H ? w : 0.f;
-#pragma unroll
-      for (int r = 0; r < kXReps; ++r)
-#pragma unroll
-        for (int b = 0; b < NR; ++b) {
-          const long long v = a.x_in[r * a.rep_stride + (int64_t)b * H + cc];
-          qr[r][b][t] = c < H ? v : 0;
-        }
-    }
+    float xv[NR][NPER];
 #pragma unroll
     for (int t = 0; t < NPER; ++t)
 #pragma unroll
@@ -1429,7 +1457,7 @@ __global__ void __launch_bounds__(512) dec_mlp32_kernel(DecMlpArgs a) {
       ss = wave_sum(ss);
       if (lane == 0) s_red[wave][b] = ss;
     }
-    __syncthreads();
+    lds_barrier();                 // the weights stay in flight
 #pragma unroll
     for (int b = 0; b < NR; ++b) {
       float tot = 0.f;
@@ -1442,7 +1470,7 @@ __global__ void __launch_bounds__(512) dec_mlp32_kernel(DecMlpArgs a) {
         if (c < H) s_row[b][c] = (f16)(xv[b][t] * inv * wv[t]);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
