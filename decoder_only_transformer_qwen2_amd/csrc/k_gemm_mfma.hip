@@ -201,7 +201,7 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <Epi EPI, int TBM, int TBN, int WVM, int WVN, int NS>
+template <Epi EPI, int TBM, int TBN, int WVM, int WVN, int NS, bool FP = false>
 __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   constexpr int NWV = WVM * WVN;                  // waves
   constexpr int XT = TBM / WVM / 16, YT = TBN / WVN / 16;   // MFMA tiles per wave
@@ -257,25 +257,18 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
     for (int y = 0; y < YT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int k = 0; k < NS - 1; ++k)
-    if (k < KT) issue(k);
-  for (int kt = 0; kt < KT; ++kt) {
-    // stage kt done (this wave's loads; later stages may stay in flight)
-    const int ahead = min(NS - 2, KT - 1 - kt);
-    static_assert((NS - 2) * PER_STAGE <= 15, "vmcnt field");
-    if (ahead >= 3)
-      __builtin_amdgcn_s_waitcnt(((3 * PER_STAGE) & 15) | (7 << 4) | (15 << 8));
-    else if (ahead == 2)
+  // wait until at most n stages of this wave's loads are still in flight
+  auto wait_stages = [&](int n) {
+    static_assert(2 * PER_STAGE <= 15, "vmcnt field");
+    if (n >= 2)
       __builtin_amdgcn_s_waitcnt(((2 * PER_STAGE) & 15) | (7 << 4) | (15 << 8));
-    else if (ahead == 1)
+    else if (n == 1)
       __builtin_amdgcn_s_waitcnt((PER_STAGE & 15) | (7 << 4) | (15 << 8));
     else
       __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
-    stage_barrier();                     // every wave's share of stage kt is in; stage kt - 1 is consumed
-    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+  };
+  auto read_frags = [&](int kt, f16x8 (&fa)[XT], f16x8 (&fb)[YT]) {
     const int st = kt % NS;
-    f16x8 fa[XT], fb[YT];
 #pragma unroll
     for (int x = 0; x < XT; ++x) {
       const int row = wm * (TBM / WVM) + x * 16 + i;
@@ -286,10 +279,62 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
       const int row = wn * 64 + y * 16 + i;
       fb[y] = sB[st][row * 4 + (g ^ lds_swz(row))];
     }
+  };
+  auto mma = [&](const f16x8 (&fa)[XT], const f16x8 (&fb)[YT]) {
 #pragma unroll
     for (int x = 0; x < XT; ++x)
 #pragma unroll
       for (int y = 0; y < YT; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k)
+    if (k < KT) issue(k);
+  if constexpr (FP) {
+    // Fragments of stage kt + 1 are read from LDS while the MFMAs of stage kt
+    // run (two register sets).  The barrier of step kt publishes stage kt + 1
+    // and ends every wave's MFMAs of step kt - 1, whose fragments were read a
+    // step earlier, so stage kt - 1's buffer takes the loads of kt + NS - 1.
+    static_assert(NS >= 3, "one stage in flight beyond the one being read");
+    f16x8 fa0[XT], fb0[YT], fa1[XT], fb1[YT];
+    if (KT > 0) {
+      wait_stages(min(NS - 2, KT - 1));
+      stage_barrier();
+      read_frags(0, fa0, fb0);
+    }
+    auto step = [&](int kt, const f16x8 (&fa)[XT], const f16x8 (&fb)[YT], f16x8 (&na)[XT], f16x8 (&nb)[YT]) {
+      if (kt + 1 < KT) {
+        wait_stages(min(NS - 3, KT - 2 - kt));
+        stage_barrier();
+        if (kt + NS - 1 < KT) issue(kt + NS - 1);
+      }
+      // unconditional (the last step re-reads its own stage, which stays
+      // valid): behind a branch the compiler waited for every LDS read here
+      read_frags(min(kt + 1, KT - 1), na, nb);
+      mma(fa, fb);
+      // issue order: the next stage's LDS reads spread between these MFMAs
+      // (a batch of them ahead of the MFMAs made the compiler wait for all)
+#pragma unroll
+      for (int q = 0; q < XT + YT; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, (XT * YT) / (XT + YT + 1), 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                           // LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, XT * YT - (XT + YT) * ((XT * YT) / (XT + YT + 1)), 0);
+    };
+    for (int kt = 0; kt < KT; kt += 2) {
+      step(kt, fa0, fb0, fa1, fb1);
+      if (kt + 1 < KT) step(kt + 1, fa1, fb1, fa0, fb0);
+    }
+  } else {
+  for (int kt = 0; kt < KT; ++kt) {
+    // stage kt done (this wave's loads; later stages may stay in flight)
+    wait_stages(min(NS - 2, KT - 1 - kt));
+    stage_barrier();                     // every wave's share of stage kt is in; stage kt - 1 is consumed
+    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+    f16x8 fa[XT], fb[YT];
+    read_frags(kt, fa, fb);
+    mma(fa, fb);
+  }
   }
 
   // acc[x][y]: lane (i, g) holds rows 4g..4g+3 of column i of MFMA tile (x, y)
@@ -432,10 +477,13 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
   if (big_tile_splits(a.M, a.N, a.K) > 0) {
     const int big = ((a.N + 255) / 256) * ((a.M + 255) / 256);
     dim3 g2(8 * ((big + 7) / 8), 1, S);
+    // four stages, the next stage's fragments read from LDS during this
+    // stage's MFMAs: gate/up of an 8x2048 prefill 25.5 -> 24.3 ms (three
+    // stages with the same pipelining: 26.1 ms)
     switch (a.epi) {
-      case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, 3>), dim3(g2), dim3(512), 0, s, a); break;
-      case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, 3>), dim3(g2), dim3(512), 0, s, a); break;
-      case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 256, 256, 2, 4, 3>), dim3(g2), dim3(512), 0, s, a); break;
+      case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, 4, true>), dim3(g2), dim3(512), 0, s, a); break;
+      case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, 4, true>), dim3(g2), dim3(512), 0, s, a); break;
+      case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 256, 256, 2, 4, 4, true>), dim3(g2), dim3(512), 0, s, a); break;
     }
   } else if (kLdsPipeline && a.K % LK == 0) {
     switch (a.epi) {
