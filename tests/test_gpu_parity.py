@@ -44,6 +44,9 @@ SMALL = {
     # more than two rows: the batched decode path (split-KV attention on the
     # matrix cores, g = 7 as in the 0.5B model; unsplit gate/up with SwiGLU)
     "bf16-hd64-g7-b5": (S.ModelShape("s64g7", 2, 448, 14, 2, 64, 896, 1100), 5, 53, 6, 96),
+    # 17..32 rows: two 16-row MFMA column blocks in the batched projections
+    # (K split with atomics for q/k/v, o and down; g = 6 as in the 1.5B model)
+    "bf16-hd64-g6-b20": (S.ModelShape("s64g6", 2, 512, 12, 2, 64, 1088, 1500), 20, 33, 5, 64),
 }
 
 
