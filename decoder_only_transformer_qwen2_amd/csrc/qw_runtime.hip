@@ -141,7 +141,9 @@ constexpr int kGemvTargetGroups = 1024;
 // With more than two rows every K slice also adds B fixed-point sums per row
 // with atomics, so fewer, longer slices pay off.
 constexpr int kGemvTargetGroupsBatched = 256;
-constexpr int kAttnTargetGroups = 1024;
+// split-KV workgroups to aim for (two per CU): at 32 rows x 8k keys 8 splits
+// of ~1k keys beat 16 of ~512 (57.3 vs 60.5 us per launch, same box)
+constexpr int kAttnTargetGroups = 512;
 // Up to this many rows, a projection normalises its own operand (each
 // workgroup reads the whole residual rows); above it a norm kernel runs.
 constexpr int kFusedNormRows = 2;
