@@ -46,7 +46,7 @@ typedef enum qw_status {
   QW_ERR_HIP = -3,            /* a HIP runtime call failed (message has it)    */
   QW_ERR_CACHE_FULL = -4,     /* the step would write past max_seq             */
   QW_ERR_BAD_STATE = -5,      /* e.g. decode before any prefill                */
-  QW_ERR_UNSUPPORTED = -6     /* valid model, but a shape this build lacks     */
+  QW_ERR_UNSUPPORTED = -6     /* valid model, but a shape no kernel covers     */
 } qw_status;
 
 /* Storage type of every weight tensor handed to qw_create.
@@ -65,7 +65,7 @@ typedef struct qw_config {
   int32_t hidden;         /* H, model width                                   */
   int32_t n_heads;        /* query heads nq                                   */
   int32_t n_kv_heads;     /* KV heads nkv; nq % nkv == 0 (GQA)                */
-  int32_t head_dim;       /* hd; 32, 64 or 128 in this build                  */
+  int32_t head_dim;       /* hd; 32, 64 or 128 (the kernels' head sizes)      */
   int32_t intermediate;   /* I, SwiGLU width                                  */
   int32_t vocab;          /* V                                                */
   float rms_eps;          /* RMSNorm epsilon (1e-6 for Qwen2.5)               */

@@ -1,7 +1,7 @@
 """The measurement model of bench.py (CPU only): the algorithmic bytes and
 FLOP that every roofline fraction divides by, checked against figures derived
-independently from the model shapes (the survey's decode-bytes and prefill-FLOP
-table), and the gating of the measured-traffic record."""
+independently from the model shapes (a hand-derived decode-bytes and
+prefill-FLOP table), and the gating of the measured-traffic record."""
 import json
 import os
 
