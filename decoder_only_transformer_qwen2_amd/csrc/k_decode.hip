@@ -1561,6 +1561,7 @@ template <int HD, int TPW>
 __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
   constexpr int NW = 4, LPK = HD / 8, KPW = 64 / LPK, KSTEP = NW * KPW, HALF = HD / 2, U = 8;
   constexpr int RB = 64 * TPW;                 // W_o rows per workgroup
+  static_assert(2 * HALF + HD <= 256, "one prologue element per thread");
   __shared__ float s_q[HD], s_k[HD], s_v[HD];
   __shared__ float s_m[NW], s_l[NW];
   __shared__ float s_o[NW][HD];
@@ -1574,6 +1575,24 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
   const int H = a.H;
   const int qd = a.n_heads * HD, kvd = a.n_kv_heads * HD, ncols = qd + 2 * kvd;
   const f16x8 zero = {};
+
+  // prologue operands first (q of head h, new k and v of KV head j: their
+  // projection sums, biases and the rotation at pos), so that bias + RoPE
+  // runs while the W_o block and the cached keys are still arriving.
+  // Thread e < HD handles a rotation pair (q for e < HALF, k above), thread
+  // HD <= e < 2 HD one value of v; addresses are clamped, unused ones
+  // discarded.
+  const long long *acc = a.qkv_fix + (int64_t)b * ncols;
+  const float2 *cs = a.rope + (int64_t)pos * HALF;
+  const int pe = tid;
+  const bool p_rot = pe < 2 * HALF, p_v = !p_rot && pe < 2 * HALF + HD;
+  const int p_ii = (pe < HALF) ? pe : (p_rot ? pe - HALF : 0);
+  const int p_c0 = p_rot ? ((pe < HALF) ? h * HD + p_ii : qd + j * HD + p_ii)
+                         : qd + kvd + j * HD + (p_v ? pe - 2 * HALF : 0);
+  const long long p_a0 = acc[p_c0], p_a1 = acc[p_rot ? p_c0 + HALF : p_c0];
+  const float p_b0 = a.bias[p_c0], p_b1 = a.bias[p_rot ? p_c0 + HALF : p_c0];
+  const float2 p_r = cs[p_ii];
+  __builtin_amdgcn_sched_barrier(0);
 
   // W_o block: lane (i, g) holds row r0 + 16 tt + i, columns h hd + 32 s + 8 g
   const int r0 = rb * RB + wave * 16 * TPW;
@@ -1603,37 +1622,26 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
       vr[u] = t < kc_end ? vv : zero;
     }
   };
-  if (kstart < kc_end) issue(kstart);
+  issue(kstart);                   // unconditional: a wave with no keys loads clamped ones and zeroes them
+  __builtin_amdgcn_sched_barrier(0);
 
   clear_share(a.clear, a.clear_n, (b * gridDim.y + h) * gridDim.x + rb, gridDim.x * gridDim.y * gridDim.z);
 
-  // prologue: q of head h, new k and v of KV head j (bias + RoPE at pos)
-  const long long *acc = a.qkv_fix + (int64_t)b * ncols;
-  const float2 *cs = a.rope + (int64_t)pos * HALF;
   const float qscale = a.softmax_scale * LOG2E;
-  for (int e = tid; e < 2 * HALF + HD; e += 256) {
-    if (e < 2 * HALF) {
-      const bool is_q = e < HALF;
-      const int ii = is_q ? e : e - HALF;
-      const int c0 = is_q ? h * HD + ii : qd + j * HD + ii;
-      const float re = from_fix(acc[c0]) + a.bias[c0];
-      const float im = from_fix(acc[c0 + HALF]) + a.bias[c0 + HALF];
-      const float2 r = cs[ii];
-      const float nre = re * r.x - im * r.y, nim = im * r.x + re * r.y;
-      if (is_q) {
-        s_q[ii] = (float)(f16)nre * qscale;
-        s_q[ii + HALF] = (float)(f16)nim * qscale;
-      } else {
-        s_k[ii] = (float)(f16)nre;
-        s_k[ii + HALF] = (float)(f16)nim;
-      }
+  if (p_rot) {
+    const float re = from_fix(p_a0) + p_b0, im = from_fix(p_a1) + p_b1;
+    const float nre = re * p_r.x - im * p_r.y, nim = im * p_r.x + re * p_r.y;
+    if (pe < HALF) {
+      s_q[p_ii] = (float)(f16)nre * qscale;
+      s_q[p_ii + HALF] = (float)(f16)nim * qscale;
     } else {
-      const int d = e - 2 * HALF;
-      const int c = qd + kvd + j * HD + d;
-      s_v[d] = (float)(f16)(from_fix(acc[c]) + a.bias[c]);
+      s_k[p_ii] = (float)(f16)nre;
+      s_k[p_ii + HALF] = (float)(f16)nim;
     }
+  } else if (p_v) {
+    s_v[pe - 2 * HALF] = (float)(f16)(from_fix(p_a0) + p_b0);
   }
-  __syncthreads();
+  lds_barrier();                   // the W_o block and the keys stay in flight
   if (rb == 0 && h % grp == 0 && tid < HD) {
     Kc[(int64_t)pos * HD + tid] = (f16)s_k[tid];
     Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
