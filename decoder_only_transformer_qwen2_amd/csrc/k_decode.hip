@@ -1187,16 +1187,66 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
   f16 *Kc = (f16 *)a.k_cache + head_base;
   f16 *Vc = (f16 *)a.v_cache + head_base;
 
+  // the wave's first batch of cached keys is loaded before the prologue, so
+  // that it arrives while bias + RoPE run; later batches at the end of each
+  // step.  Keys past the split's end load a clamped (valid) row.
+  const int kc_end = min(kb1, pos);             // cached keys of this split
+  const int klast = max(kc_end - 1, 0);
+  // K rows of the two 16-key tiles: tile y, row i is key k0 + 8 (i / 4) + 4y + i % 4;
+  // V^T operand: lane (i, g) holds dim 16d + i of keys k0 + 8g .. k0 + 8g + 7
+  f16x8 kf[2][KS], vf[DT];
+  auto load_kv = [&](int k0) {
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int key = min(k0 + 8 * (i >> 2) + 4 * y + (i & 3), klast);
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) kf[y][s2] = load8(Kc + (int64_t)key * HD + 32 * s2 + 8 * g);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f16 *vrow = Vc + (int64_t)min(k0 + 8 * g + e, klast) * HD + i;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) vf[d][e] = vrow[16 * d];
+    }
+  };
+  // prologue operands (q of the group's heads, new k and v: projection sums,
+  // biases, the rotation at pos) are loaded first, then the first key batch,
+  // so that bias + RoPE waits only for its own loads.  Element e < (G+1) HALF
+  // is a rotation pair of q (head e / HALF) or k, the rest one value of v;
+  // addresses of unused elements are clamped and their values discarded.
+  constexpr int NE = (G + 1) * HALF + HD, NI = (NE + 255) / 256;
+  long long pa0[NI], pa1[NI];
+  float pb0[NI], pb1[NI];
+  float2 pr[NI];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = tid + 256 * it;
+    const bool rot = e < (G + 1) * HALF, val = e < NE;
+    const int hh = rot ? e / HALF : 0, ii = rot ? e % HALF : 0;
+    const int c0 = rot ? ((hh < G) ? (j * G + hh) * HD + ii : qd + j * HD + ii)
+                       : qd + kvd + j * HD + (val ? e - (G + 1) * HALF : 0);
+    const int c1 = rot ? c0 + HALF : c0;
+    pa0[it] = acc[c0];
+    pa1[it] = acc[c1];
+    pb0[it] = a.bias[c0];
+    pb1[it] = a.bias[c1];
+    pr[it] = cs[ii];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int kfirst = kb0 + 32 * wave;
+  load_kv(kfirst);
+  __builtin_amdgcn_sched_barrier(0);
+
   clear_share(a.clear, a.clear_n, (b * gridDim.y + j) * S + split, S * gridDim.y * gridDim.z);
 
   // q of the group's heads (rounded to f16, unscaled), new k and v
-  for (int e = tid; e < (G + 1) * HALF + HD; e += 256) {
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = tid + 256 * it;
     if (e < (G + 1) * HALF) {
       const int hh = e / HALF, ii = e % HALF;
-      const int c0 = (hh < G) ? (j * G + hh) * HD + ii : qd + j * HD + ii;
-      const float re = from_fix(acc[c0]) + a.bias[c0];
-      const float im = from_fix(acc[c0 + HALF]) + a.bias[c0 + HALF];
-      const float2 r = cs[ii];
+      const float re = from_fix(pa0[it]) + pb0[it], im = from_fix(pa1[it]) + pb1[it];
+      const float2 r = pr[it];
       const float nre = re * r.x - im * r.y, nim = im * r.x + re * r.y;
       if (hh < G) {
         s_q[hh][ii] = (float)(f16)nre;
@@ -1205,13 +1255,11 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
         s_k[ii] = (float)(f16)nre;
         s_k[ii + HALF] = (float)(f16)nim;
       }
-    } else {
-      const int d = e - (G + 1) * HALF;
-      const int c = qd + kvd + j * HD + d;
-      s_v[d] = (float)(f16)(from_fix(acc[c]) + a.bias[c]);
+    } else if (e < NE) {
+      s_v[e - (G + 1) * HALF] = (float)(f16)(from_fix(pa0[it]) + pb0[it]);
     }
   }
-  __syncthreads();
+  lds_barrier();                   // the first key batch stays in flight
   if (has_new && tid < HD) {
     Kc[(int64_t)pos * HD + tid] = (f16)s_k[tid];
     Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
@@ -1229,25 +1277,7 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
 #pragma unroll
   for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int kc_end = min(kb1, pos);             // cached keys of this split
-  for (int k0 = kb0 + 32 * wave; k0 < kc_end; k0 += 32 * NW) {
-    const int klast = kc_end - 1;
-    // K rows of the two 16-key tiles: tile y, row i is key k0 + 8 (i / 4) + 4y + i % 4
-    f16x8 kf[2][KS];
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int key = min(k0 + 8 * (i >> 2) + 4 * y + (i & 3), klast);
-#pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) kf[y][s2] = load8(Kc + (int64_t)key * HD + 32 * s2 + 8 * g);
-    }
-    // V^T operand: lane (i, g) holds dim 16d + i of keys k0 + 8g .. k0 + 8g + 7
-    f16x8 vf[DT];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const f16 *vrow = Vc + (int64_t)min(k0 + 8 * g + e, klast) * HD + i;
-#pragma unroll
-      for (int d = 0; d < DT; ++d) vf[d][e] = vrow[16 * d];
-    }
+  for (int k0 = kfirst; k0 < kc_end; k0 += 32 * NW) {
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int y = 0; y < 2; ++y)
@@ -1285,6 +1315,7 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
       o[d] *= corr;
       o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[d], pb, o[d], 0, 0, 0);
     }
+    if (k0 + 32 * NW < kc_end) load_kv(k0 + 32 * NW);
   }
   if (has_new && wave == 0) {
     // the new key, from LDS: head i's score, then its share of dims 16d + 4g + r
