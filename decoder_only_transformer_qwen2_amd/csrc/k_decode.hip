@@ -1865,7 +1865,11 @@ int dec_gemv_splits(int N, int K, int M, int target_groups) {
   const int nblk = (N + 63) / 64;
   const int units = K / 32;
   int splits = (target_groups + nblk - 1) / nblk;
-  int max_splits = (units + 3) / 4;            // at least 128 k per slice
+  // at least 128 k per slice, 256 from K = 1024 on: every slice repeats the
+  // norm prologue over the whole row (1.5B, one row: 1.553 -> 1.473 ms/step
+  // with 256; 0.5B prefers 128: 0.6173 vs 0.6186 ms/step)
+  const int minu = K >= 1024 ? 8 : 4;
+  int max_splits = (units + minu - 1) / minu;
   // keep the atomic traffic (8 bytes per output per slice) under the weight bytes
   const int atomic_cap = (K * 2) / (8 * (M < 1 ? 1 : M));
   if (atomic_cap >= 1 && max_splits > atomic_cap) max_splits = atomic_cap;
