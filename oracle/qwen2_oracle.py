@@ -41,6 +41,7 @@ Readings where the pages are silent (each is listed in the design doc):
 """
 from __future__ import annotations
 
+import os
 from typing import Dict, Optional
 
 import numpy as np
@@ -98,27 +99,62 @@ def attention_weights(q: np.ndarray, k: np.ndarray, q_pos: np.ndarray, k_pos: np
     """One head: [S] "Attention" (scores q.k / sqrt(d_k)), "What's up with
     Softmax?" (max-subtracted softmax over keys) and "Every token with every
     other token" (a query at position p sees only keys at positions <= p).
-    q [T, hd], k [S, hd] -> probabilities [T, S]; masked entries are 0."""
-    scores = (q @ k.T) / np.sqrt(q.shape[-1])
-    visible = k_pos[None, :] <= q_pos[:, None]
-    scores = np.where(visible, scores, -np.inf)
-    scores = scores - scores.max(axis=-1, keepdims=True)
-    e = np.exp(scores)
-    return e / e.sum(axis=-1, keepdims=True)
+    q [T, hd], k [S, hd] -> probabilities [T, S]; masked entries are 0.
+    (Each step works in place on the one [T, S] array: the same values as
+    fresh arrays per step, without allocating several of them at long
+    contexts.)"""
+    scores = q @ k.T
+    scores /= np.sqrt(q.shape[-1])
+    hidden = k_pos[None, :] > q_pos[:, None]
+    scores[hidden] = -np.inf
+    scores -= scores.max(axis=-1, keepdims=True)
+    np.exp(scores, out=scores)
+    scores /= scores.sum(axis=-1, keepdims=True)
+    return scores
+
+
+# Query rows per block in causal_gqa_attention.
+_ROWS_PER_BLOCK = 512
 
 
 def causal_gqa_attention(q, k, v, q_pos, k_pos):
     """[S] "Grouped Query Attention GQA" / [A] grouped-query attention: query
     head h reads KV head floor(h / g), g = n_heads / n_kv_heads (consecutive
     query heads share one KV head, as repeating each KV head g times does).
-    q [T, nq, hd]; k, v [S, nkv, hd] -> [T, nq, hd]."""
+    q [T, nq, hd]; k, v [S, nkv, hd] -> [T, nq, hd].
+
+    Evaluation order only (no arithmetic changes): every output row depends
+    on its own query row alone, so rows are taken in blocks, and a block
+    meets only the keys at or before its last row's position (k_pos must be
+    ascending); any key past that is masked for every row of the block and
+    would get weight exactly 0.  Heads are independent and run on a thread
+    pool, with the matrix library single-threaded inside each head."""
     nq, nkv = q.shape[1], k.shape[1]
     g = nq // nkv
+    k_pos = np.asarray(k_pos)
+    q_pos = np.asarray(q_pos)
+    if k_pos.size > 1 and np.any(np.diff(k_pos) <= 0):
+        raise ValueError("key positions must be ascending")
     out = np.empty(q.shape, dtype=np.float64)
-    for h in range(nq):
+
+    def one_head(h):
         j = h // g
-        p = attention_weights(q[:, h, :], k[:, j, :], q_pos, k_pos)
-        out[:, h, :] = p @ v[:, j, :]
+        for a in range(0, q.shape[0], _ROWS_PER_BLOCK):
+            b = min(a + _ROWS_PER_BLOCK, q.shape[0])
+            n_keys = int(np.searchsorted(k_pos, q_pos[a:b].max(), side="right"))
+            p = attention_weights(q[a:b, h, :], k[:n_keys, j, :], q_pos[a:b], k_pos[:n_keys])
+            out[a:b, h, :] = p @ v[:n_keys, j, :]
+
+    work = q.shape[0] * k.shape[0]
+    if nq == 1 or work < (1 << 22):
+        for h in range(nq):
+            one_head(h)
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    threads = max(1, min(nq, len(os.sched_getaffinity(0))))
+    with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one_head, range(nq)))
     return out
 
 
@@ -195,16 +231,19 @@ class OracleModel:
         return x + swiglu_mlp(u2, lw["mlp.gate_proj.weight"], lw["mlp.up_proj.weight"],
                               lw["mlp.down_proj.weight"])
 
-    def forward(self, ids, start: int, cache, logits_rows: Optional[slice] = None) -> np.ndarray:
+    def forward(self, ids, start: int, cache, logits_rows: Optional[slice] = None, progress=None) -> np.ndarray:
         """Tokens `ids` at positions start.., given a cache holding 0..start-1.
         Returns logits [V] of the last row, or [rows, V] for `logits_rows`
-        ([A] full forward pass: embeddings, layers, final norm, LM head)."""
+        ([A] full forward pass: embeddings, layers, final norm, LM head).
+        `progress`, if given, is called with each finished layer's index."""
         ids = np.asarray(ids, dtype=np.int64).reshape(-1)
         if start != cache["len"]:
             raise ValueError("forward must continue the cached sequence")
         x = self.embed[ids]                                              # [T, H]
         for l in range(self.m.n_layers):
             x = self._block(l, x, start, cache)
+            if progress:
+                progress(l)
         cache["len"] = start + len(ids)
         rows = x[-1:] if logits_rows is None else x[logits_rows]
         y = rms_norm(rows, self.final_norm, self.m.rms_eps)
@@ -224,7 +263,7 @@ class OracleModel:
             toks.append(greedy_token(logits[-1]))
         return np.array(toks), np.stack(logits)
 
-    def teacher_forced(self, prompt, fed) -> np.ndarray:
+    def teacher_forced(self, prompt, fed, progress=None) -> np.ndarray:
         """Logits after the prompt and after each token of `fed` (the ids a
         decoder emitted), from one uncached forward over prompt + fed:
         [len(fed) + 1, V].  By causality row i equals what a cached decode
@@ -233,4 +272,4 @@ class OracleModel:
         fed = list(np.asarray(fed).reshape(-1))
         seq = prompt + fed
         cache = self.new_cache(len(seq))
-        return self.forward(seq, 0, cache, logits_rows=slice(len(prompt) - 1, len(seq)))
+        return self.forward(seq, 0, cache, logits_rows=slice(len(prompt) - 1, len(seq)), progress=progress)
