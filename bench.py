@@ -5,17 +5,24 @@ batch's prompts (the TTFT token), then the workload's greedy decode steps,
 each through the C ABI of libqw.so.  Inputs (weights, token ids) are seeded
 synthetic data resident in HBM before the timed region starts.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 0.5b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1.5b-longctx]
+
+The default workload is the largest one that fits one GPU: Qwen2.5-1.5B
+shapes, batch 32 x 8192 prompt tokens, 128 greedy decode steps.
 
 Prints one JSON line.  `value` is decode tokens/s over the timed steps;
 prefill tokens/s and TTFT ride along.  `roofline` covers the kernel family
 with the most decode time, timed with HIP events on the model's stream over
-an extra, eagerly launched pass (same kernels, same data); `cpu_baseline` is
-the CPU oracle timed on a bounded sample of the same workload.
+an extra, eagerly launched pass (same kernels, same data); the whole decode
+step and the prefill's dominant GEMM get roofline objects of their own.
+Fractions are given against the published peaks and against peaks measured
+in the same run (an HBM copy and an MFMA-only loop).  `cpu_baseline` is the
+CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -31,9 +38,10 @@ import synthetic as S  # noqa: E402
 
 METRIC = "decode tokens/s + prefill tokens/s (TTFT) at 1 MI355X; % HBM / MFMA roofline"
 HBM_PEAK_GBS = 8000.0
-# committed rocprofv3 counter summary for the dominant decode kernel
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dec_mlp_0.5b_hbm_traffic.json")
+# committed rocprofv3 counter summaries (FETCH_SIZE / WRITE_SIZE per launch)
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "*_hbm_traffic.json")
 MFMA_F16_PEAK_TFLOPS = 2500.0
+DEFAULT_WORKLOAD = "1.5b-longctx"
 DESCRIPTIONS = {
     "tiny": "tiny Qwen2-style decoder, fp32 (2 layers, hidden 128), batch 1, prompt 16, 8 greedy decode steps",
     "0.5b": "Qwen2.5-0.5B shapes, bf16 weights, batch 1, prompt 128, 128 greedy decode steps, cache 2048",
@@ -71,21 +79,24 @@ def decode_family_bytes(w: S.Workload, family: str, ctx_mean: float) -> float:
     return float("nan")
 
 
-def measured_traffic(workload: str, family: str):
-    """HBM bytes per launch of a kernel family from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for
-    a copy of known size), or None when the summary is for another workload or
-    family, or the kernel's source file has changed since it was taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            d = json.load(f)
-        with open(os.path.join(ROOT, d["kernel_source"]), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-    except (OSError, ValueError, KeyError):
-        return None
-    if sha != d.get("kernel_source_sha256") or d.get("workload") != workload or d.get("family") != family:
-        return None
-    return int(d["fetch_bytes_per_launch"] + d["write_bytes_per_launch"])
+def measured_traffic(workload: str, family: str, pattern: str = None):
+    """HBM bytes per launch of a kernel family from a committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
+    for a copy of known size), or None when no summary covers this workload
+    and family, or the kernel's source file has changed since it was taken."""
+    for path in sorted(glob.glob(pattern or TRAFFIC_GLOB)):
+        try:
+            with open(path) as f:
+                d = json.load(f)
+            if d.get("workload") != workload or d.get("family") != family:
+                continue
+            with open(os.path.join(ROOT, d["kernel_source"]), "rb") as f:
+                sha = hashlib.sha256(f.read()).hexdigest()
+        except (OSError, ValueError, KeyError):
+            continue
+        if sha == d.get("kernel_source_sha256"):
+            return int(d["fetch_bytes_per_launch"] + d["write_bytes_per_launch"])
+    return None
 
 
 def decode_step_bytes(w: S.Workload, ctx_mean: float) -> float:
@@ -135,31 +146,82 @@ def run_step(model, ids, toks, D, torch, ev=None):
         ev[2].record()
 
 
-def cpu_baseline(w: S.Workload, W, ids, budget_s: float = 15.0):
-    """The oracle, untuned, on batch row 0: prefill, then decode steps until
-    the time budget is spent.  Reports decode tokens/s of the sample."""
-    import oracle as O
+def cpu_info():
+    """CPU model name and the number of cores this process may run on."""
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+# Prompt tokens of the oracle's sample: its decode rate is set by streaming
+# every weight once per token (12.3 GB in float64 at 1.5B shapes), which a
+# context of this size already shows; an 8k-token float64 prefill alone takes
+# minutes.
+CPU_SAMPLE_PROMPT = 512
+
+
+def cpu_baseline(w: S.Workload, W, ids, budget_s: float = 15.0):
+    """The oracle, untuned, on a bounded sample of batch row 0: prefill of
+    its first CPU_SAMPLE_PROMPT prompt tokens, then decode steps until the
+    time budget is spent.  Reports decode tokens/s of the sample."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model_name, affinity = cpu_info()
+    P = min(w.prompt_len, CPU_SAMPLE_PROMPT)
     om = O.OracleModel(w.model, W)
-    cache = om.new_cache(w.prompt_len + w.decode_steps)
+    cache = om.new_cache(P + w.decode_steps)
     t0 = time.perf_counter()
-    lg = om.forward(ids[0], 0, cache)
+    lg = om.forward(ids[0, :P], 0, cache)
     t_prefill = time.perf_counter() - t0
     tok = O.greedy_token(lg)
     n, t1 = 0, time.perf_counter()
     while n < w.decode_steps and (time.perf_counter() - t1) < budget_s:
-        lg = om.forward([tok], w.prompt_len + n, cache)
+        lg = om.forward([tok], P + n, cache)
         tok = O.greedy_token(lg)
         n += 1
     t_dec = time.perf_counter() - t1
+    # the oracle's attention runs one thread per head (at most the affinity
+    # count); its matrix products use the BLAS pool
+    cores = max(blas_threads, min(w.model.n_heads, affinity))
     return {"value": round(n / t_dec, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"batch row 0 of {w.batch}: prefill of {w.prompt_len} tokens "
-                      f"({w.prompt_len / t_prefill:.1f} tokens/s, TTFT {t_prefill * 1e3:.0f} ms), "
-                      f"then the first {n} decode steps (fp64 numpy oracle)"}
+            "cpu_model": model_name, "sched_affinity_cores": affinity, "blas_threads": blas_threads,
+            "sample": f"batch row 0 of {w.batch}: the first {P} of its {w.prompt_len} prompt tokens prefilled "
+                      f"({P / t_prefill:.1f} tokens/s, {t_prefill * 1e3:.0f} ms), then the first {n} greedy "
+                      f"decode steps (float64 numpy oracle; decode tokens/s)"}
+
+
+def measure_peaks(torch, Q):
+    """HBM copy rate (GB/s) and MFMA-only fp16 rate (TFLOP/s) measured now,
+    on this GPU, by the library's peak helpers."""
+    n = 1 << 30
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream().cuda_stream
+    Q.qw_peak_copy(dst.data_ptr(), src.data_ptr(), n, 2, st)            # warm
+    gbs = Q.qw_peak_copy(dst.data_ptr(), src.data_ptr(), n, 10, st)
+    del src, dst
+    Q.qw_peak_mfma(2000, st)
+    tflops = Q.qw_peak_mfma(100000, st)
+    return {"copy_GBps": round(gbs, 1), "copy_bytes": n, "mfma_f16_TFLOPs": round(tflops, 1),
+            "mfma": "8192 waves x 100000 rounds of 8 independent v_mfma_f32_16x16x32_f16"}
+
+
+def roof(bound, kernel, achieved, peak, measured_peak, unit, **extra):
+    out = {"bound": bound, "kernel": kernel, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4)}
+    if measured_peak:
+        out["measured_peak"] = measured_peak
+        out["frac_of_measured"] = round(achieved / measured_peak, 4)
+    out.update(extra)
+    return out
 
 
 def main():
@@ -167,9 +229,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="0.5b", choices=sorted(S.WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(S.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the in-run copy and MFMA peak measurements")
     ap.add_argument("--eager", action="store_true",
                     help="launch decode kernels one by one instead of replaying the captured graph "
                          "(same kernels; for counter collection, which does not follow graph launches)")
@@ -199,10 +262,15 @@ def main():
     w = S.WORKLOADS[args.workload]
     m = w.model
     B, P, D = w.batch, w.prompt_len, w.decode_steps
+    peaks = None
+    if not args.no_peaks:
+        print("[bench] measured peaks (copy, MFMA)", file=sys.stderr, flush=True)
+        peaks = measure_peaks(torch, Q)
     print(f"[bench] {args.workload}: generating weights", file=sys.stderr, flush=True)
     W = S.make_weights(m, w.weight_seed)
     ids_np = S.make_ids(w)
     model = Q.Model(m, Q.device_tensors(m, W), B, w.max_seq)
+    torch.cuda.empty_cache()
     if args.eager:
         model.set_graph(False)
     ids = torch.from_numpy(ids_np).cuda()
@@ -225,20 +293,27 @@ def main():
     decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     decode_tps = B * D / (decode_ms / 1e3)
     prefill_tps = B * P / (prefill_ms / 1e3)
+    model.check_numerics()
 
     out = {"metric": METRIC, "value": round(decode_tps, 2), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 3),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16" if m.dtype == "bf16" else "f32",
-           "data": "synthetic (seeded random-init weights N(0, 0.02), uniform token ids)",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f16" if m.dtype == "bf16" else "f32",
+           "data": "synthetic (seeded random-init weights N(0, 0.02) stored as bf16, uniform token ids)",
            "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}", "batch": B, "prompt_len": P,
-                      "decode_steps": D, "max_seq": w.max_seq},
+                      "decode_steps": D, "max_seq": w.max_seq,
+                      "step": f"one prefill of {B} x {P} tokens + {D} greedy decode steps"},
            "prefill_tokens_per_s": round(prefill_tps, 1), "ttft_ms": round(prefill_ms, 3),
            "decode_ms_per_token_step": round(decode_ms / D, 4)}
+    if peaks:
+        out["measured_peaks"] = peaks
+    hbm_meas = peaks["copy_GBps"] if peaks else None
+    mfma_meas = peaks["mfma_f16_TFLOPs"] if peaks else None
 
     if not args.no_roofline:
         # per-family decode time, each family timed over one eager pass
-        fams = ["gemm_qkv", "rope_cache", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "mlp", "attn_o", "attn_merge", "lm_head",
-                "argmax", "rmsnorm", "embed"]
+        fams = ["gemm_qkv", "rope_cache", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "mlp", "attn_o",
+                "attn_merge", "lm_head", "argmax", "rmsnorm", "embed"]
         per = {}
         for f in fams:
             model.prefill(ids, next_ids=toks[0])
@@ -255,17 +330,14 @@ def main():
         avg_s = ms / n / 1e3
         ctx_mean = P + (D - 1) / 2.0
         bytes_per = decode_family_bytes(w, dom, ctx_mean)
-        achieved = bytes_per / avg_s / 1e9
-        out["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": measured_traffic(args.workload, dom),
-                           "avg_launch_us": round(avg_s * 1e6, 3), "launches": n,
-                           "algorithmic_bytes_per_launch": int(bytes_per)}
+        out["roofline"] = roof("hbm", dom, bytes_per / avg_s / 1e9, HBM_PEAK_GBS, hbm_meas, "GB/s",
+                               traffic=measured_traffic(args.workload, dom), avg_launch_us=round(avg_s * 1e6, 3),
+                               launches=n, algorithmic_bytes_per_launch=int(bytes_per))
         out["decode_family_ms_per_step"] = {f: round(per[f][0] / D, 4) for f in per}
-        step_gbs = decode_step_bytes(w, ctx_mean) / (decode_ms / D / 1e3) / 1e9
-        out["decode_step_roofline"] = {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
-                                       "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
-                                       "bytes_per_step": int(decode_step_bytes(w, ctx_mean))}
+        step_bytes = decode_step_bytes(w, ctx_mean)
+        out["decode_step_roofline"] = roof("hbm", "whole decode step (graph replay)",
+                                           step_bytes / (decode_ms / D / 1e3) / 1e9, HBM_PEAK_GBS, hbm_meas, "GB/s",
+                                           bytes_per_step=int(step_bytes))
         # prefill: per-family time over one eager prefill each
         pper = {}
         for f in ("gemm_qkv", "attention", "gemm_o", "gemm_gate_up", "gemm_down", "rope_cache", "rmsnorm", "lm_head"):
@@ -275,12 +347,17 @@ def main():
             model.timing_enable(None)
             pper[f] = (ms, n)
         pdom = max(("gemm_qkv", "attention", "gemm_o", "gemm_gate_up", "gemm_down"), key=lambda f: pper[f][0])
-        ms, n = pper[pdom]
-        tflops = prefill_family_flops(w, pdom) / (ms / n / 1e3) / 1e12
-        out["prefill_roofline"] = {"bound": "mfma", "kernel": pdom, "achieved": round(tflops, 1),
-                                   "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                   "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                                   "avg_launch_us": round(ms / n * 1e3, 3), "launches": n}
+        for key, f in (("prefill_roofline", pdom), ("prefill_attention_roofline", "attention")):
+            ms, n = pper[f]
+            tflops = prefill_family_flops(w, f) / (ms / n / 1e3) / 1e12
+            out[key] = roof("mfma", f, tflops, MFMA_F16_PEAK_TFLOPS, mfma_meas, "TFLOP/s",
+                            avg_launch_us=round(ms / n * 1e3, 3), launches=n,
+                            flop_per_launch=prefill_family_flops(w, f))
+        pflop = sum(prefill_family_flops(w, f) for f in ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down",
+                                                          "attention")) * m.n_layers
+        pflop += prefill_family_flops(w, "lm_head")
+        out["prefill_whole_roofline"] = roof("mfma", "whole prefill (TTFT)", pflop / (prefill_ms / 1e3) / 1e12,
+                                             MFMA_F16_PEAK_TFLOPS, mfma_meas, "TFLOP/s", flop=pflop)
         out["prefill_family_ms"] = {f: round(pper[f][0], 3) for f in pper}
 
     if not args.no_cpu_baseline:

@@ -23,7 +23,7 @@ __global__ void __launch_bounds__(256) embed_kernel(const int32_t *__restrict__ 
   const int r = blockIdx.x;
   int id = ids[r];
   if (id < 0 || id >= vocab) {
-    if (threadIdx.x == 0) atomicOr(bad, 1);
+    if (threadIdx.x == 0) atomicOr(bad, kFlagBadId);
     id = 0;
   }
   const T *src = emb + (int64_t)id * hidden;
@@ -134,14 +134,18 @@ hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &
 // ---------------------------------------------------------------- argmax
 // One block per row.  Ties go to the lowest index; NaN never wins.
 __global__ void __launch_bounds__(256) argmax_kernel(const float *__restrict__ logits, int vocab, int64_t stride,
-                                                     int32_t *__restrict__ next_ids, int *pos_dev, int pos_add) {
+                                                     int32_t *__restrict__ next_ids, int *pos_dev, int pos_add,
+                                                     int *flag) {
   const float *row = logits + (int64_t)blockIdx.x * stride;
   float best = -INFINITY;
   int bi = 0x7fffffff;
+  bool finite = true;
   for (int v = threadIdx.x; v < vocab; v += blockDim.x) {
     const float x = row[v];
     if (x > best) { best = x; bi = v; }      // v increases, so the first max is kept
+    finite = finite && (fabsf(x) <= 3.4e38f);
   }
+  if (!finite) atomicOr(flag, kFlagNonFinite);
   for (int o = 32; o > 0; o >>= 1) {
     const float ob = __shfl_xor(best, o, 64);
     const int oi = __shfl_xor(bi, o, 64);
@@ -161,9 +165,10 @@ __global__ void __launch_bounds__(256) argmax_kernel(const float *__restrict__ l
 }
 
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
-                         int32_t *next_ids, int *pos_dev, int pos_add) {
+                         int32_t *next_ids, int *pos_dev, int pos_add, int *flag) {
   if (rows <= 0) return hipSuccess;
-  QW_LAUNCH((argmax_kernel), dim3(rows), dim3(256), 0, s, logits, vocab, row_stride, next_ids, pos_dev, pos_add);
+  QW_LAUNCH((argmax_kernel), dim3(rows), dim3(256), 0, s, logits, vocab, row_stride, next_ids, pos_dev, pos_add,
+            flag);
   return hipGetLastError();
 }
 
@@ -210,12 +215,16 @@ __device__ __forceinline__ float load_src(const void *p, int64_t i, bool bf16) {
 
 // Largest |value| of a tensor, as the bit pattern of a non-negative float
 // (ordered like the floats themselves, so an integer max works).
+// Largest |value| as float bits.  Magnitudes are compared as unsigned bit
+// patterns (the same order for non-negative floats), which keeps an inf or
+// NaN as the maximum so that qw_create can reject it.
 __global__ void __launch_bounds__(256) absmax_kernel(const void *src, int64_t n, bool bf16, unsigned *out) {
-  float m = 0.f;
+  unsigned m = 0u;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    m = fmaxf(m, fabsf(load_src(src, i, bf16)));
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomicMax(out, __float_as_uint(m));
+    m = max(m, __float_as_uint(fabsf(load_src(src, i, bf16))));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, m);
 }
 
 hipError_t launch_absmax(hipStream_t s, bool src_bf16, const void *src, int64_t n, unsigned *out_bits) {

@@ -48,13 +48,19 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr int CH = 256;                             // k per staged chunk
 constexpr int MERGE_MAX_S = 16;                     // split-KV partials merged per head
 
-__device__ __forceinline__ long long to_fix(float v) {
+// A fixed-point value spans +-2^31.  Every addend is checked against 2^23
+// (so no sum of the at most a few hundred addends of one value can wrap);
+// one beyond it, or NaN, sets kFlagFixRange in the model's status word
+// (qw_check_numerics) and is clamped so the conversion stays defined.
+constexpr float FIX_ADDEND_MAX = 8388608.0f;        // 2^23
+__device__ __forceinline__ long long to_fix(float v, int *flag) {
+  if (!(fabsf(v) <= FIX_ADDEND_MAX)) atomicOr(flag, kFlagFixRange);
   v = fminf(fmaxf(v, -1.0e9f), 1.0e9f);
   return __float2ll_rn(v * FIX_ONE);
 }
 __device__ __forceinline__ float from_fix(long long q) { return (float)q * FIX_INV; }
-__device__ __forceinline__ void fix_add(long long *p, float v) {
-  atomicAdd(reinterpret_cast<unsigned long long *>(p), (unsigned long long)to_fix(v));
+__device__ __forceinline__ void fix_add(long long *p, float v, int *flag) {
+  atomicAdd(reinterpret_cast<unsigned long long *>(p), (unsigned long long)to_fix(v, flag));
 }
 __device__ __forceinline__ f16x8 load8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 
@@ -114,11 +120,11 @@ __global__ void __launch_bounds__(256) dec_embed_kernel(const int32_t *ids, cons
   const int b = blockIdx.x;
   int id = ids[b];
   if (id < 0 || id >= V) {
-    if (threadIdx.x == 0) atomicOr(bad, 1);
+    if (threadIdx.x == 0) atomicOr(bad, kFlagBadId);
     id = 0;
   }
   const f16 *row = emb + (int64_t)id * H;
-  for (int c = threadIdx.x; c < H; c += blockDim.x) x_fix[(int64_t)b * H + c] = to_fix((float)row[c] * emb_scale);
+  for (int c = threadIdx.x; c < H; c += blockDim.x) x_fix[(int64_t)b * H + c] = to_fix((float)row[c] * emb_scale, bad);
   clear_share(clr0, n0, b, gridDim.x);
   clear_share(clr1, n1, b, gridDim.x);
 }
@@ -428,7 +434,7 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
       if (b >= a.M) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (nw + r < a.N) fix_add(a.out_fix + (int64_t)b * a.ldo + nw + r, acc[nb][r] * a.scale);
+        if (nw + r < a.N) fix_add(a.out_fix + (int64_t)b * a.ldo + nw + r, acc[nb][r] * a.scale, a.num_flag);
     }
   } else if constexpr (OM == DecOut::SwiGLUOut) {
     // full K in this workgroup: waves 0/1 hold the gate/up rows of feature
@@ -461,6 +467,7 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
         if (n < a.N && b < a.M) {
           if (a.logits) a.logits[(int64_t)b * a.ldo + n] = v;
           if (v > best) { best = v; bi = n; }     // n increases with r
+          if (!(fabsf(v) <= 3.4e38f)) atomicOr(a.num_flag, kFlagNonFinite);
         }
       }
       // lanes i, i+16, i+32, i+48 share batch column i
@@ -620,11 +627,11 @@ __global__ void __launch_bounds__(256) dec_rows_kernel(DecGemvArgs a) {
       if (n >= a.N || b >= a.M) continue;
       long long *p = a.out_fix + (int64_t)b * a.ldo + n;
       if constexpr (ATOMIC) {
-        fix_add(p, total(nl, b));
+        fix_add(p, total(nl, b), a.num_flag);
       } else {
         // sole writer: a residual row adds to its value, a projection sum
         // (cleared beforehand) is simply its value
-        *p += to_fix(total(nl, b));
+        *p += to_fix(total(nl, b), a.num_flag);
       }
     }
   } else if constexpr (OM == DecOut::SwiGLUOut) {
@@ -652,6 +659,7 @@ __global__ void __launch_bounds__(256) dec_rows_kernel(DecGemvArgs a) {
       if (n < a.N && b < a.M) {
         if (a.logits) a.logits[(int64_t)b * a.ldo + n] = v;
         if (v > best) { best = v; bi = n; }      // n increases with j
+        if (!(fabsf(v) <= 3.4e38f)) atomicOr(a.num_flag, kFlagNonFinite);
       }
     }
 #pragma unroll
@@ -868,7 +876,7 @@ __global__ void __launch_bounds__(256) dec_mlp_kernel(DecMlpArgs a) {
       const int cl = t * 256 + tid;
       if (cl < H) {
         const int c = (cl + rot) % H;
-        const long long v = to_fix(s_y[b * H + c]) + (p == 0 ? xq[b][t] : 0);
+        const long long v = to_fix(s_y[b * H + c], a.num_flag) + (p == 0 ? xq[b][t] : 0);
         atomicAdd(reinterpret_cast<unsigned long long *>(xo + (int64_t)b * H + c), (unsigned long long)v);
       }
     }
@@ -1572,7 +1580,7 @@ dec_mlp32_kernel(DecMlpArgs a) {
         } else {
           xin = (p == 0) ? xq[b][t] : 0;
         }
-        const long long q = to_fix(v * a.down_scale) + xin;
+        const long long q = to_fix(v * a.down_scale, a.num_flag) + xin;
         atomicAdd(reinterpret_cast<unsigned long long *>(xo + (int64_t)b * H + c), (unsigned long long)q);
       }
     }
@@ -1787,7 +1795,7 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = r0 + 16 * tt + 4 * g + r;
-        if (row < H) fix_add(a.x_out + (int64_t)b * H + row, pacc[tt][r] * a.o_scale);
+        if (row < H) fix_add(a.x_out + (int64_t)b * H + row, pacc[tt][r] * a.o_scale, a.num_flag);
       }
   }
 }

@@ -34,6 +34,17 @@ constexpr int GU_BLOCK = 16;
 
 typedef _Float16 f16;
 
+// Bits of a model's status word on the device.  Kernels set them with
+// atomicOr; qw_check_ids and qw_check_numerics read and clear them.
+constexpr int kFlagBadId = 1;       // a token id outside [0, V) was read as id 0
+constexpr int kFlagNonFinite = 2;   // a logit of a greedy row was inf or NaN
+constexpr int kFlagFixRange = 4;    // a fixed-point addend of the decode residual or sums exceeded 2^23
+
+// The calling thread's qw_last_error message: report() sets it and returns
+// `st`; clear_error() empties it (every entry point starts with it).
+int report(int st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
 // ------------------------------------------------------------ device helpers
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(f16 v) { return (float)v; }
@@ -133,6 +144,7 @@ struct DecGemvArgs {
   float *logits;
   float *arg_v;             // [M, ceil(N / 64)]
   int *arg_i;
+  int *num_flag;            // status word (kFlagFixRange, kFlagNonFinite)
 };
 
 // Decode-step attention, see k_decode.hip.
@@ -168,6 +180,7 @@ struct DecAttnOArgs {
   long long *x_out;                  // [batch, H] fixed-point residual (atomic adds)
   long long *clear;                  // side job: zero clear[0 .. clear_n)
   int64_t clear_n;
+  int *num_flag;                     // status word (kFlagFixRange)
 };
 bool dec_attn_o_supported(int head_dim, int hidden);
 
@@ -193,6 +206,7 @@ struct DecMlpArgs {
   int M, H, I;
   long long *clear;                  // side job: zero clear[0 .. clear_n) (may be NULL)
   int64_t clear_n;
+  int *num_flag;                     // status word (kFlagFixRange)
 };
 bool dec_mlp_supported(int hidden, int inter);
 
@@ -231,8 +245,9 @@ hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a);
 hipError_t launch_dec_merge(hipStream_t s, const float *pm, const float *pl, const float *po, int S, int B, int nq,
                             int hd, void *o);
 hipError_t launch_dec_attn_o(hipStream_t s, const DecAttnOArgs &a);
+// also sets kFlagNonFinite in *flag when a row holds an inf or NaN logit
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
-                         int32_t *next_ids, int *pos_dev, int pos_add);
+                         int32_t *next_ids, int *pos_dev, int pos_add, int *flag);
 hipError_t launch_set_int(hipStream_t s, int *p, int v);
 hipError_t launch_copy_i32(hipStream_t s, int32_t *dst, const int32_t *src, int n);
 // next_dst[0..b) = next_src; if logits_dst, logits_dst[0..n_logits) = logits_src

@@ -32,10 +32,11 @@ thread_local LaunchTiming launch_timing;
 }
 
 namespace {
-
 thread_local std::string g_err;
+}
 
-qw_status fail(qw_status st, const char *fmt, ...) {
+namespace qw {
+int report(int st, const char *fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -44,6 +45,12 @@ qw_status fail(qw_status st, const char *fmt, ...) {
   g_err = buf;
   return st;
 }
+void clear_error() { g_err.clear(); }
+}  // namespace qw
+
+namespace {
+
+#define fail(ST, ...) ((qw_status)::qw::report((ST), __VA_ARGS__))
 
 #define HIP_TRY(expr)                                                                         \
   do {                                                                                        \
@@ -95,7 +102,8 @@ struct qw_model {
   float2 *rope = nullptr;
   float *x = nullptr, *qkv = nullptr, *logits = nullptr;
   void *u = nullptr, *q = nullptr, *o = nullptr, *h = nullptr;
-  int *pos_dev = nullptr, *bad_ids = nullptr;
+  int *pos_dev = nullptr;
+  int *status = nullptr;     // status word: kFlagBadId | kFlagNonFinite | kFlagFixRange
   int32_t *ids_stage = nullptr, *next_stage = nullptr;   // [max_batch] rows the decode graph reads / writes
   // decode-step state (bf16-weight mode): fixed-point residual stream and
   // projection accumulators, LM-head argmax partials
@@ -108,7 +116,7 @@ struct qw_model {
   int *arg_i = nullptr;
   float *att_m = nullptr, *att_l = nullptr, *att_o = nullptr;   // split-KV partials
   void *v_t = nullptr;               // prefill: V of the prompt transposed (f16 mode)
-  float *splitk_ws = nullptr;        // prefill split-K slices (grown on demand)
+  float *splitk_ws = nullptr;        // prefill split-K slices, sized at creation
   size_t splitk_bytes = 0;
   int batch = 0, pos = 0;
   // decode graph, captured against the staging rows (so caller pointers may
@@ -208,19 +216,8 @@ hipError_t gemm(qw_model *m, hipStream_t s, Family fam, const void *A, int M, in
   if (m->f16 && gemm_mfma_supported(a)) {
     const int S = gemm_mfma_splits(M, N, K);
     if (S > 1) {
-      const size_t need = (size_t)S * M * N * 4;
-      if (need > m->splitk_bytes) {          // grow-only; the stream is synchronised before a free
-        if (m->splitk_ws) {
-          hipError_t e = hipStreamSynchronize(s);
-          if (e != hipSuccess) return e;
-          (void)hipFree(m->splitk_ws);
-        }
-        m->splitk_ws = nullptr;
-        m->splitk_bytes = 0;
-        hipError_t e = hipMalloc((void **)&m->splitk_ws, need);
-        if (e != hipSuccess) return e;
-        m->splitk_bytes = need;
-      }
+      // sized in qw_create for every shape a call can reach (splitk_bytes_for)
+      if ((size_t)S * M * N * 4 > m->splitk_bytes) return hipErrorInvalidValue;
       a.splits = S;
       a.ws = m->splitk_ws;
     }
@@ -313,7 +310,7 @@ hipError_t run_head(qw_model *m, hipStream_t s, const float *x_rows, int rows, i
            nullptr, c.vocab);
   if (e != hipSuccess) return e;
   return timed(m, s, F_ARGMAX,
-               [&] { return launch_argmax(s, arg_logits, arg_rows, c.vocab, arg_stride, next, pos_dev, pos_add); });
+               [&] { return launch_argmax(s, arg_logits, arg_rows, c.vocab, arg_stride, next, pos_dev, pos_add, m->status); });
 }
 
 // Generic decode step (fp32 mode): the prefill kernels on one row per sequence.
@@ -321,7 +318,7 @@ hipError_t decode_generic(qw_model *m, hipStream_t s, const int32_t *ids, int32_
   const qw_config &c = m->cfg;
   const int B = m->batch;
   hipError_t e = timed(m, s, F_EMBED, [&] {
-    return launch_embed(s, m->f16, ids, B, m->emb, m->emb_scale, c.hidden, c.vocab, m->x, m->bad_ids);
+    return launch_embed(s, m->f16, ids, B, m->emb, m->emb_scale, c.hidden, c.vocab, m->x, m->status);
   });
   if (e != hipSuccess) return e;
   e = run_layers(m, s, B, 1, 0, m->pos_dev);
@@ -329,8 +326,10 @@ hipError_t decode_generic(qw_model *m, hipStream_t s, const int32_t *ids, int32_
   return run_head(m, s, m->x, B, c.hidden, m->logits, m->logits, B, c.vocab, next, m->pos_dev, 1);
 }
 
-DecGemvArgs dec_args(const void *W, int M, int N, int K, float scale, int target = kGemvTargetGroups) {
+DecGemvArgs dec_args(int *status, const void *W, int M, int N, int K, float scale,
+                     int target = kGemvTargetGroups) {
   DecGemvArgs g{};
+  g.num_flag = status;
   g.W = W;
   g.M = M;
   g.N = N;
@@ -368,7 +367,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   hipError_t e = timed(m, s, F_EMBED, [&] {
     // the embedding goes to replica 0; the other replicas and the q/k/v
     // accumulator are cleared (attention clears the gate/up accumulator)
-    return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, m->x_fix, m->bad_ids, m->qkv_fix, n_qkv,
+    return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, m->x_fix, m->status, m->qkv_fix, n_qkv,
                             m->x_fix + xs, (kXReps - 1) * xs);
   });
   if (e != hipSuccess) return e;
@@ -396,7 +395,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     char *vc = (char *)m->v_cache + (int64_t)l * m->cache_layer_elems * m->esz;
     if ((e = norm(Lw.in_norm)) != hipSuccess) return e;
     const int gemv_target = fused_norm ? kGemvTargetGroups : kGemvTargetGroupsBatched;
-    DecGemvArgs g = dec_args(Lw.w_qkv, B, m->nqkv, H, Lw.s_qkv, gemv_target);
+    DecGemvArgs g = dec_args(m->status, Lw.w_qkv, B, m->nqkv, H, Lw.s_qkv, gemv_target);
     normed(g, Lw.in_norm);
     g.out_fix = m->qkv_fix;
     g.ldo = m->nqkv;
@@ -422,6 +421,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       ao.x_out = xr;
       ao.clear = fused_mlp ? xo : m->gu_fix;
       ao.clear_n = fused_mlp ? kXReps * xs : n_gu;
+      ao.num_flag = m->status;
       e = timed(m, s, F_ATTN_O, [&] { return launch_dec_attn_o(s, ao); });
       if (e != hipSuccess) return e;
     } else {
@@ -448,7 +448,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       da.clear_n = fused_mlp ? kXReps * xs : n_gu;
       e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
       if (e != hipSuccess) return e;
-      g = dec_args(Lw.w_o, B, H, m->qd, Lw.s_o, gemv_target);
+      g = dec_args(m->status, Lw.w_o, B, H, m->qd, Lw.s_o, gemv_target);
       if (S > 1 && !fused_norm) {
         // many rows: merge once, then an f16 operand
         e = timed(m, s, F_ATTN_MERGE, [&] {
@@ -493,6 +493,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       ma.I = I;
       ma.clear = attn_o ? m->qkv_fix : nullptr;
       ma.clear_n = n_qkv;
+      ma.num_flag = m->status;
       e = timed(m, s, F_MLP, [&] { return launch_dec_mlp(s, ma); });
       if (e != hipSuccess) return e;
       std::swap(xr, xo);
@@ -501,7 +502,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     if ((e = norm(Lw.post_norm)) != hipSuccess) return e;
     // every workgroup of a norm-fused projection re-reads the residual rows,
     // so fewer, larger K slices pay off when there are many row blocks
-    g = dec_args(Lw.w_gu, B, 2 * I, H, Lw.s_gu, fused_norm ? kGemvTargetGroups / 2 : kGemvTargetGroups);
+    g = dec_args(m->status, Lw.w_gu, B, 2 * I, H, Lw.s_gu, fused_norm ? kGemvTargetGroups / 2 : kGemvTargetGroups);
     normed(g, Lw.post_norm);
     g.role_gate_up = 1;
     g.out_fix = m->gu_fix;
@@ -519,7 +520,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     g.ldo = 2 * I;
     e = timed(m, s, F_GEMM_GATE_UP, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
-    g = dec_args(Lw.w_down, B, H, I, Lw.s_down, gemv_target);
+    g = dec_args(m->status, Lw.w_down, B, H, I, Lw.s_down, gemv_target);
     if (fused_norm) {
       g.act_mode = 2;
       g.act_fix = m->gu_fix;
@@ -537,7 +538,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   }
   // the LM head has thousands of workgroups: the final row is normalised once
   // by a kernel of its own rather than in every workgroup's prologue
-  DecGemvArgs g = dec_args(m->head, B, V, H, m->head_scale);
+  DecGemvArgs g = dec_args(m->status, m->head, B, V, H, m->head_scale);
   if (kHeadNormKernel || !fused_norm) {
     e = timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, m->final_norm, c.rms_eps, m->u); });
     if (e != hipSuccess) return e;
@@ -615,10 +616,35 @@ float f16_scale_for(float absmax) {
   return ldexpf(1.f, k);
 }
 
-struct Src {
-  const void *p;
-  int64_t n;
-};
+// Largest split-K workspace a call can need: the prefill projections (q/k/v,
+// o, gate/up, down) and the LM head over up to max_batch * max_seq rows (all
+// of them with logits_all), and the generic decode step over max_batch rows.
+// Every GEMM has enough tiles for one K slice once M passes 256 * 512 rows,
+// so the rows beyond 2^18 need no look.
+size_t splitk_bytes_for(const qw_model *m) {
+  if (!m->f16) return 0;
+  const qw_config &c = m->cfg;
+  struct Shape { int N, K; Epi epi; };
+  const Shape shapes[] = {{m->nqkv, c.hidden, Epi::StoreF32}, {c.hidden, m->qd, Epi::ResidAdd},
+                          {2 * c.intermediate, c.hidden, Epi::SwiGLU}, {c.hidden, c.intermediate, Epi::ResidAdd},
+                          {c.vocab, c.hidden, Epi::StoreF32}};
+  const int64_t mmax = m->rows_cap < (1 << 18) ? m->rows_cap : (1 << 18);
+  size_t most = 0;
+  for (const Shape &sh : shapes)
+    for (int64_t M = 1; M <= mmax; ++M) {
+      GemmArgs a;
+      a.M = (int)M;
+      a.N = sh.N;
+      a.K = sh.K;
+      a.lda = sh.K;
+      a.epi = sh.epi;
+      if (!gemm_mfma_supported(a)) continue;
+      const int S = gemm_mfma_splits(a.M, a.N, a.K);
+      const size_t need = S > 1 ? (size_t)S * M * sh.N * 4 : 0;
+      if (need > most) most = need;
+    }
+  return most;
+}
 
 }  // namespace
 
@@ -694,6 +720,9 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
     for (int g = 0; g < n_groups; ++g) {
       float f;
       memcpy(&f, &bits[g], 4);
+      if (!isfinite(f))
+        return cleanup_fail(fail(QW_ERR_UNSUPPORTED, "qw_create: a weight of %s is inf or NaN",
+                                 g < 4 * c.n_layers ? "a decoder layer" : "the embedding or LM head"));
       scale[g] = f16_scale_for(f);
     }
   }
@@ -773,10 +802,12 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   CREATE_TRY(m->alloc(&m->o, R * m->qd * es));
   CREATE_TRY(m->alloc(&m->h, R * I * es));
   CREATE_TRY(m->alloc((void **)&m->logits, (size_t)c.max_batch * V * 4));
+  m->splitk_bytes = splitk_bytes_for(m);
+  if (m->splitk_bytes) CREATE_TRY(m->alloc((void **)&m->splitk_ws, m->splitk_bytes));
   if (m->f16)
     CREATE_TRY(m->alloc(&m->v_t, (size_t)c.max_batch * c.n_kv_heads * c.head_dim * ((c.max_seq + 63) / 64 * 64) * 2));
   CREATE_TRY(m->alloc((void **)&m->pos_dev, 256));
-  CREATE_TRY(m->alloc((void **)&m->bad_ids, 256));
+  CREATE_TRY(m->alloc((void **)&m->status, 256));
   CREATE_TRY(m->alloc((void **)&m->ids_stage, (size_t)c.max_batch * 4));
   if (m->fast_decode) {
     const size_t nb = (size_t)c.max_batch;
@@ -793,7 +824,7 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   }
   CREATE_TRY(m->alloc((void **)&m->next_stage, (size_t)c.max_batch * 4));
   CREATE_TRY(hipMemsetAsync(m->pos_dev, 0, 256, s));
-  CREATE_TRY(hipMemsetAsync(m->bad_ids, 0, 256, s));
+  CREATE_TRY(hipMemsetAsync(m->status, 0, 256, s));
   CREATE_TRY(hipStreamSynchronize(s));
 #undef CREATE_TRY
   *out = m;
@@ -816,7 +847,7 @@ qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t pro
   const int T = batch * prompt_len, H = c.hidden, V = c.vocab;
   m->batch = 0;          // invalid until the enqueue succeeds
   HIP_TRY(timed(m, s, F_EMBED, [&] {
-    return launch_embed(s, m->f16, ids, T, m->emb, m->emb_scale, H, V, m->x, m->bad_ids);
+    return launch_embed(s, m->f16, ids, T, m->emb, m->emb_scale, H, V, m->x, m->status);
   }));
   HIP_TRY(run_layers(m, s, T, prompt_len, 0, nullptr));
   if (logits_all) {
@@ -898,7 +929,6 @@ static void release_model(qw_model *m) {
     (void)hipEventDestroy(e.second);
   }
   for (void *p : m->allocs) (void)hipFree(p);
-  if (m->splitk_ws) (void)hipFree(m->splitk_ws);
   if (m->cap) (void)hipStreamDestroy(m->cap);
   delete m;
 }
@@ -913,16 +943,39 @@ qw_status qw_get_state(const qw_model *m, int32_t *batch, int32_t *pos) {
   return QW_OK;
 }
 
+// Reads the status word after the stream is idle, clears the bits in `mask`
+// and returns those of them that were set.
+static qw_status read_status(qw_model *m, int mask, int *bits) {
+  HIP_TRY(hipStreamSynchronize(m->stream));
+  int word = 0;
+  HIP_TRY(hipMemcpy(&word, m->status, sizeof(int), hipMemcpyDeviceToHost));
+  *bits = word & mask;
+  if (*bits) {
+    word &= ~mask;
+    HIP_TRY(hipMemcpy(m->status, &word, sizeof(int), hipMemcpyHostToDevice));
+  }
+  return QW_OK;
+}
+
 qw_status qw_check_ids(qw_model *m) {
   g_err.clear();
   if (!m) return fail(QW_ERR_INVALID_ARG, "qw_check_ids: model is NULL");
-  HIP_TRY(hipStreamSynchronize(m->stream));
-  int flag = 0;
-  HIP_TRY(hipMemcpy(&flag, m->bad_ids, sizeof(int), hipMemcpyDeviceToHost));
-  if (flag) {
-    HIP_TRY(hipMemset(m->bad_ids, 0, sizeof(int)));
-    return fail(QW_ERR_INVALID_ARG, "a token id outside [0, %d) was passed; it was read as id 0", m->cfg.vocab);
-  }
+  int bits = 0;
+  qw_status st = read_status(m, kFlagBadId, &bits);
+  if (st != QW_OK) return st;
+  if (bits) return fail(QW_ERR_INVALID_ARG, "a token id outside [0, %d) was passed; it was read as id 0", m->cfg.vocab);
+  return QW_OK;
+}
+
+qw_status qw_check_numerics(qw_model *m) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_check_numerics: model is NULL");
+  int bits = 0;
+  qw_status st = read_status(m, kFlagNonFinite | kFlagFixRange, &bits);
+  if (st != QW_OK) return st;
+  if (bits)
+    return fail(QW_ERR_NUMERICS, "since the last check:%s%s", (bits & kFlagNonFinite) ? " a logit was inf or NaN;" : "",
+                (bits & kFlagFixRange) ? " a decode residual or projection addend exceeded 2^23 in magnitude;" : "");
   return QW_OK;
 }
 

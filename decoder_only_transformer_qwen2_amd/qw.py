@@ -16,14 +16,16 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqw.so")
 
 QW_OK, QW_ERR_INVALID_ARG, QW_ERR_OUT_OF_MEMORY, QW_ERR_HIP = 0, -1, -2, -3
-QW_ERR_CACHE_FULL, QW_ERR_BAD_STATE, QW_ERR_UNSUPPORTED = -4, -5, -6
+QW_ERR_CACHE_FULL, QW_ERR_BAD_STATE, QW_ERR_UNSUPPORTED, QW_ERR_NUMERICS = -4, -5, -6, -7
 QW_F32, QW_BF16 = 0, 1
 
 STATUS_NAMES = {0: "QW_OK", -1: "QW_ERR_INVALID_ARG", -2: "QW_ERR_OUT_OF_MEMORY", -3: "QW_ERR_HIP",
-                -4: "QW_ERR_CACHE_FULL", -5: "QW_ERR_BAD_STATE", -6: "QW_ERR_UNSUPPORTED"}
+                -4: "QW_ERR_CACHE_FULL", -5: "QW_ERR_BAD_STATE", -6: "QW_ERR_UNSUPPORTED",
+                -7: "QW_ERR_NUMERICS"}
 
 EXPORTED = ("qw_create", "qw_prefill", "qw_decode_step", "qw_destroy", "qw_last_error", "qw_get_state",
-            "qw_check_ids", "qw_set_graph", "qw_timing_enable", "qw_timing_read", "qw_kernel_names")
+            "qw_check_ids", "qw_check_numerics", "qw_set_graph", "qw_timing_enable", "qw_timing_read", "qw_kernel_names", "qw_peak_copy",
+            "qw_peak_mfma")
 
 
 class QwError(RuntimeError):
@@ -74,10 +76,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qw_last_error": (ctypes.c_char_p, []),
         "qw_get_state": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "qw_check_ids": (I32, [P]),
+        "qw_check_numerics": (I32, [P]),
         "qw_set_graph": (I32, [P, I32]),
         "qw_timing_enable": (I32, [P, ctypes.c_char_p]),
         "qw_timing_read": (I32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]),
         "qw_kernel_names": (ctypes.c_char_p, []),
+        "qw_peak_copy": (I32, [P, P, I64, I32, P, ctypes.POINTER(ctypes.c_double)]),
+        "qw_peak_mfma": (I32, [I32, P, ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -130,6 +135,10 @@ def qw_check_ids(model: int) -> None:
     _check(load_library().qw_check_ids(model))
 
 
+def qw_check_numerics(model: int) -> None:
+    _check(load_library().qw_check_numerics(model))
+
+
 def qw_set_graph(model: int, enable: bool) -> None:
     _check(load_library().qw_set_graph(model, int(bool(enable))))
 
@@ -142,6 +151,20 @@ def qw_timing_read(model: int, reset: bool = True):
     ms, n = ctypes.c_double(), ctypes.c_int64()
     _check(load_library().qw_timing_read(model, ctypes.byref(ms), ctypes.byref(n), int(reset)))
     return ms.value, n.value
+
+
+def qw_peak_copy(dst: int, src: int, nbytes: int, iters: int, stream: int = 0) -> float:
+    """HBM copy rate in GB/s (bytes read + written per second / 1e9)."""
+    r = ctypes.c_double()
+    _check(load_library().qw_peak_copy(dst, src, nbytes, iters, ctypes.c_void_p(stream), ctypes.byref(r)))
+    return r.value
+
+
+def qw_peak_mfma(iters: int, stream: int = 0) -> float:
+    """Dense fp16 MFMA rate in TFLOP/s of an MFMA-only loop."""
+    r = ctypes.c_double()
+    _check(load_library().qw_peak_mfma(iters, ctypes.c_void_p(stream), ctypes.byref(r)))
+    return r.value
 
 
 # ---------------------------------------------------------------- convenience wrapper
@@ -209,6 +232,9 @@ class Model:
 
     def check_ids(self):
         qw_check_ids(self.handle)
+
+    def check_numerics(self):
+        qw_check_numerics(self.handle)
 
     def set_graph(self, enable: bool):
         qw_set_graph(self.handle, enable)

@@ -22,8 +22,11 @@
  *     on the current device) unless a comment says "host".
  *   - All work is enqueued on the hipStream_t given to qw_create (0 = the
  *     legacy default stream).  Outputs are valid once the caller synchronises
- *     that stream.  No call blocks on the GPU except qw_create (which waits
- *     for its own set-up work) and qw_destroy.
+ *     that stream.  qw_prefill and qw_decode_step do not wait for the GPU
+ *     and make no device allocation of their own (qw_decode_step captures
+ *     and instantiates a HIP graph on its first call for a batch size and
+ *     context range); qw_create waits for its own set-up work, and
+ *     qw_destroy and the check and timing helpers synchronise the stream.
  *   - Every call returns a qw_status.  On anything but QW_OK, qw_last_error()
  *     returns a message for the calling thread; argument and state errors
  *     are detected on the host before anything is enqueued, so the model is
@@ -46,16 +49,25 @@ typedef enum qw_status {
   QW_ERR_HIP = -3,            /* a HIP runtime call failed (message has it)    */
   QW_ERR_CACHE_FULL = -4,     /* the step would write past max_seq             */
   QW_ERR_BAD_STATE = -5,      /* e.g. decode before any prefill                */
-  QW_ERR_UNSUPPORTED = -6     /* valid model, but a shape no kernel covers     */
+  QW_ERR_UNSUPPORTED = -6,    /* valid model, but a shape no kernel covers     */
+  QW_ERR_NUMERICS = -7        /* qw_check_numerics: a value left its range     */
 } qw_status;
 
 /* Storage type of every weight tensor handed to qw_create.
  *   QW_F32 : float32 weights; the whole forward runs in fp32 arithmetic.
  *   QW_BF16: bf16 weights.  GEMM operands (weights and activations) are held
- *            in fp16 with fp32 accumulation; weights are converted exactly
- *            (per-tensor power-of-two scale, so every bf16 value maps to an
- *            fp16 value without rounding); the residual stream, softmax,
- *            norms' statistics and logits are fp32. */
+ *            in fp16 with fp32 accumulation; the residual stream, softmax,
+ *            norms' statistics and logits are fp32.  Each weight group
+ *            (a layer's q/k/v, o, gate/up, down; the embedding; the LM head)
+ *            is multiplied by a power of two 2^k that puts its largest
+ *            magnitude A in [2^14, 2^15) and rounded to fp16, which the
+ *            kernels undo exactly.  A value v converts without rounding when
+ *            |v| >= A * 2^-32 (bf16's 8 significant bits still fit fp16's
+ *            normal or subnormal spacing); a smaller v is rounded with an
+ *            absolute error below A * 2^-39.  Activations held in fp16 must
+ *            stay below 65504 in magnitude: qw_check_numerics reports a
+ *            forward that left that range (it surfaces as an inf or NaN
+ *            logit) or the decode residual's fixed-point range. */
 typedef enum qw_dtype { QW_F32 = 0, QW_BF16 = 1 } qw_dtype;
 
 /* Model and capacity.  Field meanings follow the Qwen2 config names the
@@ -105,12 +117,17 @@ typedef struct qw_model qw_model;
  * the caller's weight buffers may be freed after this returns.  Allocates the
  * KV cache (2 * n_layers * max_batch * nkv * max_seq * hd elements of the
  * compute type), a RoPE cos/sin table for max_seq positions, and workspace for
- * max_batch * max_seq prefill rows.  `hip_stream` (a hipStream_t) is the
- * stream all later work is enqueued on.  Waits for its set-up work.
+ * max_batch * max_seq prefill rows (including the split-K slices of every
+ * GEMM shape a later call can reach, so prefill and decode never allocate).
+ * `hip_stream` (a hipStream_t) is the stream all later work is enqueued on.
+ * Waits for its set-up work.
  * Errors: INVALID_ARG (NULL pointers, non-positive sizes, nq % nkv != 0, odd
  * head_dim, qkv_bias != 1, lm_head NULL while untied), UNSUPPORTED (head_dim
- * not in {32, 64, 128}, hidden or intermediate not a multiple of 64),
- * OUT_OF_MEMORY, HIP.  On error *out is set to NULL. */
+ * not in {32, 64, 128}, hidden or intermediate not a multiple of 64, an inf
+ * or NaN projection or embedding weight in bf16 mode), OUT_OF_MEMORY, HIP.
+ * On error *out is set to NULL.
+ * Source: "augur" (preallocated KV cache); "LLM Speedrun: Architecture",
+ * harness listing (weight names and [out, in] layouts). */
 qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_stream,
                     qw_model **out);
 
@@ -127,7 +144,11 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
  * Token ids outside [0, V) are read as id 0 (never out of bounds) and make
  * qw_check_ids report an error.
  * Errors: INVALID_ARG (NULL ids/next_ids, batch < 1 or > max_batch,
- * prompt_len < 1), CACHE_FULL (prompt_len > max_seq), HIP. */
+ * prompt_len < 1), CACHE_FULL (prompt_len > max_seq), HIP.
+ * Source: "Building a Qwen2.5-1.5B Inference Engine From Scratch", section 1
+ * (prefill runs the whole prompt at once and fills the KV cache); "augur"
+ * (causal masking, greedy generation, lowest index among equal maxima read
+ * from the harness listing's argmax). */
 qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t prompt_len,
                      float *logits, int32_t logits_all, int32_t *next_ids);
 
@@ -137,11 +158,14 @@ qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t pro
  * [batch] and, if non-NULL, fp32 logits[batch][V].  The position advances on
  * the device, so steps may be enqueued back to back without host syncs.
  * Errors: INVALID_ARG (NULL ids/next_ids), BAD_STATE (no prefill yet),
- * CACHE_FULL (the cache already holds max_seq positions), HIP. */
+ * CACHE_FULL (the cache already holds max_seq positions), HIP.
+ * Source: "Building a Qwen2.5-1.5B Inference Engine From Scratch", section 1
+ * (decode feeds one new token per step against the cache); "LLM Speedrun:
+ * Architecture", "Decoding" and the harness listing's generation loop. */
 qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t *next_ids);
 
 /* Free everything the model owns.  Synchronises its stream first.  NULL is a
- * no-op. */
+ * no-op.  Source: "augur" (the preallocated cache lives as long as the model). */
 qw_status qw_destroy(qw_model *m);
 
 /* Message of the calling thread's last error ("" if none).  The pointer stays
@@ -159,6 +183,13 @@ qw_status qw_get_state(const qw_model *m, int32_t *batch, int32_t *pos);
  * (and the flag is cleared), QW_OK otherwise. */
 qw_status qw_check_ids(qw_model *m);
 
+/* Synchronise the stream and report whether, since the last check, a logit
+ * of a greedy row was inf or NaN (an fp16 activation overflowed, or a weight
+ * was non-finite) or an addend of the decode step's fixed-point residual or
+ * projection sums exceeded 2^23 in magnitude (it was clamped):
+ * QW_ERR_NUMERICS if so (those flags are cleared), QW_OK otherwise. */
+qw_status qw_check_numerics(qw_model *m);
+
 /* Decode-step execution: 1 (default) replays a captured HIP graph of the whole
  * step; 0 launches its kernels one by one.  Both run the same kernels on the
  * same data and give identical results. */
@@ -174,6 +205,19 @@ qw_status qw_timing_read(qw_model *m, double *total_ms, int64_t *launches, int32
 
 /* Comma-separated names of the kernel families the library launches. */
 const char *qw_kernel_names(void);
+
+/* Measured peaks, the denominators a run can reach beside the published
+ * ones (not on the forward pass).  Both enqueue on `hip_stream`, wait for
+ * their own work, and report through qw_last_error.
+ * qw_peak_copy: copies `bytes` (a positive multiple of 16) from src to dst
+ *   (device pointers, not overlapping) `iters` times with a 16-byte-per-lane
+ *   grid-stride kernel; *gbs = (bytes read + bytes written) / seconds / 1e9.
+ * qw_peak_mfma: 8192 waves each issue `iters` rounds of eight independent
+ *   16x16x32 fp16 matrix products (v_mfma_f32_16x16x32_f16) on register
+ *   operands; *tflops = dense fp16 FLOP / seconds / 1e12.
+ * Errors: INVALID_ARG (NULL output or pointers, bad sizes), HIP. */
+qw_status qw_peak_copy(void *dst, const void *src, int64_t bytes, int32_t iters, void *hip_stream, double *gbs);
+qw_status qw_peak_mfma(int32_t iters, void *hip_stream, double *tflops);
 
 #ifdef __cplusplus
 }

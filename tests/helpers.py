@@ -48,10 +48,12 @@ def gpu_generate(model, ids_np, steps, want_logits=True, graph=True):
     return t, lg
 
 
-def compare_row(oracle_model, prompt, gpu_tokens, gpu_logits, dtype, label=""):
+def compare_row(oracle_model, prompt, gpu_tokens, gpu_logits, dtype, label="", ref=None):
     """Teacher-forced check of one sequence: the oracle is fed the GPU's own
-    token stream, so every step is compared on the same prefix."""
-    ref = oracle_model.teacher_forced(prompt, gpu_tokens[:-1])
+    token stream, so every step is compared on the same prefix.  `ref` may
+    hold the oracle's teacher-forced logits when the caller has them."""
+    if ref is None:
+        ref = oracle_model.teacher_forced(prompt, gpu_tokens[:-1])
     err = np.abs(gpu_logits.astype(np.float64) - ref)
     per_step = err.max(axis=1)
     tol = LOGIT_TOL[dtype]

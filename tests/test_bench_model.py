@@ -58,18 +58,31 @@ def test_mlp_family_bytes_is_three_weight_matrices(bench):
     assert bench.decode_family_bytes(w, "mlp", 0.0) == 3 * m.intermediate * m.hidden * 2 + 2 * m.hidden * 8
 
 
-def test_traffic_record_is_gated(bench, tmp_path, monkeypatch):
+def test_traffic_record_is_gated(bench, tmp_path):
     rec = {"family": "mlp", "workload": "0.5b", "kernel_source": "bench.py",
            "fetch_bytes_per_launch": 100, "write_bytes_per_launch": 20}
     import hashlib
     sha = hashlib.sha256(open(os.path.join(ROOT, "bench.py"), "rb").read()).hexdigest()
-    f = tmp_path / "t.json"
+    f = tmp_path / "a_hbm_traffic.json"
     f.write_text(json.dumps(dict(rec, kernel_source_sha256=sha)))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.measured_traffic("0.5b", "mlp") == 120
-    assert bench.measured_traffic("1.5b", "mlp") is None          # other workload
-    assert bench.measured_traffic("0.5b", "attention") is None    # other kernel family
+    pat = str(tmp_path / "*_hbm_traffic.json")
+    assert bench.measured_traffic("0.5b", "mlp", pat) == 120
+    assert bench.measured_traffic("1.5b", "mlp", pat) is None          # other workload
+    assert bench.measured_traffic("0.5b", "attention", pat) is None    # other kernel family
+    g = tmp_path / "b_hbm_traffic.json"
+    g.write_text(json.dumps(dict(rec, family="attention", fetch_bytes_per_launch=7, kernel_source_sha256=sha)))
+    assert bench.measured_traffic("0.5b", "attention", pat) == 27      # a second record
     f.write_text(json.dumps(dict(rec, kernel_source_sha256="0" * 64)))
-    assert bench.measured_traffic("0.5b", "mlp") is None          # source changed since the counters
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
-    assert bench.measured_traffic("0.5b", "mlp") is None
+    assert bench.measured_traffic("0.5b", "mlp", pat) is None          # source changed since the counters
+    assert bench.measured_traffic("0.5b", "mlp", str(tmp_path / "none_*.json")) is None
+
+
+def test_default_workload_is_the_largest_single_gpu_config(bench):
+    w = S.WORKLOADS[bench.DEFAULT_WORKLOAD]
+    assert (w.batch, w.prompt_len, w.decode_steps) == (32, 8192, 128)
+    assert w.model.hidden == 1536 and w.model.n_layers == 28
+
+
+def test_cpu_info(bench):
+    model, n = bench.cpu_info()
+    assert isinstance(model, str) and n >= 1

@@ -1,0 +1,144 @@
+"""Edge cases of the HIP library through its C ABI: the greedy tie rule, the
+numerics status word, and the generic decode path across prefills of
+different lengths."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+from tests.helpers import compare_row, gpu_generate
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def Q():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decoder_only_transformer_qwen2_amd as Q
+    Q.load_library()
+    return Q
+
+
+def make(Q, shape, W, max_batch, max_seq):
+    return Q.Model(shape, Q.device_tensors(shape, W), max_batch, max_seq)
+
+
+TIE_SHAPE = S.ModelShape("tie", 2, 256, 4, 2, 64, 512, 1500)
+
+
+def test_argmax_ties_take_the_lowest_index(Q):
+    """Greedy choice among equal maxima is the lowest index ("LLM Speedrun:
+    Architecture", harness listing: argmax; "augur": greedy generation).
+
+    A first run picks a token i that the model emits.  Copying i's embedding
+    row into row j (j = i +- 256, so both rows sit at the same offset of
+    their 64-, 128- and 256-row blocks and the LM head sums them in the same
+    order) makes logits i and j bit-identical at every step, and feeding j is
+    feeding i.  Wherever i held the maximum, the token must now be min(i, j):
+    in the prefill's argmax and across the decode LM head's blocks."""
+    shape = TIE_SHAPE
+    V = shape.vocab
+    B, P, D = 3, 20, 6
+    W0 = S.make_weights(shape, 11)
+    ids = np.random.default_rng(12).integers(0, V, (B, P)).astype(np.int32)
+    m = make(Q, shape, W0, B, 64)
+    toks, _ = gpu_generate(m, ids, D, want_logits=False)
+    m.close()
+    used = set(ids.ravel().tolist()) | set(toks.ravel().tolist())
+    # one partner below i and one above it, each a row no input uses
+    found = {"below": None, "above": None}
+    for i in sorted(set(toks.ravel().tolist())):
+        for j, side in ((i - 256, "below"), (i + 256, "above"), (i - 512, "below"), (i + 512, "above")):
+            if found[side] is None and 0 <= j < V and j not in used:
+                found[side] = (i, j)
+    pairs = [p for p in found.values() if p]
+    assert pairs, "no token with a free partner row"
+    om_checked = False
+    for i, j in pairs:
+        W = dict(W0)
+        E = W["model.embed_tokens.weight"].copy()
+        E[j] = E[i]
+        W["model.embed_tokens.weight"] = E
+        m = make(Q, shape, W, B, 64)
+        t2, l2 = gpu_generate(m, ids, D)
+        m.close()
+        assert np.array_equal(l2[..., i], l2[..., j]), f"logits {i} and {j} differ"
+        at_max = l2[..., i] == l2.max(axis=2)
+        say(f"tie {i} / {j}: {int(at_max.sum())} steps with the pair at the maximum")
+        assert at_max.any()
+        assert np.all(t2[at_max] == min(i, j)), f"ties of {i} and {j} gave {t2[at_max]}"
+        if not om_checked:
+            om = O.OracleModel(shape, W)
+            b = int(np.nonzero(at_max.any(axis=1))[0][0])
+            compare_row(om, ids[b], t2[b], l2[b], "bf16", f"tie row {b}")
+            om_checked = True
+
+
+def test_numerics_status_word(Q):
+    """qw_check_numerics: clean on a normal model; an fp16 activation pushed
+    past 65504 (layer 0's up projection scaled by 1e7) reaches the logits as
+    inf or NaN; an embedding entry of 1e7 fed to a decode step exceeds the
+    fixed-point residual's addend bound.  Each is reported once."""
+    import torch
+    shape = S.ModelShape("num", 2, 256, 4, 2, 64, 512, 999)
+    W = S.make_weights(shape, 13)
+    ids = np.random.default_rng(14).integers(0, shape.vocab, (1, 12)).astype(np.int32)
+    m = make(Q, shape, W, 1, 32)
+    gpu_generate(m, ids, 3, want_logits=False)
+    m.check_numerics()
+    m.check_ids()
+    m.close()
+
+    W2 = dict(W)
+    up = O.decode_storage(W["model.layers.0.mlp.up_proj.weight"]).astype(np.float32) * 1e7
+    W2["model.layers.0.mlp.up_proj.weight"] = S.f32_to_bf16_bits(up)
+    m = make(Q, shape, W2, 1, 32)
+    gpu_generate(m, ids, 2, want_logits=False)
+    with pytest.raises(Q.QwError) as e:
+        m.check_numerics()
+    assert e.value.status == -7                          # QW_ERR_NUMERICS
+    say(f"overflowed model: {e.value}")
+    m.check_numerics()                                     # cleared by the first check
+    m.close()
+
+    W3 = dict(W)
+    E = O.decode_storage(W["model.embed_tokens.weight"]).astype(np.float32)
+    E[5, 0] = 1e7
+    W3["model.embed_tokens.weight"] = S.f32_to_bf16_bits(E)
+    m = make(Q, shape, W3, 1, 32)
+    t = torch.from_numpy(ids).cuda()
+    nxt = m.prefill(t)
+    m.check_numerics()                                     # prompt without token 5: nothing to report
+    m.decode_step(torch.tensor([5], dtype=torch.int32, device="cuda"), next_ids=nxt)
+    with pytest.raises(Q.QwError) as e:
+        m.check_numerics()
+    assert e.value.status == -7 and "2^23" in str(e.value)
+    m.close()
+
+
+def test_generic_decode_across_prefill_lengths(Q):
+    """More than 32 sequences of capacity selects the generic decode step
+    (the prefill kernels on one row per sequence, captured as a graph).  A
+    short prefill, decode steps, a longer prefill (other split-K shapes in
+    its projections), more decode steps: each run matches the oracle."""
+    shape = S.ModelShape("gen", 2, 256, 4, 2, 64, 512, 999)
+    W = S.make_weights(shape, 15)
+    om = O.OracleModel(shape, W)
+    m = make(Q, shape, W, 33, 96)
+    rng = np.random.default_rng(16)
+    for P in (20, 70, 9):
+        ids = rng.integers(0, shape.vocab, (2, P)).astype(np.int32)
+        toks, logits = gpu_generate(m, ids, 4)
+        for b in range(2):
+            err, _ = compare_row(om, ids[b], toks[b], logits[b], "bf16", f"P={P} row {b}")
+            say(f"generic decode P={P} row {b}: max err {err:.2e}")
+    m.close()
