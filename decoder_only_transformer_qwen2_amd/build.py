@@ -35,6 +35,9 @@ CFLAGS = [
 # and back in once per key block.
 EXTRA = {
     "k_attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # the MFMA-only peak loop: with accumulation registers the compiler
+    # rotated every accumulator through VGPRs once per iteration
+    "k_peak.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -162,6 +162,21 @@ constexpr bool kHeadNormKernel = true;
 // kernel wins at 0.5B / 256 keys, the split pair at 1.5B / 513-768 keys).
 constexpr int kAttnOMaxCtx = 256;
 
+// Per-step buffers of the fast decode step.  Everything in them is written
+// and read within one step; the accumulators are cleared by the step's own
+// kernels before they are added into, so their contents between steps do
+// not matter.
+struct DecodeScratch {
+  long long *x_fix = nullptr, *x_fix2 = nullptr;   // [kXReps][B, H] each (two residual buffers)
+  long long *qkv_fix = nullptr;                    // [B, nqkv]
+  long long *gu_fix = nullptr;                     // [B, 2I]; only the one/two-row path without the fused MLP
+  float *arg_v = nullptr;                          // [B, ceil(V / 64)]
+  int *arg_i = nullptr;
+  float *att_m = nullptr, *att_l = nullptr, *att_o = nullptr;   // [B][nq][16] (+ [hd])
+  void *u = nullptr, *o = nullptr, *h = nullptr;   // f16 [B, H], [B, qd], [B, I]
+  float *logits = nullptr;                         // [B, V], or NULL (argmax partials only)
+};
+
 // Which decode step the next decode call runs: 1 = attention merged with the
 // o projection (short context), 2 + S = split-KV attention over S splits,
 // then the o projection (S follows the context length, so it grows as the
@@ -348,14 +363,29 @@ DecGemvArgs dec_args(int *status, const void *W, int M, int N, int K, float scal
 // from one buffer and accumulates into the other; for larger batches a norm
 // kernel, the gate/up projection and the down projection (SwiGLU on its
 // operand) run separately on one residual buffer.
-hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next) {
+// Which per-step buffers a fast decode step of B rows uses.
+struct DecodeNeeds {
+  bool fused_norm, fused_mlp, gu_fix;
+};
+DecodeNeeds decode_needs(const qw_model *m, int B) {
+  DecodeNeeds n;
+  n.fused_norm = B <= kFusedNormRows && m->cfg.hidden <= 4096;
+  n.fused_mlp = n.fused_norm && m->L[0].w_down_t != nullptr;
+  n.gu_fix = n.fused_norm && !n.fused_mlp;
+  return n;
+}
+
+hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next, const DecodeScratch &d) {
   const qw_config &c = m->cfg;
   const int B = m->batch, H = c.hidden, I = c.intermediate, V = c.vocab;
-  const bool fused_norm = B <= kFusedNormRows && H <= 4096;
+  const DecodeNeeds need = decode_needs(m, B);
+  const bool fused_norm = need.fused_norm;
   // one-kernel MLP: reads the residual from xr and accumulates xr + MLP into
   // xo, then the two swap
-  const bool fused_mlp = fused_norm && m->L[0].w_down_t != nullptr;
-  long long *xr = m->x_fix, *xo = m->x_fix2;
+  const bool fused_mlp = need.fused_mlp;
+  // the gate/up sums of the unfused one/two-row MLP (cleared by attention)
+  long long *gu_clear = need.gu_fix ? d.gu_fix : nullptr;
+  long long *xr = d.x_fix, *xo = d.x_fix2;
   // attention merged with the o projection: the q/k/v sums are still being
   // read in that kernel, so the next projection clears them instead
   const int variant = decode_variant(m);
@@ -367,8 +397,8 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   hipError_t e = timed(m, s, F_EMBED, [&] {
     // the embedding goes to replica 0; the other replicas and the q/k/v
     // accumulator are cleared (attention clears the gate/up accumulator)
-    return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, m->x_fix, m->status, m->qkv_fix, n_qkv,
-                            m->x_fix + xs, (kXReps - 1) * xs);
+    return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, d.x_fix, m->status, d.qkv_fix, n_qkv,
+                            d.x_fix + xs, (kXReps - 1) * xs);
   });
   if (e != hipSuccess) return e;
   // operand of a projection that follows an RMSNorm
@@ -382,12 +412,12 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       g.eps = c.rms_eps;
     } else {
       g.act_mode = 0;
-      g.act = m->u;
+      g.act = d.u;
     }
   };
   auto norm = [&](const float *w) -> hipError_t {
     if (fused_norm) return hipSuccess;
-    return timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, w, c.rms_eps, m->u); });
+    return timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, w, c.rms_eps, d.u); });
   };
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerBuf &Lw = m->L[l];
@@ -397,13 +427,13 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     const int gemv_target = fused_norm ? kGemvTargetGroups : kGemvTargetGroupsBatched;
     DecGemvArgs g = dec_args(m->status, Lw.w_qkv, B, m->nqkv, H, Lw.s_qkv, gemv_target);
     normed(g, Lw.in_norm);
-    g.out_fix = m->qkv_fix;
+    g.out_fix = d.qkv_fix;
     g.ldo = m->nqkv;
     e = timed(m, s, F_GEMM_QKV, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
     if (attn_o) {
       DecAttnOArgs ao{};
-      ao.qkv_fix = m->qkv_fix;
+      ao.qkv_fix = d.qkv_fix;
       ao.bias = Lw.b_qkv;
       ao.rope = m->rope;
       ao.k_cache = kc;
@@ -419,22 +449,22 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       ao.o_scale = Lw.s_o;
       ao.H = H;
       ao.x_out = xr;
-      ao.clear = fused_mlp ? xo : m->gu_fix;
+      ao.clear = fused_mlp ? xo : gu_clear;
       ao.clear_n = fused_mlp ? kXReps * xs : n_gu;
       ao.num_flag = m->status;
       e = timed(m, s, F_ATTN_O, [&] { return launch_dec_attn_o(s, ao); });
       if (e != hipSuccess) return e;
     } else {
       DecAttnArgs da{};
-      da.qkv_fix = m->qkv_fix;
+      da.qkv_fix = d.qkv_fix;
       da.bias = Lw.b_qkv;
       da.rope = m->rope;
       da.k_cache = kc;
       da.v_cache = vc;
-      da.o = m->o;
-      da.part_m = m->att_m;
-      da.part_l = m->att_l;
-      da.part_o = m->att_o;
+      da.o = d.o;
+      da.part_m = d.att_m;
+      da.part_l = d.att_l;
+      da.part_o = d.att_o;
       da.splits = S;
       da.head_parallel = B <= kFusedNormRows;      // latency-bound: split the heads over the waves
       da.batch = B;
@@ -444,7 +474,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       da.max_seq = c.max_seq;
       da.pos_dev = m->pos_dev;
       da.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
-      da.clear = fused_mlp ? xo : m->gu_fix;
+      da.clear = fused_mlp ? xo : gu_clear;
       da.clear_n = fused_mlp ? kXReps * xs : n_gu;
       e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
       if (e != hipSuccess) return e;
@@ -452,27 +482,27 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       if (S > 1 && !fused_norm) {
         // many rows: merge once, then an f16 operand
         e = timed(m, s, F_ATTN_MERGE, [&] {
-          return launch_dec_merge(s, m->att_m, m->att_l, m->att_o, S, B, c.n_heads, c.head_dim, m->o);
+          return launch_dec_merge(s, d.att_m, d.att_l, d.att_o, S, B, c.n_heads, c.head_dim, d.o);
         });
         if (e != hipSuccess) return e;
         g.act_mode = 0;
-        g.act = m->o;
+        g.act = d.o;
       } else if (S > 1) {
         g.act_mode = 3;
-        g.part_m = m->att_m;
-        g.part_l = m->att_l;
-        g.part_o = m->att_o;
+        g.part_m = d.att_m;
+        g.part_l = d.att_l;
+        g.part_o = d.att_o;
         g.attn_splits = S;
         g.n_heads = c.n_heads;
         g.head_dim = c.head_dim;
       } else {
         g.act_mode = 0;
-        g.act = m->o;
+        g.act = d.o;
       }
       g.lda = m->qd;
       g.out_fix = xr;
       g.ldo = H;
-      g.clear = m->qkv_fix;
+      g.clear = d.qkv_fix;
       g.clear_n = n_qkv;
       e = timed(m, s, F_GEMM_O, [&] { return launch_dec_gemv(s, g); });
       if (e != hipSuccess) return e;
@@ -491,7 +521,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       ma.M = B;
       ma.H = H;
       ma.I = I;
-      ma.clear = attn_o ? m->qkv_fix : nullptr;
+      ma.clear = attn_o ? d.qkv_fix : nullptr;
       ma.clear_n = n_qkv;
       ma.num_flag = m->status;
       e = timed(m, s, F_MLP, [&] { return launch_dec_mlp(s, ma); });
@@ -505,16 +535,16 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     g = dec_args(m->status, Lw.w_gu, B, 2 * I, H, Lw.s_gu, fused_norm ? kGemvTargetGroups / 2 : kGemvTargetGroups);
     normed(g, Lw.post_norm);
     g.role_gate_up = 1;
-    g.out_fix = m->gu_fix;
+    g.out_fix = d.gu_fix;
     if (!fused_norm) {
       // many rows: full K per workgroup, SwiGLU in the epilogue, f16 h out
       g.splits = 1;
       g.swiglu_out = 1;
-      g.h_out = m->h;
+      g.h_out = d.h;
       g.ldh = I;
     }
     if (attn_o) {
-      g.clear = m->qkv_fix;
+      g.clear = d.qkv_fix;
       g.clear_n = n_qkv;
     }
     g.ldo = 2 * I;
@@ -523,12 +553,12 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     g = dec_args(m->status, Lw.w_down, B, H, I, Lw.s_down, gemv_target);
     if (fused_norm) {
       g.act_mode = 2;
-      g.act_fix = m->gu_fix;
+      g.act_fix = d.gu_fix;
       g.lda = 2 * I;
     } else {
       // many rows: h was written by the gate/up epilogue
       g.act_mode = 0;
-      g.act = m->h;
+      g.act = d.h;
       g.lda = I;
     }
     g.out_fix = xr;
@@ -540,28 +570,47 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   // by a kernel of its own rather than in every workgroup's prologue
   DecGemvArgs g = dec_args(m->status, m->head, B, V, H, m->head_scale);
   if (kHeadNormKernel || !fused_norm) {
-    e = timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, m->final_norm, c.rms_eps, m->u); });
+    e = timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, m->final_norm, c.rms_eps, d.u); });
     if (e != hipSuccess) return e;
     g.act_mode = 0;
-    g.act = m->u;
+    g.act = d.u;
     g.lda = H;
   } else {
     normed(g, m->final_norm);
   }
   g.ldo = V;
   g.logits_mode = 1;
-  g.logits = m->logits;
-  g.arg_v = m->arg_v;
-  g.arg_i = m->arg_i;
+  g.logits = d.logits;
+  g.arg_v = d.arg_v;
+  g.arg_i = d.arg_i;
   e = timed(m, s, F_LM_HEAD, [&] { return launch_dec_gemv(s, g); });
   if (e != hipSuccess) return e;
   return timed(m, s, F_ARGMAX,
-               [&] { return launch_dec_end(s, m->arg_v, m->arg_i, (V + 63) / 64, B, next, m->pos_dev); });
+               [&] { return launch_dec_end(s, d.arg_v, d.arg_i, (V + 63) / 64, B, next, m->pos_dev); });
+}
+
+// The model's own per-step buffers (allocated by qw_create).
+DecodeScratch model_scratch(const qw_model *m) {
+  DecodeScratch d;
+  d.x_fix = m->x_fix;
+  d.x_fix2 = m->x_fix2;
+  d.qkv_fix = m->qkv_fix;
+  d.gu_fix = m->gu_fix;
+  d.arg_v = m->arg_v;
+  d.arg_i = m->arg_i;
+  d.att_m = m->att_m;
+  d.att_l = m->att_l;
+  d.att_o = m->att_o;
+  d.u = m->u;
+  d.o = m->o;
+  d.h = m->h;
+  d.logits = m->logits;
+  return d;
 }
 
 // One decode step writing next ids to `next` and logits to m->logits.
 hipError_t decode_body(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next) {
-  return m->fast_decode ? decode_fast(m, s, ids, next) : decode_generic(m, s, ids, next);
+  return m->fast_decode ? decode_fast(m, s, ids, next, model_scratch(m)) : decode_generic(m, s, ids, next);
 }
 
 void drop_graph(qw_model *m) {

@@ -81,7 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qw_timing_enable": (I32, [P, ctypes.c_char_p]),
         "qw_timing_read": (I32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]),
         "qw_kernel_names": (ctypes.c_char_p, []),
-        "qw_peak_copy": (I32, [P, P, I64, I32, P, ctypes.POINTER(ctypes.c_double)]),
+        "qw_peak_copy": (I32, [P, P, I64, I32, I32, P, ctypes.POINTER(ctypes.c_double)]),
         "qw_peak_mfma": (I32, [I32, P, ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
@@ -153,10 +153,12 @@ def qw_timing_read(model: int, reset: bool = True):
     return ms.value, n.value
 
 
-def qw_peak_copy(dst: int, src: int, nbytes: int, iters: int, stream: int = 0) -> float:
-    """HBM copy rate in GB/s (bytes read + written per second / 1e9)."""
+def qw_peak_copy(dst: int, src: int, nbytes: int, iters: int, read_only: bool = False, stream: int = 0) -> float:
+    """HBM rate in GB/s of a copy (bytes read + written per second / 1e9) or,
+    with read_only, of a pass that reads every byte once."""
     r = ctypes.c_double()
-    _check(load_library().qw_peak_copy(dst, src, nbytes, iters, ctypes.c_void_p(stream), ctypes.byref(r)))
+    _check(load_library().qw_peak_copy(dst, src, nbytes, iters, int(bool(read_only)), ctypes.c_void_p(stream),
+                                       ctypes.byref(r)))
     return r.value
 
 

@@ -209,14 +209,21 @@ const char *qw_kernel_names(void);
 /* Measured peaks, the denominators a run can reach beside the published
  * ones (not on the forward pass).  Both enqueue on `hip_stream`, wait for
  * their own work, and report through qw_last_error.
- * qw_peak_copy: copies `bytes` (a positive multiple of 16) from src to dst
- *   (device pointers, not overlapping) `iters` times with a 16-byte-per-lane
- *   grid-stride kernel; *gbs = (bytes read + bytes written) / seconds / 1e9.
+ * qw_peak_copy: `iters` passes of a 16-byte-per-lane grid-stride kernel
+ *   over `bytes` (a positive multiple of 64 MiB) of src (device pointers,
+ *   src and dst not overlapping, dst as large as src).  read_only = 0: dst
+ *   = src, *gbs = (bytes read + bytes written) / seconds / 1e9.  read_only
+ *   = 1: every byte of src is read once per pass and at most 16 MiB of dst
+ *   written (one combination of its reads per thread); the pass runs with
+ *   two load layouts at 4, 8 and 16 workgroups per CU and *gbs is the best
+ *   bytes read / seconds / 1e9 (the pattern of the decode step, which reads
+ *   far more than it writes).
  * qw_peak_mfma: 8192 waves each issue `iters` rounds of eight independent
  *   16x16x32 fp16 matrix products (v_mfma_f32_16x16x32_f16) on register
  *   operands; *tflops = dense fp16 FLOP / seconds / 1e12.
  * Errors: INVALID_ARG (NULL output or pointers, bad sizes), HIP. */
-qw_status qw_peak_copy(void *dst, const void *src, int64_t bytes, int32_t iters, void *hip_stream, double *gbs);
+qw_status qw_peak_copy(void *dst, const void *src, int64_t bytes, int32_t iters, int32_t read_only,
+                       void *hip_stream, double *gbs);
 qw_status qw_peak_mfma(int32_t iters, void *hip_stream, double *tflops);
 
 #ifdef __cplusplus
