@@ -21,6 +21,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -83,8 +84,24 @@ struct LayerBuf {
 
 }  // namespace
 
+// Per-step buffers of qw_decode_step_noalloc: one static array per GPU,
+// held until the process ends.  In host code `scratch` is only a handle for
+// hipGetSymbolAddress; its device address (one per GPU) is looked up once
+// per device when the first model is created there and kept in
+// g_scratch_dev, which is what kernels receive.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static_assert(kNoAllocScratchBytes == QW_NOALLOC_SCRATCH_BYTES, "the header states the array's size");
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];
+}  // namespace
+
 struct qw_model {
   qw_config cfg{};
+  int device = 0;            // HIP device the model lives on
   bool f16 = false;          // compute type: f16 (bf16 weights) or f32
   size_t esz = 4;
   int qd = 0, kvd = 0, nqkv = 0;
@@ -741,6 +758,18 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
 
   CREATE_TRY(hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking));
   hipStream_t s = m->stream;
+  CREATE_TRY(hipGetDevice(&m->device));
+  if (m->device < 0 || m->device >= kMaxDevices)
+    return cleanup_fail(fail(QW_ERR_UNSUPPORTED, "qw_create: device ordinal %d beyond %d", m->device, kMaxDevices));
+  {
+    // the allocation-free decode step's array on this device (once per device)
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[m->device]) {
+      void *p = nullptr;
+      CREATE_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+      g_scratch_dev[m->device] = p;
+    }
+  }
 
   // --- per-tensor-group absmax (only needed for the exact f16 scaling)
   // groups: per layer {qkv, o, gu, down}, then embed, then head (if untied)
@@ -951,6 +980,70 @@ qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t
     HIP_TRY(hipGraphLaunch(m->gexec, s));
   }
   HIP_TRY(launch_stage_out(s, next_ids, m->next_stage, m->batch, logits, m->logits, (int64_t)m->batch * m->cfg.vocab));
+  m->pos += 1;
+  return QW_OK;
+}
+
+qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits, int32_t *next_ids) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_decode_step_noalloc: model is NULL");
+  if (!ids || !next_ids) return fail(QW_ERR_INVALID_ARG, "qw_decode_step_noalloc: ids and next_ids must be non-NULL");
+  if (m->batch == 0) return fail(QW_ERR_BAD_STATE, "qw_decode_step_noalloc: no prefill has run");
+  if (m->pos >= m->cfg.max_seq)
+    return fail(QW_ERR_CACHE_FULL, "qw_decode_step_noalloc: cache holds max_seq=%d positions", m->cfg.max_seq);
+  if (!m->fast_decode)
+    return fail(QW_ERR_UNSUPPORTED, "qw_decode_step_noalloc: covers the bf16 decode step of up to 32 rows and GQA "
+                                    "groups of up to 8 (this model takes the generic step)");
+  const qw_config &c = m->cfg;
+  const int64_t B = m->batch, H = c.hidden, I = c.intermediate, V = c.vocab;
+  const DecodeNeeds need = decode_needs(m, (int)B);
+  // carve the step's buffers out of this device's array, 256-byte aligned
+  const int64_t sizes[] = {
+      kXReps * B * H * 8, kXReps * B * H * 8,             // x_fix, x_fix2
+      B * m->nqkv * 8,                                   // qkv_fix
+      need.gu_fix ? B * 2 * I * 8 : 0,                   // gu_fix
+      B * ((V + 63) / 64) * 4, B * ((V + 63) / 64) * 4,   // arg_v, arg_i
+      B * c.n_heads * 16 * 4, B * c.n_heads * 16 * 4,     // att_m, att_l (at most 16 splits)
+      B * c.n_heads * 16 * c.head_dim * 4,               // att_o
+      B * H * 2, B * m->qd * 2, B * I * 2,               // u, o, h (f16)
+  };
+  constexpr int kParts = sizeof(sizes) / sizeof(sizes[0]);
+  int64_t off[kParts], total = 0;
+  for (int k = 0; k < kParts; ++k) {
+    off[k] = total;
+    total += (sizes[k] + 255) / 256 * 256;
+  }
+  if (total > (int64_t)kNoAllocScratchBytes)
+    return fail(QW_ERR_UNSUPPORTED, "qw_decode_step_noalloc: a step of %d rows at these shapes needs %lld bytes of "
+                "scratch, more than the %zu of the static array", m->batch, (long long)total, kNoAllocScratchBytes);
+  char *base = (char *)g_scratch_dev[m->device];
+  if (!base) return fail(QW_ERR_BAD_STATE, "qw_decode_step_noalloc: no scratch address for device %d", m->device);
+  int dev_now = -1;
+  HIP_TRY(hipGetDevice(&dev_now));
+  if (dev_now != m->device)
+    return fail(QW_ERR_BAD_STATE, "qw_decode_step_noalloc: the model lives on device %d, device %d is current",
+                m->device, dev_now);
+  DecodeScratch d;
+  d.x_fix = (long long *)(base + off[0]);
+  d.x_fix2 = (long long *)(base + off[1]);
+  d.qkv_fix = (long long *)(base + off[2]);
+  d.gu_fix = need.gu_fix ? (long long *)(base + off[3]) : nullptr;
+  d.arg_v = (float *)(base + off[4]);
+  d.arg_i = (int *)(base + off[5]);
+  d.att_m = (float *)(base + off[6]);
+  d.att_l = (float *)(base + off[7]);
+  d.att_o = (float *)(base + off[8]);
+  d.u = base + off[9];
+  d.o = base + off[10];
+  d.h = base + off[11];
+  d.logits = logits;                 // the caller's buffer, or none
+  // launched one by one on the model's stream (nothing captured or
+  // instantiated); kernel timing stays off (it would create events)
+  const int fam = m->timing_family;
+  m->timing_family = -1;
+  hipError_t e = decode_fast(m, m->stream, ids, next_ids, d);
+  m->timing_family = fam;
+  HIP_TRY(e);
   m->pos += 1;
   return QW_OK;
 }

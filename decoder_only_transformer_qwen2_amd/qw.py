@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "QW_OK", -1: "QW_ERR_INVALID_ARG", -2: "QW_ERR_OUT_OF_MEMORY"
                 -4: "QW_ERR_CACHE_FULL", -5: "QW_ERR_BAD_STATE", -6: "QW_ERR_UNSUPPORTED",
                 -7: "QW_ERR_NUMERICS"}
 
-EXPORTED = ("qw_create", "qw_prefill", "qw_decode_step", "qw_destroy", "qw_last_error", "qw_get_state",
+EXPORTED = ("qw_create", "qw_prefill", "qw_decode_step", "qw_decode_step_noalloc", "qw_destroy", "qw_last_error", "qw_get_state",
             "qw_check_ids", "qw_check_numerics", "qw_set_graph", "qw_timing_enable", "qw_timing_read", "qw_kernel_names", "qw_peak_copy",
             "qw_peak_mfma")
 
@@ -72,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qw_create": (I32, [ctypes.POINTER(qw_config), ctypes.POINTER(qw_weights), P, ctypes.POINTER(P)]),
         "qw_prefill": (I32, [P, P, I32, I32, P, I32, P]),
         "qw_decode_step": (I32, [P, P, P, P]),
+        "qw_decode_step_noalloc": (I32, [P, P, P, P]),
         "qw_destroy": (I32, [P]),
         "qw_last_error": (ctypes.c_char_p, []),
         "qw_get_state": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
@@ -119,6 +120,10 @@ def qw_prefill(model: int, ids: int, batch: int, prompt_len: int, logits: int, l
 
 def qw_decode_step(model: int, ids: int, logits: int, next_ids: int) -> None:
     _check(load_library().qw_decode_step(model, ids, logits or None, next_ids))
+
+
+def qw_decode_step_noalloc(model: int, ids: int, logits: int, next_ids: int) -> None:
+    _check(load_library().qw_decode_step_noalloc(model, ids, logits or None, next_ids))
 
 
 def qw_destroy(model: int) -> None:
@@ -227,6 +232,14 @@ class Model:
             next_ids = torch.empty(ids.shape[0], dtype=torch.int32, device=ids.device)
         qw_decode_step(self.handle, ids.data_ptr(), logits.data_ptr() if logits is not None else 0,
                        next_ids.data_ptr())
+        return next_ids
+
+    def decode_step_noalloc(self, ids, logits=None, next_ids=None):
+        import torch
+        if next_ids is None:
+            next_ids = torch.empty(ids.shape[0], dtype=torch.int32, device=ids.device)
+        qw_decode_step_noalloc(self.handle, ids.data_ptr(), logits.data_ptr() if logits is not None else 0,
+                               next_ids.data_ptr())
         return next_ids
 
     def state(self):

@@ -164,6 +164,28 @@ qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t pro
  * Architecture", "Decoding" and the harness listing's generation loop. */
 qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t *next_ids);
 
+/* Size of the static device array behind qw_decode_step_noalloc (per GPU). */
+#define QW_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * decode step as qw_decode_step (same kernels, same results, bit for bit),
+ * launched one kernel at a time on the model's stream (nothing is captured
+ * or instantiated, no event created), with every per-step buffer (the
+ * fixed-point residual and projection sums, split-KV partials, LM-head argmax
+ * partials, f16 activations) in one static device array of
+ * QW_NOALLOC_SCRATCH_BYTES that the library holds on each GPU until the
+ * process ends.  logits (fp32 [batch][V], device, or NULL) and next_ids
+ * [batch] are written directly.  The step's kernels clear what they
+ * accumulate into, so stale contents of the array do not matter; but every
+ * call on one GPU (any model) shares the array, so calls that overlap on one
+ * GPU race: the caller serialises them.  The model's device must be current.
+ * Errors: as qw_decode_step; UNSUPPORTED when the model takes the generic
+ * step (fp32 weights, max_batch > 32, more than 8 query heads per KV head)
+ * or the step's buffers exceed QW_NOALLOC_SCRATCH_BYTES (about 7 MB at
+ * batch 32 of the 1.5B shapes); BAD_STATE when another device is current. */
+qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits, int32_t *next_ids);
+
 /* Free everything the model owns.  Synchronises its stream first.  NULL is a
  * no-op.  Source: "augur" (the preallocated cache lives as long as the model). */
 qw_status qw_destroy(qw_model *m);
