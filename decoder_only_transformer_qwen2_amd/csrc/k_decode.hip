@@ -34,6 +34,9 @@
 #include "qw_internal.h"
 
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 namespace qw {
 
@@ -550,10 +553,11 @@ hipError_t launch_gemv_nb(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
 // of its outputs: q/k/v sums are stored, residual rows read-modify-written,
 // and no atomics are needed.  With one, the slices add fixed-point values
 // atomically (deterministic, as above).
-template <int RT, int NB, int MAXU, DecOut OM, bool ATOMIC>
-__global__ void __launch_bounds__(256) dec_rows_kernel(DecGemvArgs a) {
-  constexpr int RB = 16 * RT, BT = 16 * NB;
-  __shared__ float s_acc[4][RB][BT + 1];
+template <int RT, int NB, int MAXU, DecOut OM, bool ATOMIC, int NW = 4>
+__global__ void __launch_bounds__(64 * NW) dec_rows_kernel(DecGemvArgs a) {
+  constexpr int RB = 16 * RT, BT = 16 * NB, NT = 64 * NW;
+  static_assert(OM != DecOut::Logits || NW == 4, "the argmax partials take 256 threads");
+  __shared__ float s_acc[NW][RB][BT + 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: unit bounds stay scalar
   const int i = lane & 15, g = lane >> 4;
@@ -561,7 +565,7 @@ __global__ void __launch_bounds__(256) dec_rows_kernel(DecGemvArgs a) {
   const int n0 = nblk * RB;
   const int units = a.K >> 5;
   const int us0 = split * a.units_per_split, us1 = min(units, us0 + a.units_per_split);
-  const int per_w = (max(0, us1 - us0) + 3) >> 2;
+  const int per_w = (max(0, us1 - us0) + NW - 1) / NW;
   const int u0 = us0 + wave * per_w, u1 = min(us1, u0 + per_w);
 
   if (a.clear)
@@ -618,11 +622,14 @@ __global__ void __launch_bounds__(256) dec_rows_kernel(DecGemvArgs a) {
       for (int q = 0; q < 4; ++q) s_acc[wave][16 * r + 4 * g + q][16 * nb + i] = acc[r][nb][q];
   __syncthreads();
   auto total = [&](int nl, int b) {
-    return (s_acc[0][nl][b] + s_acc[1][nl][b] + s_acc[2][nl][b] + s_acc[3][nl][b]) * a.scale;
+    float t = s_acc[0][nl][b];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) t += s_acc[w2][nl][b];
+    return t * a.scale;
   };
 
   if constexpr (OM == DecOut::FixAdd) {
-    for (int e = tid; e < RB * BT; e += 256) {
+    for (int e = tid; e < RB * BT; e += NT) {
       const int nl = e % RB, b = e / RB, n = n0 + nl;
       if (n >= a.N || b >= a.M) continue;
       long long *p = a.out_fix + (int64_t)b * a.ldo + n;
@@ -637,7 +644,7 @@ __global__ void __launch_bounds__(256) dec_rows_kernel(DecGemvArgs a) {
   } else if constexpr (OM == DecOut::SwiGLUOut) {
     static_assert(RT % 2 == 0, "gate/up rows come in GU_BLOCK pairs");
     f16 *h = (f16 *)a.h_out;
-    for (int e = tid; e < (RB / 2) * BT; e += 256) {
+    for (int e = tid; e < (RB / 2) * BT; e += NT) {
       const int fl = e % (RB / 2), b = e / (RB / 2);
       const int p = fl / GU_BLOCK, j = fl % GU_BLOCK;
       const int f = nblk * (RB / 2) + fl;
@@ -679,35 +686,113 @@ __global__ void __launch_bounds__(256) dec_rows_kernel(DecGemvArgs a) {
 template <int RT, int NB>
 constexpr int rows_maxu() { return (RT + NB) * 4 * 16 <= 200 ? 16 : (RT + NB) * 4 * 12 <= 200 ? 12 : 8; }
 
-template <int NB>
-hipError_t launch_rows_nb(hipStream_t s, const DecGemvArgs &a, int splits) {
-  if (a.logits_mode) {
-    const dim3 grid((a.N + 63) / 64, 1);
-    QW_LAUNCH((dec_rows_kernel<4, NB, rows_maxu<4, NB>(), DecOut::Logits, false>), dim3(grid), dim3(256), 0, s, a);
-  } else if (a.swiglu_out) {
-    const dim3 grid((a.N + 31) / 32, 1);
-    QW_LAUNCH((dec_rows_kernel<2, NB, rows_maxu<2, NB>(), DecOut::SwiGLUOut, false>), dim3(grid), dim3(256), 0, s, a);
-  } else {
-    const dim3 grid((a.N + 15) / 16, splits);
-    if (splits > 1)
-      QW_LAUNCH((dec_rows_kernel<1, NB, rows_maxu<1, NB>(), DecOut::FixAdd, true>), dim3(grid), dim3(256), 0, s, a);
-    else
-      QW_LAUNCH((dec_rows_kernel<1, NB, rows_maxu<1, NB>(), DecOut::FixAdd, false>), dim3(grid), dim3(256), 0, s, a);
-  }
+// How a batched projection is cut: RT 16-row tiles per workgroup, NW waves
+// splitting each workgroup's K slice, `splits` K slices (atomics when > 1).
+// Every workgroup reads the whole activation block of its K slice from L2, and
+// the per-CU path to L2 (not HBM) bounds these kernels, so more rows per
+// workgroup cut the traffic that matters; more waves keep each wave's share
+// within one batch of loads.
+struct RowsPlan {
+  int rt, nw, splits;
+};
+
+template <int NB, int RT, int NW>
+hipError_t launch_rows_fix(hipStream_t s, const DecGemvArgs &a, int splits) {
+  constexpr int MU = rows_maxu<RT, NB>();
+  const dim3 grid((a.N + 16 * RT - 1) / (16 * RT), splits);
+  if (splits > 1)
+    QW_LAUNCH((dec_rows_kernel<RT, NB, MU, DecOut::FixAdd, true, NW>), dim3(grid), dim3(64 * NW), 0, s, a);
+  else
+    QW_LAUNCH((dec_rows_kernel<RT, NB, MU, DecOut::FixAdd, false, NW>), dim3(grid), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
-// K slices of a batched FixAdd projection: about `target` workgroups of 16
-// rows, and no more slices than keep a wave's share within one batch of loads
-// ... unless the row blocks alone are fewer than half the target
-// about two workgroups per CU for the split projections (measured: 256 -> 512
-// took the 32-row decode step from 3.92 to 3.76 ms, 1024 was slower again)
-constexpr int kRowsTargetGroups = 512;
-int rows_splits(int N, int units, int maxu, int target) {
-  const int nb16 = (N + 15) / 16;
-  int rs = (target + nb16 / 2) / nb16;
-  rs = max(rs, (units + 4 * maxu - 1) / (4 * maxu));   // one batch of loads per wave
-  return max(1, min(rs, units / 8));                    // at least 2 units per wave
+template <int NB, int RT, int NW>
+hipError_t launch_rows_swiglu(hipStream_t s, const DecGemvArgs &a) {
+  constexpr int MU = rows_maxu<RT, NB>();
+  const dim3 grid((a.N + 16 * RT - 1) / (16 * RT), 1);
+  QW_LAUNCH((dec_rows_kernel<RT, NB, MU, DecOut::SwiGLUOut, false, NW>), dim3(grid), dim3(64 * NW), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_rows_nb(hipStream_t s, const DecGemvArgs &a, const RowsPlan &p) {
+  if (a.logits_mode) {
+    const dim3 grid((a.N + 63) / 64, 1);
+    QW_LAUNCH((dec_rows_kernel<4, NB, rows_maxu<4, NB>(), DecOut::Logits, false>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  const int key = p.rt * 10 + p.nw;
+  if (a.swiglu_out) {
+    switch (key) {
+      case 24: return launch_rows_swiglu<NB, 2, 4>(s, a);
+      case 28: return launch_rows_swiglu<NB, 2, 8>(s, a);
+      case 44: return launch_rows_swiglu<NB, 4, 4>(s, a);
+      case 48: return launch_rows_swiglu<NB, 4, 8>(s, a);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (key) {
+    case 14: return launch_rows_fix<NB, 1, 4>(s, a, p.splits);
+    case 18: return launch_rows_fix<NB, 1, 8>(s, a, p.splits);
+    case 24: return launch_rows_fix<NB, 2, 4>(s, a, p.splits);
+    case 28: return launch_rows_fix<NB, 2, 8>(s, a, p.splits);
+    case 44: return launch_rows_fix<NB, 4, 4>(s, a, p.splits);
+    case 48: return launch_rows_fix<NB, 4, 8>(s, a, p.splits);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int rows_maxu_rt(int rt, int nb) {
+  switch (rt * 10 + nb) {
+    case 11: return rows_maxu<1, 1>();
+    case 12: return rows_maxu<1, 2>();
+    case 21: return rows_maxu<2, 1>();
+    case 22: return rows_maxu<2, 2>();
+    case 41: return rows_maxu<4, 1>();
+    default: return rows_maxu<4, 2>();
+  }
+}
+
+// K slices of a split batched projection: about `target` workgroups of RT
+// tiles, at least enough slices that each wave's share is one batch of loads,
+// at most one unit per wave.
+int rows_splits(int N, int units, int rt, int nw, int target, int nb) {
+  const int blocks = (N + 16 * rt - 1) / (16 * rt);
+  const int mu = rows_maxu_rt(rt, nb);
+  int rs = (target + blocks / 2) / blocks;
+  rs = max(rs, (units + nw * mu - 1) / (nw * mu));
+  return max(1, min(rs, units / nw));
+}
+
+// The cut of each batched projection (the gate/up one is never split: its
+// SwiGLU epilogue needs whole sums).  Measured at 32 rows on the 1.5B shapes
+// (ms per decode step, 28 layers): the split projections with 32-row tiles,
+// 8 waves and about 256 workgroups against 16-row tiles, 4 waves and about
+// 512 (down 0.480 -> 0.378, o 0.201 -> 0.183, q/k/v 0.201 -> 0.185); larger
+// gate/up tiles were slower (64 rows: 0.715 -> 0.76-0.78, 280 workgroups
+// spread unevenly over 256 CUs).
+RowsPlan rows_plan(const DecGemvArgs &a, int units) {
+  const int nb = a.M <= 16 ? 1 : 2;
+  RowsPlan p;
+  if (a.swiglu_out) {
+    p = {2, 4, 1};
+  } else if (nb == 2) {
+    p = {2, 8, rows_splits(a.N, units, 2, 8, 256, nb)};
+  } else {
+    p = {1, 4, rows_splits(a.N, units, 1, 4, 512, nb)};
+  }
+#ifdef QW_TUNING
+  // tuning builds only: QW_ROWS_PLAN="gu=RT,NW;fix=RT,NW,TARGET" overrides the cut
+  if (const char *env = getenv("QW_ROWS_PLAN")) {
+    int rt, nw, tg;
+    const char *gu = strstr(env, "gu="), *fx = strstr(env, "fix=");
+    if (a.swiglu_out && gu && sscanf(gu, "gu=%d,%d", &rt, &nw) == 2) p = {rt, nw, 1};
+    if (!a.swiglu_out && fx && sscanf(fx, "fix=%d,%d,%d", &rt, &nw, &tg) == 3)
+      p = {rt, nw, rows_splits(a.N, units, rt, nw, tg, nb)};
+  }
+#endif
+  return p;
 }
 
 // ---------------------------------------------------------------- fused MLP
@@ -1933,12 +2018,10 @@ hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &in) {
   // (the LM head stays on dec_gemv_kernel: 0.099 vs 0.110 ms per step at 8 rows)
   if (a.M > 2 && a.act_mode == (int)DecAct::F16 && !a.logits_mode) {
     // batched rows: K split only for FixAdd outputs
-    int rs = 1;
-    if (!a.logits_mode && !a.swiglu_out)
-      rs = rows_splits(a.N, units, a.M <= 16 ? rows_maxu<1, 1>() : rows_maxu<1, 2>(), kRowsTargetGroups);
-    a.units_per_split = (units + rs - 1) / rs;
-    rs = (units + a.units_per_split - 1) / a.units_per_split;
-    return a.M <= 16 ? launch_rows_nb<1>(s, a, rs) : launch_rows_nb<2>(s, a, rs);
+    RowsPlan p = rows_plan(a, units);
+    a.units_per_split = (units + p.splits - 1) / p.splits;
+    p.splits = (units + a.units_per_split - 1) / a.units_per_split;
+    return a.M <= 16 ? launch_rows_nb<1>(s, a, p) : launch_rows_nb<2>(s, a, p);
   }
   dim3 grid((a.N + 63) / 64, splits);
   return a.M <= 16 ? launch_gemv_nb<1>(s, a, grid) : launch_gemv_nb<2>(s, a, grid);

@@ -13,7 +13,8 @@ import os
 from typing import Dict, Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqw.so")
+# QW_LIB names another build of the same library (e.g. to compare two builds)
+LIB_PATH = os.environ.get("QW_LIB") or os.path.join(_PKG, "libqw.so")
 
 QW_OK, QW_ERR_INVALID_ARG, QW_ERR_OUT_OF_MEMORY, QW_ERR_HIP = 0, -1, -2, -3
 QW_ERR_CACHE_FULL, QW_ERR_BAD_STATE, QW_ERR_UNSUPPORTED, QW_ERR_NUMERICS = -4, -5, -6, -7
