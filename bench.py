@@ -48,6 +48,8 @@ DESCRIPTIONS = {
     "1.5b": "Qwen2.5-1.5B shapes, bf16 weights, batch 1, prompt 512, 256 greedy decode steps, cache 1024",
     "1.5b-prefill": "Qwen2.5-1.5B shapes, bf16 weights, batch 8 x prompt 2048, 32 greedy decode steps, cache 4096",
     "1.5b-longctx": "Qwen2.5-1.5B shapes, bf16 weights, batch 32 x prompt 8192, 128 greedy decode steps, cache 8320",
+    "coder-7b": "Qwen2.5-Coder-7B shapes (untied LM head), bf16 weights, batch 1, prompt 512, 128 greedy decode "
+                "steps, cache 1024",
 }
 
 
@@ -216,6 +218,40 @@ def measure_peaks(torch, Q):
             "mfma": "8192 waves x 100000 rounds of 8 independent v_mfma_f32_16x16x32_f16"}
 
 
+def cache_compare(torch, Q, w: S.Workload, steps: int, reps: int, warmup: int):
+    """Greedy generation of `steps` tokens after the workload's prompts, with
+    the KV cache (one prefill, then decode steps) and without it (a prefill
+    over the whole sequence at every step), each timed over `reps` runs with
+    HIP events: the pages' cache benchmark ("augur", cache benchmarking:
+    generation speed, prefill and decode time, cached against uncached)."""
+    m = w.model
+    B, P = w.batch, w.prompt_len
+    W = S.make_weights(m, w.weight_seed)
+    model = Q.Model(m, Q.device_tensors(m, W), B, P + steps + 1)
+    ids = torch.from_numpy(S.make_ids(w)).cuda()
+    out = {}
+    toks = {}
+    for use_cache in (True, False):
+        for _ in range(warmup):
+            model.generate(ids, steps, use_cache=use_cache)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            t = model.generate(ids, steps, use_cache=use_cache)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        key = "cached" if use_cache else "uncached"
+        toks[key] = t.cpu().numpy()
+        out[key] = {"ms_per_generation": round(ms, 3), "new_tokens_per_s": round(B * (steps + 1) / (ms / 1e3), 1)}
+    model.close()
+    agree = (toks["cached"] == toks["uncached"]).all(axis=1)
+    return {"metric": "greedy generation with and without the KV cache", "workload": w.name, "batch": B,
+            "prompt_len": P, "new_tokens": steps + 1, "reps": reps, **out,
+            "speedup": round(out["uncached"]["ms_per_generation"] / out["cached"]["ms_per_generation"], 2),
+            "rows_with_identical_tokens": int(agree.sum())}
+
+
 def roof(bound, kernel, achieved, peak, measured_peak, unit, **extra):
     out = {"bound": bound, "kernel": kernel, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
            "frac": round(achieved / peak, 4)}
@@ -240,6 +276,9 @@ def main():
                          "(same kernels; for counter collection, which does not follow graph launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 4 device copies of 256 MiB (the reference for HBM byte counters)")
+    ap.add_argument("--cache-compare", type=int, default=0, metavar="STEPS",
+                    help="only compare greedy generation of STEPS tokens with and without the KV cache "
+                         "(qw_generate) on the workload's prompts; prints its own JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
@@ -264,6 +303,9 @@ def main():
     w = S.WORKLOADS[args.workload]
     m = w.model
     B, P, D = w.batch, w.prompt_len, w.decode_steps
+    if args.cache_compare:
+        print(json.dumps(cache_compare(torch, Q, w, args.cache_compare, args.steps, args.warmup)), flush=True)
+        return
     peaks = None
     if not args.no_peaks:
         print("[bench] measured peaks (copy, MFMA)", file=sys.stderr, flush=True)

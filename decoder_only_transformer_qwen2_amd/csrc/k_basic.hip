@@ -16,12 +16,15 @@
 namespace qw {
 
 // ---------------------------------------------------------------- embed
+// Row r is token t = r % rows_per_seq of sequence b = r / rows_per_seq, whose
+// id sits at ids[b * ids_stride + t].
 template <typename T>
-__global__ void __launch_bounds__(256) embed_kernel(const int32_t *__restrict__ ids, const T *__restrict__ emb,
+__global__ void __launch_bounds__(256) embed_kernel(const int32_t *__restrict__ ids, int rows_per_seq,
+                                                    int64_t ids_stride, const T *__restrict__ emb,
                                                     float emb_scale, int hidden, int vocab,
                                                     float *__restrict__ x, int *__restrict__ bad) {
   const int r = blockIdx.x;
-  int id = ids[r];
+  int id = ids[(int64_t)(r / rows_per_seq) * ids_stride + r % rows_per_seq];
   if (id < 0 || id >= vocab) {
     if (threadIdx.x == 0) atomicOr(bad, kFlagBadId);
     id = 0;
@@ -31,13 +34,17 @@ __global__ void __launch_bounds__(256) embed_kernel(const int32_t *__restrict__ 
   for (int c = threadIdx.x; c < hidden; c += blockDim.x) dst[c] = to_f32(src[c]) * emb_scale;
 }
 
-hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int rows, const void *emb,
-                        float emb_scale, int hidden, int vocab, float *x, int *bad) {
+hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int rows, int rows_per_seq,
+                        int64_t ids_stride, const void *emb, float emb_scale, int hidden, int vocab, float *x,
+                        int *bad) {
   if (rows <= 0) return hipSuccess;
+  if (rows_per_seq < 1) return hipErrorInvalidValue;
   if (f16_mode)
-    QW_LAUNCH((embed_kernel<f16>), dim3(rows), dim3(256), 0, s, ids, (const f16 *)emb, emb_scale, hidden, vocab, x, bad);
+    QW_LAUNCH((embed_kernel<f16>), dim3(rows), dim3(256), 0, s, ids, rows_per_seq, ids_stride, (const f16 *)emb,
+              emb_scale, hidden, vocab, x, bad);
   else
-    QW_LAUNCH((embed_kernel<float>), dim3(rows), dim3(256), 0, s, ids, (const float *)emb, emb_scale, hidden, vocab, x, bad);
+    QW_LAUNCH((embed_kernel<float>), dim3(rows), dim3(256), 0, s, ids, rows_per_seq, ids_stride,
+              (const float *)emb, emb_scale, hidden, vocab, x, bad);
   return hipGetLastError();
 }
 
@@ -203,59 +210,97 @@ hipError_t launch_stage_out(hipStream_t s, int32_t *next_dst, const int32_t *nex
   return hipGetLastError();
 }
 
+// Generation bookkeeping: dst[b * dst_stride + dst_col] = src[b] for b < B
+// (and, if seq is non-NULL, seq[b * seq_stride + seq_col] = src[b]).
+__global__ void __launch_bounds__(64) put_column_kernel(int32_t *dst, int64_t dst_stride, int dst_col,
+                                                        int32_t *seq, int64_t seq_stride, int seq_col,
+                                                        const int32_t *src, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  dst[(int64_t)b * dst_stride + dst_col] = src[b];
+  if (seq) seq[(int64_t)b * seq_stride + seq_col] = src[b];
+}
+
+hipError_t launch_put_column(hipStream_t s, int32_t *dst, int64_t dst_stride, int dst_col, int32_t *seq,
+                             int64_t seq_stride, int seq_col, const int32_t *src, int B) {
+  put_column_kernel<<<(B + 63) / 64, 64, 0, s>>>(dst, dst_stride, dst_col, seq, seq_stride, seq_col, src, B);
+  return hipGetLastError();
+}
+
+// dst[r * dst_stride + c] = src[r * src_stride + c] for r < rows, c < n
+// (int32 rows when bytes == 4 ... both callers move int32 or float rows).
+__global__ void __launch_bounds__(256) copy_rows_kernel(uint32_t *dst, int64_t dst_stride, const uint32_t *src,
+                                                        int64_t src_stride, int64_t n) {
+  const int r = blockIdx.y;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n; c += (int64_t)gridDim.x * blockDim.x)
+    dst[r * dst_stride + c] = src[r * src_stride + c];
+}
+
+hipError_t launch_copy_rows(hipStream_t s, void *dst, int64_t dst_stride, const void *src, int64_t src_stride,
+                            int rows, int64_t n) {
+  if (rows <= 0 || n <= 0) return hipSuccess;
+  int64_t bx = (n + 255) / 256;
+  if (bx > 1024) bx = 1024;
+  copy_rows_kernel<<<dim3((unsigned)bx, rows), 256, 0, s>>>((uint32_t *)dst, dst_stride, (const uint32_t *)src,
+                                                             src_stride, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_set_int(hipStream_t s, int *p, int v) {
   set_int_kernel<<<1, 1, 0, s>>>(p, v);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- set-up
-__device__ __forceinline__ float load_src(const void *p, int64_t i, bool bf16) {
-  return bf16 ? bf16_bits_to_f32(((const uint16_t *)p)[i]) : ((const float *)p)[i];
+// Element i of a weight tensor stored as kind (kWeightF32, kWeightBF16 or
+// kWeightF16), as a float (exact for all three).
+__device__ __forceinline__ float load_src(const void *p, int64_t i, int kind) {
+  if (kind == kWeightBF16) return bf16_bits_to_f32(((const uint16_t *)p)[i]);
+  if (kind == kWeightF16) return (float)((const f16 *)p)[i];
+  return ((const float *)p)[i];
 }
 
-// Largest |value| of a tensor, as the bit pattern of a non-negative float
-// (ordered like the floats themselves, so an integer max works).
 // Largest |value| as float bits.  Magnitudes are compared as unsigned bit
 // patterns (the same order for non-negative floats), which keeps an inf or
 // NaN as the maximum so that qw_create can reject it.
-__global__ void __launch_bounds__(256) absmax_kernel(const void *src, int64_t n, bool bf16, unsigned *out) {
+__global__ void __launch_bounds__(256) absmax_kernel(const void *src, int64_t n, int kind, unsigned *out) {
   unsigned m = 0u;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    m = max(m, __float_as_uint(fabsf(load_src(src, i, bf16))));
+    m = max(m, __float_as_uint(fabsf(load_src(src, i, kind))));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, o, 64));
   if ((threadIdx.x & 63) == 0) atomicMax(out, m);
 }
 
-hipError_t launch_absmax(hipStream_t s, bool src_bf16, const void *src, int64_t n, unsigned *out_bits) {
+hipError_t launch_absmax(hipStream_t s, int src_kind, const void *src, int64_t n, unsigned *out_bits) {
   int blocks = (int)((n + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  absmax_kernel<<<blocks, 256, 0, s>>>(src, n, src_bf16, out_bits);
+  absmax_kernel<<<blocks, 256, 0, s>>>(src, n, src_kind, out_bits);
   return hipGetLastError();
 }
 
 template <typename D>
-__global__ void __launch_bounds__(256) convert_kernel(const void *src, int64_t n, bool bf16, D *dst, float scale) {
+__global__ void __launch_bounds__(256) convert_kernel(const void *src, int64_t n, int kind, D *dst, float scale) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    dst[i] = from_f32<D>(load_src(src, i, bf16) * scale);
+    dst[i] = from_f32<D>(load_src(src, i, kind) * scale);
 }
 
-hipError_t launch_convert(hipStream_t s, bool src_bf16, const void *src, int64_t n, bool dst_f16, void *dst,
+hipError_t launch_convert(hipStream_t s, int src_kind, const void *src, int64_t n, bool dst_f16, void *dst,
                           int64_t dst_offset, float scale) {
   if (n <= 0) return hipSuccess;
   int blocks = (int)((n + 255) / 256);
   if (blocks > 16384) blocks = 16384;
   if (dst_f16)
-    convert_kernel<f16><<<blocks, 256, 0, s>>>(src, n, src_bf16, (f16 *)dst + dst_offset, scale);
+    convert_kernel<f16><<<blocks, 256, 0, s>>>(src, n, src_kind, (f16 *)dst + dst_offset, scale);
   else
-    convert_kernel<float><<<blocks, 256, 0, s>>>(src, n, src_bf16, (float *)dst + dst_offset, scale);
+    convert_kernel<float><<<blocks, 256, 0, s>>>(src, n, src_kind, (float *)dst + dst_offset, scale);
   return hipGetLastError();
 }
 
 template <typename D>
 __global__ void __launch_bounds__(256) convert_gu_kernel(const void *gate, const void *up, int inter, int hidden,
-                                                         bool bf16, D *dst, float scale) {
+                                                         int kind, D *dst, float scale) {
   const int64_t n = 2LL * inter * hidden;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t drow = i / hidden;
@@ -264,33 +309,33 @@ __global__ void __launch_bounds__(256) convert_gu_kernel(const void *gate, const
     const int within = (int)(drow % (2 * GU_BLOCK));
     const bool is_up = within >= GU_BLOCK;
     const int64_t f = blk * GU_BLOCK + (is_up ? within - GU_BLOCK : within);
-    dst[i] = from_f32<D>(load_src(is_up ? up : gate, f * hidden + c, bf16) * scale);
+    dst[i] = from_f32<D>(load_src(is_up ? up : gate, f * hidden + c, kind) * scale);
   }
 }
 
-hipError_t launch_convert_gu(hipStream_t s, bool src_bf16, const void *gate, const void *up, int inter, int hidden,
+hipError_t launch_convert_gu(hipStream_t s, int src_kind, const void *gate, const void *up, int inter, int hidden,
                              bool dst_f16, void *dst, float scale) {
   const int64_t n = 2LL * inter * hidden;
   int blocks = (int)((n + 255) / 256);
   if (blocks > 16384) blocks = 16384;
   if (dst_f16)
-    convert_gu_kernel<f16><<<blocks, 256, 0, s>>>(gate, up, inter, hidden, src_bf16, (f16 *)dst, scale);
+    convert_gu_kernel<f16><<<blocks, 256, 0, s>>>(gate, up, inter, hidden, src_kind, (f16 *)dst, scale);
   else
-    convert_gu_kernel<float><<<blocks, 256, 0, s>>>(gate, up, inter, hidden, src_bf16, (float *)dst, scale);
+    convert_gu_kernel<float><<<blocks, 256, 0, s>>>(gate, up, inter, hidden, src_kind, (float *)dst, scale);
   return hipGetLastError();
 }
 
 // dst[c][r] = src[r][c] * scale for a [rows, cols] source (f16 destination):
 // the down projection's [I, H] copy that the decode MLP reads row by row.
 // 32 x 32 tiles through LDS so both sides are read and written along rows.
-__global__ void __launch_bounds__(256) convert_t_kernel(const void *src, int rows, int cols, bool bf16, f16 *dst,
+__global__ void __launch_bounds__(256) convert_t_kernel(const void *src, int rows, int cols, int kind, f16 *dst,
                                                         float scale) {
   __shared__ float t[32][33];
   const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int y = ty; y < 32; y += 8) {
     const int r = r0 + y, c = c0 + tx;
-    t[y][tx] = (r < rows && c < cols) ? load_src(src, (int64_t)r * cols + c, bf16) * scale : 0.f;
+    t[y][tx] = (r < rows && c < cols) ? load_src(src, (int64_t)r * cols + c, kind) * scale : 0.f;
   }
   __syncthreads();
   for (int y = ty; y < 32; y += 8) {
@@ -299,11 +344,11 @@ __global__ void __launch_bounds__(256) convert_t_kernel(const void *src, int row
   }
 }
 
-hipError_t launch_convert_t(hipStream_t s, bool src_bf16, const void *src, int rows, int cols, void *dst,
+hipError_t launch_convert_t(hipStream_t s, int src_kind, const void *src, int rows, int cols, void *dst,
                             float scale) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
   dim3 grid((cols + 31) / 32, (rows + 31) / 32);
-  convert_t_kernel<<<grid, 256, 0, s>>>(src, rows, cols, src_bf16, (f16 *)dst, scale);
+  convert_t_kernel<<<grid, 256, 0, s>>>(src, rows, cols, src_kind, (f16 *)dst, scale);
   return hipGetLastError();
 }
 

@@ -213,8 +213,10 @@ bool dec_mlp_supported(int hidden, int inter);
 // ------------------------------------------------------------ launchers
 // Each returns the hipError_t of its launch.  `f16_mode` selects the compute
 // type (f16 when true, float when false).
-hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int rows, const void *emb,
-                        float emb_scale, int hidden, int vocab, float *x, int *bad_id_flag);
+// row r reads ids[(r / rows_per_seq) * ids_stride + r % rows_per_seq]
+hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int rows, int rows_per_seq,
+                        int64_t ids_stride, const void *emb, float emb_scale, int hidden, int vocab, float *x,
+                        int *bad_id_flag);
 hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows, int row_stride,
                           int hidden, const float *w, float eps, void *out);
 hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a);
@@ -249,19 +251,36 @@ hipError_t launch_dec_attn_o(hipStream_t s, const DecAttnOArgs &a);
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
                          int32_t *next_ids, int *pos_dev, int pos_add, int *flag);
 hipError_t launch_set_int(hipStream_t s, int *p, int v);
+// dst[b * dst_stride + dst_col] = src[b] (and seq[b * seq_stride + seq_col] = src[b] if seq)
+hipError_t launch_put_column(hipStream_t s, int32_t *dst, int64_t dst_stride, int dst_col, int32_t *seq,
+                             int64_t seq_stride, int seq_col, const int32_t *src, int B);
+// rows x n four-byte values from src (row stride src_stride) to dst (dst_stride)
+hipError_t launch_copy_rows(hipStream_t s, void *dst, int64_t dst_stride, const void *src, int64_t src_stride,
+                            int rows, int64_t n);
 hipError_t launch_copy_i32(hipStream_t s, int32_t *dst, const int32_t *src, int n);
 // next_dst[0..b) = next_src; if logits_dst, logits_dst[0..n_logits) = logits_src
 hipError_t launch_stage_out(hipStream_t s, int32_t *next_dst, const int32_t *next_src, int b, float *logits_dst,
                             const float *logits_src, int64_t n_logits);
 
-// set-up kernels (qw_create)
-hipError_t launch_absmax(hipStream_t s, bool src_bf16, const void *src, int64_t n, unsigned *out_bits);
+// Sampling of the next token from B rows of logits (row stride row_stride)
+// by the counter-based draw for n = *pos_dev tokens before it; with finished
+// non-NULL the end-of-sequence rule for `eos` applies.  See k_sample.hip.
+hipError_t launch_sample(hipStream_t s, const float *logits, int64_t row_stride, int B, int V, float temperature,
+                         int top_k, float top_p, uint64_t seed, const int *pos_dev, int32_t *next, int *finished,
+                         int eos);
+hipError_t launch_eos(hipStream_t s, int32_t *next, int *finished, int eos, int B);
+hipError_t launch_fill_int(hipStream_t s, int *p, int v, int n);
+
+// set-up kernels (qw_create); src_kind is the storage type of the caller's
+// weights
+constexpr int kWeightF32 = 0, kWeightBF16 = 1, kWeightF16 = 2;
+hipError_t launch_absmax(hipStream_t s, int src_kind, const void *src, int64_t n, unsigned *out_bits);
 // dst[dst_offset + i] = src[i] * scale for i < n (scale: exact power of two)
-hipError_t launch_convert(hipStream_t s, bool src_bf16, const void *src, int64_t n, bool dst_f16, void *dst,
+hipError_t launch_convert(hipStream_t s, int src_kind, const void *src, int64_t n, bool dst_f16, void *dst,
                           int64_t dst_offset, float scale);
-hipError_t launch_convert_gu(hipStream_t s, bool src_bf16, const void *gate, const void *up, int inter,
+hipError_t launch_convert_gu(hipStream_t s, int src_kind, const void *gate, const void *up, int inter,
                              int hidden, bool dst_f16, void *dst, float scale);
-hipError_t launch_convert_t(hipStream_t s, bool src_bf16, const void *src, int rows, int cols, void *dst,
+hipError_t launch_convert_t(hipStream_t s, int src_kind, const void *src, int rows, int cols, void *dst,
                             float scale);   // f16 dst[cols][rows]
 hipError_t launch_rope_table(hipStream_t s, float2 *table, int max_seq, int head_dim, double theta);
 

@@ -122,6 +122,15 @@ struct qw_model {
   int *pos_dev = nullptr;
   int *status = nullptr;     // status word: kFlagBadId | kFlagNonFinite | kFlagFixRange
   int32_t *ids_stage = nullptr, *next_stage = nullptr;   // [max_batch] rows the decode graph reads / writes
+  int32_t *seq_ids = nullptr;        // [max_batch][max_seq] sequences of the uncached generation
+  // sampling instead of the greedy choice (qw_set_sampling) and the
+  // end-of-sequence rule (qw_set_eos)
+  bool sampling = false;
+  float temperature = 1.f, top_p = 1.f;
+  int top_k = 1;
+  uint64_t seed = 0;
+  int eos = -1;
+  int *finished = nullptr;           // [max_batch] 1 once a sequence emitted eos
   // decode-step state (bf16-weight mode): fixed-point residual stream and
   // projection accumulators, LM-head argmax partials
   bool fast_decode = false;
@@ -345,17 +354,31 @@ hipError_t run_head(qw_model *m, hipStream_t s, const float *x_rows, int rows, i
                [&] { return launch_argmax(s, arg_logits, arg_rows, c.vocab, arg_stride, next, pos_dev, pos_add, m->status); });
 }
 
+// After the greedy choice of `next` and the position update: the sampled
+// choice instead (logits rows of stride `row_stride`), and the end-of-
+// sequence rule.
+hipError_t choose_next(qw_model *m, hipStream_t s, const float *logits, int64_t row_stride, int B, int32_t *next) {
+  int *fin = m->eos >= 0 ? m->finished : nullptr;
+  if (m->sampling)
+    return launch_sample(s, logits, row_stride, B, m->cfg.vocab, m->temperature, m->top_k, m->top_p, m->seed,
+                         m->pos_dev, next, fin, m->eos);
+  if (fin) return launch_eos(s, next, fin, m->eos, B);
+  return hipSuccess;
+}
+
 // Generic decode step (fp32 mode): the prefill kernels on one row per sequence.
 hipError_t decode_generic(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *next) {
   const qw_config &c = m->cfg;
   const int B = m->batch;
   hipError_t e = timed(m, s, F_EMBED, [&] {
-    return launch_embed(s, m->f16, ids, B, m->emb, m->emb_scale, c.hidden, c.vocab, m->x, m->status);
+    return launch_embed(s, m->f16, ids, B, 1, 1, m->emb, m->emb_scale, c.hidden, c.vocab, m->x, m->status);
   });
   if (e != hipSuccess) return e;
   e = run_layers(m, s, B, 1, 0, m->pos_dev);
   if (e != hipSuccess) return e;
-  return run_head(m, s, m->x, B, c.hidden, m->logits, m->logits, B, c.vocab, next, m->pos_dev, 1);
+  e = run_head(m, s, m->x, B, c.hidden, m->logits, m->logits, B, c.vocab, next, m->pos_dev, 1);
+  if (e != hipSuccess) return e;
+  return choose_next(m, s, m->logits, c.vocab, B, next);
 }
 
 DecGemvArgs dec_args(int *status, const void *W, int M, int N, int K, float scale,
@@ -602,8 +625,10 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   g.arg_i = d.arg_i;
   e = timed(m, s, F_LM_HEAD, [&] { return launch_dec_gemv(s, g); });
   if (e != hipSuccess) return e;
-  return timed(m, s, F_ARGMAX,
-               [&] { return launch_dec_end(s, d.arg_v, d.arg_i, (V + 63) / 64, B, next, m->pos_dev); });
+  e = timed(m, s, F_ARGMAX,
+            [&] { return launch_dec_end(s, d.arg_v, d.arg_i, (V + 63) / 64, B, next, m->pos_dev); });
+  if (e != hipSuccess) return e;
+  return choose_next(m, s, d.logits, V, B, next);
 }
 
 // The model's own per-step buffers (allocated by qw_create).
@@ -644,7 +669,8 @@ qw_status validate_config(const qw_config *c) {
     return fail(QW_ERR_INVALID_ARG, "qw_create: n_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_heads,
                 c->n_kv_heads);
   if (c->head_dim % 2 != 0) return fail(QW_ERR_INVALID_ARG, "qw_create: head_dim must be even (split-half RoPE)");
-  if (c->dtype != QW_F32 && c->dtype != QW_BF16) return fail(QW_ERR_INVALID_ARG, "qw_create: unknown dtype");
+  if (c->dtype != QW_F32 && c->dtype != QW_BF16 && c->dtype != QW_F16)
+    return fail(QW_ERR_INVALID_ARG, "qw_create: unknown dtype");
   if (c->qkv_bias != 1) return fail(QW_ERR_INVALID_ARG, "qw_create: Qwen2 q/k/v projections carry a bias (qkv_bias=1)");
   if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps)) return fail(QW_ERR_INVALID_ARG, "qw_create: rms_eps must be finite and >= 0");
   if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return fail(QW_ERR_INVALID_ARG, "qw_create: rope_theta must be finite and > 0");
@@ -735,14 +761,14 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   qw_model *m = new qw_model();
   const qw_config &c = *cfg;
   m->cfg = c;
-  m->f16 = (c.dtype == QW_BF16);
+  m->f16 = (c.dtype != QW_F32);
   m->esz = m->f16 ? 2 : 4;
   m->qd = c.n_heads * c.head_dim;
   m->kvd = c.n_kv_heads * c.head_dim;
   m->nqkv = m->qd + 2 * m->kvd;
   m->rows_cap = (int64_t)c.max_batch * c.max_seq;
   m->stream = (hipStream_t)hip_stream;
-  const bool src_bf16 = (c.dtype == QW_BF16);
+  const int src_kind = c.dtype == QW_BF16 ? kWeightBF16 : c.dtype == QW_F16 ? kWeightF16 : kWeightF32;
   const int H = c.hidden, I = c.intermediate, V = c.vocab;
   auto cleanup_fail = [&](qw_status s) {
     release_model(m);     // keeps the error message
@@ -781,17 +807,17 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
     CREATE_TRY(hipMemsetAsync(amax_dev, 0, n_groups * sizeof(unsigned), s));
     for (int l = 0; l < c.n_layers; ++l) {
       const qw_layer_weights &Lw = weights->layers[l];
-      CREATE_TRY(launch_absmax(s, true, Lw.q_w, (int64_t)m->qd * H, amax_dev + 4 * l));
-      CREATE_TRY(launch_absmax(s, true, Lw.k_w, (int64_t)m->kvd * H, amax_dev + 4 * l));
-      CREATE_TRY(launch_absmax(s, true, Lw.v_w, (int64_t)m->kvd * H, amax_dev + 4 * l));
-      CREATE_TRY(launch_absmax(s, true, Lw.o_w, (int64_t)H * m->qd, amax_dev + 4 * l + 1));
-      CREATE_TRY(launch_absmax(s, true, Lw.gate_w, (int64_t)I * H, amax_dev + 4 * l + 2));
-      CREATE_TRY(launch_absmax(s, true, Lw.up_w, (int64_t)I * H, amax_dev + 4 * l + 2));
-      CREATE_TRY(launch_absmax(s, true, Lw.down_w, (int64_t)H * I, amax_dev + 4 * l + 3));
+      CREATE_TRY(launch_absmax(s, src_kind, Lw.q_w, (int64_t)m->qd * H, amax_dev + 4 * l));
+      CREATE_TRY(launch_absmax(s, src_kind, Lw.k_w, (int64_t)m->kvd * H, amax_dev + 4 * l));
+      CREATE_TRY(launch_absmax(s, src_kind, Lw.v_w, (int64_t)m->kvd * H, amax_dev + 4 * l));
+      CREATE_TRY(launch_absmax(s, src_kind, Lw.o_w, (int64_t)H * m->qd, amax_dev + 4 * l + 1));
+      CREATE_TRY(launch_absmax(s, src_kind, Lw.gate_w, (int64_t)I * H, amax_dev + 4 * l + 2));
+      CREATE_TRY(launch_absmax(s, src_kind, Lw.up_w, (int64_t)I * H, amax_dev + 4 * l + 2));
+      CREATE_TRY(launch_absmax(s, src_kind, Lw.down_w, (int64_t)H * I, amax_dev + 4 * l + 3));
     }
-    CREATE_TRY(launch_absmax(s, true, weights->embed, (int64_t)V * H, amax_dev + 4 * c.n_layers));
+    CREATE_TRY(launch_absmax(s, src_kind, weights->embed, (int64_t)V * H, amax_dev + 4 * c.n_layers));
     if (!c.tie_embeddings)
-      CREATE_TRY(launch_absmax(s, true, weights->lm_head, (int64_t)V * H, amax_dev + 4 * c.n_layers + 1));
+      CREATE_TRY(launch_absmax(s, src_kind, weights->lm_head, (int64_t)V * H, amax_dev + 4 * c.n_layers + 1));
     std::vector<unsigned> bits(n_groups);
     CREATE_TRY(hipMemcpyAsync(bits.data(), amax_dev, n_groups * sizeof(unsigned), hipMemcpyDeviceToHost, s));
     CREATE_TRY(hipStreamSynchronize(s));
@@ -824,22 +850,22 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
     CREATE_TRY(m->alloc((void **)&B.in_norm, (size_t)H * 4));
     CREATE_TRY(m->alloc((void **)&B.post_norm, (size_t)H * 4));
     const float sq = scale[4 * l], so = scale[4 * l + 1], sg = scale[4 * l + 2], sd = scale[4 * l + 3];
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.q_w, (int64_t)m->qd * H, dst_f16, B.w_qkv, 0, sq));
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.k_w, (int64_t)m->kvd * H, dst_f16, B.w_qkv, (int64_t)m->qd * H, sq));
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.v_w, (int64_t)m->kvd * H, dst_f16, B.w_qkv,
+    CREATE_TRY(launch_convert(s, src_kind, Lw.q_w, (int64_t)m->qd * H, dst_f16, B.w_qkv, 0, sq));
+    CREATE_TRY(launch_convert(s, src_kind, Lw.k_w, (int64_t)m->kvd * H, dst_f16, B.w_qkv, (int64_t)m->qd * H, sq));
+    CREATE_TRY(launch_convert(s, src_kind, Lw.v_w, (int64_t)m->kvd * H, dst_f16, B.w_qkv,
                               (int64_t)(m->qd + m->kvd) * H, sq));
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.q_b, m->qd, false, B.b_qkv, 0, 1.f));
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.k_b, m->kvd, false, B.b_qkv, m->qd, 1.f));
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.v_b, m->kvd, false, B.b_qkv, m->qd + m->kvd, 1.f));
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.o_w, (int64_t)H * m->qd, dst_f16, B.w_o, 0, so));
-    CREATE_TRY(launch_convert_gu(s, src_bf16, Lw.gate_w, Lw.up_w, I, H, dst_f16, B.w_gu, sg));
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.down_w, (int64_t)H * I, dst_f16, B.w_down, 0, sd));
+    CREATE_TRY(launch_convert(s, src_kind, Lw.q_b, m->qd, false, B.b_qkv, 0, 1.f));
+    CREATE_TRY(launch_convert(s, src_kind, Lw.k_b, m->kvd, false, B.b_qkv, m->qd, 1.f));
+    CREATE_TRY(launch_convert(s, src_kind, Lw.v_b, m->kvd, false, B.b_qkv, m->qd + m->kvd, 1.f));
+    CREATE_TRY(launch_convert(s, src_kind, Lw.o_w, (int64_t)H * m->qd, dst_f16, B.w_o, 0, so));
+    CREATE_TRY(launch_convert_gu(s, src_kind, Lw.gate_w, Lw.up_w, I, H, dst_f16, B.w_gu, sg));
+    CREATE_TRY(launch_convert(s, src_kind, Lw.down_w, (int64_t)H * I, dst_f16, B.w_down, 0, sd));
     if (with_down_t) {
       CREATE_TRY(m->alloc(&B.w_down_t, (size_t)I * H * es));
-      CREATE_TRY(launch_convert_t(s, src_bf16, Lw.down_w, H, I, B.w_down_t, sd));
+      CREATE_TRY(launch_convert_t(s, src_kind, Lw.down_w, H, I, B.w_down_t, sd));
     }
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.input_norm, H, false, B.in_norm, 0, 1.f));
-    CREATE_TRY(launch_convert(s, src_bf16, Lw.post_norm, H, false, B.post_norm, 0, 1.f));
+    CREATE_TRY(launch_convert(s, src_kind, Lw.input_norm, H, false, B.in_norm, 0, 1.f));
+    CREATE_TRY(launch_convert(s, src_kind, Lw.post_norm, H, false, B.post_norm, 0, 1.f));
     B.s_qkv = 1.f / sq;
     B.s_o = 1.f / so;
     B.s_gu = 1.f / sg;
@@ -848,7 +874,7 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   {
     const float se = scale[4 * c.n_layers];
     CREATE_TRY(m->alloc(&m->emb, (size_t)V * H * es));
-    CREATE_TRY(launch_convert(s, src_bf16, weights->embed, (int64_t)V * H, dst_f16, m->emb, 0, se));
+    CREATE_TRY(launch_convert(s, src_kind, weights->embed, (int64_t)V * H, dst_f16, m->emb, 0, se));
     m->emb_scale = 1.f / se;
     if (c.tie_embeddings) {
       m->head = m->emb;
@@ -856,11 +882,11 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
     } else {
       const float sh = scale[4 * c.n_layers + 1];
       CREATE_TRY(m->alloc(&m->head, (size_t)V * H * es));
-      CREATE_TRY(launch_convert(s, src_bf16, weights->lm_head, (int64_t)V * H, dst_f16, m->head, 0, sh));
+      CREATE_TRY(launch_convert(s, src_kind, weights->lm_head, (int64_t)V * H, dst_f16, m->head, 0, sh));
       m->head_scale = 1.f / sh;
     }
     CREATE_TRY(m->alloc((void **)&m->final_norm, (size_t)H * 4));
-    CREATE_TRY(launch_convert(s, src_bf16, weights->final_norm, H, false, m->final_norm, 0, 1.f));
+    CREATE_TRY(launch_convert(s, src_kind, weights->final_norm, H, false, m->final_norm, 0, 1.f));
   }
 
   // --- cache, RoPE table, workspace
@@ -901,6 +927,9 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
     CREATE_TRY(m->alloc((void **)&m->att_o, ns * c.head_dim * 4));
   }
   CREATE_TRY(m->alloc((void **)&m->next_stage, (size_t)c.max_batch * 4));
+  CREATE_TRY(m->alloc((void **)&m->seq_ids, (size_t)c.max_batch * c.max_seq * 4));
+  CREATE_TRY(m->alloc((void **)&m->finished, (size_t)c.max_batch * 4));
+  CREATE_TRY(hipMemsetAsync(m->finished, 0, (size_t)c.max_batch * 4, s));
   CREATE_TRY(hipMemsetAsync(m->pos_dev, 0, 256, s));
   CREATE_TRY(hipMemsetAsync(m->status, 0, 256, s));
   CREATE_TRY(hipStreamSynchronize(s));
@@ -908,6 +937,45 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   *out = m;
   return QW_OK;
 }
+
+}  // extern "C"
+
+namespace {
+
+// The enqueue of a prefill whose arguments are valid: `batch` sequences of
+// `prompt_len` ids, sequence b's at ids + b * ids_stride.
+hipError_t prefill_enqueue(qw_model *m, const int32_t *ids, int64_t ids_stride, int batch, int prompt_len,
+                           float *logits, int logits_all, int32_t *next_ids, bool new_sequences = true) {
+  const qw_config &c = m->cfg;
+  hipStream_t s = m->stream;
+  const int T = batch * prompt_len, H = c.hidden, V = c.vocab;
+  hipError_t e = timed(m, s, F_EMBED, [&] {
+    return launch_embed(s, m->f16, ids, T, prompt_len, ids_stride, m->emb, m->emb_scale, H, V, m->x, m->status);
+  });
+  if (e != hipSuccess) return e;
+  if ((e = run_layers(m, s, T, prompt_len, 0, nullptr)) != hipSuccess) return e;
+  const float *last;                  // each sequence's last-row logits, rows `stride` apart
+  int64_t stride;
+  if (logits_all) {
+    last = logits + (int64_t)(prompt_len - 1) * V;
+    stride = (int64_t)prompt_len * V;
+    e = run_head(m, s, m->x, T, H, logits, last, batch, stride, next_ids, nullptr, 0);
+  } else {
+    float *lg = logits ? logits : m->logits;
+    last = lg;
+    stride = V;
+    e = run_head(m, s, m->x + (int64_t)(prompt_len - 1) * H, batch, prompt_len * H, lg, lg, batch, V, next_ids,
+                 nullptr, 0);
+  }
+  if (e != hipSuccess) return e;
+  if ((e = launch_set_int(s, m->pos_dev, prompt_len)) != hipSuccess) return e;
+  if (new_sequences && m->eos >= 0 && (e = launch_fill_int(s, m->finished, 0, batch)) != hipSuccess) return e;
+  return choose_next(m, s, last, stride, batch, next_ids);
+}
+
+}  // namespace
+
+extern "C" {
 
 qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t prompt_len, float *logits,
                      int32_t logits_all, int32_t *next_ids) {
@@ -921,22 +989,8 @@ qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t pro
   if (prompt_len > c.max_seq)
     return fail(QW_ERR_CACHE_FULL, "qw_prefill: prompt_len %d exceeds max_seq %d", prompt_len, c.max_seq);
   if (logits_all && !logits) return fail(QW_ERR_INVALID_ARG, "qw_prefill: logits_all needs a logits buffer");
-  hipStream_t s = m->stream;
-  const int T = batch * prompt_len, H = c.hidden, V = c.vocab;
   m->batch = 0;          // invalid until the enqueue succeeds
-  HIP_TRY(timed(m, s, F_EMBED, [&] {
-    return launch_embed(s, m->f16, ids, T, m->emb, m->emb_scale, H, V, m->x, m->status);
-  }));
-  HIP_TRY(run_layers(m, s, T, prompt_len, 0, nullptr));
-  if (logits_all) {
-    HIP_TRY(run_head(m, s, m->x, T, H, logits, logits + (int64_t)(prompt_len - 1) * V, batch,
-                     (int64_t)prompt_len * V, next_ids, nullptr, 0));
-  } else {
-    float *lg = logits ? logits : m->logits;
-    HIP_TRY(run_head(m, s, m->x + (int64_t)(prompt_len - 1) * H, batch, prompt_len * H, lg, lg, batch, V, next_ids,
-                     nullptr, 0));
-  }
-  HIP_TRY(launch_set_int(s, m->pos_dev, prompt_len));
+  HIP_TRY(prefill_enqueue(m, ids, prompt_len, batch, prompt_len, logits, logits_all, next_ids));
   m->batch = batch;
   m->pos = prompt_len;
   return QW_OK;
@@ -994,6 +1048,8 @@ qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits,
   if (!m->fast_decode)
     return fail(QW_ERR_UNSUPPORTED, "qw_decode_step_noalloc: covers the bf16 decode step of up to 32 rows and GQA "
                                     "groups of up to 8 (this model takes the generic step)");
+  if (m->sampling && !logits)
+    return fail(QW_ERR_INVALID_ARG, "qw_decode_step_noalloc: sampling reads the logits: pass a logits buffer");
   const qw_config &c = m->cfg;
   const int64_t B = m->batch, H = c.hidden, I = c.intermediate, V = c.vocab;
   const DecodeNeeds need = decode_needs(m, (int)B);
@@ -1045,6 +1101,57 @@ qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits,
   m->timing_family = fam;
   HIP_TRY(e);
   m->pos += 1;
+  return QW_OK;
+}
+
+qw_status qw_generate(qw_model *m, const int32_t *ids, int32_t batch, int32_t prompt_len, int32_t steps,
+                      int32_t use_cache, int32_t *out_ids, float *logits) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_generate: model is NULL");
+  if (!ids || !out_ids) return fail(QW_ERR_INVALID_ARG, "qw_generate: ids and out_ids must be non-NULL");
+  const qw_config &c = m->cfg;
+  if (batch < 1 || batch > c.max_batch)
+    return fail(QW_ERR_INVALID_ARG, "qw_generate: batch %d outside [1, max_batch=%d]", batch, c.max_batch);
+  if (prompt_len < 1 || steps < 0) return fail(QW_ERR_INVALID_ARG, "qw_generate: prompt_len >= 1 and steps >= 0");
+  if ((int64_t)prompt_len + steps > c.max_seq)
+    return fail(QW_ERR_CACHE_FULL, "qw_generate: prompt_len %d + steps %d exceeds max_seq %d", prompt_len, steps,
+                c.max_seq);
+  hipStream_t s = m->stream;
+  const int V = c.vocab;
+  const int64_t cols = (int64_t)steps + 1;
+  // step k's logits are rows b * cols + k of `logits`; its token column k of out_ids
+  auto put_logits = [&](int k) -> hipError_t {
+    if (!logits) return hipSuccess;
+    return launch_copy_rows(s, logits + (int64_t)k * V, cols * V, m->logits, V, batch, V);
+  };
+  m->batch = 0;
+  if (use_cache) {
+    HIP_TRY(prefill_enqueue(m, ids, prompt_len, batch, prompt_len, logits ? m->logits : nullptr, 0, m->next_stage));
+    m->batch = batch;
+    m->pos = prompt_len;
+    HIP_TRY(put_logits(0));
+    HIP_TRY(launch_put_column(s, out_ids, cols, 0, nullptr, 0, 0, m->next_stage, batch));
+    for (int k = 1; k <= steps; ++k) {
+      // the step reads the staging row in place (ids may alias next ids)
+      qw_status st = qw_decode_step(m, m->next_stage, logits ? m->logits : nullptr, m->next_stage);
+      if (st != QW_OK) return st;
+      HIP_TRY(put_logits(k));
+      HIP_TRY(launch_put_column(s, out_ids, cols, k, nullptr, 0, 0, m->next_stage, batch));
+    }
+    return QW_OK;
+  }
+  // no cache reuse: step k runs a prefill over the prompt and the k tokens
+  // generated so far, kept in seq_ids (row stride max_seq)
+  const int64_t ss = c.max_seq;
+  HIP_TRY(launch_copy_rows(s, m->seq_ids, ss, ids, prompt_len, batch, prompt_len));
+  for (int k = 0; k <= steps; ++k) {
+    const int L = prompt_len + k;
+    HIP_TRY(prefill_enqueue(m, m->seq_ids, ss, batch, L, logits ? m->logits : nullptr, 0, m->next_stage, k == 0));
+    HIP_TRY(put_logits(k));
+    HIP_TRY(launch_put_column(s, out_ids, cols, k, k < steps ? m->seq_ids : nullptr, ss, L, m->next_stage, batch));
+  }
+  m->batch = batch;
+  m->pos = prompt_len + steps;
   return QW_OK;
 }
 
@@ -1118,6 +1225,49 @@ qw_status qw_check_numerics(qw_model *m) {
   if (bits)
     return fail(QW_ERR_NUMERICS, "since the last check:%s%s", (bits & kFlagNonFinite) ? " a logit was inf or NaN;" : "",
                 (bits & kFlagFixRange) ? " a decode residual or projection addend exceeded 2^23 in magnitude;" : "");
+  return QW_OK;
+}
+
+qw_status qw_set_sampling(qw_model *m, float temperature, int32_t top_k, float top_p, uint64_t seed) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_set_sampling: model is NULL");
+  if (top_k == 0) {
+    m->sampling = false;
+  } else {
+    if (!(temperature > 0.f) || !isfinite(temperature) || top_k < 1 || top_k > 1024 || !(top_p > 0.f) ||
+        !(top_p <= 1.f))
+      return fail(QW_ERR_INVALID_ARG, "qw_set_sampling: need temperature > 0, 1 <= top_k <= 1024 (0: greedy), "
+                                      "0 < top_p <= 1");
+    m->sampling = true;
+    m->temperature = temperature;
+    m->top_k = top_k;
+    m->top_p = top_p;
+    m->seed = seed;
+  }
+  drop_graph(m);
+  return QW_OK;
+}
+
+qw_status qw_set_eos(qw_model *m, int32_t eos_id) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_set_eos: model is NULL");
+  if (eos_id < -1 || eos_id >= m->cfg.vocab)
+    return fail(QW_ERR_INVALID_ARG, "qw_set_eos: eos_id %d outside [-1, %d)", eos_id, m->cfg.vocab);
+  m->eos = eos_id;
+  drop_graph(m);
+  return QW_OK;
+}
+
+qw_status qw_get_finished(qw_model *m, int32_t *finished, int32_t n) {
+  g_err.clear();
+  if (!m || !finished || n < 0 || n > m->cfg.max_batch)
+    return fail(QW_ERR_INVALID_ARG, "qw_get_finished: model, host buffer and 0 <= n <= max_batch needed");
+  HIP_TRY(hipStreamSynchronize(m->stream));
+  if (m->eos < 0) {
+    memset(finished, 0, (size_t)n * 4);
+    return QW_OK;
+  }
+  HIP_TRY(hipMemcpy(finished, m->finished, (size_t)n * 4, hipMemcpyDeviceToHost));
   return QW_OK;
 }
 

@@ -18,14 +18,14 @@ LIB_PATH = os.environ.get("QW_LIB") or os.path.join(_PKG, "libqw.so")
 
 QW_OK, QW_ERR_INVALID_ARG, QW_ERR_OUT_OF_MEMORY, QW_ERR_HIP = 0, -1, -2, -3
 QW_ERR_CACHE_FULL, QW_ERR_BAD_STATE, QW_ERR_UNSUPPORTED, QW_ERR_NUMERICS = -4, -5, -6, -7
-QW_F32, QW_BF16 = 0, 1
+QW_F32, QW_BF16, QW_F16 = 0, 1, 2
 
 STATUS_NAMES = {0: "QW_OK", -1: "QW_ERR_INVALID_ARG", -2: "QW_ERR_OUT_OF_MEMORY", -3: "QW_ERR_HIP",
                 -4: "QW_ERR_CACHE_FULL", -5: "QW_ERR_BAD_STATE", -6: "QW_ERR_UNSUPPORTED",
                 -7: "QW_ERR_NUMERICS"}
 
-EXPORTED = ("qw_create", "qw_prefill", "qw_decode_step", "qw_decode_step_noalloc", "qw_destroy", "qw_last_error", "qw_get_state",
-            "qw_check_ids", "qw_check_numerics", "qw_set_graph", "qw_timing_enable", "qw_timing_read", "qw_kernel_names", "qw_peak_copy",
+EXPORTED = ("qw_create", "qw_prefill", "qw_decode_step", "qw_decode_step_noalloc", "qw_generate", "qw_destroy", "qw_last_error", "qw_get_state",
+            "qw_check_ids", "qw_check_numerics", "qw_set_sampling", "qw_set_eos", "qw_get_finished", "qw_set_graph", "qw_timing_enable", "qw_timing_read", "qw_kernel_names", "qw_peak_copy",
             "qw_peak_mfma")
 
 
@@ -74,11 +74,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "qw_prefill": (I32, [P, P, I32, I32, P, I32, P]),
         "qw_decode_step": (I32, [P, P, P, P]),
         "qw_decode_step_noalloc": (I32, [P, P, P, P]),
+        "qw_generate": (I32, [P, P, I32, I32, I32, I32, P, P]),
         "qw_destroy": (I32, [P]),
         "qw_last_error": (ctypes.c_char_p, []),
         "qw_get_state": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "qw_check_ids": (I32, [P]),
         "qw_check_numerics": (I32, [P]),
+        "qw_set_sampling": (I32, [P, ctypes.c_float, I32, ctypes.c_float, ctypes.c_uint64]),
+        "qw_set_eos": (I32, [P, I32]),
+        "qw_get_finished": (I32, [P, ctypes.POINTER(I32), I32]),
         "qw_set_graph": (I32, [P, I32]),
         "qw_timing_enable": (I32, [P, ctypes.c_char_p]),
         "qw_timing_read": (I32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64), I32]),
@@ -127,6 +131,12 @@ def qw_decode_step_noalloc(model: int, ids: int, logits: int, next_ids: int) -> 
     _check(load_library().qw_decode_step_noalloc(model, ids, logits or None, next_ids))
 
 
+def qw_generate(model: int, ids: int, batch: int, prompt_len: int, steps: int, use_cache: bool, out_ids: int,
+                logits: int) -> None:
+    _check(load_library().qw_generate(model, ids, batch, prompt_len, steps, int(bool(use_cache)), out_ids,
+                                      logits or None))
+
+
 def qw_destroy(model: int) -> None:
     _check(load_library().qw_destroy(model))
 
@@ -143,6 +153,20 @@ def qw_check_ids(model: int) -> None:
 
 def qw_check_numerics(model: int) -> None:
     _check(load_library().qw_check_numerics(model))
+
+
+def qw_set_sampling(model: int, temperature: float, top_k: int, top_p: float, seed: int) -> None:
+    _check(load_library().qw_set_sampling(model, temperature, top_k, top_p, seed))
+
+
+def qw_set_eos(model: int, eos_id: int) -> None:
+    _check(load_library().qw_set_eos(model, eos_id))
+
+
+def qw_get_finished(model: int, n: int) -> list:
+    buf = (ctypes.c_int32 * max(n, 1))()
+    _check(load_library().qw_get_finished(model, buf, n))
+    return [int(buf[i]) for i in range(n)]
 
 
 def qw_set_graph(model: int, enable: bool) -> None:
@@ -189,15 +213,16 @@ def make_config(shape, max_batch: int, max_seq: int) -> qw_config:
     """qw_config from any object with the ModelShape field names."""
     return qw_config(shape.n_layers, shape.hidden, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                      shape.intermediate, shape.vocab, shape.rms_eps, shape.rope_theta, 1,
-                     int(shape.tie_embeddings), QW_BF16 if shape.dtype == "bf16" else QW_F32,
+                     int(shape.tie_embeddings), {"bf16": QW_BF16, "f16": QW_F16, "f32": QW_F32}[shape.dtype],
                      max_batch, max_seq)
 
 
 class Model:
     """A libqw model built from device tensors keyed by HF Qwen2 names.
 
-    `tensors` values are torch CUDA tensors (torch.bfloat16 for bf16 shapes,
-    torch.float32 for f32 shapes), contiguous, in HF [out, in] layouts.  The
+    `tensors` values are torch CUDA tensors (torch.bfloat16, torch.float16 or
+    torch.float32 as the shape's dtype says), contiguous, in HF [out, in]
+    layouts.  The
     library copies what it needs at creation, so they may be dropped after.
     """
 
@@ -205,7 +230,7 @@ class Model:
         import torch
         self.shape = shape
         self.cfg = make_config(shape, max_batch, max_seq)
-        want = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+        want = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[shape.dtype]
         for k, t in tensors.items():
             if t.dtype != want or not t.is_cuda or not t.is_contiguous():
                 raise ValueError(f"{k}: need a contiguous CUDA {want} tensor")
@@ -243,6 +268,17 @@ class Model:
                                next_ids.data_ptr())
         return next_ids
 
+    def generate(self, ids, steps: int, use_cache: bool = True, logits=None, out_ids=None):
+        """Greedy tokens [B, steps + 1] (and logits [B, steps + 1, V] if a
+        buffer is given) with or without the KV cache."""
+        import torch
+        B, P = ids.shape
+        if out_ids is None:
+            out_ids = torch.empty((B, steps + 1), dtype=torch.int32, device=ids.device)
+        qw_generate(self.handle, ids.data_ptr(), B, P, steps, use_cache, out_ids.data_ptr(),
+                    logits.data_ptr() if logits is not None else 0)
+        return out_ids
+
     def state(self):
         return qw_get_state(self.handle)
 
@@ -251,6 +287,15 @@ class Model:
 
     def check_numerics(self):
         qw_check_numerics(self.handle)
+
+    def set_sampling(self, temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0, seed: int = 0):
+        qw_set_sampling(self.handle, temperature, top_k, top_p, seed)
+
+    def set_eos(self, eos_id: int):
+        qw_set_eos(self.handle, eos_id)
+
+    def finished(self, n: int):
+        return qw_get_finished(self.handle, n)
 
     def set_graph(self, enable: bool):
         qw_set_graph(self.handle, enable)
@@ -274,14 +319,17 @@ class Model:
 
 
 def device_tensors(shape, weights: Dict[str, "object"], device="cuda"):
-    """Move seeded numpy weights (uint16 bf16 bit patterns or float32) to the
-    device as torch tensors of the matching dtype (a bit-exact copy)."""
+    """Move seeded numpy weights (uint16 bf16 bit patterns, float16 or
+    float32) to the device as torch tensors of the matching dtype (a
+    bit-exact copy)."""
     import numpy as np
     import torch
     out = {}
     for k, a in weights.items():
         if a.dtype == np.uint16:
             t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+        elif a.dtype == np.float16:
+            t = torch.from_numpy(np.ascontiguousarray(a))
         else:
             t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
         out[k] = t.to(device).contiguous()

@@ -67,8 +67,12 @@ typedef enum qw_status {
  *            absolute error below A * 2^-39.  Activations held in fp16 must
  *            stay below 65504 in magnitude: qw_check_numerics reports a
  *            forward that left that range (it surfaces as an inf or NaN
- *            logit) or the decode residual's fixed-point range. */
-typedef enum qw_dtype { QW_F32 = 0, QW_BF16 = 1 } qw_dtype;
+ *            logit) or the decode residual's fixed-point range.
+ *   QW_F16 : fp16 weights ("Building a Qwen2.5-1.5B Inference Engine From
+ *            Scratch", section 1.1: FP16 as the next experiment after FP32);
+ *            the same arithmetic as QW_BF16, the weights scaled the same way
+ *            (exact while |v| >= A * 2^-32 as above). */
+typedef enum qw_dtype { QW_F32 = 0, QW_BF16 = 1, QW_F16 = 2 } qw_dtype;
 
 /* Model and capacity.  Field meanings follow the Qwen2 config names the
  * "augur" feature list enumerates. */
@@ -164,6 +168,28 @@ qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t pro
  * Architecture", "Decoding" and the harness listing's generation loop. */
 qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t *next_ids);
 
+/* Greedy generation of `steps` tokens after `batch` equal-length prompts
+ * ids[batch][prompt_len] (device), all enqueued on the model's stream without
+ * host synchronisation: the pages' generation loop (the prompt once, then one
+ * token per step: "LLM Speedrun: Architecture", harness listing; "augur",
+ * greedy generation and cache benchmarking; "Building a Qwen2.5-1.5B
+ * Inference Engine From Scratch", section 1.1, use_cache=False as ground
+ * truth).
+ *   use_cache != 0: qw_prefill, then `steps` KV-cached decode steps.
+ *   use_cache == 0: step k (0 .. steps) runs a prefill over the prompt and
+ *     the k tokens generated so far (positions 0 .. prompt_len + k - 1) and
+ *     takes the greedy token of its last row; no step reuses keys or values
+ *     an earlier step computed.
+ * Outputs (device): out_ids [batch][steps + 1] (the prefill's token, then one
+ * per step); logits NULL or fp32 [batch][steps + 1][V].  Afterwards the model
+ * holds the sequences' cache (positions 0 .. prompt_len + steps - 1), so
+ * qw_decode_step may continue them.
+ * Errors: INVALID_ARG (NULL ids/out_ids, batch outside [1, max_batch],
+ * prompt_len < 1, steps < 0), CACHE_FULL (prompt_len + steps > max_seq),
+ * HIP. */
+qw_status qw_generate(qw_model *m, const int32_t *ids, int32_t batch, int32_t prompt_len, int32_t steps,
+                      int32_t use_cache, int32_t *out_ids, float *logits);
+
 /* Size of the static device array behind qw_decode_step_noalloc (per GPU). */
 #define QW_NOALLOC_SCRATCH_BYTES (16u << 20)
 
@@ -211,6 +237,34 @@ qw_status qw_check_ids(qw_model *m);
  * projection sums exceeded 2^23 in magnitude (it was clamped):
  * QW_ERR_NUMERICS if so (those flags are cleared), QW_OK otherwise. */
 qw_status qw_check_numerics(qw_model *m);
+
+/* Sampling instead of the greedy choice for every later prefill, decode step
+ * and generation ("augur": temperature, top-k and top-p sampling).  The pages
+ * give no formulas, so the plain reading is used: keep the top_k largest
+ * logits (ties: lower index first), weight them by exp((l - l_max) /
+ * temperature), keep the shortest prefix of that order whose cumulative
+ * weight reaches top_p of their total, and pick the first kept token whose
+ * cumulative weight exceeds u times the kept total.  u in [0, 1) is the top
+ * 24 bits of the first word of Philox-4x64-10 (Salmon et al., SC 2011) at
+ * counter (n, b, 0, 0) and key (seed, 0), where b is the batch row and n the
+ * number of tokens the sequence holds before the chosen one; so the draws
+ * depend only on (seed, row, position), with or without the cache.
+ * Arguments: temperature > 0, 1 <= top_k <= 1024, 0 < top_p <= 1;
+ * top_k = 0 restores the greedy choice.  Errors: INVALID_ARG. */
+qw_status qw_set_sampling(qw_model *m, float temperature, int32_t top_k, float top_p, uint64_t seed);
+
+/* End of sequence ("augur": EOS stopping; the speedrun harness stops on the
+ * end-of-stream token): with eos_id >= 0, a sequence that emits eos_id is
+ * finished, and every later prefill-free step emits eos_id for it again, on
+ * the device, inside the decode step (no host round trip).  Each qw_prefill
+ * (and qw_generate) starts its sequences unfinished.  eos_id = -1 turns the
+ * rule off.  Errors: INVALID_ARG (eos_id outside [-1, V)). */
+qw_status qw_set_eos(qw_model *m, int32_t eos_id);
+
+/* Synchronise the stream and copy the finished flags of the first n
+ * sequences (0 or 1) to the HOST array finished[n] (all 0 while no eos is
+ * set).  Errors: INVALID_ARG (NULL, n outside [0, max_batch]), HIP. */
+qw_status qw_get_finished(qw_model *m, int32_t *finished, int32_t n);
 
 /* Decode-step execution: 1 (default) replays a captured HIP graph of the whole
  * step; 0 launches its kernels one by one.  Both run the same kernels on the

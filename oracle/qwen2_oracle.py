@@ -9,7 +9,8 @@ library (the two meet only in the seeded inputs of `synthetic`).
 Precision: every value is float64.  Weights are read exactly (bf16 storage is
 the top half of an IEEE float32; see `decode_storage`).  No activation is
 rounded to bf16: the oracle is the real-valued forward pass of the given
-weights, so it is the same reference for the library's fp32 and bf16 modes.
+weights, so it is the same reference for the library's fp32, bf16 and fp16
+weight modes.
 
 Layout: rows are tokens, so activations are [T, features] and a projection
 with an HF-layout weight W [out, in] is `u @ W.T`.
@@ -49,7 +50,7 @@ import numpy as np
 __all__ = [
     "decode_storage", "rms_norm", "rope_inverse_frequencies", "rope_rotate",
     "attention_weights", "causal_gqa_attention", "silu", "swiglu_mlp",
-    "greedy_token", "OracleModel",
+    "greedy_token", "philox4x64_10", "sampling_draw", "sample_token", "OracleModel",
 ]
 
 
@@ -57,10 +58,11 @@ __all__ = [
 def decode_storage(a: np.ndarray) -> np.ndarray:
     """Exact float64 value of stored weights.  [S] harness listing's tensor
     reader: a bf16 word is the high 16 bits of a float32, so shifting it left
-    by 16 and reinterpreting gives the value exactly.  float32 passes through."""
+    by 16 and reinterpreting gives the value exactly.  float16 and float32
+    widen exactly."""
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    if a.dtype in (np.float32, np.float64):
+    if a.dtype in (np.float16, np.float32, np.float64):
         return a.astype(np.float64)
     raise ValueError(f"unsupported weight storage dtype {a.dtype}")
 
@@ -174,6 +176,57 @@ def greedy_token(logits: np.ndarray) -> int:
     """[A] greedy generation / [S] decoder step: the index of the largest
     logit; among equal maxima, the lowest index."""
     return int(np.argmax(logits))
+
+
+# ---------------------------------------------------------------- sampling
+# "augur" lists temperature, top-k and top-p sampling as not yet built; the
+# pages give no formulas for them, so the plain reading is taken (listed in
+# DESIGN.md): keep the top_k largest logits (ties: lower index first), weight
+# them by exp((l - l_max) / temperature), keep the shortest prefix of that
+# order whose weight reaches top_p of the total, and pick by the inverse
+# cumulative distribution of one uniform draw u in [0, 1).
+
+_M64 = (1 << 64) - 1
+
+
+def philox4x64_10(counter, key):
+    """Philox-4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel
+    random numbers: as easy as 1, 2, 3", SC 2011): each round multiplies
+    words 0 and 2 by the two round multipliers, crosses the high halves with
+    words 1 and 3 and the key, and the key is bumped by the two Weyl
+    constants between rounds.  counter: 4 ints, key: 2 ints (each < 2^64)."""
+    c = [int(x) & _M64 for x in counter]
+    k = [int(x) & _M64 for x in key]
+    for _ in range(10):
+        p0 = 0xD2E7470EE14C6C93 * c[0]
+        p1 = 0xCA5A826395121157 * c[2]
+        c = [(p1 >> 64) ^ c[1] ^ k[0], p1 & _M64, (p0 >> 64) ^ c[3] ^ k[1], p0 & _M64]
+        k = [(k[0] + 0x9E3779B97F4A7C15) & _M64, (k[1] + 0xBB67AE8584CAA73B) & _M64]
+    return c
+
+
+def sampling_draw(seed: int, sequence: int, n: int) -> float:
+    """The uniform draw for the token that follows the first n tokens of
+    batch row `sequence`: the top 24 bits of the first Philox word of counter
+    (n, sequence, 0, 0) under key (seed, 0), as a multiple of 2^-24."""
+    w = philox4x64_10([n, sequence, 0, 0], [seed, 0])[0]
+    return (w >> 40) * 2.0 ** -24
+
+
+def sample_token(logits: np.ndarray, temperature: float, top_k: int, top_p: float, u: float):
+    """The sampled index and the cumulative weights it was chosen from
+    (float64): (token, candidates in order, cumulative weights C, kept m,
+    threshold r = u * C[m-1]).  The token is the first kept candidate j with
+    C[j] > r."""
+    logits = np.asarray(logits, dtype=np.float64)
+    order = np.lexsort((np.arange(logits.size), -logits))[:top_k]   # value desc, index asc
+    w = np.exp((logits[order] - logits[order[0]]) / temperature)
+    C = np.cumsum(w)
+    m = int(np.searchsorted(C, top_p * C[-1], side="left")) + 1
+    m = min(max(m, 1), len(C))
+    r = u * C[m - 1]
+    j = int(np.searchsorted(C[:m], r, side="right"))
+    return int(order[min(j, m - 1)]), order, C, m, r
 
 
 # ---------------------------------------------------------------- the model

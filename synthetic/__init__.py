@@ -17,7 +17,8 @@ Drawing rule (one reading, since the pages fix no seeds):
   * non-norm tensors (projection weights, q/k/v biases, the embedding) are
     float32 standard normals times 0.02; norm weights are exactly 1;
   * bf16 models store the nearest bf16 (round-to-nearest-even) of that draw,
-    as raw uint16 bit patterns; fp32 models store the float32 draw;
+    as raw uint16 bit patterns; fp16 models the nearest float16; fp32 models
+    the float32 draw;
   * token ids are uniform integers in [0, vocab) from default_rng(seed + 1).
 """
 from __future__ import annotations
@@ -44,7 +45,7 @@ class ModelShape:
     head_dim: int
     intermediate: int
     vocab: int
-    dtype: str = "bf16"          # storage and GEMM-input dtype: "bf16" or "f32"
+    dtype: str = "bf16"          # weight storage: "bf16", "f16" or "f32"
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
     qkv_bias: bool = True
@@ -93,7 +94,13 @@ QWEN25_05B = ModelShape("qwen2.5-0.5b", n_layers=24, hidden=896, n_heads=14, n_k
 QWEN25_15B = ModelShape("qwen2.5-1.5b", n_layers=28, hidden=1536, n_heads=12, n_kv_heads=2,
                         head_dim=128, intermediate=8960, vocab=151936)
 
-MODEL_SHAPES = {m.name: m for m in (TINY, QWEN25_05B, QWEN25_15B)}
+# Qwen2.5-Coder-7B ("LLM Speedrun: Architecture", "Plugging in the specific
+# parameters" and the harness listing's config): 28/4 heads of 128, a
+# separate (untied) LM head over a 152064-entry vocabulary.
+QWEN25_CODER_7B = ModelShape("qwen2.5-coder-7b", n_layers=28, hidden=3584, n_heads=28, n_kv_heads=4,
+                             head_dim=128, intermediate=18944, vocab=152064, tie_embeddings=False)
+
+MODEL_SHAPES = {m.name: m for m in (TINY, QWEN25_05B, QWEN25_15B, QWEN25_CODER_7B)}
 
 # The five workloads.  The 1.5B runs leave the cache size open; the readings
 # are 1024 for the 512+256 run and 8192+128 = 8320 for the long-context run.
@@ -105,6 +112,9 @@ WORKLOADS: Dict[str, Workload] = {
                              decode_steps=32, max_seq=4096),
     "1.5b-longctx": Workload("1.5b-longctx", QWEN25_15B, batch=32, prompt_len=8192,
                              decode_steps=128, max_seq=8320),
+    # the second model family the pages name (not one of the five graded
+    # workloads): one sequence, as the speedrun harness runs it
+    "coder-7b": Workload("coder-7b", QWEN25_CODER_7B, batch=1, prompt_len=512, decode_steps=128, max_seq=1024),
 }
 
 _LAYER_TENSORS = (
@@ -170,7 +180,11 @@ def _draw(m: ModelShape, name: str, index: int, seed: int) -> np.ndarray:
         rng = np.random.default_rng(np.random.SeedSequence([seed, index]))
         f = rng.standard_normal(size=shape, dtype=np.float32)
         f *= np.float32(0.02)
-    return f32_to_bf16_bits(f) if m.dtype == "bf16" else f
+    if m.dtype == "bf16":
+        return f32_to_bf16_bits(f)
+    if m.dtype == "f16":
+        return f.astype(np.float16)                  # nearest fp16 (ties to even)
+    return f
 
 
 def make_weights(m: ModelShape, seed: int = 0, only=None) -> Dict[str, np.ndarray]:

@@ -10,7 +10,7 @@ import synthetic as S
 # margin above which the greedy token must match exactly.  The bf16-weight
 # mode computes with fp16 operands and fp32 accumulation; fp32 mode is fp32
 # throughout.
-LOGIT_TOL = {"f32": 1e-3, "bf16": 5e-2}
+LOGIT_TOL = {"f32": 1e-3, "bf16": 5e-2, "f16": 5e-2}
 TOKEN_MARGIN = 0.1
 # fp32 mode is also held to exact tokens wherever the margin exceeds twice the
 # logit tolerance (a flip there would need an error above the tolerance).
@@ -25,7 +25,8 @@ def with_random_norms(W, m, seed=21):
     for k in W:
         if k.endswith("layernorm.weight") or k == "model.norm.weight":
             f = (1.0 + 0.3 * rng.standard_normal(W[k].shape)).astype(np.float32)
-            W[k] = S.f32_to_bf16_bits(f) if W[k].dtype == np.uint16 else f
+            W[k] = (S.f32_to_bf16_bits(f) if W[k].dtype == np.uint16
+                    else f.astype(W[k].dtype))
     return W
 
 

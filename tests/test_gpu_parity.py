@@ -41,6 +41,9 @@ SMALL = {
     "bf16-hd64-mqa": (S.ModelShape("s64", 2, 384, 6, 1, 64, 1024, 777), 2, 70, 5, 96),
     "bf16-hd128": (S.ModelShape("s128", 2, 512, 4, 2, 128, 1536, 2049), 2, 130, 4, 160),
     "f32-hd64": (S.ModelShape("f64", 2, 192, 6, 3, 64, 448, 513, dtype="f32"), 2, 21, 5, 32),
+    # fp16 weights (the same kernels; the caller's fp16 tensors are scaled like bf16 ones)
+    "f16-hd128": (S.ModelShape("h128", 2, 512, 4, 2, 128, 1536, 2049, dtype="f16"), 2, 130, 4, 160),
+    "f16-hd64-g7-b5": (S.ModelShape("h64g7", 2, 448, 14, 2, 64, 896, 1100, dtype="f16"), 5, 53, 6, 96),
     # more than two rows: the batched decode path (split-KV attention on the
     # matrix cores, g = 7 as in the 0.5B model; unsplit gate/up with SwiGLU)
     "bf16-hd64-g7-b5": (S.ModelShape("s64g7", 2, 448, 14, 2, 64, 896, 1100), 5, 53, 6, 96),
@@ -61,6 +64,15 @@ SMALL = {
     # weights; one row crosses the 256-key switch to the split-KV pair
     "bf16-h1536-b1": (S.ModelShape("s1536", 2, 1536, 12, 2, 128, 8960, 3001), 1, 250, 10, 272),
     "bf16-h1536-b2": (S.ModelShape("s1536", 2, 1536, 12, 2, 128, 8960, 3001), 2, 61, 5, 72),
+    # the Coder-7B widths (hidden 3584, 28/4 heads of 128, intermediate 18944,
+    # untied LM head) in two layers: one row across the 256-key switch (norm
+    # prologues over K = 3584, the MLP as two projections since hidden exceeds
+    # the one-kernel MLP), and five rows (batched projections, g = 7 at head
+    # dim 128)
+    "bf16-h3584-g7-b1": (S.ModelShape("s3584", 2, 3584, 28, 4, 128, 18944, 5003, tie_embeddings=False),
+                         1, 250, 10, 272),
+    "bf16-h3584-g7-b5": (S.ModelShape("s3584", 2, 3584, 28, 4, 128, 18944, 5003, tie_embeddings=False),
+                         5, 40, 5, 64),
 }
 
 
@@ -202,11 +214,14 @@ def test_error_paths(Q):
         m.timing_enable("no_such_kernel")
 
 
-@pytest.mark.parametrize("name", ["0.5b", "1.5b"])
+@pytest.mark.parametrize("name", ["0.5b", "1.5b", "0.5b-f16"])
 def test_full_workload(Q, name):
     """The workload at full size against the oracle, with norm weights drawn
-    around 1 (the workloads' own norms are exactly 1)."""
-    w = S.WORKLOADS[name]
+    around 1 (the workloads' own norms are exactly 1); "0.5b-f16" is the 0.5B
+    workload with fp16 weights."""
+    w = S.WORKLOADS[name.replace("-f16", "")]
+    if name.endswith("-f16"):
+        w = w.replace(model=w.model.replace(dtype="f16"))
     say(f"{name}: generating weights")
     W = with_random_norms(S.make_weights(w.model, w.weight_seed), w.model)
     ids = S.make_ids(w)
@@ -216,8 +231,28 @@ def test_full_workload(Q, name):
     m.close()
     say(f"{name}: oracle teacher-forced")
     om = O.OracleModel(w.model, W)
-    err, n = compare_row(om, ids[0], toks[0], logits[0], "bf16", name)
+    err, n = compare_row(om, ids[0], toks[0], logits[0], w.model.dtype, name)
     say(f"{name}: max err {err:.3e} over {w.decode_steps + 1} steps; {n} with margin > 0.1")
+
+
+def test_full_workload_coder7b(Q):
+    """The second model family: Qwen2.5-Coder-7B shapes with an untied LM head
+    (28 layers, 15 GB of bf16 weights), one sequence of 512 prompt tokens and
+    128 decode steps, against the oracle at every step, norm weights drawn
+    around 1."""
+    w = S.WORKLOADS["coder-7b"]
+    say("coder-7b: generating weights")
+    W = with_random_norms(S.make_weights(w.model, w.weight_seed), w.model)
+    ids = S.make_ids(w)
+    say(f"coder-7b: GPU B={w.batch} P={w.prompt_len} D={w.decode_steps}")
+    m = make(Q, w.model, W, w.batch, w.max_seq)
+    toks, logits = gpu_generate(m, ids, w.decode_steps)
+    m.check_numerics()
+    m.close()
+    say("coder-7b: oracle teacher-forced")
+    om = O.OracleModel(w.model, W)
+    err, n = compare_row(om, ids[0], toks[0], logits[0], "bf16", "coder-7b")
+    say(f"coder-7b: max err {err:.3e} over {w.decode_steps + 1} steps; {n} with margin > 0.1")
 
 
 LONG = {

@@ -67,6 +67,13 @@ def test_bf16_reading_is_exact_vs_torch():
     assert np.array_equal(O.decode_storage(bits), via_torch.double().numpy())
 
 
+def test_f16_reading_is_exact_vs_torch():
+    rng = np.random.default_rng(6)
+    f = (rng.standard_normal(4096).astype(np.float32) * np.float32(0.02)).astype(np.float16)
+    f[:3] = [0.0, 6.0e-8, 65504.0]                            # zero, smallest subnormal, largest normal
+    assert np.array_equal(O.decode_storage(f), torch.from_numpy(f).double().numpy())
+
+
 # ------------------------------------------------------------ RoPE
 def test_rope_matches_complex_multiplication():
     """Split-half RoPE is multiplication of (x_i + i x_{i+hd/2}) by exp(i pos f_i)."""
@@ -350,3 +357,55 @@ def test_pins_catch_planted_mistakes(monkeypatch, name, fake):
     om = O.OracleModel(m, W)
     got = om.forward(ids, 0, om.new_cache(16), logits_rows=slice(0, 13))
     assert np.abs(got - _hf_logits(m, W, ids)).max() > 100 * HF_TOL
+
+
+# ------------------------------------------------------------ sampling
+def test_philox_matches_numpy():
+    """The oracle's Philox-4x64-10 against numpy's bit generator of the same
+    name (numpy's first block uses counter + 1)."""
+    for key, ctr in (([5, 7], [0, 0, 0, 0]), ([2 ** 64 - 1, 3], [41, 9, 0, 2 ** 63])):
+        g = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=np.array(ctr, dtype=np.uint64))
+        want = [int(x) for x in g.random_raw(4)]
+        c1 = list(ctr)
+        c1[0] = (c1[0] + 1) % 2 ** 64
+        assert O.philox4x64_10(c1, key) == want
+
+
+def test_sampling_draw_range():
+    us = [O.sampling_draw(3, b, n) for b in range(4) for n in range(200)]
+    assert all(0.0 <= u < 1.0 for u in us)
+    assert abs(np.mean(us) - 0.5) < 0.05 and len(set(us)) == len(us)
+
+
+def test_sample_token_special_cases():
+    rng = np.random.default_rng(9)
+    lg = rng.standard_normal(50)
+    am = int(np.argmax(lg))
+    for u in (0.0, 0.3, 0.999):
+        assert O.sample_token(lg, 1.0, 1, 1.0, u)[0] == am          # top_k = 1 is greedy
+        assert O.sample_token(lg, 1e-4, 50, 1.0, u)[0] == am         # a cold temperature too
+        assert O.sample_token(lg, 0.7, 50, 1e-9, u)[0] == am         # top_p -> 0 keeps one token
+    tie = np.array([0.0, 2.0, 2.0, 1.0])
+    assert O.sample_token(tie, 1.0, 1, 1.0, 0.5)[0] == 1             # equal maxima: lower index
+
+
+def test_sample_token_is_the_inverse_cdf_of_the_filtered_softmax():
+    """Brute force: a fine grid of draws u maps to each kept token with the
+    frequency of its renormalised probability, and top-p keeps the shortest
+    prefix reaching top_p."""
+    lg = np.log(np.array([0.1, 0.5, 0.05, 0.3, 0.05]))
+    # top_k = 4 drops one 0.05 (index 4, the higher index of the tie)
+    _, order, C, m, _ = O.sample_token(lg, 1.0, 4, 1.0, 0.0)
+    assert list(order) == [1, 3, 0, 2] and m == 4
+    # top_p = 0.8 of the top-4 mass 0.95 is 0.76: prefix sums 0.5, 0.8, ... reach it at the second
+    _, _, C, m, _ = O.sample_token(lg, 1.0, 4, 0.8, 0.0)
+    assert m == 2
+    grid = (np.arange(100000) + 0.5) / 100000
+    toks = np.array([O.sample_token(lg, 1.0, 4, 0.8, u)[0] for u in grid])
+    assert set(toks) == {1, 3}
+    assert abs((toks == 1).mean() - 0.5 / 0.8) < 1e-4
+    # temperature 2 flattens: weights p ** (1 / 2)
+    p2 = np.sqrt(np.array([0.1, 0.5, 0.05, 0.3, 0.05]))
+    toks = np.array([O.sample_token(lg, 2.0, 5, 1.0, u)[0] for u in grid[::10]])
+    for i in range(5):
+        assert abs((toks == i).mean() - p2[i] / p2.sum()) < 2e-4

@@ -39,8 +39,24 @@ def test_ids_uniform_in_vocab():
 
 def test_workload_table():
     W = S.WORKLOADS
-    assert [W[k].batch for k in W] == [1, 1, 1, 8, 32]
-    assert [W[k].prompt_len for k in W] == [16, 128, 512, 2048, 8192]
-    assert [W[k].decode_steps for k in W] == [8, 128, 256, 32, 128]
+    five = ["tiny", "0.5b", "1.5b", "1.5b-prefill", "1.5b-longctx"]
+    assert [W[k].batch for k in five] == [1, 1, 1, 8, 32]
+    assert [W[k].prompt_len for k in five] == [16, 128, 512, 2048, 8192]
+    assert [W[k].decode_steps for k in five] == [8, 128, 256, 32, 128]
+    assert set(W) == set(five) | {"coder-7b"}
     for w in W.values():
         assert w.prompt_len + w.decode_steps <= w.max_seq
+
+
+def test_coder7b_shape_matches_the_listed_config():
+    """The 7B workload's shape is the config the speedrun page prints
+    (tests/golden/qwen25_coder_7b_config.json), with an untied LM head."""
+    import json
+    import os
+    c = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "qwen25_coder_7b_config.json")))
+    m = S.WORKLOADS["coder-7b"].model
+    assert (m.n_layers, m.hidden, m.n_heads, m.n_kv_heads, m.head_dim, m.intermediate, m.vocab) == (
+        c["num_layers"], c["hidden_size"], c["num_heads"], c["num_kv_heads"], c["head_dim"],
+        c["intermediate_size"], c["vocab_size"])
+    assert m.rope_theta == c["rope_theta"] and m.rms_eps == c["rms_norm_eps"]
+    assert not m.tie_embeddings and "lm_head.weight" in S.tensor_names(m)
