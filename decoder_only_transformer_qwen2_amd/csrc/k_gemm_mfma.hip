@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   constexpr int NWV = WVM * WVN;                  // waves
   constexpr int XT = TBM / WVM / 16, YT = TBN / WVN / 16;   // MFMA tiles per wave
   constexpr int QA = TBM / 16 / NWV, QB = TBN / 16 / NWV;   // load instructions per wave and stage
-  static_assert(TBN / WVN == 64, "a wave's 64 columns hold two gate/up pairs");
+  static_assert((TBN / WVN) % (2 * GU_BLOCK) == 0, "a wave's columns hold whole gate/up pairs");
   __shared__ f16x8 sA[NS][TBM * 4];
   __shared__ f16x8 sB[NS][TBN * 4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -258,14 +258,19 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
     for (int y = 0; y < YT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // wait until at most n stages of this wave's loads are still in flight
+  // s_waitcnt immediate: vmcnt is 6 bits, [3:0] at bit 0 and [5:4] at bit 14;
+  // expcnt and lgkmcnt at their maxima (no wait on them)
   auto wait_stages = [&](int n) {
-    static_assert(2 * PER_STAGE <= 15, "vmcnt field");
+    static_assert(2 * PER_STAGE <= 63, "vmcnt field");
+    constexpr unsigned kRest = (7u << 4) | (15u << 8);
+    constexpr unsigned kTwo = ((2 * PER_STAGE) & 15) | (((2 * PER_STAGE) >> 4) << 14) | kRest;
+    constexpr unsigned kOne = (PER_STAGE & 15) | ((PER_STAGE >> 4) << 14) | kRest;
     if (n >= 2)
-      __builtin_amdgcn_s_waitcnt(((2 * PER_STAGE) & 15) | (7 << 4) | (15 << 8));
+      __builtin_amdgcn_s_waitcnt(kTwo);
     else if (n == 1)
-      __builtin_amdgcn_s_waitcnt((PER_STAGE & 15) | (7 << 4) | (15 << 8));
+      __builtin_amdgcn_s_waitcnt(kOne);
     else
-      __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+      __builtin_amdgcn_s_waitcnt(kRest);
   };
   auto read_frags = [&](int kt, f16x8 (&fa)[XT], f16x8 (&fb)[YT]) {
     const int st = kt % NS;
@@ -276,7 +281,7 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int y = 0; y < YT; ++y) {
-      const int row = wn * 64 + y * 16 + i;
+      const int row = wn * (TBN / WVN) + y * 16 + i;
       fb[y] = sB[st][row * 4 + (g ^ lds_swz(row))];
     }
   };
@@ -338,7 +343,7 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   }
 
   // acc[x][y]: lane (i, g) holds rows 4g..4g+3 of column i of MFMA tile (x, y)
-  const int rw0 = m0 + wm * (TBM / WVM), cw0 = n0 + wn * 64;
+  const int rw0 = m0 + wm * (TBM / WVM), cw0 = n0 + wn * (TBN / WVN);
   if (gridDim.z > 1) {
     float *ws = a.ws + (int64_t)blockIdx.z * a.M * a.N;
 #pragma unroll
@@ -360,7 +365,7 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
     for (int x = 0; x < XT; ++x)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
+      for (int p = 0; p < YT / 2; ++p) {
         const int f = cw0 / 2 + p * GU_BLOCK + i;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
