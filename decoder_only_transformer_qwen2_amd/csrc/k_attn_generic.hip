@@ -27,16 +27,21 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(AttnArgs a) {
   const int t = active ? (int)(gw / a.n_heads) : 0, h = active ? (int)(gw % a.n_heads) : 0;
   const int hd = a.head_dim;
   const int g = a.n_heads / a.n_kv_heads, j = h / g;
-  const int b = t / a.rows_per_seq;
-  const int pos = (a.pos0_dev ? *a.pos0_dev : a.pos0) + (t % a.rows_per_seq);
+  int b, pos;
+  if (a.rag.cu) {
+    b = ragged_seq(a.rag.cu, a.rag.n, t);
+    pos = t - a.rag.cu[b];
+  } else {
+    b = t / a.rows_per_seq;
+    pos = (a.pos0_dev ? a.pos0_dev[b] : a.pos0) + (t % a.rows_per_seq);
+  }
   const int qd = a.n_heads * hd;
   const T *q = (const T *)a.q + (int64_t)t * qd + h * hd;
   for (int d = lane; d < hd; d += 64) qs[wv][d] = to_f32(q[d]) * a.softmax_scale;
   __syncthreads();
   if (!active) return;
-  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * hd;
-  const T *K = (const T *)a.k_cache + head_base;
-  const T *V = (const T *)a.v_cache + head_base;
+  const T *K = (const T *)a.k_cache;
+  const T *V = (const T *)a.v_cache;
 
   float m = -INFINITY, l = 0.f;
   float o0 = 0.f, o1 = 0.f;                   // dims lane and lane + 64
@@ -45,7 +50,7 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(AttnArgs a) {
     const int tau = c0 + lane;
     float s = -INFINITY;
     if (tau < n_keys) {
-      const T *kr = K + (int64_t)tau * hd;
+      const T *kr = K + kv_offset(a.kv, a.n_kv_heads, hd, b, j, tau);
       float dot = 0.f;
       for (int d = 0; d < hd; ++d) dot = fmaf(qs[wv][d], to_f32(kr[d]), dot);
       s = dot;
@@ -60,7 +65,7 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(AttnArgs a) {
     const int cnt = min(64, n_keys - c0);
     for (int u = 0; u < cnt; ++u) {
       const float pu = __shfl(p, u, 64);
-      const T *vr = V + (int64_t)(c0 + u) * hd;
+      const T *vr = V + kv_offset(a.kv, a.n_kv_heads, hd, b, j, c0 + u);
       if (lane < hd) o0 = fmaf(pu, to_f32(vr[lane]), o0);
       if (lane + 64 < hd) o1 = fmaf(pu, to_f32(vr[lane + 64]), o1);
     }

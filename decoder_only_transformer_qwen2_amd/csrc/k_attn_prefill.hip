@@ -56,25 +56,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, g = lane >> 4;
   const int nq = a.n_heads, grp = a.n_heads / a.n_kv_heads;
-  const int P = a.rows_per_seq;
   // work item: heaviest query tiles first; the g heads of a group adjacent,
-  // and adjacent items on one XCD (workgroups go round-robin over 8 XCDs)
-  const int total = n_qt * nq * (a.T / P);
+  // and adjacent items on one XCD (workgroups go round-robin over 8 XCDs).
+  // Ragged batches take (sequence, query tile) from a list in that order.
+  const int total = a.tiles ? a.n_tiles * nq : n_qt * nq * (a.T / a.rows_per_seq);
   const int L = blockIdx.x;
   const int per_x = (total + 7) / 8;
   int w = (L % 8) * per_x + L / 8;
   if (w >= total) return;
   const int h = w % nq;
-  const int qt = n_qt - 1 - (w / nq) % n_qt;
-  const int b = w / (nq * n_qt);
+  int qt, b, P, r0;
+  if (a.tiles) {
+    const int it = a.tiles[w / nq];
+    b = it >> 16;
+    qt = it & 0xffff;
+    r0 = a.rag.cu[b];
+    P = a.rag.cu[b + 1] - r0;
+  } else {
+    P = a.rows_per_seq;
+    qt = n_qt - 1 - (w / nq) % n_qt;
+    b = w / (nq * n_qt);
+    r0 = b * P;
+  }
   const int j = h / grp;
   const int q0 = qt * BQ + wave * 32;                 // this wave's first query
   const int qd = nq * HD;
 
-  const f16 *Q = (const f16 *)a.q + (int64_t)b * P * qd + h * HD;
-  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
-  const f16 *Kc = (const f16 *)a.k_cache + head_base;
-  const f16 *Vc = (const f16 *)a.v_cache + head_base;
+  const f16 *Q = (const f16 *)a.q + (int64_t)r0 * qd + h * HD;
+  const f16 *Kc = (const f16 *)a.k_cache;
   const f16x8 zero8 = {};
 
   // queries as B operands: lane (i, g) holds query q0 + 16t + i, dims 32s + 8g .. +8
@@ -101,13 +110,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   // K rows [key][d] from the cache, V^T rows [d][key] from the transposed
   // copy (rows of round_up(P, 64) keys, zero past P): both as 16-byte vectors
   const int PP = (P + BKEY - 1) / BKEY * BKEY;
-  const f16 *Vt = (const f16 *)a.v_t + ((int64_t)b * a.n_kv_heads + j) * HD * PP;
+  const int64_t vt_seq = a.tiles ? (int64_t)a.rag.pcu[b] : (int64_t)b * PP;   // padded rows before sequence b
+  const f16 *Vt = (const f16 *)a.v_t + (vt_seq * a.n_kv_heads + (int64_t)j * PP) * HD;
+  static_assert(BKEY == kKvBlock, "a key tile is one cache block");
   auto gload = [&](int kb) {
+    const f16 *Kt = Kc + kv_offset(a.kv, a.n_kv_heads, HD, b, j, kb * BKEY);
 #pragma unroll
     for (int t = 0; t < VPT; ++t) {
       const int v = tid + 256 * t;
-      const int key = kb * BKEY + v / (HD / 8), c = (v % (HD / 8)) * 8;
-      rk[t] = key < P ? *reinterpret_cast<const f16x8 *>(Kc + (int64_t)key * HD + c) : zero8;
+      const int kk = v / (HD / 8), key = kb * BKEY + kk, c = (v % (HD / 8)) * 8;
+      rk[t] = key < P ? *reinterpret_cast<const f16x8 *>(Kt + (int64_t)kk * HD + c) : zero8;
       const int d = v / (BKEY / 8), kc = (v % (BKEY / 8)) * 8;
       rv[t] = *reinterpret_cast<const f16x8 *>(Vt + (int64_t)d * PP + kb * BKEY + kc);
     }
@@ -235,7 +247,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   }
 
   // O^T: lane (i, g) holds dims 16d + 4g + r of query q0 + 16t + i
-  f16 *O = (f16 *)a.o + (int64_t)b * P * qd + h * HD;
+  f16 *O = (f16 *)a.o + (int64_t)r0 * qd + h * HD;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int q = q0 + 16 * t + i;
@@ -256,17 +268,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
 bool attn_prefill_supported(int head_dim) { return head_dim == 32 || head_dim == 64 || head_dim == 128; }
 
 // 64 keys x 64 dims per workgroup through LDS, so that both the reads (rows
-// of the cache) and the writes (rows of V^T) are contiguous.
-__global__ void __launch_bounds__(256) transpose_v_kernel(const f16 *v_cache, int n_kv_heads, int max_seq, int hd,
-                                                          int P, int PP, f16 *v_t) {
+// of the cache) and the writes (rows of V^T) are contiguous.  Sequence b is
+// P keys long (ragged: cu[b+1] - cu[b]); its V^T rows are round_up(P, 64)
+// long and start at (padded rows before b) * nkv * hd.
+__global__ void __launch_bounds__(256) transpose_v_kernel(const f16 *v_cache, KvMap kv, RaggedRows rag, int n_kv_heads,
+                                                          int hd, int P_eq, f16 *v_t) {
   __shared__ f16 tile[64][66];
-  const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64, bj = blockIdx.z;
-  const f16 *src = v_cache + (int64_t)bj * max_seq * hd;
-  f16 *dst = v_t + (int64_t)bj * hd * PP;
+  const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+  const int b = blockIdx.z / n_kv_heads, j = blockIdx.z % n_kv_heads;
+  const int P = rag.cu ? rag.cu[b + 1] - rag.cu[b] : P_eq;
+  const int PP = (P + 63) / 64 * 64;
+  if (t0 >= PP) return;                         // past this sequence (ragged: shorter than the longest)
+  const int64_t seq_rows = rag.cu ? (int64_t)rag.pcu[b] : (int64_t)b * PP;
+  const f16 *src = v_cache + kv_offset(kv, n_kv_heads, hd, b, j, t0);   // keys t0 .. t0 + 63: one cache block
+  f16 *dst = v_t + (seq_rows * n_kv_heads + (int64_t)j * PP) * hd;
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int r = e / 64, c = e % 64;            // key r, dim c
+    const int r = e / 64, c = e % 64;            // key t0 + r, dim d0 + c
     const int key = t0 + r, d = d0 + c;
-    tile[r][c] = (key < P && d < hd) ? src[(int64_t)key * hd + d] : (f16)0.f;
+    tile[r][c] = (key < P && d < hd) ? src[(int64_t)r * hd + d] : (f16)0.f;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
@@ -276,22 +295,28 @@ __global__ void __launch_bounds__(256) transpose_v_kernel(const f16 *v_cache, in
   }
 }
 
-hipError_t launch_transpose_v(hipStream_t s, const void *v_cache, int B, int n_kv_heads, int max_seq, int head_dim,
-                              int P, void *v_t) {
-  if (P <= 0) return hipSuccess;
-  const int PP = (P + BKEY - 1) / BKEY * BKEY;
+hipError_t launch_transpose_v(hipStream_t s, const void *v_cache, const KvMap &kv, const RaggedRows &rag, int B,
+                              int n_kv_heads, int head_dim, int P, int max_len, void *v_t) {
+  if (max_len <= 0) return hipSuccess;
+  const int PP = (max_len + BKEY - 1) / BKEY * BKEY;
   dim3 grid(PP / 64, (head_dim + 63) / 64, B * n_kv_heads);
-  QW_LAUNCH((transpose_v_kernel), dim3(grid), dim3(256), 0, s, (const f16 *)v_cache, n_kv_heads, max_seq, head_dim,
-            P, PP, (f16 *)v_t);
+  QW_LAUNCH((transpose_v_kernel), dim3(grid), dim3(256), 0, s, (const f16 *)v_cache, kv, rag, n_kv_heads, head_dim,
+            P, (f16 *)v_t);
   return hipGetLastError();
 }
 
 hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a) {
   if (a.T <= 0) return hipSuccess;
-  if (a.pos0_dev || a.pos0 != 0 || a.T % a.rows_per_seq) return hipErrorInvalidValue;
-  const int P = a.rows_per_seq, B = a.T / P;
-  const int n_qt = (P + BQ - 1) / BQ;
-  const int total = n_qt * a.n_heads * B;
+  if (a.pos0_dev || a.pos0 != 0) return hipErrorInvalidValue;
+  int n_qt = 0, total;
+  if (a.tiles) {
+    if (!a.rag.cu || a.n_tiles < 1) return hipErrorInvalidValue;
+    total = a.n_tiles * a.n_heads;
+  } else {
+    if (a.T % a.rows_per_seq) return hipErrorInvalidValue;
+    n_qt = (a.rows_per_seq + BQ - 1) / BQ;
+    total = n_qt * a.n_heads * (a.T / a.rows_per_seq);
+  }
   const int per_x = (total + 7) / 8;
   dim3 grid(per_x * 8);
   switch (a.head_dim) {

@@ -91,12 +91,21 @@ hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows
 // ---------------------------------------------------------------- bias + RoPE + cache write
 // One block per row.  Work item i enumerates (head, pair) over the q heads,
 // then the k heads (both rotated), then the v heads (copied).
+// Rows of equal-length sequences (row t is position t % rows_per_seq of
+// sequence t / rows_per_seq, after pos0 or pos0_dev[b]), or ragged ones
+// (sequence s holds rows cu[s] .. cu[s+1]-1 from position 0).
 template <typename T>
 __global__ void __launch_bounds__(256) rope_cache_kernel(RopeCacheArgs a) {
   const int t = blockIdx.x;
   const int half = a.head_dim >> 1;
-  const int b = t / a.rows_per_seq;
-  const int pos = (a.pos0_dev ? *a.pos0_dev : a.pos0) + (t % a.rows_per_seq);
+  int b, pos;
+  if (a.rag.cu) {
+    b = ragged_seq(a.rag.cu, a.rag.n, t);
+    pos = t - a.rag.cu[b];
+  } else {
+    b = t / a.rows_per_seq;
+    pos = (a.pos0_dev ? a.pos0_dev[b] : a.pos0) + (t % a.rows_per_seq);
+  }
   const int qd = a.n_heads * a.head_dim, kvd = a.n_kv_heads * a.head_dim;
   const int ncols = qd + 2 * kvd;
   const float *row = a.qkv + (int64_t)t * ncols;
@@ -122,7 +131,7 @@ __global__ void __launch_bounds__(256) rope_cache_kernel(RopeCacheArgs a) {
       const bool is_k = head < a.n_heads + a.n_kv_heads;
       const int j = is_k ? head - a.n_heads : head - a.n_heads - a.n_kv_heads;
       T *cache = (T *)(is_k ? a.k_cache : a.v_cache);
-      T *dst = cache + (((int64_t)b * a.n_kv_heads + j) * a.max_seq + pos) * a.head_dim;
+      T *dst = cache + kv_offset(a.kv, a.n_kv_heads, a.head_dim, b, j, pos);
       dst[i] = from_f32<T>(re);
       dst[i + half] = from_f32<T>(im);
     }
@@ -167,7 +176,7 @@ __global__ void __launch_bounds__(256) argmax_kernel(const float *__restrict__ l
     for (int w = 1; w < 4; ++w)
       if (sb[w] > best || (sb[w] == best && si[w] < bi)) { best = sb[w]; bi = si[w]; }
     next_ids[blockIdx.x] = (bi == 0x7fffffff) ? 0 : bi;     // all-NaN row: 0
-    if (pos_dev && blockIdx.x == 0) *pos_dev += pos_add;
+    if (pos_dev) pos_dev[blockIdx.x] += pos_add;
   }
 }
 
@@ -179,7 +188,6 @@ hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab
   return hipGetLastError();
 }
 
-__global__ void set_int_kernel(int *p, int v) { *p = v; }
 
 // Copies around the captured decode graph: caller ids into the staging row the
 // graph reads, and the graph's next ids (and logits, when asked) out to the
@@ -246,8 +254,40 @@ hipError_t launch_copy_rows(hipStream_t s, void *dst, int64_t dst_stride, const 
   return hipGetLastError();
 }
 
-hipError_t launch_set_int(hipStream_t s, int *p, int v) {
-  set_int_kernel<<<1, 1, 0, s>>>(p, v);
+struct PutChunk {
+  int n;
+  int idx[kPutChunk], val[kPutChunk];
+};
+
+__global__ void __launch_bounds__(256) put_ints_kernel(int *dst, PutChunk c) {
+  const int k = threadIdx.x;
+  if (k < c.n) dst[c.idx[k]] = c.val[k];
+}
+
+hipError_t launch_put_ints(hipStream_t s, int *dst, const int *idx, const int *val, int n) {
+  for (int k0 = 0; k0 < n; k0 += kPutChunk) {
+    PutChunk c;
+    c.n = n - k0 < kPutChunk ? n - k0 : kPutChunk;
+    for (int k = 0; k < c.n; ++k) {
+      c.idx[k] = idx[k0 + k];
+      c.val[k] = val[k0 + k];
+    }
+    put_ints_kernel<<<1, 256, 0, s>>>(dst, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+__global__ void __launch_bounds__(256) gather_last_rows_kernel(float *dst, const float *src, const int *cu, int H) {
+  const int k = blockIdx.x;
+  const float *row = src + (int64_t)(cu[k + 1] - 1) * H;
+  for (int c = threadIdx.x; c < H; c += 256) dst[(int64_t)k * H + c] = row[c];
+}
+
+hipError_t launch_gather_last_rows(hipStream_t s, float *dst, const float *src, const int *cu, int n, int H) {
+  if (n <= 0) return hipSuccess;
+  gather_last_rows_kernel<<<n, 256, 0, s>>>(dst, src, cu, H);
   return hipGetLastError();
 }
 

@@ -177,7 +177,7 @@ __global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, i
 }
 
 // Reduce the LM head's per-block (max, index) pairs: lowest index among equal
-// maxima.  Advances the device-side position.
+// maxima.  Advances the row's device-side position.
 __global__ void __launch_bounds__(256) dec_end_kernel(const float *pv, const int *pi, int nblk, int32_t *next,
                                                       int *pos_dev) {
   const int b = blockIdx.x;
@@ -201,7 +201,7 @@ __global__ void __launch_bounds__(256) dec_end_kernel(const float *pv, const int
     for (int w = 1; w < 4; ++w)
       if (sb[w] > best || (sb[w] == best && si[w] < bi)) { best = sb[w]; bi = si[w]; }
     next[b] = (bi == 0x7fffffff) ? 0 : bi;
-    if (b == 0) *pos_dev += 1;
+    pos_dev[b] += 1;
   }
 }
 
@@ -999,7 +999,7 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
   const int slot = lane / LPK, dl = lane % LPK, d0 = dl * 8;
   const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int S = gridDim.x;
-  const int pos = *a.pos_dev;
+  const int pos = a.pos_dev[b];
   const int n_keys = pos + 1;
   int per = (n_keys + S - 1) / S;
   per = (per + NW * KPW - 1) / (NW * KPW) * (NW * KPW);
@@ -1010,9 +1010,8 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
   // the heads this wave carries: h_lo + t for t < nh
   const int h_lo = KEYPAR ? 0 : wave * WH;
   const int nh = KEYPAR ? G : max(0, min(WH, G - h_lo));
-  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
-  f16 *Kc = (f16 *)a.k_cache + head_base;
-  f16 *Vc = (f16 *)a.v_cache + head_base;
+  f16 *Kc = (f16 *)a.k_cache;
+  f16 *Vc = (f16 *)a.v_cache;
 
   // cached keys of this split, U loads per lane in flight: the first batch
   // goes out before the prologue (it does not depend on it), each next batch
@@ -1027,7 +1026,8 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
       const int t = kb + u * KSTEP + slot;
       // out-of-range keys get weight 0; their values must be finite
       const int tc = min(t, max(kc_end - 1, 0));
-      const f16x8 kv = load8(Kc + (int64_t)tc * HD + d0), vv = load8(Vc + (int64_t)tc * HD + d0);
+      const int64_t off = kv_offset(a.kv, a.n_kv_heads, HD, b, j, tc) + d0;
+      const f16x8 kv = load8(Kc + off), vv = load8(Vc + off);
       kr[u] = t < kc_end ? kv : f16x8{};
       vr[u] = t < kc_end ? vv : f16x8{};
     }
@@ -1067,8 +1067,9 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
   }
   __syncthreads();
   if (has_new && tid < HD) {
-    Kc[(int64_t)pos * HD + tid] = (f16)s_k[tid];
-    Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
+    const int64_t np = kv_offset(a.kv, a.n_kv_heads, HD, b, j, pos);
+    Kc[np + tid] = (f16)s_k[tid];
+    Vc[np + tid] = (f16)s_v[tid];
   }
 
   float q[WH][8];
@@ -1264,7 +1265,7 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
   const int i = lane & 15, g = lane >> 4;
   const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int S = gridDim.x;
-  const int pos = *a.pos_dev;
+  const int pos = a.pos_dev[b];
   const int n_keys = pos + 1;
   int per = (n_keys + S - 1) / S;
   per = (per + 31) / 32 * 32;
@@ -1276,28 +1277,34 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
   const int ncols = qd + 2 * kvd;
   const long long *acc = a.qkv_fix + (int64_t)b * ncols;
   const float2 *cs = a.rope + (int64_t)pos * HALF;
-  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
-  f16 *Kc = (f16 *)a.k_cache + head_base;
-  f16 *Vc = (f16 *)a.v_cache + head_base;
+  f16 *Kc = (f16 *)a.k_cache;
+  f16 *Vc = (f16 *)a.v_cache;
 
   // the wave's first batch of cached keys is loaded before the prologue, so
   // that it arrives while bias + RoPE run; later batches at the end of each
   // step.  Keys past the split's end load a clamped (valid) row.
   const int kc_end = min(kb1, pos);             // cached keys of this split
   const int klast = max(kc_end - 1, 0);
+  // A batch is 32 keys from a multiple of 32 (clamped to klast), so it lies in
+  // one cache block: its rows are addressed from the block's first position.
+  auto batch_base = [&](int k0) -> int64_t {
+    return kv_offset(a.kv, a.n_kv_heads, HD, b, j, min(k0, klast) & ~(kKvBlock - 1));
+  };
   // K rows of the two 16-key tiles: tile y, row i is key k0 + 8 (i / 4) + 4y + i % 4;
   // V^T operand: lane (i, g) holds dim 16d + i of keys k0 + 8g .. k0 + 8g + 7
   f16x8 kf[2][KS], vf[DT];
-  auto load_kv = [&](int k0) {
+  auto load_kv = [&](int k0, int64_t base) {
+    const int kb = min(k0, klast) & ~(kKvBlock - 1);
+    const f16 *Kb = Kc + base, *Vb = Vc + base;
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
-      const int key = min(k0 + 8 * (i >> 2) + 4 * y + (i & 3), klast);
+      const int key = min(k0 + 8 * (i >> 2) + 4 * y + (i & 3), klast) - kb;
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) kf[y][s2] = load8(Kc + (int64_t)key * HD + 32 * s2 + 8 * g);
+      for (int s2 = 0; s2 < KS; ++s2) kf[y][s2] = load8(Kb + (int64_t)key * HD + 32 * s2 + 8 * g);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const f16 *vrow = Vc + (int64_t)min(k0 + 8 * g + e, klast) * HD + i;
+      const f16 *vrow = Vb + (int64_t)(min(k0 + 8 * g + e, klast) - kb) * HD + i;
 #pragma unroll
       for (int d = 0; d < DT; ++d) vf[d][e] = vrow[16 * d];
     }
@@ -1327,7 +1334,7 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
   const int kfirst = kb0 + 32 * wave;
-  load_kv(kfirst);
+  load_kv(kfirst, batch_base(kfirst));
   __builtin_amdgcn_sched_barrier(0);
 
   clear_share(a.clear, a.clear_n, (b * gridDim.y + j) * S + split, S * gridDim.y * gridDim.z);
@@ -1354,11 +1361,11 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
   }
   lds_barrier();                   // the first key batch stays in flight
   if (has_new && tid < HD) {
-    Kc[(int64_t)pos * HD + tid] = (f16)s_k[tid];
-    Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
+    const int64_t np = kv_offset(a.kv, a.n_kv_heads, HD, b, j, pos);
+    Kc[np + tid] = (f16)s_k[tid];
+    Vc[np + tid] = (f16)s_v[tid];
   }
 
-  const f16x8 zero = {};
   f16x8 qf[KS];
 #pragma unroll
   for (int s2 = 0; s2 < KS; ++s2)
@@ -1371,6 +1378,8 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
   for (int d = 0; d < DT; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int k0 = kfirst; k0 < kc_end; k0 += 32 * NW) {
+    // the next batch's block, looked up while this batch is multiplied
+    const int64_t next_base = batch_base(k0 + 32 * NW);
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int y = 0; y < 2; ++y)
@@ -1408,7 +1417,7 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
       o[d] *= corr;
       o[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[d], pb, o[d], 0, 0, 0);
     }
-    if (k0 + 32 * NW < kc_end) load_kv(k0 + 32 * NW);
+    if (k0 + 32 * NW < kc_end) load_kv(k0 + 32 * NW, next_base);
   }
   if (has_new && wave == 0) {
     // the new key, from LDS: head i's score, then its share of dims 16d + 4g + r
@@ -1695,7 +1704,7 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
   const int i = lane & 15, g = lane >> 4;
   const int rb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int grp = a.n_heads / a.n_kv_heads, j = h / grp;
-  const int pos = *a.pos_dev;
+  const int pos = a.pos_dev[b];
   const int H = a.H;
   const int qd = a.n_heads * HD, kvd = a.n_kv_heads * HD, ncols = qd + 2 * kvd;
   const f16x8 zero = {};
@@ -1729,9 +1738,8 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
       wf[tt][s2] = load8((const f16 *)a.w_o + (int64_t)min(row, H - 1) * qd + h * HD + 32 * s2 + 8 * g);  // rows >= H: never stored
   }
   // cached keys 0 .. pos - 1: first batch before the prologue
-  const int64_t head_base = ((int64_t)b * a.n_kv_heads + j) * a.max_seq * HD;
-  f16 *Kc = (f16 *)a.k_cache + head_base;
-  f16 *Vc = (f16 *)a.v_cache + head_base;
+  f16 *Kc = (f16 *)a.k_cache;
+  f16 *Vc = (f16 *)a.v_cache;
   const int kc_end = pos;
   const int kstart = wave * KPW;
   f16x8 kr[U], vr[U];
@@ -1741,7 +1749,8 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
       const int t = kb + u * KSTEP + slot;
       // out-of-range keys get weight 0; their values must be finite
       const int tc = min(t, max(kc_end - 1, 0));
-      const f16x8 kv = load8(Kc + (int64_t)tc * HD + d0), vv = load8(Vc + (int64_t)tc * HD + d0);
+      const int64_t off = kv_offset(a.kv, a.n_kv_heads, HD, b, j, tc) + d0;
+      const f16x8 kv = load8(Kc + off), vv = load8(Vc + off);
       kr[u] = t < kc_end ? kv : zero;
       vr[u] = t < kc_end ? vv : zero;
     }
@@ -1767,8 +1776,9 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
   }
   lds_barrier();                   // the W_o block and the keys stay in flight
   if (rb == 0 && h % grp == 0 && tid < HD) {
-    Kc[(int64_t)pos * HD + tid] = (f16)s_k[tid];
-    Vc[(int64_t)pos * HD + tid] = (f16)s_v[tid];
+    const int64_t np = kv_offset(a.kv, a.n_kv_heads, HD, b, j, pos);
+    Kc[np + tid] = (f16)s_k[tid];
+    Vc[np + tid] = (f16)s_v[tid];
   }
 
   float q[8], o[8], m = -INFINITY, l = 0.f;

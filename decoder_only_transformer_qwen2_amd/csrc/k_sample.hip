@@ -190,7 +190,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(const float *__r
   const int m = min(k, 1 + block_count(tid < k && C < thr, s_c));
   if (tid == m - 1) s_cm = C;
   __syncthreads();
-  const int n = *pos_dev;             // tokens before the one chosen here
+  const int n = pos_dev[b];           // tokens the sequence holds before the one chosen here
   const uint64_t word = philox_word0((uint64_t)n, (uint64_t)b, seed);
   const float u = (float)(word >> 40) * (1.0f / 16777216.0f);
   const float r = u * s_cm;

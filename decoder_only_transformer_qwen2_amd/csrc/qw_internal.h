@@ -69,6 +69,49 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// ------------------------------------------------------------ KV cache layout
+// Positions of a sequence are grouped in blocks of kKvBlock.  Dense layout
+// (table == NULL): a layer's cache is [max_batch][nkv][max_seq][hd].  Paged
+// layout: a layer's cache is a pool [num_blocks][nkv][kKvBlock][hd], and
+// table[b * blocks_per_seq + p] names the pool block that holds positions
+// kKvBlock p .. kKvBlock p + kKvBlock - 1 of sequence b.
+constexpr int kKvBlock = 64;
+
+struct KvMap {
+  const int *table = nullptr;  // paged: [max_batch][blocks_per_seq]; NULL: dense
+  int blocks_per_seq = 0;
+  int max_seq = 0;             // dense: positions per sequence
+};
+
+// Element offset of (sequence b, KV head j, position pos) from a layer's base.
+__device__ __forceinline__ int64_t kv_offset(const KvMap &m, int nkv, int hd, int b, int j, int pos) {
+  if (m.table) {
+    const int blk = m.table[b * m.blocks_per_seq + (pos / kKvBlock)];
+    return (((int64_t)blk * nkv + j) * kKvBlock + (pos % kKvBlock)) * hd;
+  }
+  return (((int64_t)b * nkv + j) * m.max_seq + pos) * hd;
+}
+
+// Ragged batches: sequence s holds rows cu[s] .. cu[s+1]-1 of the packed
+// prompt rows; its transposed V copy starts at pcu[s] * nkv * hd elements,
+// pcu being the prefix sums of round_up(length, kKvBlock).
+struct RaggedRows {
+  const int *cu = nullptr;     // [n + 1], or NULL for equal-length sequences
+  const int *pcu = nullptr;    // [n + 1]
+  int n = 0;
+};
+
+// The sequence of packed row t (cu[s] <= t < cu[s+1]).
+__device__ __forceinline__ int ragged_seq(const int *cu, int n, int t) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // ------------------------------------------------------------ launch params
 enum class Epi : int {
   StoreF32 = 0,   // out_f32[m, n] = acc * scale
@@ -94,20 +137,26 @@ struct RopeCacheArgs {
   const float *bias;     // [nq*hd + 2*nkv*hd]
   const float2 *rope;    // [max_seq, hd/2] (cos, sin)
   void *q_out;           // [T, nq*hd] compute type
-  void *k_cache, *v_cache;  // layer base: [max_batch][nkv][max_seq][hd]
-  int T, rows_per_seq, n_heads, n_kv_heads, head_dim, max_seq;
+  void *k_cache, *v_cache;  // layer base (layout: kv)
+  KvMap kv;
+  RaggedRows rag;        // rag.cu set: sequence s is rows cu[s] .. cu[s+1]-1 from position 0
+  int T, rows_per_seq, n_heads, n_kv_heads, head_dim;
   int pos0;              // position of each sequence's first row ...
-  const int *pos0_dev;   // ... or, if non-null, read from the device
+  const int *pos0_dev;   // ... or, if non-null, pos0_dev[b] for sequence b
 };
 
 struct AttnArgs {
   const void *q;              // [T, nq*hd]
-  const void *k_cache, *v_cache;  // layer base
+  const void *k_cache, *v_cache;  // layer base (layout: kv)
+  KvMap kv;
+  RaggedRows rag;             // as in RopeCacheArgs
+  const int *tiles;           // ragged prefill: (sequence << 16 | query tile) work list, or NULL
+  int n_tiles;
   const void *v_t;            // prefill (f16): V of the prompt transposed, [B][nkv][hd][round_up(P, 64)]
   void *o;                    // [T, nq*hd]
-  int T, rows_per_seq, n_heads, n_kv_heads, head_dim, max_seq;
+  int T, rows_per_seq, n_heads, n_kv_heads, head_dim;
   int pos0;
-  const int *pos0_dev;
+  const int *pos0_dev;        // pos0_dev[b] for sequence b
   float softmax_scale;
 };
 
@@ -152,13 +201,14 @@ struct DecAttnArgs {
   const long long *qkv_fix;          // [batch, nq*hd + 2*nkv*hd] fixed-point projection sums
   const float *bias;                 // [nq*hd + 2*nkv*hd]
   const float2 *rope;                // [max_seq, hd/2]
-  void *k_cache, *v_cache;           // layer base [max_batch][nkv][max_seq][hd]
+  void *k_cache, *v_cache;           // layer base (layout: kv)
+  KvMap kv;
   void *o;                           // splits == 1: [batch, nq*hd] f16
   float *part_m, *part_l, *part_o;   // splits > 1: [batch][nq][splits] (+ [hd])
   int splits;
   int head_parallel;                 // 1: waves split the heads (short contexts), 0: waves split the keys
-  int batch, n_heads, n_kv_heads, head_dim, max_seq;
-  const int *pos_dev;                // position of the new row
+  int batch, n_heads, n_kv_heads, head_dim;
+  const int *pos_dev;                // pos_dev[b]: position of row b's new token
   float softmax_scale;
   long long *clear;                  // side job: zero clear[0 .. clear_n)
   int64_t clear_n;
@@ -170,9 +220,10 @@ struct DecAttnOArgs {
   const long long *qkv_fix;          // [batch, nq*hd + 2*nkv*hd] fixed-point projection sums
   const float *bias;                 // [nq*hd + 2*nkv*hd]
   const float2 *rope;                // [max_seq, hd/2]
-  void *k_cache, *v_cache;           // layer base [max_batch][nkv][max_seq][hd]
-  int batch, n_heads, n_kv_heads, head_dim, max_seq;
-  const int *pos_dev;                // position of the new row
+  void *k_cache, *v_cache;           // layer base (layout: kv)
+  KvMap kv;
+  int batch, n_heads, n_kv_heads, head_dim;
+  const int *pos_dev;                // pos_dev[b]: position of row b's new token
   float softmax_scale;
   const void *w_o;                   // [H, nq*hd] f16
   float o_scale;
@@ -223,9 +274,11 @@ hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &
 hipError_t launch_attention_generic(hipStream_t s, bool f16_mode, const AttnArgs &a);
 bool attn_prefill_supported(int head_dim);
 hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a);   // f16, prompt from position 0
-// v_t[b][j][d][t] = V cache[b][j][t][d] for t < P, 0 for P <= t < round_up(P, 64)
-hipError_t launch_transpose_v(hipStream_t s, const void *v_cache, int B, int n_kv_heads, int max_seq, int head_dim,
-                              int P, void *v_t);
+// v_t[b][j][d][t] = V cache[b][j][t][d] for t < P, 0 for P <= t < round_up(P, 64);
+// with rag.cu set, sequence s (length cu[s+1] - cu[s]) at pcu[s] * nkv * hd,
+// its rows round_up(length, 64) long; max_len bounds the lengths
+hipError_t launch_transpose_v(hipStream_t s, const void *v_cache, const KvMap &kv, const RaggedRows &rag, int B,
+                              int n_kv_heads, int head_dim, int P, int max_len, void *v_t);
 hipError_t launch_gemm_generic(hipStream_t s, bool f16_mode, const GemmArgs &a);
 bool gemm_mfma_supported(const GemmArgs &a);
 int gemm_mfma_splits(int M, int N, int K);
@@ -237,6 +290,7 @@ hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void
                             long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1);
 hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int64_t rep_stride, int B, int H,
                            const float *w, float eps, void *u);
+// also advances pos_dev[b] for every row b
 hipError_t launch_dec_end(hipStream_t s, const float *arg_v, const int *arg_i, int nblk, int B, int32_t *next,
                           int *pos_dev);
 hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &a);
@@ -247,10 +301,10 @@ hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a);
 hipError_t launch_dec_merge(hipStream_t s, const float *pm, const float *pl, const float *po, int S, int B, int nq,
                             int hd, void *o);
 hipError_t launch_dec_attn_o(hipStream_t s, const DecAttnOArgs &a);
-// also sets kFlagNonFinite in *flag when a row holds an inf or NaN logit
+// also sets kFlagNonFinite in *flag when a row holds an inf or NaN logit, and
+// adds pos_add to pos_dev[r] for every row r (when pos_dev is non-NULL)
 hipError_t launch_argmax(hipStream_t s, const float *logits, int rows, int vocab, int64_t row_stride,
                          int32_t *next_ids, int *pos_dev, int pos_add, int *flag);
-hipError_t launch_set_int(hipStream_t s, int *p, int v);
 // dst[b * dst_stride + dst_col] = src[b] (and seq[b * seq_stride + seq_col] = src[b] if seq)
 hipError_t launch_put_column(hipStream_t s, int32_t *dst, int64_t dst_stride, int dst_col, int32_t *seq,
                              int64_t seq_stride, int seq_col, const int32_t *src, int B);
@@ -263,13 +317,22 @@ hipError_t launch_stage_out(hipStream_t s, int32_t *next_dst, const int32_t *nex
                             const float *logits_src, int64_t n_logits);
 
 // Sampling of the next token from B rows of logits (row stride row_stride)
-// by the counter-based draw for n = *pos_dev tokens before it; with finished
+// by the counter-based draw for n = pos_dev[b] tokens before it in row b; with finished
 // non-NULL the end-of-sequence rule for `eos` applies.  See k_sample.hip.
 hipError_t launch_sample(hipStream_t s, const float *logits, int64_t row_stride, int B, int V, float temperature,
                          int top_k, float top_p, uint64_t seed, const int *pos_dev, int32_t *next, int *finished,
                          int eos);
 hipError_t launch_eos(hipStream_t s, int32_t *next, int *finished, int eos, int B);
 hipError_t launch_fill_int(hipStream_t s, int *p, int v, int n);
+
+// Small host-to-device updates carried in the kernel arguments (nothing is
+// staged in host memory, so later host changes cannot race the copy):
+// dst[idx[k]] = val[k] for k < n, in launches of up to kPutChunk pairs.
+constexpr int kPutChunk = 240;
+hipError_t launch_put_ints(hipStream_t s, int *dst, const int *idx, const int *val, int n);
+// the last row of each ragged sequence: dst[k * H + c] = src[(cu[k+1] - 1) * H + c]
+// for k < n, c < H (fp32; cu on the device)
+hipError_t launch_gather_last_rows(hipStream_t s, float *dst, const float *src, const int *cu, int n, int H);
 
 // set-up kernels (qw_create); src_kind is the storage type of the caller's
 // weights

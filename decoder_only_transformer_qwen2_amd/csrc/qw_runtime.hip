@@ -21,6 +21,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -116,6 +117,23 @@ struct qw_model {
   float *final_norm = nullptr;
   void *k_cache = nullptr, *v_cache = nullptr;
   int64_t cache_layer_elems = 0;
+  // Paged cache (qw_create_paged): each layer's cache is a pool of num_blocks
+  // blocks of kKvBlock positions, and block_table[b][p] names the block that
+  // holds positions kKvBlock p .. of sequence b.  The host keeps the free list
+  // and each sequence's blocks; blocks are handed out as sequences reach them
+  // (prefill: the prompt's; decode: one more every kKvBlock steps) and all
+  // return to the pool when a prefill starts a new batch.
+  bool paged = false;
+  int num_blocks = 0, blocks_per_seq = 0;
+  int *block_table = nullptr;                  // device [max_batch][blocks_per_seq]
+  std::vector<int> free_blocks;                // popped from the back
+  std::vector<std::vector<int>> seq_blocks;    // [max_batch] blocks in position order
+  // tokens each sequence holds (host mirror of pos_dev; ragged batches differ)
+  std::vector<int> pos_host;
+  // ragged prefill: cu [max_batch + 1], pcu [max_batch + 1], query-tile list
+  int *rag_meta = nullptr;
+  int rag_tiles_cap = 0;
+  float *x_last = nullptr;                     // [max_batch, H] last rows of a ragged prefill
   float2 *rope = nullptr;
   float *x = nullptr, *qkv = nullptr, *logits = nullptr;
   void *u = nullptr, *q = nullptr, *o = nullptr, *h = nullptr;
@@ -158,6 +176,14 @@ struct qw_model {
   double timing_ms = 0;
   int64_t timing_n = 0;
   std::vector<void *> allocs;
+
+  KvMap kv() const {
+    KvMap k;
+    k.table = paged ? block_table : nullptr;
+    k.blocks_per_seq = blocks_per_seq;
+    k.max_seq = cfg.max_seq;
+    return k;
+  }
 
   hipError_t alloc(void **p, size_t bytes) {
     *p = nullptr;
@@ -267,10 +293,20 @@ hipError_t gemm(qw_model *m, hipStream_t s, Family fam, const void *A, int M, in
   return timed(m, s, fam, [&] { return launch_gemm_generic(s, m->f16, a); });
 }
 
+// A ragged prefill's layout on the device (cu, pcu and the query-tile list
+// in rag_meta) and the longest sequence.
+struct RaggedPlan {
+  RaggedRows rows;
+  const int *tiles = nullptr;
+  int n_tiles = 0, max_len = 0;
+};
+
 // The decoder blocks over T rows (rows_per_seq rows per sequence, the first at
-// position pos0, or at *pos_dev when pos_dev is given); x holds the embedded
-// rows on entry and the final residual stream on exit.
-hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int pos0, const int *pos_dev) {
+// position pos0, or at pos_dev[b] when pos_dev is given; or the ragged
+// sequences of `rag`, each from position 0); x holds the embedded rows on
+// entry and the final residual stream on exit.
+hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int pos0, const int *pos_dev,
+                      const RaggedPlan *rag = nullptr) {
   const qw_config &c = m->cfg;
   const int H = c.hidden, I = c.intermediate;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -289,12 +325,13 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
     ra.q_out = m->q;
     ra.k_cache = kc;
     ra.v_cache = vc;
+    ra.kv = m->kv();
+    if (rag) ra.rag = rag->rows;
     ra.T = T;
     ra.rows_per_seq = rows_per_seq;
     ra.n_heads = c.n_heads;
     ra.n_kv_heads = c.n_kv_heads;
     ra.head_dim = c.head_dim;
-    ra.max_seq = c.max_seq;
     ra.pos0 = pos0;
     ra.pos0_dev = pos_dev;
     e = timed(m, s, F_ROPE_CACHE, [&] { return launch_rope_cache(s, m->f16, ra); });
@@ -303,21 +340,30 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
     aa.q = m->q;
     aa.k_cache = kc;
     aa.v_cache = vc;
+    aa.kv = m->kv();
+    aa.tiles = nullptr;
+    aa.n_tiles = 0;
+    if (rag) {
+      aa.rag = rag->rows;
+      aa.tiles = rag->tiles;
+      aa.n_tiles = rag->n_tiles;
+    }
     aa.o = m->o;
     aa.T = T;
     aa.rows_per_seq = rows_per_seq;
     aa.n_heads = c.n_heads;
     aa.n_kv_heads = c.n_kv_heads;
     aa.head_dim = c.head_dim;
-    aa.max_seq = c.max_seq;
     aa.pos0 = pos0;
     aa.pos0_dev = pos_dev;
     aa.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
     aa.v_t = m->v_t;
     if (m->f16 && !pos_dev && pos0 == 0 && attn_prefill_supported(c.head_dim)) {
-      const int B = T / rows_per_seq;
+      const int B = rag ? rag->rows.n : T / rows_per_seq;
+      const int max_len = rag ? rag->max_len : rows_per_seq;
       e = timed(m, s, F_ROPE_CACHE, [&] {
-        return launch_transpose_v(s, vc, B, c.n_kv_heads, c.max_seq, c.head_dim, rows_per_seq, m->v_t);
+        return launch_transpose_v(s, vc, m->kv(), aa.rag, B, c.n_kv_heads, c.head_dim, rows_per_seq, max_len,
+                                  m->v_t);
       });
       if (e != hipSuccess) return e;
       e = timed(m, s, F_ATTENTION, [&] { return launch_attention_prefill(s, aa); });
@@ -482,7 +528,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       ao.n_heads = c.n_heads;
       ao.n_kv_heads = c.n_kv_heads;
       ao.head_dim = c.head_dim;
-      ao.max_seq = c.max_seq;
+      ao.kv = m->kv();
       ao.pos_dev = m->pos_dev;
       ao.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
       ao.w_o = Lw.w_o;
@@ -511,7 +557,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       da.n_heads = c.n_heads;
       da.n_kv_heads = c.n_kv_heads;
       da.head_dim = c.head_dim;
-      da.max_seq = c.max_seq;
+      da.kv = m->kv();
       da.pos_dev = m->pos_dev;
       da.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
       da.clear = fused_mlp ? xo : gu_clear;
@@ -655,6 +701,15 @@ hipError_t decode_body(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   return m->fast_decode ? decode_fast(m, s, ids, next, model_scratch(m)) : decode_generic(m, s, ids, next);
 }
 
+// Every block back in the pool.  Blocks are handed out from the highest
+// index down, so a sequence's consecutive positions never sit in adjacent
+// ascending blocks (any kernel that ignored the table would read wrong keys).
+void reset_blocks(qw_model *m) {
+  m->free_blocks.resize(m->num_blocks);
+  for (int k = 0; k < m->num_blocks; ++k) m->free_blocks[k] = k;
+  for (auto &v : m->seq_blocks) v.clear();
+}
+
 void drop_graph(qw_model *m) {
   if (m->gexec) (void)hipGraphExecDestroy(m->gexec);
   m->gexec = nullptr;
@@ -748,8 +803,11 @@ const char *qw_last_error(void) { return g_err.c_str(); }
 
 const char *qw_kernel_names(void) { return kFamilyList; }
 
-qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_stream, qw_model **out) {
-  g_err.clear();
+}  // extern "C"
+
+// qw_create (num_blocks == 0: dense cache) and qw_create_paged.
+static qw_status create_model(const qw_config *cfg, const qw_weights *weights, void *hip_stream, int num_blocks,
+                              qw_model **out) {
   if (!out) return fail(QW_ERR_INVALID_ARG, "qw_create: out is NULL");
   *out = nullptr;
   if (!cfg || !weights) return fail(QW_ERR_INVALID_ARG, "qw_create: cfg or weights is NULL");
@@ -890,7 +948,20 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   }
 
   // --- cache, RoPE table, workspace
-  m->cache_layer_elems = (int64_t)c.max_batch * c.n_kv_heads * c.max_seq * c.head_dim;
+  m->pos_host.assign(c.max_batch, 0);
+  m->seq_blocks.resize(c.max_batch);
+  if (num_blocks > 0) {
+    m->paged = true;
+    m->num_blocks = num_blocks;
+    m->blocks_per_seq = (c.max_seq + kKvBlock - 1) / kKvBlock;
+    m->cache_layer_elems = (int64_t)num_blocks * c.n_kv_heads * kKvBlock * c.head_dim;
+    const size_t tb = (size_t)c.max_batch * m->blocks_per_seq * 4;
+    CREATE_TRY(m->alloc((void **)&m->block_table, tb));
+    CREATE_TRY(hipMemsetAsync(m->block_table, 0, tb, s));    // block 0: every stray entry stays in bounds
+    reset_blocks(m);
+  } else {
+    m->cache_layer_elems = (int64_t)c.max_batch * c.n_kv_heads * c.max_seq * c.head_dim;
+  }
   const size_t cache_bytes = (size_t)c.n_layers * m->cache_layer_elems * es;
   CREATE_TRY(m->alloc(&m->k_cache, cache_bytes));
   CREATE_TRY(m->alloc(&m->v_cache, cache_bytes));
@@ -910,7 +981,11 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   if (m->splitk_bytes) CREATE_TRY(m->alloc((void **)&m->splitk_ws, m->splitk_bytes));
   if (m->f16)
     CREATE_TRY(m->alloc(&m->v_t, (size_t)c.max_batch * c.n_kv_heads * c.head_dim * ((c.max_seq + 63) / 64 * 64) * 2));
-  CREATE_TRY(m->alloc((void **)&m->pos_dev, 256));
+  const size_t pos_bytes = std::max<size_t>(256, (size_t)c.max_batch * 4);
+  CREATE_TRY(m->alloc((void **)&m->pos_dev, pos_bytes));
+  m->rag_tiles_cap = c.max_batch * ((c.max_seq + 127) / 128);
+  CREATE_TRY(m->alloc((void **)&m->rag_meta, ((size_t)2 * (c.max_batch + 1) + m->rag_tiles_cap) * 4));
+  CREATE_TRY(m->alloc((void **)&m->x_last, (size_t)c.max_batch * H * 4));
   CREATE_TRY(m->alloc((void **)&m->status, 256));
   CREATE_TRY(m->alloc((void **)&m->ids_stage, (size_t)c.max_batch * 4));
   if (m->fast_decode) {
@@ -930,7 +1005,7 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   CREATE_TRY(m->alloc((void **)&m->seq_ids, (size_t)c.max_batch * c.max_seq * 4));
   CREATE_TRY(m->alloc((void **)&m->finished, (size_t)c.max_batch * 4));
   CREATE_TRY(hipMemsetAsync(m->finished, 0, (size_t)c.max_batch * 4, s));
-  CREATE_TRY(hipMemsetAsync(m->pos_dev, 0, 256, s));
+  CREATE_TRY(hipMemsetAsync(m->pos_dev, 0, pos_bytes, s));
   CREATE_TRY(hipMemsetAsync(m->status, 0, 256, s));
   CREATE_TRY(hipStreamSynchronize(s));
 #undef CREATE_TRY
@@ -938,9 +1013,101 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
   return QW_OK;
 }
 
+extern "C" {
+
+qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_stream, qw_model **out) {
+  g_err.clear();
+  return create_model(cfg, weights, hip_stream, 0, out);
+}
+
+qw_status qw_create_paged(const qw_config *cfg, const qw_weights *weights, int32_t num_blocks, void *hip_stream,
+                          qw_model **out) {
+  g_err.clear();
+  if (out) *out = nullptr;
+  if (num_blocks < 1) return fail(QW_ERR_INVALID_ARG, "qw_create_paged: num_blocks must be >= 1");
+  if (cfg && (int64_t)num_blocks * cfg->n_kv_heads * kKvBlock * cfg->head_dim > ((int64_t)1 << 40))
+    return fail(QW_ERR_INVALID_ARG, "qw_create_paged: %d blocks is beyond any device", num_blocks);
+  return create_model(cfg, weights, hip_stream, num_blocks, out);
+}
+
 }  // extern "C"
 
 namespace {
+
+int blocks_for(int positions) { return (positions + kKvBlock - 1) / kKvBlock; }
+
+// Paged cache: fail with CACHE_FULL (changing nothing) unless a new batch of
+// n sequences holding lens[b] positions each (len_eq when lens is NULL) fits
+// the pool.
+qw_status check_pool(const qw_model *m, const int *lens, int len_eq, int n, const char *who) {
+  if (!m->paged) return QW_OK;
+  int64_t need = 0;
+  for (int b = 0; b < n; ++b) need += blocks_for(lens ? lens[b] : len_eq);
+  if (need > m->num_blocks)
+    return fail(QW_ERR_CACHE_FULL, "%s: the sequences need %lld cache blocks of %d positions, the pool holds %d", who,
+                (long long)need, kKvBlock, m->num_blocks);
+  return QW_OK;
+}
+
+// Paged cache: a new batch.  Every block returns to the pool, then sequence b
+// takes the blocks of its first lens[b] positions; the table entries go to
+// the device in kernel arguments.  The pool was checked (check_pool).
+hipError_t assign_blocks(qw_model *m, hipStream_t s, const int *lens, int len_eq, int n) {
+  if (!m->paged) return hipSuccess;
+  reset_blocks(m);
+  std::vector<int> idx, val;
+  for (int b = 0; b < n; ++b) {
+    const int nb = blocks_for(lens ? lens[b] : len_eq);
+    for (int p = 0; p < nb; ++p) {
+      const int blk = m->free_blocks.back();
+      m->free_blocks.pop_back();
+      m->seq_blocks[b].push_back(blk);
+      idx.push_back(b * m->blocks_per_seq + p);
+      val.push_back(blk);
+    }
+  }
+  return launch_put_ints(s, m->block_table, idx.data(), val.data(), (int)idx.size());
+}
+
+// Paged cache, before a decode step: the block of every sequence whose new
+// token starts one.  CACHE_FULL (changing nothing) when the pool has too few.
+qw_status reserve_step_blocks(qw_model *m, hipStream_t s, const char *who) {
+  if (!m->paged) return QW_OK;
+  std::vector<int> need;
+  for (int b = 0; b < m->batch; ++b)
+    if (m->pos_host[b] / kKvBlock >= (int)m->seq_blocks[b].size()) need.push_back(b);
+  if (need.empty()) return QW_OK;
+  if ((int)need.size() > (int)m->free_blocks.size())
+    return fail(QW_ERR_CACHE_FULL, "%s: %d sequences start a new cache block, %d blocks are free", who,
+                (int)need.size(), (int)m->free_blocks.size());
+  std::vector<int> idx, val;
+  for (int b : need) {
+    const int blk = m->free_blocks.back();
+    m->free_blocks.pop_back();
+    idx.push_back(b * m->blocks_per_seq + (int)m->seq_blocks[b].size());
+    val.push_back(blk);
+    m->seq_blocks[b].push_back(blk);
+  }
+  const hipError_t e = launch_put_ints(s, m->block_table, idx.data(), val.data(), (int)idx.size());
+  if (e != hipSuccess) return fail(QW_ERR_HIP, "%s: block table update: %s", who, hipGetErrorString(e));
+  return QW_OK;
+}
+
+// Host positions after a prefill of n sequences (lens[b], or len_eq each).
+void set_positions(qw_model *m, const int *lens, int len_eq, int n) {
+  int mx = 0;
+  for (int b = 0; b < m->cfg.max_batch; ++b) {
+    m->pos_host[b] = b < n ? (lens ? lens[b] : len_eq) : 0;
+    mx = std::max(mx, m->pos_host[b]);
+  }
+  m->pos = mx;
+}
+
+// Host positions after a decode step: every sequence of the batch holds one more.
+void advance_positions(qw_model *m) {
+  for (int b = 0; b < m->batch; ++b) m->pos_host[b] += 1;
+  m->pos += 1;
+}
 
 // The enqueue of a prefill whose arguments are valid: `batch` sequences of
 // `prompt_len` ids, sequence b's at ids + b * ids_stride.
@@ -949,7 +1116,9 @@ hipError_t prefill_enqueue(qw_model *m, const int32_t *ids, int64_t ids_stride, 
   const qw_config &c = m->cfg;
   hipStream_t s = m->stream;
   const int T = batch * prompt_len, H = c.hidden, V = c.vocab;
-  hipError_t e = timed(m, s, F_EMBED, [&] {
+  hipError_t e = assign_blocks(m, s, nullptr, prompt_len, batch);
+  if (e != hipSuccess) return e;
+  e = timed(m, s, F_EMBED, [&] {
     return launch_embed(s, m->f16, ids, T, prompt_len, ids_stride, m->emb, m->emb_scale, H, V, m->x, m->status);
   });
   if (e != hipSuccess) return e;
@@ -968,9 +1137,68 @@ hipError_t prefill_enqueue(qw_model *m, const int32_t *ids, int64_t ids_stride, 
                  nullptr, 0);
   }
   if (e != hipSuccess) return e;
-  if ((e = launch_set_int(s, m->pos_dev, prompt_len)) != hipSuccess) return e;
+  if ((e = launch_fill_int(s, m->pos_dev, prompt_len, batch)) != hipSuccess) return e;
   if (new_sequences && m->eos >= 0 && (e = launch_fill_int(s, m->finished, 0, batch)) != hipSuccess) return e;
   return choose_next(m, s, last, stride, batch, next_ids);
+}
+
+// The enqueue of a ragged prefill whose arguments are valid (lens: host).
+hipError_t prefill_ragged_enqueue(qw_model *m, const int32_t *ids, const int32_t *lens, int n, float *logits,
+                                  int32_t *next_ids) {
+  const qw_config &c = m->cfg;
+  hipStream_t s = m->stream;
+  const int H = c.hidden, V = c.vocab;
+  hipError_t e = assign_blocks(m, s, lens, 0, n);
+  if (e != hipSuccess) return e;
+  // device layout: cu [n + 1], pcu [n + 1] (after max_batch + 1 entries),
+  // then the query tiles, longest first: (sequence << 16) | tile
+  const int off_pcu = c.max_batch + 1, off_tiles = 2 * (c.max_batch + 1);
+  std::vector<int> idx, val;
+  int T = 0, PT = 0, max_len = 0, max_qt = 0;
+  for (int b = 0; b <= n; ++b) {
+    idx.push_back(b);
+    val.push_back(T);
+    idx.push_back(off_pcu + b);
+    val.push_back(PT);
+    if (b < n) {
+      T += lens[b];
+      PT += blocks_for(lens[b]) * kKvBlock;
+      max_len = std::max(max_len, lens[b]);
+      max_qt = std::max(max_qt, (lens[b] + 127) / 128);
+    }
+  }
+  int n_tiles = 0;
+  for (int qt = max_qt - 1; qt >= 0; --qt)
+    for (int b = 0; b < n; ++b)
+      if ((lens[b] + 127) / 128 > qt) {
+        idx.push_back(off_tiles + n_tiles++);
+        val.push_back((b << 16) | qt);
+      }
+  if ((e = launch_put_ints(s, m->rag_meta, idx.data(), val.data(), (int)idx.size())) != hipSuccess) return e;
+  RaggedPlan plan;
+  plan.rows.cu = m->rag_meta;
+  plan.rows.pcu = m->rag_meta + off_pcu;
+  plan.rows.n = n;
+  plan.tiles = m->rag_meta + off_tiles;
+  plan.n_tiles = n_tiles;
+  plan.max_len = max_len;
+  e = timed(m, s, F_EMBED, [&] {
+    return launch_embed(s, m->f16, ids, T, T, T, m->emb, m->emb_scale, H, V, m->x, m->status);
+  });
+  if (e != hipSuccess) return e;
+  if ((e = run_layers(m, s, T, T, 0, nullptr, &plan)) != hipSuccess) return e;
+  // the last row of each sequence
+  if ((e = launch_gather_last_rows(s, m->x_last, m->x, plan.rows.cu, n, H)) != hipSuccess) return e;
+  float *lg = logits ? logits : m->logits;
+  if ((e = run_head(m, s, m->x_last, n, H, lg, lg, n, V, next_ids, nullptr, 0)) != hipSuccess) return e;
+  std::vector<int> pidx(n), pval(n);
+  for (int b = 0; b < n; ++b) {
+    pidx[b] = b;
+    pval[b] = lens[b];
+  }
+  if ((e = launch_put_ints(s, m->pos_dev, pidx.data(), pval.data(), n)) != hipSuccess) return e;
+  if (m->eos >= 0 && (e = launch_fill_int(s, m->finished, 0, n)) != hipSuccess) return e;
+  return choose_next(m, s, lg, V, n, next_ids);
 }
 
 }  // namespace
@@ -989,10 +1217,54 @@ qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t pro
   if (prompt_len > c.max_seq)
     return fail(QW_ERR_CACHE_FULL, "qw_prefill: prompt_len %d exceeds max_seq %d", prompt_len, c.max_seq);
   if (logits_all && !logits) return fail(QW_ERR_INVALID_ARG, "qw_prefill: logits_all needs a logits buffer");
+  qw_status st = check_pool(m, nullptr, prompt_len, batch, "qw_prefill");
+  if (st != QW_OK) return st;
   m->batch = 0;          // invalid until the enqueue succeeds
   HIP_TRY(prefill_enqueue(m, ids, prompt_len, batch, prompt_len, logits, logits_all, next_ids));
   m->batch = batch;
-  m->pos = prompt_len;
+  set_positions(m, nullptr, prompt_len, batch);
+  return QW_OK;
+}
+
+qw_status qw_prefill_ragged(qw_model *m, const int32_t *ids, const int32_t *lens, int32_t n_seqs, float *logits,
+                            int32_t *next_ids) {
+  g_err.clear();
+  if (!m) return fail(QW_ERR_INVALID_ARG, "qw_prefill_ragged: model is NULL");
+  if (!ids || !lens || !next_ids)
+    return fail(QW_ERR_INVALID_ARG, "qw_prefill_ragged: ids, lens and next_ids must be non-NULL");
+  const qw_config &c = m->cfg;
+  if (n_seqs < 1 || n_seqs > c.max_batch)
+    return fail(QW_ERR_INVALID_ARG, "qw_prefill_ragged: n_seqs %d outside [1, max_batch=%d]", n_seqs, c.max_batch);
+  if (n_seqs >= (1 << 15))
+    return fail(QW_ERR_INVALID_ARG, "qw_prefill_ragged: n_seqs %d beyond the tile list's 15 bits", n_seqs);
+  for (int b = 0; b < n_seqs; ++b) {
+    if (lens[b] < 1) return fail(QW_ERR_INVALID_ARG, "qw_prefill_ragged: lens[%d] = %d (must be >= 1)", b, lens[b]);
+    if (lens[b] > c.max_seq)
+      return fail(QW_ERR_CACHE_FULL, "qw_prefill_ragged: lens[%d] = %d exceeds max_seq %d", b, lens[b], c.max_seq);
+  }
+  qw_status st = check_pool(m, lens, 0, n_seqs, "qw_prefill_ragged");
+  if (st != QW_OK) return st;
+  m->batch = 0;          // invalid until the enqueue succeeds
+  HIP_TRY(prefill_ragged_enqueue(m, ids, lens, n_seqs, logits, next_ids));
+  m->batch = n_seqs;
+  set_positions(m, lens, 0, n_seqs);
+  return QW_OK;
+}
+
+qw_status qw_get_positions(const qw_model *m, int32_t *pos, int32_t n) {
+  g_err.clear();
+  if (!m || !pos) return fail(QW_ERR_INVALID_ARG, "qw_get_positions: NULL argument");
+  if (n < 0 || n > m->cfg.max_batch)
+    return fail(QW_ERR_INVALID_ARG, "qw_get_positions: n %d outside [0, max_batch=%d]", n, m->cfg.max_batch);
+  for (int b = 0; b < n; ++b) pos[b] = b < m->batch ? m->pos_host[b] : 0;
+  return QW_OK;
+}
+
+qw_status qw_kv_blocks(const qw_model *m, int32_t *free_blocks, int32_t *total_blocks) {
+  g_err.clear();
+  if (!m || !free_blocks || !total_blocks) return fail(QW_ERR_INVALID_ARG, "qw_kv_blocks: NULL argument");
+  *total_blocks = m->paged ? m->num_blocks : 0;
+  *free_blocks = m->paged ? (int32_t)m->free_blocks.size() : 0;
   return QW_OK;
 }
 
@@ -1004,6 +1276,8 @@ qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t
   if (m->pos >= m->cfg.max_seq)
     return fail(QW_ERR_CACHE_FULL, "qw_decode_step: cache holds max_seq=%d positions", m->cfg.max_seq);
   hipStream_t s = m->stream;
+  qw_status st = reserve_step_blocks(m, s, "qw_decode_step");
+  if (st != QW_OK) return st;
   const bool graph = m->use_graph && m->timing_family < 0;
   if (!graph) {
     HIP_TRY(decode_body(m, s, ids, m->next_stage));
@@ -1034,7 +1308,7 @@ qw_status qw_decode_step(qw_model *m, const int32_t *ids, float *logits, int32_t
     HIP_TRY(hipGraphLaunch(m->gexec, s));
   }
   HIP_TRY(launch_stage_out(s, next_ids, m->next_stage, m->batch, logits, m->logits, (int64_t)m->batch * m->cfg.vocab));
-  m->pos += 1;
+  advance_positions(m);
   return QW_OK;
 }
 
@@ -1079,6 +1353,8 @@ qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits,
   if (dev_now != m->device)
     return fail(QW_ERR_BAD_STATE, "qw_decode_step_noalloc: the model lives on device %d, device %d is current",
                 m->device, dev_now);
+  qw_status st = reserve_step_blocks(m, m->stream, "qw_decode_step_noalloc");
+  if (st != QW_OK) return st;
   DecodeScratch d;
   d.x_fix = (long long *)(base + off[0]);
   d.x_fix2 = (long long *)(base + off[1]);
@@ -1100,7 +1376,7 @@ qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits,
   hipError_t e = decode_fast(m, m->stream, ids, next_ids, d);
   m->timing_family = fam;
   HIP_TRY(e);
-  m->pos += 1;
+  advance_positions(m);
   return QW_OK;
 }
 
@@ -1116,6 +1392,8 @@ qw_status qw_generate(qw_model *m, const int32_t *ids, int32_t batch, int32_t pr
   if ((int64_t)prompt_len + steps > c.max_seq)
     return fail(QW_ERR_CACHE_FULL, "qw_generate: prompt_len %d + steps %d exceeds max_seq %d", prompt_len, steps,
                 c.max_seq);
+  qw_status st0 = check_pool(m, nullptr, prompt_len + steps, batch, "qw_generate");
+  if (st0 != QW_OK) return st0;
   hipStream_t s = m->stream;
   const int V = c.vocab;
   const int64_t cols = (int64_t)steps + 1;
@@ -1128,7 +1406,7 @@ qw_status qw_generate(qw_model *m, const int32_t *ids, int32_t batch, int32_t pr
   if (use_cache) {
     HIP_TRY(prefill_enqueue(m, ids, prompt_len, batch, prompt_len, logits ? m->logits : nullptr, 0, m->next_stage));
     m->batch = batch;
-    m->pos = prompt_len;
+    set_positions(m, nullptr, prompt_len, batch);
     HIP_TRY(put_logits(0));
     HIP_TRY(launch_put_column(s, out_ids, cols, 0, nullptr, 0, 0, m->next_stage, batch));
     for (int k = 1; k <= steps; ++k) {
@@ -1151,7 +1429,7 @@ qw_status qw_generate(qw_model *m, const int32_t *ids, int32_t batch, int32_t pr
     HIP_TRY(launch_put_column(s, out_ids, cols, k, k < steps ? m->seq_ids : nullptr, ss, L, m->next_stage, batch));
   }
   m->batch = batch;
-  m->pos = prompt_len + steps;
+  set_positions(m, nullptr, prompt_len + steps, batch);
   return QW_OK;
 }
 

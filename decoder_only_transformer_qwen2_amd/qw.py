@@ -24,9 +24,13 @@ STATUS_NAMES = {0: "QW_OK", -1: "QW_ERR_INVALID_ARG", -2: "QW_ERR_OUT_OF_MEMORY"
                 -4: "QW_ERR_CACHE_FULL", -5: "QW_ERR_BAD_STATE", -6: "QW_ERR_UNSUPPORTED",
                 -7: "QW_ERR_NUMERICS"}
 
-EXPORTED = ("qw_create", "qw_prefill", "qw_decode_step", "qw_decode_step_noalloc", "qw_generate", "qw_destroy", "qw_last_error", "qw_get_state",
-            "qw_check_ids", "qw_check_numerics", "qw_set_sampling", "qw_set_eos", "qw_get_finished", "qw_set_graph", "qw_timing_enable", "qw_timing_read", "qw_kernel_names", "qw_peak_copy",
-            "qw_peak_mfma")
+EXPORTED = ("qw_create", "qw_create_paged", "qw_prefill", "qw_prefill_ragged", "qw_decode_step",
+            "qw_decode_step_noalloc", "qw_generate", "qw_destroy", "qw_last_error", "qw_get_state",
+            "qw_get_positions", "qw_kv_blocks", "qw_check_ids", "qw_check_numerics", "qw_set_sampling",
+            "qw_set_eos", "qw_get_finished", "qw_set_graph", "qw_timing_enable", "qw_timing_read",
+            "qw_kernel_names", "qw_peak_copy", "qw_peak_mfma")
+
+QW_KV_BLOCK = 64
 
 
 class QwError(RuntimeError):
@@ -71,7 +75,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sig = {
         "qw_create": (I32, [ctypes.POINTER(qw_config), ctypes.POINTER(qw_weights), P, ctypes.POINTER(P)]),
+        "qw_create_paged": (I32, [ctypes.POINTER(qw_config), ctypes.POINTER(qw_weights), I32, P,
+                                  ctypes.POINTER(P)]),
         "qw_prefill": (I32, [P, P, I32, I32, P, I32, P]),
+        "qw_prefill_ragged": (I32, [P, P, ctypes.POINTER(I32), I32, P, P]),
+        "qw_get_positions": (I32, [P, ctypes.POINTER(I32), I32]),
+        "qw_kv_blocks": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "qw_decode_step": (I32, [P, P, P, P]),
         "qw_decode_step_noalloc": (I32, [P, P, P, P]),
         "qw_generate": (I32, [P, P, I32, I32, I32, I32, P, P]),
@@ -118,9 +127,35 @@ def qw_create(cfg: qw_config, weights: qw_weights, stream: int = 0) -> int:
     return h.value
 
 
+def qw_create_paged(cfg: qw_config, weights: qw_weights, num_blocks: int, stream: int = 0) -> int:
+    h = ctypes.c_void_p()
+    _check(load_library().qw_create_paged(ctypes.byref(cfg), ctypes.byref(weights), num_blocks,
+                                          ctypes.c_void_p(stream), ctypes.byref(h)))
+    return h.value
+
+
 def qw_prefill(model: int, ids: int, batch: int, prompt_len: int, logits: int, logits_all: int,
                next_ids: int) -> None:
     _check(load_library().qw_prefill(model, ids, batch, prompt_len, logits or None, logits_all, next_ids))
+
+
+def qw_prefill_ragged(model: int, ids: int, lens, logits: int, next_ids: int) -> None:
+    """lens: host sequence of prompt lengths (ids holds the prompts packed)."""
+    n = len(lens)
+    buf = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in lens])
+    _check(load_library().qw_prefill_ragged(model, ids, buf, n, logits or None, next_ids))
+
+
+def qw_get_positions(model: int, n: int) -> list:
+    buf = (ctypes.c_int32 * max(n, 1))()
+    _check(load_library().qw_get_positions(model, buf, n))
+    return [int(buf[i]) for i in range(n)]
+
+
+def qw_kv_blocks(model: int):
+    f, t = ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().qw_kv_blocks(model, ctypes.byref(f), ctypes.byref(t)))
+    return f.value, t.value
 
 
 def qw_decode_step(model: int, ids: int, logits: int, next_ids: int) -> None:
@@ -226,7 +261,10 @@ class Model:
     library copies what it needs at creation, so they may be dropped after.
     """
 
-    def __init__(self, shape, tensors: Dict[str, "object"], max_batch: int, max_seq: int, stream=None):
+    def __init__(self, shape, tensors: Dict[str, "object"], max_batch: int, max_seq: int, stream=None,
+                 kv_blocks: Optional[int] = None):
+        """kv_blocks: a paged cache of that many QW_KV_BLOCK-position blocks
+        (qw_create_paged) instead of the dense max_batch x max_seq one."""
         import torch
         self.shape = shape
         self.cfg = make_config(shape, max_batch, max_seq)
@@ -241,7 +279,10 @@ class Model:
         w = qw_weights(tensors["model.embed_tokens.weight"].data_ptr(), tensors["model.norm.weight"].data_ptr(),
                        tensors["lm_head.weight"].data_ptr() if "lm_head.weight" in tensors else None, layers)
         self.stream = stream if stream is not None else torch.cuda.current_stream()
-        self.handle = qw_create(self.cfg, w, self.stream.cuda_stream)
+        if kv_blocks is None:
+            self.handle = qw_create(self.cfg, w, self.stream.cuda_stream)
+        else:
+            self.handle = qw_create_paged(self.cfg, w, kv_blocks, self.stream.cuda_stream)
 
     def prefill(self, ids, logits=None, logits_all: bool = False, next_ids=None):
         import torch
@@ -251,6 +292,26 @@ class Model:
         qw_prefill(self.handle, ids.data_ptr(), B, P, logits.data_ptr() if logits is not None else 0,
                    int(logits_all), next_ids.data_ptr())
         return next_ids
+
+    def prefill_ragged(self, ids, lens, logits=None, next_ids=None):
+        """ids: int32 CUDA tensor of the prompts packed back to back; lens:
+        their lengths (host ints)."""
+        import torch
+        lens = [int(x) for x in lens]
+        if ids.numel() != sum(lens):
+            raise ValueError(f"ids holds {ids.numel()} tokens, lens sum to {sum(lens)}")
+        if next_ids is None:
+            next_ids = torch.empty(len(lens), dtype=torch.int32, device=ids.device)
+        qw_prefill_ragged(self.handle, ids.data_ptr(), lens, logits.data_ptr() if logits is not None else 0,
+                          next_ids.data_ptr())
+        return next_ids
+
+    def positions(self, n: int):
+        return qw_get_positions(self.handle, n)
+
+    def kv_blocks(self):
+        """(free, total) blocks of a paged cache; (0, 0) when dense."""
+        return qw_kv_blocks(self.handle)
 
     def decode_step(self, ids, logits=None, next_ids=None):
         import torch

@@ -135,6 +135,23 @@ typedef struct qw_model qw_model;
 qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_stream,
                     qw_model **out);
 
+/* Paged KV cache ("augur", "Not yet" list: paged attention).  The same model
+ * as qw_create, but each layer's cache is a pool of `num_blocks` blocks of
+ * QW_KV_BLOCK positions (2 * n_layers * num_blocks * nkv * QW_KV_BLOCK * hd
+ * elements of the compute type in all), and every sequence holds a table of
+ * the blocks its positions live in, so the pool is sized for the positions
+ * actually held rather than max_batch * max_seq.  The library owns the pool:
+ * a prefill (qw_prefill, qw_prefill_ragged, qw_generate) returns every block
+ * to it and gives each sequence the blocks of its prompt; a decode step gives
+ * a sequence one more block each time its new token starts one.  max_seq
+ * still bounds each sequence and sizes the RoPE table and the block tables.
+ * All other calls behave as on a dense model, with the same results bit for
+ * bit (the kernels do the same arithmetic; only addresses differ).
+ * Errors: as qw_create; INVALID_ARG (num_blocks < 1). */
+#define QW_KV_BLOCK 64
+qw_status qw_create_paged(const qw_config *cfg, const qw_weights *weights, int32_t num_blocks, void *hip_stream,
+                          qw_model **out);
+
 /* Prefill: run `batch` equal-length prompts ids[batch][prompt_len] (int32,
  * device, each in [0, V)) through the model at positions 0 .. prompt_len-1,
  * writing their keys and values into the cache.  Every sequence restarts at
@@ -156,13 +173,29 @@ qw_status qw_create(const qw_config *cfg, const qw_weights *weights, void *hip_s
 qw_status qw_prefill(qw_model *m, const int32_t *ids, int32_t batch, int32_t prompt_len,
                      float *logits, int32_t logits_all, int32_t *next_ids);
 
+/* Ragged prefill ("augur", "Not yet" list: batching of prompts of different
+ * lengths): n_seqs prompts of lens[b] tokens (lens: HOST array, each in
+ * [1, max_seq]) packed back to back in ids[sum(lens)] (device), no padding.
+ * Sequence b goes to batch row b at positions 0 .. lens[b] - 1; every row
+ * attends causally within its own sequence only.  Outputs as qw_prefill
+ * without logits_all: next_ids[n_seqs]; logits NULL or fp32 [n_seqs][V] of
+ * each sequence's last position.  Later qw_decode_step calls continue every
+ * sequence from its own position.  Works on dense and paged models.
+ * Errors: INVALID_ARG (NULL pointers, n_seqs outside [1, max_batch], a length
+ * < 1), CACHE_FULL (a length > max_seq, or a paged pool too small for the
+ * prompts), HIP. */
+qw_status qw_prefill_ragged(qw_model *m, const int32_t *ids, const int32_t *lens, int32_t n_seqs, float *logits,
+                            int32_t *next_ids);
+
 /* One greedy decode step for every sequence of the last prefill: feeds
- * ids[batch] (device; may alias the previous call's next_ids) at the next
- * position, appends their keys and values to the cache, and writes next_ids
- * [batch] and, if non-NULL, fp32 logits[batch][V].  The position advances on
- * the device, so steps may be enqueued back to back without host syncs.
+ * ids[batch] (device; may alias the previous call's next_ids) at each
+ * sequence's next position (its own after a ragged prefill), appends their
+ * keys and values to the cache, and writes next_ids[batch] and, if non-NULL,
+ * fp32 logits[batch][V].  Positions advance on the device, so steps may be
+ * enqueued back to back without host syncs.
  * Errors: INVALID_ARG (NULL ids/next_ids), BAD_STATE (no prefill yet),
- * CACHE_FULL (the cache already holds max_seq positions), HIP.
+ * CACHE_FULL (a sequence already holds max_seq positions, or a paged pool has
+ * no free block for a sequence that needs one), HIP.
  * Source: "Building a Qwen2.5-1.5B Inference Engine From Scratch", section 1
  * (decode feeds one new token per step against the cache); "LLM Speedrun:
  * Architecture", "Decoding" and the harness listing's generation loop. */
@@ -223,8 +256,17 @@ const char *qw_last_error(void);
 /* ---- inspection and measurement helpers (not on the hot path) ----------- */
 
 /* Host view of the state: *batch of the last prefill (0 if none) and *pos,
- * the number of cache positions each sequence holds. */
+ * the number of cache positions the longest sequence holds. */
 qw_status qw_get_state(const qw_model *m, int32_t *batch, int32_t *pos);
+
+/* Cache positions held by each of the first n sequences, into the HOST array
+ * pos[n] (0 past the batch).  No synchronisation: host bookkeeping.
+ * Errors: INVALID_ARG (NULL, n outside [0, max_batch]). */
+qw_status qw_get_positions(const qw_model *m, int32_t *pos, int32_t n);
+
+/* Paged models: free and total blocks of the pool (HOST outputs); 0 and 0 on
+ * a dense model.  Errors: INVALID_ARG (NULL). */
+qw_status qw_kv_blocks(const qw_model *m, int32_t *free_blocks, int32_t *total_blocks);
 
 /* Synchronise the stream and report whether any token id handed to prefill or
  * decode since the last check was outside [0, V): QW_ERR_INVALID_ARG if so

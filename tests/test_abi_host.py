@@ -99,7 +99,25 @@ def test_calls_on_null_model(Q):
     lib = Q.load_library()
     assert lib.qw_prefill(None, None, 1, 1, None, 0, None) == -1
     assert lib.qw_decode_step(None, None, None, None) == -1
+    assert lib.qw_prefill_ragged(None, None, None, 1, None, None) == -1
+    assert lib.qw_get_positions(None, None, 0) == -1
+    assert lib.qw_kv_blocks(None, None, None) == -1
     assert lib.qw_destroy(None) == 0
+
+
+@pytest.mark.parametrize("blocks", [0, -3])
+def test_create_paged_rejects_an_empty_pool(Q, blocks):
+    w, _keep = _weights(Q)
+    with pytest.raises(Q.QwError) as e:
+        Q.qw_create_paged(_cfg(Q), w, blocks, 0)
+    assert e.value.status == -1 and "num_blocks" in str(e.value)
+
+
+def test_create_paged_validates_the_config_first(Q):
+    w, _keep = _weights(Q)
+    with pytest.raises(Q.QwError) as e:
+        Q.qw_create_paged(_cfg(Q, n_heads=5), w, 8, 0)
+    assert e.value.status == -1
 
 
 def test_create_without_a_device_reports_the_hip_call(Q):
