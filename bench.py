@@ -252,6 +252,94 @@ def cache_compare(torch, Q, w: S.Workload, steps: int, reps: int, warmup: int):
             "rows_with_identical_tokens": int(agree.sum())}
 
 
+def ragged_compare(torch, Q, name: str, reps: int, warmup: int, padded: bool = True):
+    """A ragged batch (prompts of different lengths, packed, no padding) on
+    the paged KV cache, against the same prompts padded to the longest one on
+    the dense cache (what a batch without ragged support computes): prefill
+    time, decode step time, and the cache each needs.  Useful tokens only
+    count toward the rates of both."""
+    rw = S.RAGGED_WORKLOADS[name]
+    m, n, D = rw.model, rw.n, rw.decode_steps
+    lens, prompts = rw.lengths(), rw.prompts()
+    L_max, T = max(lens), sum(lens)
+    max_seq = L_max + D
+    W = S.make_weights(m, rw.weight_seed)
+    tensors = Q.device_tensors(m, W)
+    blk = Q.QW_KV_BLOCK
+    n_blocks = sum((x + D + blk - 1) // blk for x in lens)
+    kv_elem_bytes = 2 * m.n_layers * m.kv_dim * 2        # K and V, all layers, f16, per position
+
+    def timed_runs(model, prefill):
+        toks = torch.empty((D + 1, n), dtype=torch.int32, device="cuda")
+
+        def one(ev=None):
+            if ev:
+                ev[0].record()
+            prefill(toks[0])
+            if ev:
+                ev[1].record()
+            for k in range(D):
+                model.decode_step(toks[k], next_ids=toks[k + 1])
+            if ev:
+                ev[2].record()
+        for _ in range(warmup):
+            one()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for e in evs:
+            one(e)
+        torch.cuda.synchronize()
+        return (float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+                float(np.mean([e[1].elapsed_time(e[2]) for e in evs])))
+
+    print(f"[bench] ragged {name}: {n} prompts, {T} tokens (longest {L_max}), paged cache", file=sys.stderr,
+          flush=True)
+    model = Q.Model(m, tensors, n, max_seq, kv_blocks=n_blocks)
+    ids = torch.from_numpy(np.concatenate(prompts)).cuda()
+    r_pre, r_dec = timed_runs(model, lambda out: model.prefill_ragged(ids, lens, next_ids=out))
+    model.check_numerics()
+    model.close()
+    torch.cuda.empty_cache()
+    p_pre = p_dec = float("nan")
+    if padded:
+        print(f"[bench] padded to {L_max}, dense cache", file=sys.stderr, flush=True)
+        pad = np.zeros((n, L_max), dtype=np.int32)
+        for b, p in enumerate(prompts):
+            pad[b, :len(p)] = p
+        model = Q.Model(m, tensors, n, max_seq)
+        pids = torch.from_numpy(pad).cuda()
+        p_pre, p_dec = timed_runs(model, lambda out: model.prefill(pids, next_ids=out))
+        model.close()
+        torch.cuda.empty_cache()
+
+    # algorithmic work of the ragged batch
+    H, I, V, qd, kvd = m.hidden, m.intermediate, m.vocab, m.q_dim, m.kv_dim
+    gemm_per_row = 2.0 * H * ((qd + 2 * kvd) + qd + 3 * I)
+    attn = sum(2.0 * m.n_heads * m.head_dim * x * (x + 1) for x in lens)
+    pflop = m.n_layers * (gemm_per_row * T + attn) + 2.0 * n * V * H
+    e = 2
+    weights = e * (m.n_layers * (H * (qd + 2 * kvd) + qd * H + 3 * H * I) + V * H)
+    ctx_mean = T / n + (D - 1) / 2.0
+    step_bytes = weights + n * m.n_layers * 2 * kvd * e * (ctx_mean + 1)
+    return {
+        "metric": "ragged batch on the paged KV cache vs the same prompts padded on the dense cache",
+        "workload": f"{name}: Qwen2.5-1.5B shapes, bf16 weights, {n} prompts of {rw.min_len}..{rw.max_len} tokens "
+                    f"(log-uniform, seed {rw.lens_seed}), {D} greedy decode steps",
+        "prompt_tokens": T, "longest": L_max, "lengths": lens, "reps": reps,
+        "ragged_paged": {"ttft_ms": round(r_pre, 3), "prefill_tokens_per_s": round(T / (r_pre / 1e3), 1),
+                         "decode_ms_per_step": round(r_dec / D, 4), "decode_tokens_per_s": round(n * D / (r_dec / 1e3), 1),
+                         "cache_blocks": n_blocks, "cache_bytes": n_blocks * blk * kv_elem_bytes},
+        "padded_dense": {"ttft_ms": round(p_pre, 3), "prefill_tokens_per_s": round(T / (p_pre / 1e3), 1),
+                         "decode_ms_per_step": round(p_dec / D, 4), "decode_tokens_per_s": round(n * D / (p_dec / 1e3), 1),
+                         "cache_bytes": n * max_seq * kv_elem_bytes},
+        "ttft_speedup": round(p_pre / r_pre, 2), "decode_speedup": round(p_dec / r_dec, 2),
+        "decode_step_roofline": roof("hbm", "whole decode step, ragged (graph replay)",
+                                     step_bytes / (r_dec / D / 1e3) / 1e9, HBM_PEAK_GBS, None, "GB/s",
+                                     bytes_per_step=int(step_bytes)),
+        "prefill_whole_roofline": roof("mfma", "whole ragged prefill (TTFT)", pflop / (r_pre / 1e3) / 1e12,
+                                       MFMA_F16_PEAK_TFLOPS, None, "TFLOP/s", flop=pflop),
+    }
+
+
 def roof(bound, kernel, achieved, peak, measured_peak, unit, **extra):
     out = {"bound": bound, "kernel": kernel, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
            "frac": round(achieved / peak, 4)}
@@ -276,6 +364,10 @@ def main():
                          "(same kernels; for counter collection, which does not follow graph launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 4 device copies of 256 MiB (the reference for HBM byte counters)")
+    ap.add_argument("--ragged", choices=sorted(S.RAGGED_WORKLOADS), default=None,
+                    help="only compare a ragged batch on the paged cache with the same prompts padded on the "
+                         "dense cache; prints its own JSON line")
+    ap.add_argument("--no-padded", action="store_true", help="--ragged without the padded baseline")
     ap.add_argument("--cache-compare", type=int, default=0, metavar="STEPS",
                     help="only compare greedy generation of STEPS tokens with and without the KV cache "
                          "(qw_generate) on the workload's prompts; prints its own JSON line")
@@ -298,6 +390,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_dispatch": n, "dispatches": 4}), flush=True)
+        return
+
+    if args.ragged:
+        print(json.dumps(ragged_compare(torch, Q, args.ragged, args.steps, args.warmup, not args.no_padded)),
+              flush=True)
         return
 
     w = S.WORKLOADS[args.workload]

@@ -58,7 +58,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   const int nq = a.n_heads, grp = a.n_heads / a.n_kv_heads;
   // work item: heaviest query tiles first; the g heads of a group adjacent,
   // and adjacent items on one XCD (workgroups go round-robin over 8 XCDs).
-  // Ragged batches take (sequence, query tile) from a list in that order.
+  // Ragged batches take (sequence, query tile) from a list the host ordered
+  // so that each XCD's range starts heaviest and the ranges weigh the same.
   const int total = a.tiles ? a.n_tiles * nq : n_qt * nq * (a.T / a.rows_per_seq);
   const int L = blockIdx.x;
   const int per_x = (total + 7) / 8;

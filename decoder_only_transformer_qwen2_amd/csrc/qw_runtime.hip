@@ -1151,7 +1151,7 @@ hipError_t prefill_ragged_enqueue(qw_model *m, const int32_t *ids, const int32_t
   hipError_t e = assign_blocks(m, s, lens, 0, n);
   if (e != hipSuccess) return e;
   // device layout: cu [n + 1], pcu [n + 1] (after max_batch + 1 entries),
-  // then the query tiles, longest first: (sequence << 16) | tile
+  // then the query-tile list, (sequence << 16) | tile, in the order below
   const int off_pcu = c.max_batch + 1, off_tiles = 2 * (c.max_batch + 1);
   std::vector<int> idx, val;
   int T = 0, PT = 0, max_len = 0, max_qt = 0;
@@ -1167,13 +1167,34 @@ hipError_t prefill_ragged_enqueue(qw_model *m, const int32_t *ids, const int32_t
       max_qt = std::max(max_qt, (lens[b] + 127) / 128);
     }
   }
-  int n_tiles = 0;
+  // The attention kernel deals work item w = tile * nq + head to XCD
+  // w / ceil(n_tiles * nq / 8) (workgroups go round-robin over the 8 XCDs,
+  // and each XCD walks its range in order).  Tiles are placed heaviest first
+  // (cost ~ qt + 1 key blocks) on the XCD with the least work so far that
+  // still has room, so the XCDs end together and each starts with its
+  // heaviest tiles.
+  std::vector<int> order;
   for (int qt = max_qt - 1; qt >= 0; --qt)
     for (int b = 0; b < n; ++b)
-      if ((lens[b] + 127) / 128 > qt) {
-        idx.push_back(off_tiles + n_tiles++);
-        val.push_back((b << 16) | qt);
-      }
+      if ((lens[b] + 127) / 128 > qt) order.push_back((b << 16) | qt);
+  const int n_tiles = (int)order.size();
+  const int64_t per_x = ((int64_t)n_tiles * c.n_heads + 7) / 8;
+  std::vector<std::vector<int>> slots(8);             // tile positions of each XCD, in order
+  for (int t = 0; t < n_tiles; ++t) slots[std::min<int64_t>(7, (int64_t)t * c.n_heads / per_x)].push_back(t);
+  std::vector<int64_t> load(8, 0);
+  std::vector<size_t> used(8, 0);
+  std::vector<int> placed(n_tiles);
+  for (int it : order) {
+    int best = -1;
+    for (int x = 0; x < 8; ++x)
+      if (used[x] < slots[x].size() && (best < 0 || load[x] < load[best])) best = x;
+    placed[slots[best][used[best]++]] = it;
+    load[best] += (it & 0xffff) + 1;
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    idx.push_back(off_tiles + t);
+    val.push_back(placed[t]);
+  }
   if ((e = launch_put_ints(s, m->rag_meta, idx.data(), val.data(), (int)idx.size())) != hipSuccess) return e;
   RaggedPlan plan;
   plan.rows.cu = m->rag_meta;

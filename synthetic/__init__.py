@@ -29,7 +29,7 @@ from typing import Dict, List
 import numpy as np
 
 __all__ = [
-    "ModelShape", "Workload", "WORKLOADS", "MODEL_SHAPES", "tensor_names",
+    "ModelShape", "Workload", "WORKLOADS", "MODEL_SHAPES", "RaggedWorkload", "RAGGED_WORKLOADS", "tensor_names",
     "tensor_shape", "make_weights", "make_ids", "param_count", "f32_to_bf16_bits",
 ]
 
@@ -115,6 +115,38 @@ WORKLOADS: Dict[str, Workload] = {
     # the second model family the pages name (not one of the five graded
     # workloads): one sequence, as the speedrun harness runs it
     "coder-7b": Workload("coder-7b", QWEN25_CODER_7B, batch=1, prompt_len=512, decode_steps=128, max_seq=1024),
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class RaggedWorkload:
+    """A batch of prompts of different lengths (ragged, no padding): n
+    lengths drawn log-uniformly from [min_len, max_len] (seeded), then
+    `decode_steps` greedy steps; a paged cache sized to the positions held."""
+    name: str
+    model: ModelShape
+    n: int
+    min_len: int
+    max_len: int
+    decode_steps: int
+    weight_seed: int = 0
+    lens_seed: int = 7
+
+    def lengths(self) -> List[int]:
+        rng = np.random.default_rng(self.lens_seed)
+        u = rng.random(self.n)
+        lens = np.exp(np.log(self.min_len) + u * (np.log(self.max_len) - np.log(self.min_len)))
+        return [int(min(self.max_len, max(self.min_len, round(x)))) for x in lens]
+
+    def prompts(self) -> List[np.ndarray]:
+        rng = np.random.default_rng(self.weight_seed + 1)
+        return [rng.integers(0, self.model.vocab, n, dtype=np.int64).astype(np.int32) for n in self.lengths()]
+
+
+# Ragged serving batch (the pages' "not yet" list: paged attention, batches
+# of prompts of different lengths): 32 prompts of 256 .. 8192 tokens.
+RAGGED_WORKLOADS: Dict[str, RaggedWorkload] = {
+    "1.5b-ragged": RaggedWorkload("1.5b-ragged", QWEN25_15B, n=32, min_len=256, max_len=8192, decode_steps=128),
 }
 
 _LAYER_TENSORS = (

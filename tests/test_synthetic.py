@@ -60,3 +60,15 @@ def test_coder7b_shape_matches_the_listed_config():
         c["intermediate_size"], c["vocab_size"])
     assert m.rope_theta == c["rope_theta"] and m.rms_eps == c["rms_norm_eps"]
     assert not m.tie_embeddings and "lm_head.weight" in S.tensor_names(m)
+
+
+def test_ragged_workload_lengths():
+    """The ragged serving batch: 32 seeded lengths within [256, 8192], the
+    prompts of those lengths with ids in range, the same on every call."""
+    w = S.RAGGED_WORKLOADS["1.5b-ragged"]
+    lens = w.lengths()
+    assert len(lens) == 32 and min(lens) >= 256 and max(lens) <= 8192
+    assert lens == w.lengths() and len(set(lens)) > 16
+    ps = w.prompts()
+    assert [len(p) for p in ps] == lens
+    assert all(p.dtype == np.int32 and p.min() >= 0 and p.max() < w.model.vocab for p in ps)
