@@ -19,7 +19,8 @@
 // LDS with two buffers, both as 16-byte vectors: V^T comes from a transposed
 // copy of the prompt's V written once per layer (transpose_v_kernel), since
 // transposing inside the kernel took 2-byte LDS stores with 16-way bank
-// conflicts.  Work items are ordered heaviest (latest
+// conflicts.  The tiles sit in LDS as swizzled 32-column sub-tiles (see swz).
+// Work items are ordered heaviest (latest
 // query tile) first and mapped so that the g query heads of a KV head and
 // query tile run on the same XCD, where they share the K/V tiles in L2.
 #include "qw_internal.h"
@@ -42,16 +43,20 @@ constexpr float RESCALE_LOG2 = 8.0f;  // largest exponent (log2) a probability m
 // float flush to zero, which a probability can afford (it is rounded to f16)
 __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS tiles are kept as 32-column sub-tiles of 64-byte rows (four 16-byte
+// chunks), chunk c of row r stored at c ^ swz(r): the 16 rows a fragment read
+// touches then fall on distinct banks (the padded 272- and 144-byte rows of
+// the first layout measured bank conflicts on 40% of the LDS cycles).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
 template <int HD>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) attn_prefill_kernel(AttnArgs a, int n_qt) {
-  constexpr int KP = HD + 8;          // padded K row
-  constexpr int VP = BKEY + 8;        // padded V^T row
-  constexpr int KS = HD / 32;         // 32-wide d steps for S
+  constexpr int KS = HD / 32;         // 32-wide d steps for S (K sub-tiles)
   constexpr int DT = HD / 16;         // 16-wide d tiles of O
   constexpr int VEC = BKEY * HD / 8;  // 16-byte vectors per K (or V) tile
   constexpr int VPT = VEC / 256;      // per thread
-  __shared__ f16 sK[2][BKEY][KP];
-  __shared__ f16 sV[2][HD][VP];
+  __shared__ f16x8 sK[2][KS * BKEY * 4];   // [ks][key row][chunk]
+  __shared__ f16x8 sV[2][2 * HD * 4];      // [u][d row][chunk]: keys 32u .. 32u + 31
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, g = lane >> 4;
@@ -97,13 +102,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
       qf[t][s] = (q < P) ? *reinterpret_cast<const f16x8 *>(Q + (int64_t)q * qd + 32 * s + 8 * g) : zero8;
     }
 
+  // Online softmax state of the lane's query column (t): the reference m
+  // (raw score units) that the exponents are taken from, and the running sum
+  // l of the probabilities, which the matrix cores accumulate: a ones tile as
+  // the A operand gives every row of lsum[t] the column sum of P^T, rescaled
+  // with O.  The reference only moves when a score exceeds it by more than
+  // RESCALE_LOG2 (in log2 units), so most blocks need no cross-lane maximum.
   const float sl2 = a.softmax_scale * 1.4426950408889634f;
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-  f32x4 o[DT][2];
+  const float thr = RESCALE_LOG2 / sl2;              // the move threshold in raw score units
+  float m[2] = {0.f, 0.f};
+  f32x4 o[DT][2], lsum[2];
 #pragma unroll
   for (int d = 0; d < DT; ++d)
 #pragma unroll
     for (int t = 0; t < 2; ++t) o[d][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  lsum[0] = lsum[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (f16)1.0f;
 
   const int q_last = min(P - 1, qt * BQ + BQ - 1);    // last query of the workgroup
   const int n_kb = q_last / BKEY + 1;                  // key blocks it needs
@@ -114,29 +130,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   const int64_t vt_seq = a.tiles ? (int64_t)a.rag.pcu[b] : (int64_t)b * PP;   // padded rows before sequence b
   const f16 *Vt = (const f16 *)a.v_t + (vt_seq * a.n_kv_heads + (int64_t)j * PP) * HD;
   static_assert(BKEY == kKvBlock, "a key tile is one cache block");
+  // Vector v of a tile: chunk v & 3 of row (v >> 2) of a 32-column sub-tile,
+  // so four lanes read 64 contiguous bytes of a cache or V^T row, and eight
+  // lanes write two swizzled LDS rows.
   auto gload = [&](int kb) {
     const f16 *Kt = Kc + kv_offset(a.kv, a.n_kv_heads, HD, b, j, kb * BKEY);
 #pragma unroll
     for (int t = 0; t < VPT; ++t) {
       const int v = tid + 256 * t;
-      const int kk = v / (HD / 8), key = kb * BKEY + kk, c = (v % (HD / 8)) * 8;
-      rk[t] = key < P ? *reinterpret_cast<const f16x8 *>(Kt + (int64_t)kk * HD + c) : zero8;
-      const int d = v / (BKEY / 8), kc = (v % (BKEY / 8)) * 8;
-      rv[t] = *reinterpret_cast<const f16x8 *>(Vt + (int64_t)d * PP + kb * BKEY + kc);
+      const int cc = v & 3, kk = (v >> 2) % BKEY, ks = (v >> 2) / BKEY;
+      rk[t] = kb * BKEY + kk < P ? *reinterpret_cast<const f16x8 *>(Kt + (int64_t)kk * HD + 32 * ks + 8 * cc) : zero8;
+      const int d = (v >> 2) % HD, u = (v >> 2) / HD;
+      rv[t] = *reinterpret_cast<const f16x8 *>(Vt + (int64_t)d * PP + kb * BKEY + 32 * u + 8 * cc);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int t = 0; t < VPT; ++t) {
       const int v = tid + 256 * t;
-      const int key = v / (HD / 8), c = (v % (HD / 8)) * 8;
+      const int cc = v & 3, key = (v >> 2) % BKEY, ks = (v >> 2) / BKEY;
       // LDS row 32u + 16h + 4q + r holds key 32u + 8q + 4h + r (u, h < 2, q,
       // r < 4): the S^T rows a lane owns (4q .. 4q+3 of tiles 2u and 2u+1)
       // are then 8 consecutive keys, read from V^T in one 16-byte load
       const int krow = (key & ~31) | (((key >> 2) & 1) << 4) | (((key >> 3) & 3) << 2) | (key & 3);
-      *reinterpret_cast<f16x8 *>(&sK[buf][krow][c]) = rk[t];
-      const int d = v / (BKEY / 8), kc = (v % (BKEY / 8)) * 8;
-      *reinterpret_cast<f16x8 *>(&sV[buf][d][kc]) = rv[t];
+      sK[buf][(ks * BKEY + krow) * 4 + (cc ^ swz(krow))] = rk[t];
+      const int d = (v >> 2) % HD, u = (v >> 2) / HD;
+      sV[buf][(u * HD + d) * 4 + (cc ^ swz(d))] = rv[t];
     }
   };
 
@@ -148,35 +167,33 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
     if (kb + 1 < n_kb) gload(kb + 1);
     const bool wave_active = kb * BKEY <= q0 + 31;     // any key of the block visible to this wave
     if (wave_active) {
-      // S^T tiles: y = 16-key tile, t = 16-query tile
+      // S^T - m tiles: y = 16-key tile, t = 16-query tile; the accumulator
+      // starts at -m, so the scores come out relative to the reference
       f32x4 s[4][2];
 #pragma unroll
       for (int y = 0; y < 4; ++y)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) s[y][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 2; ++t) s[y][t] = f32x4{-m[t], -m[t], -m[t], -m[t]};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-          const f16x8 kf = *reinterpret_cast<const f16x8 *>(&sK[cur][16 * y + i][32 * ks + 8 * g]);
+          const int row = 16 * y + i;
+          const f16x8 kf = sK[cur][(ks * BKEY + row) * 4 + (g ^ swz(row))];
 #pragma unroll
           for (int t = 0; t < 2; ++t) s[y][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[t][ks], s[y][t], 0, 0, 0);
         }
-      // online softmax per query column; lane (i, g) holds, for S^T tile y,
-      // keys 32 (y / 2) + 8g + 4 (y % 2) + r (the permuted K rows).
-      // Scores stay unscaled: the scale goes into the exponent's FMA, and
-      // only blocks that reach past the wave's first query are masked.  The
-      // running max is finite from block 0 on (key 0 is visible to every
-      // query), and masked scores are -inf, so exp2 needs no guards.
+      // lane (i, g) holds, for S^T tile y, keys 32 (y / 2) + 8g + 4 (y % 2) + r
+      // (the permuted K rows) of its query column.  Only blocks that reach
+      // past the wave's first query are masked; masked scores are -inf, so
+      // exp2 gives 0 without guards.
       const bool diag = kb * BKEY + BKEY - 1 > q0;
-      f16x8 pb[2][2];
-      float corr[2];
-      bool any_move = false;
+      float lm[2];
+      if (diag) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int q = q0 + 16 * t + i;
-        float mx = -INFINITY;
-        if (diag) {
+        for (int t = 0; t < 2; ++t) {
+          const int q = q0 + 16 * t + i;
+          float mx = -INFINITY;
 #pragma unroll
           for (int y = 0; y < 4; ++y)
 #pragma unroll
@@ -186,62 +203,70 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
               s[y][t][r] = v;
               mx = fmaxf(mx, v);
             }
-        } else {
+          lm[t] = mx;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float mx = -INFINITY;
 #pragma unroll
           for (int y = 0; y < 4; ++y)
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[y][t][r]);
+          lm[t] = mx;
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // The reference point of the exponent only moves when the block's
-        // max exceeds it by more than RESCALE_LOG2 (in log2 units): softmax
-        // is invariant to the reference, and a stale one keeps every p below
-        // 2^RESCALE_LOG2.  Block 0 always moves it off -inf.
-        const float mn = fmaxf(m[t], mx);
-        const bool move = (mn - m[t]) * sl2 > RESCALE_LOG2;
-        const float mref = move ? mn : m[t];
-        corr[t] = move ? exp2_raw((m[t] - mn) * sl2) : 1.0f;
-        any_move |= move;
-        const float nb = -mref * sl2;
-        float sum = 0.f;
+      }
+      // Block 0 sets the reference (key 0 is visible to every query, so the
+      // column maximum is finite); later blocks move it only for a column
+      // with a score above m + thr.  Every lane of a column sees the same
+      // column maximum, so the 4 lanes agree on the move.
+      const bool first = kb == 0;
+      if (__builtin_amdgcn_ballot_w64(first || lm[0] > thr || lm[1] > thr) != 0) {
 #pragma unroll
-        for (int y = 0; y < 4; ++y)
+        for (int t = 0; t < 2; ++t) {
+          float cm = lm[t];
+          cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+          cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+          const float delta = (first || cm > thr) ? cm : 0.f;
+          if (delta != 0.f) {
+            const float corr = first ? 0.f : exp2_raw(-delta * sl2);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = exp2_raw(fmaf(s[y][t][r], sl2, nb));
-            s[y][t][r] = p;
-            sum += p;
+            for (int d = 0; d < DT; ++d) o[d][t] *= corr;
+            lsum[t] *= corr;
+#pragma unroll
+            for (int y = 0; y < 4; ++y)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) s[y][t][r] -= delta;
+            m[t] += delta;
           }
-        sum += __shfl_xor(sum, 16, 64);
-        sum += __shfl_xor(sum, 32, 64);
-        l[t] = l[t] * corr[t] + sum;
-        m[t] = mref;
-        // B operand of step u: keys 32u + 8g + e (tile 2u gives e < 4, tile 2u + 1 the rest)
+        }
+      }
+      // probabilities, packed as the B operand of step u: keys 32u + 8g + e
+      // (tile 2u gives e < 4, tile 2u + 1 the rest)
+      f16x8 pb[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pb[t][u][e] = (f16)s[2 * u][t][e];
-            pb[t][u][e + 4] = (f16)s[2 * u + 1][t][e];
+            pb[t][u][e] = (f16)exp2_raw(s[2 * u][t][e] * sl2);
+            pb[t][u][e + 4] = (f16)exp2_raw(s[2 * u + 1][t][e] * sl2);
           }
-      }
-      // rescale the accumulators only when some query of the wave moved its reference
-      if (__builtin_amdgcn_ballot_w64(any_move) != 0) {
+      // O^T += V^T . P^T (A operand from the transposed V tile with the same
+      // key order) and l += ones . P^T
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int d = 0; d < DT; ++d) o[d][t] *= corr[t];
-      }
-      // O^T += V^T . P^T, A operand from the transposed V tile with the same key order
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
-          const f16x8 vf = *reinterpret_cast<const f16x8 *>(&sV[cur][16 * d + i][32 * u + 8 * g]);
+          const int row = 16 * d + i;
+          const f16x8 vf = sV[cur][(u * HD + row) * 4 + (g ^ swz(row))];
 #pragma unroll
           for (int t = 0; t < 2; ++t) o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[t][u], o[d][t], 0, 0, 0);
         }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[t][u], lsum[t], 0, 0, 0);
+      }
     }
     if (kb + 1 < n_kb) lstore(cur ^ 1);
     __syncthreads();
@@ -253,7 +278,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   for (int t = 0; t < 2; ++t) {
     const int q = q0 + 16 * t + i;
     if (q >= P) continue;
-    const float inv = 1.0f / l[t];
+    const float inv = 1.0f / lsum[t][0];
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
       f16x4 v;
