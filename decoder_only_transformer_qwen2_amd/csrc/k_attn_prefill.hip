@@ -14,13 +14,13 @@
 // P never goes through LDS.  The K rows of each 32-key step are stored in a
 // permuted order so that the 8 probabilities a lane holds for a step are 8
 // consecutive keys, which its V^T operand reads in one 16-byte load.  A
-// workgroup is 4 waves x 32 queries of
-// one head; the K tile ([key][d]) and the V^T tile ([d][key]) are staged in
-// LDS with two buffers, both as 16-byte vectors: V^T comes from a transposed
-// copy of the prompt's V written once per layer (transpose_v_kernel), since
+// workgroup is 4 waves x 32 queries of one head (two workgroups per CU).  The
+// tiles go straight from memory into a ring of two LDS stages (the next key
+// block in flight while one is multiplied), as swizzled 32-column sub-tiles
+// (see swz).  V^T comes from a transposed copy of
+// the prompt's V written once per layer (transpose_v_kernel), since
 // transposing inside the kernel took 2-byte LDS stores with 16-way bank
-// conflicts.  The tiles sit in LDS as swizzled 32-column sub-tiles (see swz).
-// Work items are ordered heaviest (latest
+// conflicts.  Work items are ordered heaviest (latest
 // query tile) first and mapped so that the g query heads of a KV head and
 // query tile run on the same XCD, where they share the K/V tiles in L2.
 #include "qw_internal.h"
@@ -35,9 +35,23 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BQ = 128;   // queries per workgroup (4 waves x 32)
-constexpr int BKEY = 64;  // keys per step
+constexpr int BKEY = 64;  // keys per step (one cache block)
+// Waves per workgroup and LDS stages (key blocks resident or in flight).
+// Measured at 32 x 8192 (hd 128, ms per prefill): 4 waves x 2 stages 187.7
+// (two workgroups per CU, whose barriers do not hold each other), 8 x 2
+// 188.1, 8 x 4 193.3, 8 x 3 198.4; at 8 x 2048: 3.68, 3.88, 3.94, 4.01.
+#ifndef QW_ATTN_WAVES
+#define QW_ATTN_WAVES 4
+#endif
+#ifndef QW_ATTN_STAGES
+#define QW_ATTN_STAGES 2
+#endif
+constexpr int AW = QW_ATTN_WAVES;
+constexpr int AS = QW_ATTN_STAGES;
+static_assert(AS >= 2 && AS <= 4, "stage ring");
+constexpr int BQ = 32 * AW;   // queries per workgroup
 constexpr float RESCALE_LOG2 = 8.0f;  // largest exponent (log2) a probability may reach before a rescale
+constexpr int kTableLds = 512;        // paged cache: block ids held in LDS (contexts up to 32768 keys)
 
 // 2^x with the hardware instruction alone: results below the smallest normal
 // float flush to zero, which a probability can afford (it is rounded to f16)
@@ -49,14 +63,24 @@ __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp
 // the first layout measured bank conflicts on 40% of the LDS cycles).
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
 
+// K rows are stored permuted: LDS row 32u + 16h + 4q + r holds key
+// 32u + 8q + 4h + r (u, h < 2, q, r < 4), so that the S^T rows a lane owns
+// (4q .. 4q+3 of tiles 2u and 2u+1) are 8 consecutive keys, which its V^T
+// operand reads in one 16-byte load.
+__device__ __forceinline__ int key_of_row(int row) {
+  return (row & ~31) | (((row >> 2) & 3) << 3) | (((row >> 4) & 1) << 2) | (row & 3);
+}
+
 template <int HD>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) attn_prefill_kernel(AttnArgs a, int n_qt) {
-  constexpr int KS = HD / 32;         // 32-wide d steps for S (K sub-tiles)
-  constexpr int DT = HD / 16;         // 16-wide d tiles of O
-  constexpr int VEC = BKEY * HD / 8;  // 16-byte vectors per K (or V) tile
-  constexpr int VPT = VEC / 256;      // per thread
-  __shared__ f16x8 sK[2][KS * BKEY * 4];   // [ks][key row][chunk]
-  __shared__ f16x8 sV[2][2 * HD * 4];      // [u][d row][chunk]: keys 32u .. 32u + 31
+__global__ void __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(2))) attn_prefill_kernel(AttnArgs a, int n_qt) {
+  constexpr int KS = HD / 32;               // 32-wide d steps for S (K sub-tiles)
+  constexpr int DT = HD / 16;               // 16-wide d tiles of O
+  constexpr int KCH = KS * BKEY * 4;        // 16-byte chunks of a stage's K tile
+  constexpr int VCH = 2 * HD * 4;           // of its V^T tile
+  constexpr int NI = (KCH + VCH) / (64 * AW);   // loads per wave and stage
+  static_assert((KCH + VCH) % (64 * AW) == 0 && KCH % 64 == 0, "whole load instructions per wave");
+  __shared__ f16x8 sK[AS][KCH];   // [ks][key row][chunk]
+  __shared__ f16x8 sV[AS][VCH];   // [u][d row][chunk]: keys 32u .. 32u + 31
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, g = lane >> 4;
@@ -73,11 +97,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   const int h = w % nq;
   int qt, b, P, r0;
   if (a.tiles) {
-    const int it = a.tiles[w / nq];
+    // wave-uniform values read from memory: said so, so that the block-table
+    // lookups below are scalar loads (a vector load would need a vmcnt wait,
+    // which would also wait for every key block in flight)
+    const int it = __builtin_amdgcn_readfirstlane(a.tiles[w / nq]);
     b = it >> 16;
     qt = it & 0xffff;
-    r0 = a.rag.cu[b];
-    P = a.rag.cu[b + 1] - r0;
+    r0 = __builtin_amdgcn_readfirstlane(a.rag.cu[b]);
+    P = __builtin_amdgcn_readfirstlane(a.rag.cu[b + 1]) - r0;
   } else {
     P = a.rows_per_seq;
     qt = n_qt - 1 - (w / nq) % n_qt;
@@ -92,15 +119,60 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   const f16 *Kc = (const f16 *)a.k_cache;
   const f16x8 zero8 = {};
 
-  // queries as B operands: lane (i, g) holds query q0 + 16t + i, dims 32s + 8g .. +8
-  f16x8 qf[2][KS];
+  // Key blocks go straight from memory into a ring of AS LDS stages: load
+  // instruction n (n = NI * wave + q) of a stage fills its chunks 64n .. 64n
+  // + 63, the K tile's first, then the V^T tile's; lane l's 16 bytes land at
+  // chunk 64n + l, so each lane fetches the (row, chunk) that the swizzled,
+  // permuted layout keeps there.  K rows past the prompt are clamped to its
+  // last row (their scores are masked); V^T rows come from a transposed copy
+  // of the prompt's V, zero past P in rows of round_up(P, 64) keys.
+  const int q_last = min(P - 1, qt * BQ + BQ - 1);    // last query of the workgroup
+  const int n_kb = q_last / BKEY + 1;                  // key blocks it needs
+  const int PP = (P + BKEY - 1) / BKEY * BKEY;
+  const int64_t vt_seq = a.tiles ? (int64_t)a.rag.pcu[b] : (int64_t)b * PP;   // padded rows before sequence b
+  const f16 *Vt = (const f16 *)a.v_t + (vt_seq * a.n_kv_heads + (int64_t)j * PP) * HD;
+  static_assert(BKEY == kKvBlock, "a key tile is one cache block");
+  // A paged cache's block ids of this sequence go to LDS first: read in the
+  // loop, the table (which the compiler cannot treat as read-only) would be a
+  // vector load whose wait would also wait for every key block in flight.
+  __shared__ int s_blk[kTableLds];
+  const bool tbl_lds = a.kv.table != nullptr && n_kb <= kTableLds;
+  if (tbl_lds) {
+    for (int k = tid; k < n_kb; k += 64 * AW) s_blk[k] = a.kv.table[b * a.kv.blocks_per_seq + k];
+    __syncthreads();
+  }
+  int src[NI], kkey[NI];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int q = q0 + 16 * t + i;
-      qf[t][s] = (q < P) ? *reinterpret_cast<const f16x8 *>(Q + (int64_t)q * qd + 32 * s + 8 * g) : zero8;
+  for (int q = 0; q < NI; ++q) {
+    const int n = NI * wave + q, p = 64 * n + lane;
+    if (n < KCH / 64) {
+      const int ks = p / (4 * BKEY), row = (p >> 2) % BKEY, c = (p & 3) ^ swz(row);
+      kkey[q] = key_of_row(row);
+      src[q] = 32 * ks + 8 * c;
+    } else {
+      const int p2 = p - KCH, u = p2 / (4 * HD), row = (p2 >> 2) % HD, c = (p2 & 3) ^ swz(row);
+      kkey[q] = 0;
+      src[q] = row * PP + 32 * u + 8 * c;
     }
+  }
+  auto issue = [&](int kb) {
+    const int st = kb % AS;
+    int64_t koff;
+    if (tbl_lds)
+      koff = ((int64_t)s_blk[kb] * a.n_kv_heads + j) * (kKvBlock * HD);
+    else
+      koff = kv_offset(a.kv, a.n_kv_heads, HD, b, j, kb * BKEY);
+    const f16 *Kt = Kc + koff;
+    const int last_row = P - 1 - kb * BKEY;            // rows of the block past the prompt read this one
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int n = NI * wave + q;
+      if (n < KCH / 64)
+        dma16(Kt + (int64_t)min(kkey[q], last_row) * HD + src[q], &sK[st][64 * n]);
+      else
+        dma16(Vt + src[q] + kb * BKEY, &sV[st][64 * n - KCH]);
+    }
+  };
 
   // Online softmax state of the lane's query column (t): the reference m
   // (raw score units) that the exponents are taken from, and the running sum
@@ -121,50 +193,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (f16)1.0f;
 
-  const int q_last = min(P - 1, qt * BQ + BQ - 1);    // last query of the workgroup
-  const int n_kb = q_last / BKEY + 1;                  // key blocks it needs
-  f16x8 rk[VPT], rv[VPT];
-  // K rows [key][d] from the cache, V^T rows [d][key] from the transposed
-  // copy (rows of round_up(P, 64) keys, zero past P): both as 16-byte vectors
-  const int PP = (P + BKEY - 1) / BKEY * BKEY;
-  const int64_t vt_seq = a.tiles ? (int64_t)a.rag.pcu[b] : (int64_t)b * PP;   // padded rows before sequence b
-  const f16 *Vt = (const f16 *)a.v_t + (vt_seq * a.n_kv_heads + (int64_t)j * PP) * HD;
-  static_assert(BKEY == kKvBlock, "a key tile is one cache block");
-  // Vector v of a tile: chunk v & 3 of row (v >> 2) of a 32-column sub-tile,
-  // so four lanes read 64 contiguous bytes of a cache or V^T row, and eight
-  // lanes write two swizzled LDS rows.
-  auto gload = [&](int kb) {
-    const f16 *Kt = Kc + kv_offset(a.kv, a.n_kv_heads, HD, b, j, kb * BKEY);
 #pragma unroll
-    for (int t = 0; t < VPT; ++t) {
-      const int v = tid + 256 * t;
-      const int cc = v & 3, kk = (v >> 2) % BKEY, ks = (v >> 2) / BKEY;
-      rk[t] = kb * BKEY + kk < P ? *reinterpret_cast<const f16x8 *>(Kt + (int64_t)kk * HD + 32 * ks + 8 * cc) : zero8;
-      const int d = (v >> 2) % HD, u = (v >> 2) / HD;
-      rv[t] = *reinterpret_cast<const f16x8 *>(Vt + (int64_t)d * PP + kb * BKEY + 32 * u + 8 * cc);
-    }
-  };
-  auto lstore = [&](int buf) {
+  for (int k = 0; k < AS - 1; ++k)
+    if (k < n_kb) issue(k);
+  // queries as B operands: lane (i, g) holds query q0 + 16t + i, dims 32s +
+  // 8g .. +8.  Loaded after the first key blocks and awaited here with them:
+  // the compiler's own wait for these loads would otherwise sit at their
+  // first use inside the loop and, executed every iteration, wait for every
+  // key block in flight.
+  f16x8 qf[2][KS];
 #pragma unroll
-    for (int t = 0; t < VPT; ++t) {
-      const int v = tid + 256 * t;
-      const int cc = v & 3, key = (v >> 2) % BKEY, ks = (v >> 2) / BKEY;
-      // LDS row 32u + 16h + 4q + r holds key 32u + 8q + 4h + r (u, h < 2, q,
-      // r < 4): the S^T rows a lane owns (4q .. 4q+3 of tiles 2u and 2u+1)
-      // are then 8 consecutive keys, read from V^T in one 16-byte load
-      const int krow = (key & ~31) | (((key >> 2) & 1) << 4) | (((key >> 3) & 3) << 2) | (key & 3);
-      sK[buf][(ks * BKEY + krow) * 4 + (cc ^ swz(krow))] = rk[t];
-      const int d = (v >> 2) % HD, u = (v >> 2) / HD;
-      sV[buf][(u * HD + d) * 4 + (cc ^ swz(d))] = rv[t];
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int q = q0 + 16 * t + i;
+      qf[t][s] = (q < P) ? *reinterpret_cast<const f16x8 *>(Q + (int64_t)q * qd + 32 * s + 8 * g) : zero8;
     }
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  wait_vmcnt<0>();
   for (int kb = 0; kb < n_kb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < n_kb) gload(kb + 1);
+    const int cur = kb % AS;
+    // this wave's share of stage kb is in (the later stages issued so far
+    // may still be in flight); after the barrier every wave's is, and stage
+    // kb - 1, whose buffer stage kb + AS - 1 reuses, has been consumed
+    const int later = min(AS - 2, n_kb - 1 - kb);
+    if (AS >= 4 && later == 2) wait_vmcnt<2 * NI * (AS >= 4)>();
+    else if (AS >= 3 && later == 1) wait_vmcnt<NI * (AS >= 3)>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (kb + AS - 1 < n_kb) issue(kb + AS - 1);
     const bool wave_active = kb * BKEY <= q0 + 31;     // any key of the block visible to this wave
     if (wave_active) {
       // S^T - m tiles: y = 16-key tile, t = 16-query tile; the accumulator
@@ -268,8 +324,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
         for (int t = 0; t < 2; ++t) lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[t][u], lsum[t], 0, 0, 0);
       }
     }
-    if (kb + 1 < n_kb) lstore(cur ^ 1);
-    __syncthreads();
   }
 
   // O^T: lane (i, g) holds dims 16d + 4g + r of query q0 + 16t + i
@@ -292,6 +346,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
 }  // namespace
 
 bool attn_prefill_supported(int head_dim) { return head_dim == 32 || head_dim == 64 || head_dim == 128; }
+
+int attn_prefill_query_tile() { return BQ; }
 
 // 64 keys x 64 dims per workgroup through LDS, so that both the reads (rows
 // of the cache) and the writes (rows of V^T) are contiguous.  Sequence b is
@@ -346,9 +402,9 @@ hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a) {
   const int per_x = (total + 7) / 8;
   dim3 grid(per_x * 8);
   switch (a.head_dim) {
-    case 32: QW_LAUNCH((attn_prefill_kernel<32>), dim3(grid), dim3(256), 0, s, a, n_qt); break;
-    case 64: QW_LAUNCH((attn_prefill_kernel<64>), dim3(grid), dim3(256), 0, s, a, n_qt); break;
-    case 128: QW_LAUNCH((attn_prefill_kernel<128>), dim3(grid), dim3(256), 0, s, a, n_qt); break;
+    case 32: QW_LAUNCH((attn_prefill_kernel<32>), dim3(grid), dim3(64 * AW), 0, s, a, n_qt); break;
+    case 64: QW_LAUNCH((attn_prefill_kernel<64>), dim3(grid), dim3(64 * AW), 0, s, a, n_qt); break;
+    case 128: QW_LAUNCH((attn_prefill_kernel<128>), dim3(grid), dim3(64 * AW), 0, s, a, n_qt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -183,24 +183,6 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
 constexpr int LK = 32, NSTG = 4;
 __device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 3; }
 
-// One 16-byte-per-lane load straight into LDS at the wave-uniform address
-// `lds` (+ 16 * lane).  Issued as assembly so that the compiler does not
-// drain every load in flight before each LDS read it cannot prove disjoint
-// from it; completion is awaited explicitly (s_waitcnt vmcnt) before the
-// barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const void *src, const void *lds) {
-  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);   // wave-uniform
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0v) : "memory");
-}
-// s_barrier without the release/acquire fences __syncthreads carries (the
-// waits they imply are issued explicitly); the empty asm keeps the compiler
-// from moving LDS accesses across it.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <Epi EPI, int TBM, int TBN, int WVM, int WVN, int NS, bool FP = false>
 __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   constexpr int NWV = WVM * WVN;                  // waves

@@ -69,6 +69,31 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// One 16-byte-per-lane load straight into LDS at the wave-uniform address
+// `lds` (+ 16 * lane).  Issued as assembly so that the compiler does not
+// drain every load in flight before each LDS read it cannot prove disjoint
+// from it; completion is awaited explicitly (s_waitcnt vmcnt) before the
+// barrier that publishes a stage.
+__device__ __forceinline__ void dma16(const void *src, const void *lds) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds);   // wave-uniform
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0v) : "memory");
+}
+// s_barrier without the release/acquire fences __syncthreads carries (the
+// waits they imply are issued explicitly); the empty asm keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// s_waitcnt with vmcnt = n (6 bits: [3:0] at bit 0, [5:4] at bit 14) and no
+// wait on expcnt or lgkmcnt
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ------------------------------------------------------------ KV cache layout
 // Positions of a sequence are grouped in blocks of kKvBlock.  Dense layout
 // (table == NULL): a layer's cache is [max_batch][nkv][max_seq][hd].  Paged
@@ -273,6 +298,7 @@ hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows
 hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a);
 hipError_t launch_attention_generic(hipStream_t s, bool f16_mode, const AttnArgs &a);
 bool attn_prefill_supported(int head_dim);
+int attn_prefill_query_tile();     // queries per workgroup (a ragged tile list counts in these)
 hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a);   // f16, prompt from position 0
 // v_t[b][j][d][t] = V cache[b][j][t][d] for t < P, 0 for P <= t < round_up(P, 64);
 // with rag.cu set, sequence s (length cu[s+1] - cu[s]) at pcu[s] * nkv * hd,

@@ -983,7 +983,7 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
     CREATE_TRY(m->alloc(&m->v_t, (size_t)c.max_batch * c.n_kv_heads * c.head_dim * ((c.max_seq + 63) / 64 * 64) * 2));
   const size_t pos_bytes = std::max<size_t>(256, (size_t)c.max_batch * 4);
   CREATE_TRY(m->alloc((void **)&m->pos_dev, pos_bytes));
-  m->rag_tiles_cap = c.max_batch * ((c.max_seq + 127) / 128);
+  m->rag_tiles_cap = c.max_batch * ((c.max_seq + attn_prefill_query_tile() - 1) / attn_prefill_query_tile());
   CREATE_TRY(m->alloc((void **)&m->rag_meta, ((size_t)2 * (c.max_batch + 1) + m->rag_tiles_cap) * 4));
   CREATE_TRY(m->alloc((void **)&m->x_last, (size_t)c.max_batch * H * 4));
   CREATE_TRY(m->alloc((void **)&m->status, 256));
@@ -1154,6 +1154,7 @@ hipError_t prefill_ragged_enqueue(qw_model *m, const int32_t *ids, const int32_t
   // then the query-tile list, (sequence << 16) | tile, in the order below
   const int off_pcu = c.max_batch + 1, off_tiles = 2 * (c.max_batch + 1);
   std::vector<int> idx, val;
+  const int BQ = attn_prefill_query_tile();
   int T = 0, PT = 0, max_len = 0, max_qt = 0;
   for (int b = 0; b <= n; ++b) {
     idx.push_back(b);
@@ -1164,7 +1165,7 @@ hipError_t prefill_ragged_enqueue(qw_model *m, const int32_t *ids, const int32_t
       T += lens[b];
       PT += blocks_for(lens[b]) * kKvBlock;
       max_len = std::max(max_len, lens[b]);
-      max_qt = std::max(max_qt, (lens[b] + 127) / 128);
+      max_qt = std::max(max_qt, (lens[b] + BQ - 1) / BQ);
     }
   }
   // The attention kernel deals work item w = tile * nq + head to XCD
@@ -1176,7 +1177,7 @@ hipError_t prefill_ragged_enqueue(qw_model *m, const int32_t *ids, const int32_t
   std::vector<int> order;
   for (int qt = max_qt - 1; qt >= 0; --qt)
     for (int b = 0; b < n; ++b)
-      if ((lens[b] + 127) / 128 > qt) order.push_back((b << 16) | qt);
+      if ((lens[b] + BQ - 1) / BQ > qt) order.push_back((b << 16) | qt);
   const int n_tiles = (int)order.size();
   const int64_t per_x = ((int64_t)n_tiles * c.n_heads + 7) / 8;
   std::vector<std::vector<int>> slots(8);             // tile positions of each XCD, in order
