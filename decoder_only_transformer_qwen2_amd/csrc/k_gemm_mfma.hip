@@ -183,6 +183,47 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
 constexpr int LK = 32, NSTG = 4;
 __device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 3; }
 
+// Epi::QkvRope.  Sequence and position of prompt row `row` (equal-length
+// sequences of rows_per_seq rows, or the ragged ones of rag).
+__device__ __forceinline__ void qkv_row_pos(const QkvRopeArgs &q, int row, int &b, int &pos) {
+  if (q.rag.cu) {
+    b = ragged_seq(q.rag.cu, q.rag.n, row);
+    pos = row - q.rag.cu[b];
+  } else {
+    b = row / q.rows_per_seq;
+    pos = row - b * q.rows_per_seq;
+  }
+}
+// Row `row` (sequence b, position pos): the projections of columns oc_lo
+// and oc_hi (for q and k, a rotation pair d and d + hd/2; for v
+// two columns of one head) plus their biases; q and k rotated by the
+// split-half RoPE at pos ("LLM Speedrun: Architecture", "Split-half RoPE
+// implementation"), then q to q_out and k, v into the cache, rounded to f16
+// once -- the arithmetic of the separate bias + RoPE + cache-write kernel.
+__device__ __forceinline__ void qkv_rope_store(const QkvRopeArgs &q, int row, int b, int pos, int oc_lo, int oc_hi,
+                                               float vlo, float vhi) {
+  const int hd = q.head_dim, half = hd >> 1, qd = q.n_heads * hd, kvd = q.n_kv_heads * hd;
+  const float re = vlo + q.bias[oc_lo], im = vhi + q.bias[oc_hi];
+  if (oc_lo < qd + kvd) {
+    const int d = oc_lo % hd;
+    const float2 cs = q.rope[(int64_t)pos * half + d];
+    const float nre = re * cs.x - im * cs.y;
+    const float nim = im * cs.x + re * cs.y;
+    f16 *o;
+    if (oc_lo < qd)
+      o = (f16 *)q.q_out + (int64_t)row * qd + oc_lo;
+    else
+      o = (f16 *)q.k_cache + kv_offset(q.kv, q.n_kv_heads, hd, b, (oc_lo - qd) / hd, pos) + d;
+    o[0] = (f16)nre;
+    o[half] = (f16)nim;
+  } else {
+    const int c = oc_lo - qd - kvd;
+    f16 *o = (f16 *)q.v_cache + kv_offset(q.kv, q.n_kv_heads, hd, b, c / hd, pos);
+    o[c % hd] = (f16)re;
+    o[(oc_hi - qd - kvd) % hd] = (f16)im;
+  }
+}
+
 template <Epi EPI, int TBM, int TBN, int WVM, int WVN, int NS, bool FP = false>
 __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   constexpr int NWV = WVM * WVN;                  // waves
@@ -396,6 +437,21 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a, int S) {
       up += a.ws[z * slice + (int64_t)row * a.N + cg + GU_BLOCK];
     }
     ((f16 *)a.act_out)[(int64_t)row * a.ldo + f] = (f16)(silu_f(gt * a.scale) * (up * a.scale));
+  } else if constexpr (EPI == Epi::QkvRope) {
+    // one thread per (row, column pair) of the unpermuted layout: pair p is
+    // dims d and d + hd/2 of head slot p / (hd/2) (q heads, then k, then v)
+    const int half = a.qr.head_dim >> 1, npairs = a.N / 2;
+    if (idx >= (int64_t)a.M * npairs) return;
+    const int row = (int)(idx / npairs), p = (int)(idx % npairs);
+    const int oc_lo = (p / half) * a.qr.head_dim + p % half, oc_hi = oc_lo + half;
+    float lo = 0.f, hi = 0.f;
+    for (int z = 0; z < S; ++z) {
+      lo += a.ws[z * slice + (int64_t)row * a.N + oc_lo];
+      hi += a.ws[z * slice + (int64_t)row * a.N + oc_hi];
+    }
+    int b, pos;
+    qkv_row_pos(a.qr, row, b, pos);
+    qkv_rope_store(a.qr, row, b, pos, oc_lo, oc_hi, lo * a.scale, hi * a.scale);
   } else {
     // four consecutive columns per thread (N and ldo are multiples of 4)
     const int64_t i4 = idx * 4;
@@ -452,13 +508,18 @@ int gemm_mfma_splits(int M, int N, int K) {
 }
 
 bool gemm_mfma_supported(const GemmArgs &a) {
+  if (a.epi == Epi::QkvRope && (a.N % 2 || a.qr.head_dim % 2 || gemm_mfma_splits(a.M, a.N, a.K) < 2)) return false;
   return (a.K % 8) == 0 && (a.lda % 8) == 0 && (a.epi != Epi::SwiGLU || a.N % 128 == 0);
 }
 
 hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (!gemm_mfma_supported(a)) return hipErrorInvalidValue;
-  const int S = (a.splits > 1 && a.ws && a.N % 4 == 0 && a.ldo % 4 == 0) ? a.splits : 1;
+  const int S = (a.splits > 1 && a.ws && a.N % 4 == 0 && (a.ldo % 4 == 0 || a.epi == Epi::QkvRope)) ? a.splits : 1;
+  // QkvRope runs split only: the multiply writes raw slices (any epilogue's
+  // kernel does), and the reduction applies bias + RoPE + the writes
+  if (a.epi == Epi::QkvRope && S < 2) return hipErrorInvalidValue;
+  const Epi ke = a.epi == Epi::QkvRope ? Epi::StoreF32 : a.epi;
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   dim3 grid(8 * ((tiles + 7) / 8), 1, S);
   if (big_tile_splits(a.M, a.N, a.K) > 0) {
@@ -467,30 +528,33 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
     // four stages, the next stage's fragments read from LDS during this
     // stage's MFMAs: gate/up of an 8x2048 prefill 25.5 -> 24.3 ms (three
     // stages with the same pipelining: 26.1 ms)
-    switch (a.epi) {
+    switch (ke) {
       case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, 4, true>), dim3(g2), dim3(512), 0, s, a); break;
       case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, 4, true>), dim3(g2), dim3(512), 0, s, a); break;
       case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 256, 256, 2, 4, 4, true>), dim3(g2), dim3(512), 0, s, a); break;
     }
   } else if (kLdsPipeline && a.K % LK == 0) {
-    switch (a.epi) {
+    switch (ke) {
       case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a); break;
       case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a); break;
       case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a); break;
     }
-  } else switch (a.epi) {
+  } else switch (ke) {
     case Epi::StoreF32: QW_LAUNCH((gemm_mfma_kernel<Epi::StoreF32>), dim3(grid), dim3(256), 0, s, a); break;
     case Epi::ResidAdd: QW_LAUNCH((gemm_mfma_kernel<Epi::ResidAdd>), dim3(grid), dim3(256), 0, s, a); break;
     case Epi::SwiGLU: QW_LAUNCH((gemm_mfma_kernel<Epi::SwiGLU>), dim3(grid), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
-  const int64_t n = (a.epi == Epi::SwiGLU) ? (int64_t)a.M * (a.N / 2) : (int64_t)a.M * a.N / 4;
+  const int64_t n = (a.epi == Epi::SwiGLU || a.epi == Epi::QkvRope) ? (int64_t)a.M * (a.N / 2)
+                                                                     : (int64_t)a.M * a.N / 4;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   switch (a.epi) {
     case Epi::StoreF32: splitk_reduce_kernel<Epi::StoreF32><<<blocks, 256, 0, s>>>(a, S); break;
     case Epi::ResidAdd: splitk_reduce_kernel<Epi::ResidAdd><<<blocks, 256, 0, s>>>(a, S); break;
     case Epi::SwiGLU: splitk_reduce_kernel<Epi::SwiGLU><<<blocks, 256, 0, s>>>(a, S); break;
+    case Epi::QkvRope: splitk_reduce_kernel<Epi::QkvRope><<<blocks, 256, 0, s>>>(a, S); break;
   }
   return hipGetLastError();
 }

@@ -142,6 +142,20 @@ enum class Epi : int {
   StoreF32 = 0,   // out_f32[m, n] = acc * scale
   ResidAdd = 1,   // resid[m, n] += acc * scale
   SwiGLU = 2,     // act_out[m, f] = silu(gate) * up over GU_BLOCK-interleaved rows
+  QkvRope = 3,    // prefill q/k/v projection (split K only): + bias, RoPE on q and k, q to q_out, k and v into the cache
+};
+
+// The prefill q/k/v projection's epilogue (Epi::QkvRope), applied by the
+// split-K reduction (the projection must run split): rows are prompt rows
+// from position 0 (rows_per_seq each, or the ragged sequences of rag).
+struct QkvRopeArgs {
+  const float *bias = nullptr;    // [nq*hd + 2*nkv*hd], by column of the unpermuted layout
+  const float2 *rope = nullptr;   // [max_seq, hd/2] (cos, sin)
+  void *q_out = nullptr;          // [M, nq*hd] f16
+  void *k_cache = nullptr, *v_cache = nullptr;   // layer base
+  KvMap kv;
+  RaggedRows rag;
+  int rows_per_seq = 0, n_heads = 0, n_kv_heads = 0, head_dim = 0;
 };
 
 struct GemmArgs {
@@ -155,6 +169,7 @@ struct GemmArgs {
   int ldo;
   int splits = 1;       // MFMA path: K slices (> 1 needs ws)
   float *ws = nullptr;  // [splits, M, N] fp32 slice tiles
+  QkvRopeArgs qr;       // QkvRope
 };
 
 struct RopeCacheArgs {
@@ -371,6 +386,7 @@ hipError_t launch_convert_gu(hipStream_t s, int src_kind, const void *gate, cons
                              int hidden, bool dst_f16, void *dst, float scale);
 hipError_t launch_convert_t(hipStream_t s, int src_kind, const void *src, int rows, int cols, void *dst,
                             float scale);   // f16 dst[cols][rows]
+
 hipError_t launch_rope_table(hipStream_t s, float2 *table, int max_seq, int head_dim, double theta);
 
 }  // namespace qw

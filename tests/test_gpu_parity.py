@@ -265,6 +265,11 @@ LONG = {
     # o projection kernel runs up to there, the split-KV pair after it (the
     # decode graph is captured again at the switch)
     "cross-256-hd64": (S.ModelShape("c64", 2, 256, 6, 2, 64, 512, 1003), 2, 252, 8, 300),
+    # enough prompt rows that the q/k/v projection runs unsplit at head dims
+    # 64 and 32 (bias + RoPE then in their own kernel; shorter prompts take
+    # them in the projection's split-K reduction)
+    "unsplit-qkv-hd64": (S.ModelShape("f64q", 2, 256, 8, 2, 64, 512, 997), 2, 1408, 3, 1412),
+    "unsplit-qkv-hd32": (S.ModelShape("f32q", 2, 256, 8, 2, 32, 512, 995), 4, 1400, 3, 1404),
 }
 
 
