@@ -1680,6 +1680,143 @@ dec_mlp32_kernel(DecMlpArgs a) {
     }
 }
 
+// One row, 16 features per workgroup and 4 waves, every weight of the
+// workgroup requested at the start: the gate/up rows into registers (wave w
+// multiplies tile w % 2 -- gate 0..15 or up 0..15 -- over K half w / 2), the
+// 16 rows of W_down^T straight into LDS (dynamic, 32 H bytes, so three
+// workgroups share a CU and all I / 16 are resident at once).  The late-down
+// kernel above loads the down rows only after the gate/up products, a second
+// dependent round trip.
+template <int KU>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+dec_mlp16_kernel(DecMlpArgs a) {
+  constexpr int F = GU_BLOCK;                   // features per workgroup
+  constexpr int NPER = 8;                       // residual values per thread (H <= 2048)
+  extern __shared__ f16x8 s_wd[];               // W_down^T rows f0 .. f0 + F - 1, [F][H / 8]
+  __shared__ f16 s_row[2048];                   // the normalised row
+  __shared__ float s_red[4];
+  __shared__ float s_gu[4][16];
+  __shared__ float s_h[F];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int p = blockIdx.x, f0 = p * F;
+  const int H = a.H;
+  const f16x8 zero = {};
+  clear_share(a.clear, a.clear_n, p, gridDim.x);
+
+  // the residual row and the norm weight first, then the gate/up rows
+  float wv[NPER];
+  long long qr[kXReps][NPER];
+#pragma unroll
+  for (int t = 0; t < NPER; ++t) {
+    const int c = t * 256 + tid, cc = min(c, H - 1);
+    const float w = a.norm_w[cc];
+    wv[t] = c < H ? w : 0.f;
+#pragma unroll
+    for (int r = 0; r < kXReps; ++r) {
+      const long long v = a.x_in[r * a.rep_stride + cc];
+      qr[r][t] = c < H ? v : 0;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int tau = wave & 1, kh = wave >> 1;
+  const f16 *Wt = (const f16 *)a.w_gu + (int64_t)(2 * f0 + 16 * tau + i) * H;
+  const int ku = H / 64;
+  const int kw0 = kh * ku * 32;
+  f16x8 wt[KU];
+#pragma unroll
+  for (int t = 0; t < KU; ++t) wt[t] = load8(Wt + kw0 + 32 * min(t, ku - 1) + 8 * g);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the norm (the weights stay in flight)
+  float xv[NPER];
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int t = 0; t < NPER; ++t) {
+      long long q = qr[0][t];
+#pragma unroll
+      for (int r = 1; r < kXReps; ++r) q += qr[r][t];
+      xv[t] = from_fix(q);
+      ss += xv[t] * xv[t];
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) s_red[wave] = ss;
+    lds_barrier();
+    const float inv = 1.0f / sqrtf((s_red[0] + s_red[1] + s_red[2] + s_red[3]) / (float)H + a.eps);
+#pragma unroll
+    for (int t = 0; t < NPER; ++t) {
+      const int c = t * 256 + tid;
+      if (c < H) s_row[c] = (f16)(xv[t] * inv * wv[t]);
+    }
+  }
+  // the down rows: F * H / 8 16-byte chunks, 64 per load instruction, H / 128
+  // instructions per wave (contiguous rows of W_down^T)
+  {
+    const f16 *Wd = (const f16 *)a.w_down_t + (int64_t)f0 * H;
+    const int per_wave = H / 128;
+    for (int q = 0; q < per_wave; ++q) {
+      const int n = wave * per_wave + q;
+      dma16(Wd + (int64_t)(64 * n + lane) * 8, &s_wd[64 * n]);
+    }
+  }
+  lds_barrier();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < KU; ++t) {
+    if (t < ku) {
+      const f16x8 xl = *reinterpret_cast<const f16x8 *>(&s_row[kw0 + 32 * t + 8 * g]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wt[t], i == 0 ? xl : zero, acc, 0, 0, 0);
+    }
+  }
+  if (i == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_gu[wave][4 * g + r] = acc[r];
+  }
+  wait_vmcnt<0>();                 // this wave's down rows are in LDS
+  __syncthreads();
+  if (tid < F) {
+    const float gt = (s_gu[0][tid] + s_gu[2][tid]) * a.gu_scale;
+    const float up = (s_gu[1][tid] + s_gu[3][tid]) * a.gu_scale;
+    s_h[tid] = silu_f(gt) * up;
+  }
+  __syncthreads();
+  // y[c] = sum_f h[f] W_down^T[f][c]: thread cb takes columns 8 cb .. 8 cb + 7
+  // (16-byte LDS reads), then y goes through LDS (over the down rows, read by
+  // then) so that a wave's atomic adds cover consecutive addresses: with 8
+  // columns per lane one add instruction touched 64 lines (1.5B MLP 0.81 ->
+  // 1.86 ms per step)
+  const int CB = H / 8;
+  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (tid < CB) {
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      const float hf = s_h[f];
+      const f16x8 w = s_wd[f * CB + tid];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = fmaf(hf, (float)w[e], y[e]);
+    }
+  }
+  __syncthreads();                 // every wave is done with the down rows
+  float *s_y = reinterpret_cast<float *>(s_wd);
+  if (tid < CB) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_y[8 * tid + e] = y[e];
+  }
+  __syncthreads();
+  long long *xo = a.x_out + (p % kXReps) * a.rep_stride;
+  const int rot = 64 * (p % (H / 64));           // the adds start at a different column block per workgroup
+  for (int cl = tid; cl < H; cl += 256) {
+    const int c = (cl + rot) % H;
+    long long xin = 0;
+    if (p == 0)                    // workgroup 0 also adds the input residual (rot = 0 there)
+      for (int r = 0; r < kXReps; ++r) xin += a.x_in[r * a.rep_stride + c];
+    const long long q = to_fix(s_y[c] * a.down_scale, a.num_flag) + xin;
+    atomicAdd(reinterpret_cast<unsigned long long *>(xo + c), (unsigned long long)q);
+  }
+}
+
 // ---------------------------------------------------------------- attention + o projection
 // One or two rows with a short context: attention and the o projection in one
 // kernel.  The o projection is a sum over heads, o . W_o^T = sum_h o_h .
@@ -1939,8 +2076,20 @@ hipError_t launch_dec_mlp32(hipStream_t s, const DecMlpArgs &a) {
 
 constexpr bool kMlp32 = true;
 
+// One row at 1024 < H <= 1536: every weight requested at the start
+// (dec_mlp16_kernel): 1.5B decode MLP 0.810 -> 0.645 ms per step (672 -> 752
+// tokens/s).  At the 0.5B width the 32-feature kernel, which loads all its
+// weights up front as well, stays faster (0.273 vs 0.291 ms per step).
+constexpr bool kMlp16 = true;
+
 hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a) {
   if (!dec_mlp_supported(a.H, a.I) || a.M < 1 || a.M > 2) return hipErrorInvalidValue;
+  // (up to H = 1536: at 2048 the 32 gate/up vectors per lane spill)
+  if (kMlp16 && a.M == 1 && a.H % 128 == 0 && a.H > 1024 && a.H <= 1536 && a.I % GU_BLOCK == 0) {
+    const size_t lds = (size_t)GU_BLOCK * a.H * 2;
+    QW_LAUNCH((dec_mlp16_kernel<24>), dim3(a.I / GU_BLOCK), dim3(256), lds, s, a);
+    return hipGetLastError();
+  }
   if (kMlp32 && a.I % (2 * GU_BLOCK) == 0 && a.H >= 512)
     return a.M == 1 ? launch_dec_mlp32<1>(s, a) : launch_dec_mlp32<2>(s, a);
   const dim3 grid(a.I / MLP_F);

@@ -481,6 +481,9 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a, int S) {
 }  // namespace
 
 constexpr bool kLdsPipeline = true;
+// stages of the 256 x 256 kernel (32 KB of LDS each); five (all 160 KB)
+// measured slower: 32 x 8192 gate/up 393.4 -> 397.9 ms per prefill
+constexpr int kBigStages = 4;
 // 256 x 256 tiles halve the operand bytes per FLOP.  One workgroup runs per
 // CU, so they pay once there are enough of them to fill the chip a few times
 // over: with at least 512 tiles K is not split; with 192 .. 511 tiles (the
@@ -529,9 +532,9 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
     // stage's MFMAs: gate/up of an 8x2048 prefill 25.5 -> 24.3 ms (three
     // stages with the same pipelining: 26.1 ms)
     switch (ke) {
-      case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, 4, true>), dim3(g2), dim3(512), 0, s, a); break;
-      case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, 4, true>), dim3(g2), dim3(512), 0, s, a); break;
-      case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 256, 256, 2, 4, 4, true>), dim3(g2), dim3(512), 0, s, a); break;
+      case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, kBigStages, true>), dim3(g2), dim3(512), 0, s, a); break;
+      case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, kBigStages, true>), dim3(g2), dim3(512), 0, s, a); break;
+      case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 256, 256, 2, 4, kBigStages, true>), dim3(g2), dim3(512), 0, s, a); break;
     }
   } else if (kLdsPipeline && a.K % LK == 0) {
     switch (ke) {
