@@ -183,6 +183,12 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
 constexpr int LK = 32, NSTG = 4;
 __device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 3; }
 
+// The 256 x 256 kernel's fp32 epilogues (store, residual add) through LDS
+#ifndef QW_ROW_EPILOGUE
+#define QW_ROW_EPILOGUE 1
+#endif
+constexpr bool kRowEpilogue = QW_ROW_EPILOGUE;
+
 // Epi::QkvRope.  Sequence and position of prompt row `row` (equal-length
 // sequences of rows_per_seq rows, or the ragged ones of rag).
 __device__ __forceinline__ void qkv_row_pos(const QkvRopeArgs &q, int row, int &b, int &pos) {
@@ -230,8 +236,11 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   constexpr int XT = TBM / WVM / 16, YT = TBN / WVN / 16;   // MFMA tiles per wave
   constexpr int QA = TBM / 16 / NWV, QB = TBN / 16 / NWV;   // load instructions per wave and stage
   static_assert((TBN / WVN) % (2 * GU_BLOCK) == 0, "a wave's columns hold whole gate/up pairs");
-  __shared__ f16x8 sA[NS][TBM * 4];
-  __shared__ f16x8 sB[NS][TBN * 4];
+  // one LDS block: the operand stages, and after the K loop the staging of
+  // the output tile for a row-contiguous epilogue
+  __shared__ f16x8 s_lds[NS * (TBM + TBN) * 4];
+  f16x8 (*sA)[TBM * 4] = reinterpret_cast<f16x8 (*)[TBM * 4]>(s_lds);
+  f16x8 (*sB)[TBN * 4] = reinterpret_cast<f16x8 (*)[TBN * 4]>(s_lds + NS * TBM * 4);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, g = lane >> 4;
   const int wm = wave / WVN, wn = wave % WVN;
@@ -399,6 +408,50 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
           }
         }
       }
+  } else if (kRowEpilogue && TBM == 256 && TBN == 256 && WVM == 2 && (a.ldo & 3) == 0 && a.N % 4 == 0) {
+    // Through LDS, a quarter of the tile (64 rows) at a time: each lane's
+    // acc holds 4 rows of one column, so direct residual reads were 4-byte
+    // loads, 128 per lane and more than one round trip.  Rows of 256 + 4
+    // floats (the pad puts a lane group's 4 rows on different banks); every
+    // thread then reads, adds and writes 8 row-contiguous float4.
+    constexpr int RS = TBN + 4;
+    float *st = reinterpret_cast<float *>(s_lds);
+    static_assert(64 * RS * 4 <= NS * (TBM + TBN) * 64, "a quarter tile fits the stages");
+    stage_barrier();               // every wave is done with the operand stages
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      // quarter qq: rows 64 qq .. 64 qq + 63, held by the waves with wm = qq / 2 (x = 4 (qq % 2) .. + 3)
+      if (wm == qq / 2) {
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx)
+#pragma unroll
+          for (int y = 0; y < YT; ++y)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              st[(xx * 16 + 4 * g + r) * RS + wn * 64 + y * 16 + i] = acc[4 * (qq % 2) + xx][y][r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = tid + 512 * k;               // float4 e of the quarter: row e / 64, columns 4 (e % 64) ..
+        const int lr = e >> 6, c4 = (e & 63) * 4;
+        const int row = m0 + 64 * qq + lr, col = n0 + c4;
+        if (row < a.M && col < a.N) {
+          const float4 v = *reinterpret_cast<const float4 *>(&st[lr * RS + c4]);
+          float4 *o = reinterpret_cast<float4 *>(a.out_f32 + (int64_t)row * a.ldo + col);
+          float4 w = {v.x * a.scale, v.y * a.scale, v.z * a.scale, v.w * a.scale};
+          if constexpr (EPI == Epi::ResidAdd) {
+            const float4 x = *o;
+            w.x += x.x;
+            w.y += x.y;
+            w.z += x.z;
+            w.w += x.w;
+          }
+          *o = w;
+        }
+      }
+      __syncthreads();
+    }
   } else {
 #pragma unroll
     for (int x = 0; x < XT; ++x)
