@@ -394,6 +394,35 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   }
   if constexpr (EPI == Epi::SwiGLU) {
     f16 *out = (f16 *)a.act_out;
+    if (kRowEpilogue && TBM == 256 && TBN == 256 && (a.ldo & 7) == 0 && (a.N / 2) % 8 == 0) {
+      // the tile's 256 x 128 values of h through LDS (rows of 128 + 8 f16),
+      // then written as 16-byte row pieces rather than 2-byte stores
+      constexpr int HS = TBN / 2 + 8;
+      f16 *sh = reinterpret_cast<f16 *>(s_lds);
+      static_assert(TBM * HS * 2 <= NS * (TBM + TBN) * 64, "the h tile fits the stages");
+      stage_barrier();             // every wave is done with the operand stages
+#pragma unroll
+      for (int x = 0; x < XT; ++x)
+#pragma unroll
+        for (int p = 0; p < YT / 2; ++p) {
+          const int fl = wn * (TBN / WVN / 2) + p * GU_BLOCK + i;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gt = acc[x][2 * p][r] * a.scale, up = acc[x][2 * p + 1][r] * a.scale;
+            sh[(wm * (TBM / WVM) + x * 16 + 4 * g + r) * HS + fl] = (f16)(silu_f(gt) * up);
+          }
+        }
+      __syncthreads();
+      constexpr int V8 = TBN / 2 / 8;              // 16-byte pieces per row
+#pragma unroll
+      for (int k = 0; k < TBM * V8 / (64 * WVM * WVN); ++k) {
+        const int e = tid + 64 * WVM * WVN * k;
+        const int lr = e / V8, v = e % V8;
+        const int row = m0 + lr, f = n0 / 2 + 8 * v;
+        if (row < a.M && f < a.N / 2)
+          *reinterpret_cast<f16x8 *>(out + (int64_t)row * a.ldo + f) = *reinterpret_cast<const f16x8 *>(&sh[lr * HS + 8 * v]);
+      }
+    } else {
 #pragma unroll
     for (int x = 0; x < XT; ++x)
 #pragma unroll
@@ -408,6 +437,7 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
           }
         }
       }
+    }
   } else if (kRowEpilogue && TBM == 256 && TBN == 256 && WVM == 2 && (a.ldo & 3) == 0 && a.N % 4 == 0) {
     // Through LDS, a quarter of the tile (64 rows) at a time: each lane's
     // acc holds 4 rows of one column, so direct residual reads were 4-byte
