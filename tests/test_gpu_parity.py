@@ -287,6 +287,27 @@ def test_long_prompts_small_model(Q, case):
         say(f"  row {b}: max err {err:.2e}")
 
 
+def test_big_tile_epilogues(Q):
+    """64 prompts of 2048 tokens on a small model: every prefill projection
+    (q/k/v, o, gate/up, down) runs unsplit on 256 x 256 tiles, whose fp32
+    store, residual-add and SwiGLU outputs go through LDS; rows 0 and 63 are
+    checked against the oracle, the batch's first decode steps included."""
+    shape = S.ModelShape("big", 2, 256, 4, 2, 64, 512, 1000)
+    B, P, D = 64, 2048, 2
+    T = B * P
+    for N in (shape.q_dim + 2 * shape.kv_dim, shape.hidden, 2 * shape.intermediate):
+        assert ((T + 255) // 256) * ((N + 255) // 256) >= 512       # the unsplit 256 x 256 kernel
+    W = with_random_norms(S.make_weights(shape, 31), shape)
+    ids = np.random.default_rng(32).integers(0, shape.vocab, (B, P)).astype(np.int32)
+    m = make(Q, shape, W, B, P + D + 2)
+    toks, logits = gpu_generate(m, ids, D)
+    m.close()
+    om = O.OracleModel(shape, W)
+    for b in (0, B - 1):
+        err, n = compare_row(om, ids[b], toks[b], logits[b], shape.dtype, f"big-tile row {b}")
+        say(f"  big-tile row {b}: max err {err:.2e}")
+
+
 def test_full_workload_prefill_heavy(Q):
     """Batch 8 x 2048 prompt tokens + 32 decode steps at Qwen2.5-1.5B shapes.
     The oracle checks rows 0 and 7 (about 6.5 TFLOP each in float64); row 7
