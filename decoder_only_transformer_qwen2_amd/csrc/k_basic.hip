@@ -138,9 +138,64 @@ __global__ void __launch_bounds__(256) rope_cache_kernel(RopeCacheArgs a) {
   }
 }
 
+// The same in f16 mode, four consecutive rotation pairs per thread: float4
+// reads of the projections, biases and (cos, sin), 8-byte writes (half a
+// head a multiple of 4).  The arithmetic of each element is unchanged.
+__global__ void __launch_bounds__(256) rope_cache4_kernel(RopeCacheArgs a) {
+  const int t = blockIdx.x;
+  const int half = a.head_dim >> 1;
+  int b, pos;
+  if (a.rag.cu) {
+    b = ragged_seq(a.rag.cu, a.rag.n, t);
+    pos = t - a.rag.cu[b];
+  } else {
+    b = t / a.rows_per_seq;
+    pos = (a.pos0_dev ? a.pos0_dev[b] : a.pos0) + (t % a.rows_per_seq);
+  }
+  const int qd = a.n_heads * a.head_dim, kvd = a.n_kv_heads * a.head_dim;
+  const int ncols = qd + 2 * kvd;
+  const float *row = a.qkv + (int64_t)t * ncols;
+  const float2 *cs = a.rope + (int64_t)pos * half;
+  const int n4 = (a.n_heads + 2 * a.n_kv_heads) * half / 4;
+  for (int it4 = threadIdx.x; it4 < n4; it4 += blockDim.x) {
+    const int it = 4 * it4, head = it / half, i = it % half;
+    const int c0 = head * a.head_dim + i, c1 = c0 + half;
+    const float4 x0 = *reinterpret_cast<const float4 *>(row + c0), x1 = *reinterpret_cast<const float4 *>(row + c1);
+    const float4 b0 = *reinterpret_cast<const float4 *>(a.bias + c0), b1 = *reinterpret_cast<const float4 *>(a.bias + c1);
+    float re[4] = {x0.x + b0.x, x0.y + b0.y, x0.z + b0.z, x0.w + b0.w};
+    float im[4] = {x1.x + b1.x, x1.y + b1.y, x1.z + b1.z, x1.w + b1.w};
+    if (head < a.n_heads + a.n_kv_heads) {
+      const float4 r01 = *reinterpret_cast<const float4 *>(cs + i), r23 = *reinterpret_cast<const float4 *>(cs + i + 2);
+      const float cr[4] = {r01.x, r01.z, r23.x, r23.z}, sr[4] = {r01.y, r01.w, r23.y, r23.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float nre = re[k] * cr[k] - im[k] * sr[k];
+        const float nim = im[k] * cr[k] + re[k] * sr[k];
+        re[k] = nre;
+        im[k] = nim;
+      }
+    }
+    f16 *dst;
+    if (head < a.n_heads) {
+      dst = (f16 *)a.q_out + (int64_t)t * qd + c0;
+    } else {
+      const bool is_k = head < a.n_heads + a.n_kv_heads;
+      const int j = is_k ? head - a.n_heads : head - a.n_heads - a.n_kv_heads;
+      dst = (f16 *)(is_k ? a.k_cache : a.v_cache) + kv_offset(a.kv, a.n_kv_heads, a.head_dim, b, j, pos) + i;
+    }
+    typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
+    const f16x4v lo = {(f16)re[0], (f16)re[1], (f16)re[2], (f16)re[3]};
+    const f16x4v hi = {(f16)im[0], (f16)im[1], (f16)im[2], (f16)im[3]};
+    *reinterpret_cast<f16x4v *>(dst) = lo;
+    *reinterpret_cast<f16x4v *>(dst + half) = hi;
+  }
+}
+
 hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a) {
   if (a.T <= 0) return hipSuccess;
-  if (f16_mode)
+  if (f16_mode && (a.head_dim / 2) % 4 == 0)
+    QW_LAUNCH((rope_cache4_kernel), dim3(a.T), dim3(256), 0, s, a);
+  else if (f16_mode)
     QW_LAUNCH((rope_cache_kernel<f16>), dim3(a.T), dim3(256), 0, s, a);
   else
     QW_LAUNCH((rope_cache_kernel<float>), dim3(a.T), dim3(256), 0, s, a);

@@ -183,7 +183,7 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
 constexpr int LK = 32, NSTG = 4;
 __device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 3; }
 
-// The 256 x 256 kernel's fp32 epilogues (store, residual add) through LDS
+// The 256 x 256 kernel's residual-add and SwiGLU epilogues through LDS
 #ifndef QW_ROW_EPILOGUE
 #define QW_ROW_EPILOGUE 1
 #endif
@@ -376,6 +376,43 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
 
   // acc[x][y]: lane (i, g) holds rows 4g..4g+3 of column i of MFMA tile (x, y)
   const int rw0 = m0 + wm * (TBM / WVM), cw0 = n0 + wn * (TBN / WVN);
+  // The 256 x 256 tile's fp32 outputs through LDS, a quarter (64 rows) at a
+  // time: each lane's acc holds 4 rows of one column, so direct writes (and
+  // residual reads) were 4-byte accesses, 128 per lane.  Rows of 256 + 4
+  // floats (the pad puts a lane group's 4 rows on different banks); then
+  // every thread passes 8 row-contiguous float4 to emit(row, col, value).
+  auto staged = [&](auto &&emit) {
+    constexpr int RS = TBN + 4;
+    float *st = reinterpret_cast<float *>(s_lds);
+    static_assert(64 * RS * 4 <= NS * (TBM + TBN) * 64, "a quarter tile fits the stages");
+    stage_barrier();               // every wave is done with the operand stages
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      // rows 64 qq .. 64 qq + 63 are held by the waves with wm = qq / 2 (x = 4 (qq % 2) .. + 3)
+      if (wm == qq / 2) {
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx)
+#pragma unroll
+          for (int y = 0; y < YT; ++y)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              st[(xx * 16 + 4 * g + r) * RS + wn * 64 + y * 16 + i] = acc[4 * (qq % 2) + xx][y][r];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = tid + 512 * k;               // float4 e of the quarter: row e / 64, columns 4 (e % 64) ..
+        const int lr = e >> 6, c4 = (e & 63) * 4;
+        const int row = m0 + 64 * qq + lr, col = n0 + c4;
+        if (row < a.M && col < a.N) emit(row, col, *reinterpret_cast<const float4 *>(&st[lr * RS + c4]));
+      }
+      __syncthreads();
+    }
+  };
+  // Used for the residual add (its reads were the exposed part); plain
+  // stores -- the q/k/v output, split-K slices -- measured no faster staged
+  // (32 x 8192 q/k/v 49.5 -> 51.1 ms per prefill).
+  constexpr bool kStageable = TBM == 256 && TBN == 256 && WVM == 2 && WVN == 4;
   if (gridDim.z > 1) {
     float *ws = a.ws + (int64_t)blockIdx.z * a.M * a.N;
 #pragma unroll
@@ -438,50 +475,19 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
         }
       }
     }
-  } else if (kRowEpilogue && TBM == 256 && TBN == 256 && WVM == 2 && (a.ldo & 3) == 0 && a.N % 4 == 0) {
-    // Through LDS, a quarter of the tile (64 rows) at a time: each lane's
-    // acc holds 4 rows of one column, so direct residual reads were 4-byte
-    // loads, 128 per lane and more than one round trip.  Rows of 256 + 4
-    // floats (the pad puts a lane group's 4 rows on different banks); every
-    // thread then reads, adds and writes 8 row-contiguous float4.
-    constexpr int RS = TBN + 4;
-    float *st = reinterpret_cast<float *>(s_lds);
-    static_assert(64 * RS * 4 <= NS * (TBM + TBN) * 64, "a quarter tile fits the stages");
-    stage_barrier();               // every wave is done with the operand stages
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      // quarter qq: rows 64 qq .. 64 qq + 63, held by the waves with wm = qq / 2 (x = 4 (qq % 2) .. + 3)
-      if (wm == qq / 2) {
-#pragma unroll
-        for (int xx = 0; xx < 4; ++xx)
-#pragma unroll
-          for (int y = 0; y < YT; ++y)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              st[(xx * 16 + 4 * g + r) * RS + wn * 64 + y * 16 + i] = acc[4 * (qq % 2) + xx][y][r];
+  } else if (EPI == Epi::ResidAdd && kStageable && kRowEpilogue && (a.ldo & 3) == 0 && a.N % 4 == 0) {
+    staged([&](int row, int col, float4 v) {
+      float4 *o = reinterpret_cast<float4 *>(a.out_f32 + (int64_t)row * a.ldo + col);
+      float4 w = {v.x * a.scale, v.y * a.scale, v.z * a.scale, v.w * a.scale};
+      if constexpr (EPI == Epi::ResidAdd) {
+        const float4 x = *o;
+        w.x += x.x;
+        w.y += x.y;
+        w.z += x.z;
+        w.w += x.w;
       }
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = tid + 512 * k;               // float4 e of the quarter: row e / 64, columns 4 (e % 64) ..
-        const int lr = e >> 6, c4 = (e & 63) * 4;
-        const int row = m0 + 64 * qq + lr, col = n0 + c4;
-        if (row < a.M && col < a.N) {
-          const float4 v = *reinterpret_cast<const float4 *>(&st[lr * RS + c4]);
-          float4 *o = reinterpret_cast<float4 *>(a.out_f32 + (int64_t)row * a.ldo + col);
-          float4 w = {v.x * a.scale, v.y * a.scale, v.z * a.scale, v.w * a.scale};
-          if constexpr (EPI == Epi::ResidAdd) {
-            const float4 x = *o;
-            w.x += x.x;
-            w.y += x.y;
-            w.z += x.z;
-            w.w += x.w;
-          }
-          *o = w;
-        }
-      }
-      __syncthreads();
-    }
+      *o = w;
+    });
   } else {
 #pragma unroll
     for (int x = 0; x < XT; ++x)
