@@ -15,12 +15,11 @@
 // permuted order so that the 8 probabilities a lane holds for a step are 8
 // consecutive keys, which its V^T operand reads in one 16-byte load.  A
 // workgroup is 4 waves x 32 queries of one head (two workgroups per CU).  The
-// tiles go straight from memory into a ring of two LDS stages (the next key
-// block in flight while one is multiplied), as swizzled 32-column sub-tiles
-// (see swz).  V^T comes from a transposed copy of
-// the prompt's V written once per layer (transpose_v_kernel), since
-// transposing inside the kernel took 2-byte LDS stores with 16-way bank
-// conflicts.  Work items are ordered heaviest (latest
+// tiles go straight from memory into LDS rings (global_load_lds) as swizzled
+// 32-column sub-tiles (see swz).  V^T comes from a transposed copy of the
+// prompt's V written once per layer (transpose_v_kernel), since transposing
+// inside the kernel took 2-byte LDS stores with 16-way bank conflicts.  Work
+// items are ordered heaviest (latest
 // query tile) first and mapped so that the g query heads of a KV head and
 // query tile run on the same XCD, where they share the K/V tiles in L2.
 #include "qw_internal.h"
@@ -36,22 +35,8 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BKEY = 64;  // keys per step (one cache block)
-// Waves per workgroup and LDS stages (key blocks resident or in flight).
-// Measured at 32 x 8192 (hd 128, ms per prefill): 4 waves x 2 stages 187.7
-// (two workgroups per CU, whose barriers do not hold each other), 8 x 2
-// 188.1, 8 x 4 193.3, 8 x 3 198.4; at 8 x 2048: 3.68, 3.88, 3.94, 4.01.
-#ifndef QW_ATTN_WAVES
-#define QW_ATTN_WAVES 4
-#endif
-#ifndef QW_ATTN_STAGES
-#define QW_ATTN_STAGES 2
-#endif
-constexpr int AW = QW_ATTN_WAVES;
-constexpr int AS = QW_ATTN_STAGES;
-static_assert(AS >= 2 && AS <= 4, "stage ring");
-constexpr int BQ = 32 * AW;   // queries per workgroup
+constexpr int BQ = 128;   // queries per workgroup: 4 waves x 32
 constexpr float RESCALE_LOG2 = 8.0f;  // largest exponent (log2) a probability may reach before a rescale
-constexpr int kTableLds = 512;        // paged cache: block ids held in LDS (contexts up to 32768 keys)
 
 // 2^x with the hardware instruction alone: results below the smallest normal
 // float flush to zero, which a probability can afford (it is rounded to f16)
@@ -71,24 +56,27 @@ __device__ __forceinline__ int key_of_row(int row) {
   return (row & ~31) | (((row >> 2) & 3) << 3) | (((row >> 4) & 1) << 2) | (row & 3);
 }
 
+// Software pipelined: block kb + 1's S^T = K . Q^T is issued in the same
+// basic block as block kb's exponentials, so that a wave can keep the matrix
+// cores busy while its softmax runs (the compiler interleaves them; a fixed
+// interleave forced with sched_group_barrier measured slower).  K tiles take
+// a ring of three LDS slots (block kb + 1 is resident while block kb is
+// finished), V^T tiles a ring of two: 80 KB at hd 128, two workgroups per
+// CU.  A paged cache's block ids of the first 128 blocks are held in two
+// registers per lane (read with readlane), the rest read from the table.
 template <int HD>
-__global__ void __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(2))) attn_prefill_kernel(AttnArgs a, int n_qt) {
-  constexpr int KS = HD / 32;               // 32-wide d steps for S (K sub-tiles)
-  constexpr int DT = HD / 16;               // 16-wide d tiles of O
-  constexpr int KCH = KS * BKEY * 4;        // 16-byte chunks of a stage's K tile
-  constexpr int VCH = 2 * HD * 4;           // of its V^T tile
-  constexpr int NI = (KCH + VCH) / (64 * AW);   // loads per wave and stage
-  static_assert((KCH + VCH) % (64 * AW) == 0 && KCH % 64 == 0, "whole load instructions per wave");
-  __shared__ f16x8 sK[AS][KCH];   // [ks][key row][chunk]
-  __shared__ f16x8 sV[AS][VCH];   // [u][d row][chunk]: keys 32u .. 32u + 31
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) attn_prefill_kernel(AttnArgs a, int n_qt) {
+  constexpr int PW = BQ / 32, PQ = BQ;      // waves, queries per workgroup
+  constexpr int KS = HD / 32, DT = HD / 16;
+  constexpr int KCH = KS * BKEY * 4, VCH = 2 * HD * 4;     // 16-byte chunks of a K / V^T tile
+  constexpr int NK = KCH / 64 / PW, NV = VCH / 64 / PW;     // load instructions per wave and tile
+  static_assert(KCH % (64 * PW) == 0 && VCH % (64 * PW) == 0, "whole load instructions per wave");
+  __shared__ f16x8 sK[3][KCH];
+  __shared__ f16x8 sV[2][VCH];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int i = lane & 15, g = lane >> 4;
   const int nq = a.n_heads, grp = a.n_heads / a.n_kv_heads;
-  // work item: heaviest query tiles first; the g heads of a group adjacent,
-  // and adjacent items on one XCD (workgroups go round-robin over 8 XCDs).
-  // Ragged batches take (sequence, query tile) from a list the host ordered
-  // so that each XCD's range starts heaviest and the ranges weigh the same.
   const int total = a.tiles ? a.n_tiles * nq : n_qt * nq * (a.T / a.rows_per_seq);
   const int L = blockIdx.x;
   const int per_x = (total + 7) / 8;
@@ -97,9 +85,6 @@ __global__ void __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(2)
   const int h = w % nq;
   int qt, b, P, r0;
   if (a.tiles) {
-    // wave-uniform values read from memory: said so, so that the block-table
-    // lookups below are scalar loads (a vector load would need a vmcnt wait,
-    // which would also wait for every key block in flight)
     const int it = __builtin_amdgcn_readfirstlane(a.tiles[w / nq]);
     b = it >> 16;
     qt = it & 0xffff;
@@ -112,76 +97,58 @@ __global__ void __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(2)
     r0 = b * P;
   }
   const int j = h / grp;
-  const int q0 = qt * BQ + wave * 32;                 // this wave's first query
+  const int q0 = qt * PQ + wave * 32;
   const int qd = nq * HD;
-
   const f16 *Q = (const f16 *)a.q + (int64_t)r0 * qd + h * HD;
   const f16 *Kc = (const f16 *)a.k_cache;
   const f16x8 zero8 = {};
-
-  // Key blocks go straight from memory into a ring of AS LDS stages: load
-  // instruction n (n = NI * wave + q) of a stage fills its chunks 64n .. 64n
-  // + 63, the K tile's first, then the V^T tile's; lane l's 16 bytes land at
-  // chunk 64n + l, so each lane fetches the (row, chunk) that the swizzled,
-  // permuted layout keeps there.  K rows past the prompt are clamped to its
-  // last row (their scores are masked); V^T rows come from a transposed copy
-  // of the prompt's V, zero past P in rows of round_up(P, 64) keys.
-  const int q_last = min(P - 1, qt * BQ + BQ - 1);    // last query of the workgroup
-  const int n_kb = q_last / BKEY + 1;                  // key blocks it needs
+  const int q_last = min(P - 1, qt * PQ + PQ - 1);
+  const int n_kb = q_last / BKEY + 1;
   const int PP = (P + BKEY - 1) / BKEY * BKEY;
-  const int64_t vt_seq = a.tiles ? (int64_t)a.rag.pcu[b] : (int64_t)b * PP;   // padded rows before sequence b
+  const int64_t vt_seq = a.tiles ? (int64_t)a.rag.pcu[b] : (int64_t)b * PP;
   const f16 *Vt = (const f16 *)a.v_t + (vt_seq * a.n_kv_heads + (int64_t)j * PP) * HD;
-  static_assert(BKEY == kKvBlock, "a key tile is one cache block");
-  // A paged cache's block ids of this sequence go to LDS first: read in the
-  // loop, the table (which the compiler cannot treat as read-only) would be a
-  // vector load whose wait would also wait for every key block in flight.
-  __shared__ int s_blk[kTableLds];
-  const bool tbl_lds = a.kv.table != nullptr && n_kb <= kTableLds;
-  if (tbl_lds) {
-    for (int k = tid; k < n_kb; k += 64 * AW) s_blk[k] = a.kv.table[b * a.kv.blocks_per_seq + k];
-    __syncthreads();
+
+  const bool paged = a.kv.table != nullptr;
+  int blk_lo = 0, blk_hi = 0;
+  if (paged) {
+    const int *tb = a.kv.table + b * a.kv.blocks_per_seq;
+    blk_lo = lane < n_kb ? tb[lane] : 0;
+    blk_hi = 64 + lane < n_kb ? tb[64 + lane] : 0;
   }
-  int src[NI], kkey[NI];
+  auto k_base = [&](int kb) -> int64_t {
+    if (!paged) return kv_offset(a.kv, a.n_kv_heads, HD, b, j, kb * BKEY);
+    const int blk = kb < 128 ? __builtin_amdgcn_readlane(kb < 64 ? blk_lo : blk_hi, kb & 63)
+                             : a.kv.table[b * a.kv.blocks_per_seq + kb];
+    return ((int64_t)blk * a.n_kv_heads + j) * (kKvBlock * HD);
+  };
+  int ksrc[NK], kkey[NK], vsrc[NV];
 #pragma unroll
-  for (int q = 0; q < NI; ++q) {
-    const int n = NI * wave + q, p = 64 * n + lane;
-    if (n < KCH / 64) {
-      const int ks = p / (4 * BKEY), row = (p >> 2) % BKEY, c = (p & 3) ^ swz(row);
-      kkey[q] = key_of_row(row);
-      src[q] = 32 * ks + 8 * c;
-    } else {
-      const int p2 = p - KCH, u = p2 / (4 * HD), row = (p2 >> 2) % HD, c = (p2 & 3) ^ swz(row);
-      kkey[q] = 0;
-      src[q] = row * PP + 32 * u + 8 * c;
-    }
+  for (int q = 0; q < NK; ++q) {
+    const int p = 64 * (NK * wave + q) + lane;
+    const int ks = p / (4 * BKEY), row = (p >> 2) % BKEY, c = (p & 3) ^ swz(row);
+    kkey[q] = key_of_row(row);
+    ksrc[q] = 32 * ks + 8 * c;
   }
-  auto issue = [&](int kb) {
-    const int st = kb % AS;
-    int64_t koff;
-    if (tbl_lds)
-      koff = ((int64_t)s_blk[kb] * a.n_kv_heads + j) * (kKvBlock * HD);
-    else
-      koff = kv_offset(a.kv, a.n_kv_heads, HD, b, j, kb * BKEY);
-    const f16 *Kt = Kc + koff;
-    const int last_row = P - 1 - kb * BKEY;            // rows of the block past the prompt read this one
 #pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      const int n = NI * wave + q;
-      if (n < KCH / 64)
-        dma16(Kt + (int64_t)min(kkey[q], last_row) * HD + src[q], &sK[st][64 * n]);
-      else
-        dma16(Vt + src[q] + kb * BKEY, &sV[st][64 * n - KCH]);
-    }
+  for (int q = 0; q < NV; ++q) {
+    const int p = 64 * (NV * wave + q) + lane;
+    const int u = p / (4 * HD), row = (p >> 2) % HD, c = (p & 3) ^ swz(row);
+    vsrc[q] = row * PP + 32 * u + 8 * c;
+  }
+  auto issue_k = [&](int kb) {
+    const f16 *Kt = Kc + k_base(kb);
+    const int last_row = P - 1 - kb * BKEY;
+#pragma unroll
+    for (int q = 0; q < NK; ++q)
+      dma16(Kt + (int64_t)min(kkey[q], last_row) * HD + ksrc[q], &sK[kb % 3][64 * (NK * wave + q)]);
+  };
+  auto issue_v = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) dma16(Vt + vsrc[q] + kb * BKEY, &sV[kb & 1][64 * (NV * wave + q)]);
   };
 
-  // Online softmax state of the lane's query column (t): the reference m
-  // (raw score units) that the exponents are taken from, and the running sum
-  // l of the probabilities, which the matrix cores accumulate: a ones tile as
-  // the A operand gives every row of lsum[t] the column sum of P^T, rescaled
-  // with O.  The reference only moves when a score exceeds it by more than
-  // RESCALE_LOG2 (in log2 units), so most blocks need no cross-lane maximum.
   const float sl2 = a.softmax_scale * 1.4426950408889634f;
-  const float thr = RESCALE_LOG2 / sl2;              // the move threshold in raw score units
+  const float thr = RESCALE_LOG2 / sl2;
   float m[2] = {0.f, 0.f};
   f32x4 o[DT][2], lsum[2];
 #pragma unroll
@@ -193,140 +160,131 @@ __global__ void __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (f16)1.0f;
 
-#pragma unroll
-  for (int k = 0; k < AS - 1; ++k)
-    if (k < n_kb) issue(k);
-  // queries as B operands: lane (i, g) holds query q0 + 16t + i, dims 32s +
-  // 8g .. +8.  Loaded after the first key blocks and awaited here with them:
-  // the compiler's own wait for these loads would otherwise sit at their
-  // first use inside the loop and, executed every iteration, wait for every
-  // key block in flight.
+  issue_k(0);
+  issue_v(0);
+  if (n_kb > 1) issue_k(1);
   f16x8 qf[2][KS];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s2 = 0; s2 < KS; ++s2) {
       const int q = q0 + 16 * t + i;
-      qf[t][s] = (q < P) ? *reinterpret_cast<const f16x8 *>(Q + (int64_t)q * qd + 32 * s + 8 * g) : zero8;
+      qf[t][s2] = (q < P) ? *reinterpret_cast<const f16x8 *>(Q + (int64_t)q * qd + 32 * s2 + 8 * g) : zero8;
     }
   wait_vmcnt<0>();
+  stage_barrier();
+
+  // S^T - m of K tile in slot sl (accumulators start at -m)
+  auto smma = [&](f32x4 (&sc)[4][2], int sl) {
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sc[y][t] = f32x4{-m[t], -m[t], -m[t], -m[t]};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int row = 16 * y + i;
+        const f16x8 kf = sK[sl][(ks * BKEY + row) * 4 + (g ^ swz(row))];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) sc[y][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[t][ks], sc[y][t], 0, 0, 0);
+      }
+  };
+  f32x4 sc[4][2];
+  smma(sc, 0);
+
   for (int kb = 0; kb < n_kb; ++kb) {
-    const int cur = kb % AS;
-    // this wave's share of stage kb is in (the later stages issued so far
-    // may still be in flight); after the barrier every wave's is, and stage
-    // kb - 1, whose buffer stage kb + AS - 1 reuses, has been consumed
-    const int later = min(AS - 2, n_kb - 1 - kb);
-    if (AS >= 4 && later == 2) wait_vmcnt<2 * NI * (AS >= 4)>();
-    else if (AS >= 3 && later == 1) wait_vmcnt<NI * (AS >= 3)>();
-    else wait_vmcnt<0>();
-    stage_barrier();
-    if (kb + AS - 1 < n_kb) issue(kb + AS - 1);
-    const bool wave_active = kb * BKEY <= q0 + 31;     // any key of the block visible to this wave
-    if (wave_active) {
-      // S^T - m tiles: y = 16-key tile, t = 16-query tile; the accumulator
-      // starts at -m, so the scores come out relative to the reference
-      f32x4 s[4][2];
+    if (kb > 0) {
+      wait_vmcnt<0>();             // K of block kb + 1 and V^T of block kb (issued one step ago) are in
+      stage_barrier();             // ... for every wave; block kb - 1 is finished by all
+    }
+    if (kb + 2 < n_kb) issue_k(kb + 2);
+    if (kb + 1 < n_kb) issue_v(kb + 1);
+
+    // masking, the column maxima and the rare reference move of block kb
+    const bool diag = kb * BKEY + BKEY - 1 > q0;
+    float lm[2];
+    if (diag) {
 #pragma unroll
-      for (int y = 0; y < 4; ++y)
+      for (int t = 0; t < 2; ++t) {
+        const int q = q0 + 16 * t + i;
+        float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) s[y][t] = f32x4{-m[t], -m[t], -m[t], -m[t]};
+        for (int y = 0; y < 4; ++y)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const int row = 16 * y + i;
-          const f16x8 kf = sK[cur][(ks * BKEY + row) * 4 + (g ^ swz(row))];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) s[y][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[t][ks], s[y][t], 0, 0, 0);
-        }
-      // lane (i, g) holds, for S^T tile y, keys 32 (y / 2) + 8g + 4 (y % 2) + r
-      // (the permuted K rows) of its query column.  Only blocks that reach
-      // past the wave's first query are masked; masked scores are -inf, so
-      // exp2 gives 0 without guards.
-      const bool diag = kb * BKEY + BKEY - 1 > q0;
-      float lm[2];
-      if (diag) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int q = q0 + 16 * t + i;
-          float mx = -INFINITY;
-#pragma unroll
-          for (int y = 0; y < 4; ++y)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = kb * BKEY + 32 * (y >> 1) + 8 * g + 4 * (y & 1) + r;
-              const float v = (key <= q) ? s[y][t][r] : -INFINITY;
-              s[y][t][r] = v;
-              mx = fmaxf(mx, v);
-            }
-          lm[t] = mx;
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int y = 0; y < 4; ++y)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[y][t][r]);
-          lm[t] = mx;
-        }
-      }
-      // Block 0 sets the reference (key 0 is visible to every query, so the
-      // column maximum is finite); later blocks move it only for a column
-      // with a score above m + thr.  Every lane of a column sees the same
-      // column maximum, so the 4 lanes agree on the move.
-      const bool first = kb == 0;
-      if (__builtin_amdgcn_ballot_w64(first || lm[0] > thr || lm[1] > thr) != 0) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float cm = lm[t];
-          cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-          cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-          const float delta = (first || cm > thr) ? cm : 0.f;
-          if (delta != 0.f) {
-            const float corr = first ? 0.f : exp2_raw(-delta * sl2);
-#pragma unroll
-            for (int d = 0; d < DT; ++d) o[d][t] *= corr;
-            lsum[t] *= corr;
-#pragma unroll
-            for (int y = 0; y < 4; ++y)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) s[y][t][r] -= delta;
-            m[t] += delta;
+          for (int r = 0; r < 4; ++r) {
+            const int key = kb * BKEY + 32 * (y >> 1) + 8 * g + 4 * (y & 1) + r;
+            const float v = (key <= q) ? sc[y][t][r] : -INFINITY;
+            sc[y][t][r] = v;
+            mx = fmaxf(mx, v);
           }
-        }
+        lm[t] = mx;
       }
-      // probabilities, packed as the B operand of step u: keys 32u + 8g + e
-      // (tile 2u gives e < 4, tile 2u + 1 the rest)
-      f16x8 pb[2][2];
+    } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int y = 0; y < 4; ++y)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pb[t][u][e] = (f16)exp2_raw(s[2 * u][t][e] * sl2);
-            pb[t][u][e + 4] = (f16)exp2_raw(s[2 * u + 1][t][e] * sl2);
-          }
-      // O^T += V^T . P^T (A operand from the transposed V tile with the same
-      // key order) and l += ones . P^T
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int d = 0; d < DT; ++d) {
-          const int row = 16 * d + i;
-          const f16x8 vf = sV[cur][(u * HD + row) * 4 + (g ^ swz(row))];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[t][u], o[d][t], 0, 0, 0);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[t][u], lsum[t], 0, 0, 0);
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[y][t][r]);
+        lm[t] = mx;
       }
     }
+    const bool first = kb == 0;
+    if (__builtin_amdgcn_ballot_w64(first || lm[0] > thr || lm[1] > thr) != 0) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float cm = lm[t];
+        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        const float delta = (first || cm > thr) ? cm : 0.f;
+        if (delta != 0.f) {
+          const float corr = first ? 0.f : exp2_raw(-delta * sl2);
+#pragma unroll
+          for (int d = 0; d < DT; ++d) o[d][t] *= corr;
+          lsum[t] *= corr;
+#pragma unroll
+          for (int y = 0; y < 4; ++y)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[y][t][r] -= delta;
+          m[t] += delta;
+        }
+      }
+    }
+
+    // one basic block: S^T of block kb + 1 (after the last iteration a
+    // stale slot, never used), the probabilities of block kb, P.V
+    f32x4 sn[4][2];
+    smma(sn, (kb + 1) % 3);
+    f16x8 pb[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[t][u][e] = (f16)exp2_raw(sc[2 * u][t][e] * sl2);
+          pb[t][u][e + 4] = (f16)exp2_raw(sc[2 * u + 1][t][e] * sl2);
+        }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const int row = 16 * d + i;
+        const f16x8 vf = sV[kb & 1][(u * HD + row) * 4 + (g ^ swz(row))];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) o[d][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[t][u], o[d][t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[t][u], lsum[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sc[y][t] = sn[y][t];
   }
 
-  // O^T: lane (i, g) holds dims 16d + 4g + r of query q0 + 16t + i
   f16 *O = (f16 *)a.o + (int64_t)r0 * qd + h * HD;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -402,9 +360,9 @@ hipError_t launch_attention_prefill(hipStream_t s, const AttnArgs &a) {
   const int per_x = (total + 7) / 8;
   dim3 grid(per_x * 8);
   switch (a.head_dim) {
-    case 32: QW_LAUNCH((attn_prefill_kernel<32>), dim3(grid), dim3(64 * AW), 0, s, a, n_qt); break;
-    case 64: QW_LAUNCH((attn_prefill_kernel<64>), dim3(grid), dim3(64 * AW), 0, s, a, n_qt); break;
-    case 128: QW_LAUNCH((attn_prefill_kernel<128>), dim3(grid), dim3(64 * AW), 0, s, a, n_qt); break;
+    case 32: QW_LAUNCH((attn_prefill_kernel<32>), dim3(grid), dim3(256), 0, s, a, n_qt); break;
+    case 64: QW_LAUNCH((attn_prefill_kernel<64>), dim3(grid), dim3(256), 0, s, a, n_qt); break;
+    case 128: QW_LAUNCH((attn_prefill_kernel<128>), dim3(grid), dim3(256), 0, s, a, n_qt); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
