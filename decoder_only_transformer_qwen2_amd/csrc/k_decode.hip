@@ -114,12 +114,138 @@ __device__ __forceinline__ void clear_share(long long *p, int64_t n, int part, i
   for (int64_t e = lo + threadIdx.x; e < hi; e += blockDim.x) p[e] = 0;
 }
 
+// ---------------------------------------------------------------- last arrival
+// A result that needs every workgroup of a kernel: the workgroup that arrives
+// last at a counter finishes it.  Everything it reads from the others was
+// written with device-scope atomics (performed where every XCD sees them) and
+// is read with device-scope atomic loads (which bypass non-coherent caches);
+// each wave waits for its own atomics to be acknowledged before the count, so
+// the count orders them.  A device-scope release fence would do the same but
+// also writes back the whole L2 of the XCD: about 15 us more per projection
+// launch at 32 rows, measured.
+__device__ __forceinline__ long long ld_coherent(const long long *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// After this workgroup's device-scope writes: true in the workgroup that
+// brings counter *c to n (which resets it for the next launch).  Uniform.
+__device__ __forceinline__ bool arrive_last(int *c, int n) {
+  __shared__ int s_last;
+  wait_vmcnt<0>();                  // this wave's writes are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int last = atomicAdd(c, 1) == n - 1;
+    if (last) atomicExch(c, 0);
+    s_last = last;
+  }
+  __syncthreads();
+  return s_last;
+}
+
+// ---------------------------------------------------------------- RMSNorm hand-off
+// Batched steps (more than two rows) have no kernel of their own for the
+// RMSNorm ("LLM Speedrun: Architecture", "Normalization").  1/rms of a row
+// needs the whole finished row, which only exists once every workgroup of the
+// producing projection has added its share (fixed-point atomics).  So the
+// workgroup that finishes a block of columns last writes the block's
+// u = f16(x * w) and the sum of x^2 of each row over the block; the next
+// projection multiplies u by its weights and scales output row b by
+// 1/sqrt(sum_blocks / H + eps), which is the same product reassociated.  The
+// sums are added in a fixed order, so the result does not depend on which
+// workgroup came last.
+
+// Consumer side: the partial sums are loaded at the start (consumed at the
+// end, so their latency hides behind the weights) and reduced to 1/rms per
+// row in LDS.  Thread t takes a run of C = round_up(ceil(parts / TPR), 4)
+// parts of row t % 32, from part C (t / 32), as float4 loads (a row holds
+// kNormPartsMax, so every load stays in it; parts past `parts` count zero).
+template <int NT>
+struct RowRstd {
+  static constexpr int TPR = NT / 32;
+  static constexpr int PER4 = (kNormPartsMax / TPR + 3) / 4;
+  float4 v[PER4];
+  int base = 0;
+  __device__ __forceinline__ void load(const RowNormIn &n, int M) {
+    const int b = threadIdx.x % 32, sub = threadIdx.x / 32;
+    const int run = ((n.parts + TPR - 1) / TPR + 3) & ~3;     // uniform
+    base = min(sub * run, kNormPartsMax - 4 * PER4);
+    const float4 *p = reinterpret_cast<const float4 *>(n.ss + (int64_t)min(b, M - 1) * n.ss_ld + base);
+#pragma unroll
+    for (int t = 0; t < PER4; ++t) {
+      v[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * t < run) v[t] = p[t];                            // uniform condition
+    }
+  }
+  // every thread calls it; s_rstd[b] holds 1/rms of row b afterwards
+  __device__ __forceinline__ void finish(const RowNormIn &n, float (*s_part)[32], float *s_rstd) {
+    const int b = threadIdx.x % 32, sub = threadIdx.x / 32;
+    const int run = ((n.parts + TPR - 1) / TPR + 3) & ~3;
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < PER4; ++k) {
+      const float e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int part = base + 4 * k + q;
+        if (4 * k + q < run && part >= sub * run && part < n.parts) t += e[q];
+      }
+    }
+    s_part[sub][b] = t;
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      float tot = 0.f;
+#pragma unroll
+      for (int k = 0; k < TPR; ++k) tot += s_part[k][threadIdx.x];
+      s_rstd[threadIdx.x] = 1.0f / sqrtf(tot / n.dim + n.eps);
+    }
+    __syncthreads();
+  }
+};
+
+// Producer side, after a FixAdd projection's residual additions: the last of
+// the gridDim.y K slices of column block nblk (RB columns from n0) forms u and
+// the block's sums of squares.  s_buf: RB * BT floats of free LDS.
+template <int RB, int BT, int NT>
+__device__ __forceinline__ void norm_tail(const DecGemvArgs &a, int n0, int nblk, float *s_buf) {
+  // K split: the residual was updated by device-scope atomics of gridDim.y
+  // workgroups; otherwise by this workgroup alone (plain stores, visible to
+  // it after the barrier)
+  const bool split = gridDim.y > 1;
+  if (split) {
+    if (!arrive_last(a.nout.counters + nblk, gridDim.y)) return;
+  } else {
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < RB * BT; e += NT) {
+    const int nl = e % RB, b = e / RB, n = n0 + nl;
+    float sq = 0.f;
+    if (n < a.N && b < a.M) {
+      long long q = 0;
+#pragma unroll
+      for (int r = 0; r < kXReps; ++r) {
+        const long long *p = a.out_fix + r * a.nout.rep_stride + (int64_t)b * a.ldo + n;
+        q += split ? ld_coherent(p) : *p;
+      }
+      const float x = from_fix(q);
+      ((f16 *)a.nout.u)[(int64_t)b * a.N + n] = (f16)(x * a.nout.w[n]);
+      sq = x * x;
+    }
+    s_buf[b * RB + nl] = sq;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < a.M) {
+    float t = 0.f;
+    for (int nl = 0; nl < RB; ++nl) t += s_buf[threadIdx.x * RB + nl];
+    a.nout.ss[(int64_t)threadIdx.x * a.nout.ss_ld + nblk] = t;
+  }
+}
+
 // ---------------------------------------------------------------- begin / norm / end
 // x_fix[b] = embedding row of ids[b] (its exact value, in fixed point); clears
-// the q/k/v and gate/up accumulators for the first layer.
+// the q/k/v and gate/up accumulators for the first layer.  With nout.w set
+// (batched steps) also the first layer's u = f16(x * w) and sum of x^2.
 __global__ void __launch_bounds__(256) dec_embed_kernel(const int32_t *ids, const f16 *emb, float emb_scale, int H,
                                                         int V, long long *x_fix, int *bad, long long *clr0,
-                                                        int64_t n0, long long *clr1, int64_t n1) {
+                                                        int64_t n0, long long *clr1, int64_t n1, RowNormOut nout) {
   const int b = blockIdx.x;
   int id = ids[b];
   if (id < 0 || id >= V) {
@@ -127,7 +253,23 @@ __global__ void __launch_bounds__(256) dec_embed_kernel(const int32_t *ids, cons
     id = 0;
   }
   const f16 *row = emb + (int64_t)id * H;
-  for (int c = threadIdx.x; c < H; c += blockDim.x) x_fix[(int64_t)b * H + c] = to_fix((float)row[c] * emb_scale, bad);
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < H; c += blockDim.x) {
+    const long long q = to_fix((float)row[c] * emb_scale, bad);
+    x_fix[(int64_t)b * H + c] = q;
+    if (nout.w) {
+      const float x = from_fix(q);
+      ((f16 *)nout.u)[(int64_t)b * H + c] = (f16)(x * nout.w[c]);
+      ss += x * x;
+    }
+  }
+  if (nout.w) {
+    __shared__ float red[4];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) nout.ss[(int64_t)b * nout.ss_ld] = red[0] + red[1] + red[2] + red[3];
+  }
   clear_share(clr0, n0, b, gridDim.x);
   clear_share(clr1, n1, b, gridDim.x);
 }
@@ -209,11 +351,10 @@ __global__ void __launch_bounds__(256) dec_end_kernel(const float *pv, const int
 // rather than in every row-block workgroup's prologue: o[b, h] = merge of the
 // S split-KV partials of head h (one workgroup per (head, row), one thread
 // per dimension).  (The gate/up projection writes silu(gate) * up itself.)
-__global__ void __launch_bounds__(128) dec_merge_kernel(const float *pm, const float *pl, const float *po, int S, int nq,
-                                                        int hd, f16 *o) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  if (d >= hd) return;
-  const int64_t st0 = ((int64_t)b * nq + h) * S;
+// Dimension d of one head's output from its S split-KV partials (max m, sum l,
+// unnormalised output o), partials st0 .. st0 + S - 1.
+__device__ __forceinline__ float merge_splits(const float *pm, const float *pl, const float *po, int64_t st0, int S,
+                                              int hd, int d) {
   float m[MERGE_MAX_S], l[MERGE_MAX_S], v[MERGE_MAX_S];
 #pragma unroll
   for (int sp = 0; sp < MERGE_MAX_S; ++sp) {
@@ -233,7 +374,14 @@ __global__ void __launch_bounds__(128) dec_merge_kernel(const float *pm, const f
     L = fmaf(c, l[sp], L);
     O = fmaf(c, v[sp], O);
   }
-  o[(int64_t)b * nq * hd + (int64_t)h * hd + d] = (f16)(O / L);
+  return O / L;
+}
+
+__global__ void __launch_bounds__(128) dec_merge_kernel(const float *pm, const float *pl, const float *po, int S, int nq,
+                                                        int hd, f16 *o) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  if (d >= hd) return;
+  o[(int64_t)b * nq * hd + (int64_t)h * hd + d] = (f16)merge_splits(pm, pl, po, ((int64_t)b * nq + h) * S, S, hd, d);
 }
 
 // ---------------------------------------------------------------- projections
@@ -267,6 +415,12 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
   // side job: clear an accumulator of the next layer, shared by all workgroups
   if (a.clear)
     clear_share(a.clear, a.clear_n, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  // LM head of a batched step: operand u without 1/rms (row sums of squares
+  // loaded now, needed at the end)
+  constexpr bool kRowScale = OM == DecOut::Logits && AM == DecAct::F16;
+  const bool nrm = kRowScale && a.nin.ss != nullptr;
+  RowRstd<256> rr;
+  if (nrm) rr.load(a.nin, a.M);
 
   f16x8 w[8];
   auto load_w = [&](int kc) {
@@ -458,15 +612,18 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
     // logits (optional copy) and this block's (max, lowest index) per batch row
     __shared__ float s_v[4][BT];
     __shared__ int s_i[4][BT];
+    __shared__ float s_part[8][32], s_rstd[32];
+    if (nrm) rr.finish(a.nin, s_part, s_rstd);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int b = nb * 16 + i;
+      const float rs = nrm ? s_rstd[b < 32 ? b : 0] : 1.f;
       float best = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int n = nw + r;
-        const float v = acc[nb][r] * a.scale;
+        const float v = nrm ? acc[nb][r] * a.scale * rs : acc[nb][r] * a.scale;
         if (n < a.N && b < a.M) {
           if (a.logits) a.logits[(int64_t)b * a.ldo + n] = v;
           if (v > best) { best = v; bi = n; }     // n increases with r
@@ -558,6 +715,7 @@ __global__ void __launch_bounds__(64 * NW) dec_rows_kernel(DecGemvArgs a) {
   constexpr int RB = 16 * RT, BT = 16 * NB, NT = 64 * NW;
   static_assert(OM != DecOut::Logits || NW == 4, "the argmax partials take 256 threads");
   __shared__ float s_acc[NW][RB][BT + 1];
+  __shared__ float s_part[NT / 32][32], s_rstd[32];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: unit bounds stay scalar
   const int i = lane & 15, g = lane >> 4;
@@ -570,6 +728,10 @@ __global__ void __launch_bounds__(64 * NW) dec_rows_kernel(DecGemvArgs a) {
 
   if (a.clear)
     clear_share(a.clear, a.clear_n, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  // operand u without 1/rms: the row sums of squares, needed at the end
+  const bool nrm = a.nin.ss != nullptr;
+  RowRstd<NT> rr;
+  if (nrm) rr.load(a.nin, a.M);
 
   // lane (i, g): weight row n0 + 16 r + i and batch row 16 nb + i, k offset 8 g
   // of each unit; rows past N or M are clamped and their results never stored
@@ -621,11 +783,12 @@ __global__ void __launch_bounds__(64 * NW) dec_rows_kernel(DecGemvArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) s_acc[wave][16 * r + 4 * g + q][16 * nb + i] = acc[r][nb][q];
   __syncthreads();
+  if (nrm) rr.finish(a.nin, s_part, s_rstd);
   auto total = [&](int nl, int b) {
     float t = s_acc[0][nl][b];
 #pragma unroll
     for (int w2 = 1; w2 < NW; ++w2) t += s_acc[w2][nl][b];
-    return t * a.scale;
+    return nrm ? t * a.scale * s_rstd[b] : t * a.scale;
   };
 
   if constexpr (OM == DecOut::FixAdd) {
@@ -641,6 +804,8 @@ __global__ void __launch_bounds__(64 * NW) dec_rows_kernel(DecGemvArgs a) {
         *p += to_fix(total(nl, b), a.num_flag);
       }
     }
+    // a residual projection hands the next RMSNorm its operand
+    if (a.nout.w) norm_tail<RB, BT, NT>(a, n0, nblk, &s_acc[0][0][0]);
   } else if constexpr (OM == DecOut::SwiGLUOut) {
     static_assert(RT % 2 == 0, "gate/up rows come in GU_BLOCK pairs");
     f16 *h = (f16 *)a.h_out;
@@ -2140,10 +2305,21 @@ int dec_attn_splits(int batch, int n_kv_heads, int ctx, int target_groups) {
 }
 
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
-                            long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1) {
-  QW_LAUNCH((dec_embed_kernel), dim3(B), dim3(256), 0, s, ids, (const f16 *)emb, emb_scale, H, V, x_fix, bad, clr0, n0, clr1, n1);
+                            long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1,
+                            const RowNormOut &nout) {
+  QW_LAUNCH((dec_embed_kernel), dim3(B), dim3(256), 0, s, ids, (const f16 *)emb, emb_scale, H, V, x_fix, bad, clr0, n0,
+            clr1, n1, nout);
   return hipGetLastError();
 }
+
+int dec_norm_parts(int M, int N, int K) {
+  if (M <= 2 || M > 32 || (K & 31)) return 0;          // the one/two-row kernels normalise their own operand
+  const int rt = M <= 16 ? 1 : 2;                        // rows_plan's tile rows for FixAdd outputs
+  const int parts = (N + 16 * rt - 1) / (16 * rt);
+  if (parts > kNormPartsMax || parts > kSyncCounters) return 0;
+  return parts;
+}
+
 
 hipError_t launch_dec_merge(hipStream_t s, const float *pm, const float *pl, const float *po, int S, int B, int nq,
                             int hd, void *o) {
@@ -2170,14 +2346,25 @@ hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &in) {
   if (a.M > 32 || (a.K & 31) || (a.lda & 7)) return hipErrorInvalidValue;
   if (a.act_mode == (int)DecAct::AttnMerge && (a.attn_splits < 1 || a.attn_splits > MERGE_MAX_S))
     return hipErrorInvalidValue;
+  const bool rows_path = a.M > 2 && a.act_mode == (int)DecAct::F16 && !a.logits_mode;
+  // the norm hand-off: u without 1/rms is read by the batched kernels and the
+  // LM head on an f16 operand; it is produced by the batched residual projections
+  if (a.nin.ss && (a.nin.parts < 1 || a.nin.parts > kNormPartsMax || a.act_mode != (int)DecAct::F16 ||
+                   !(rows_path || a.logits_mode)))
+    return hipErrorInvalidValue;
+  if (a.nout.w && (!rows_path || a.swiglu_out || dec_norm_parts(a.M, a.N, a.K) == 0 || !a.nout.counters ||
+                   !a.nout.u || !a.nout.ss || a.nout.ss_ld < dec_norm_parts(a.M, a.N, a.K)))
+    return hipErrorInvalidValue;
   const int units = a.K / 32;
   int splits = (a.logits_mode || a.swiglu_out) ? 1 : (a.splits < 1 ? 1 : a.splits);
   a.units_per_split = (units + splits - 1) / splits;
   splits = (units + a.units_per_split - 1) / a.units_per_split;
   // (the LM head stays on dec_gemv_kernel: 0.099 vs 0.110 ms per step at 8 rows)
-  if (a.M > 2 && a.act_mode == (int)DecAct::F16 && !a.logits_mode) {
+  if (rows_path) {
     // batched rows: K split only for FixAdd outputs
     RowsPlan p = rows_plan(a, units);
+    // the hand-off's column blocks are the tiles dec_norm_parts assumes
+    if (a.nout.w && (a.N + 16 * p.rt - 1) / (16 * p.rt) != dec_norm_parts(a.M, a.N, a.K)) return hipErrorInvalidValue;
     a.units_per_split = (units + p.splits - 1) / p.splits;
     p.splits = (units + a.units_per_split - 1) / a.units_per_split;
     return a.M <= 16 ? launch_rows_nb<1>(s, a, p) : launch_rows_nb<2>(s, a, p);

@@ -200,6 +200,27 @@ struct AttnArgs {
   float softmax_scale;
 };
 
+// RMSNorm hand-off between the batched decode projections (more than two
+// rows), see k_decode.hip.  The projection that finishes a block of residual
+// columns writes the next projection's operand without the row scale,
+// u = f16(x * w), and the block's sum of x^2 per row; the projection that
+// reads u multiplies each output row by 1/rms of its row.
+constexpr int kNormPartsMax = 128;     // sums of squares per row (column blocks of the producer)
+constexpr int kSyncCounters = 256;     // last-arrival counters of one decode step
+struct RowNormOut {
+  const float *w;           // norm weight [N] of the consumer; NULL: no hand-off
+  void *u;                  // f16 [M, N]
+  float *ss;                // [M, ss_ld]: column block c's sum of x^2 at column c
+  int ss_ld;
+  int *counters;            // one per column block, zero between launches
+  int64_t rep_stride;       // residual replicas of out_fix (value = their sum)
+};
+struct RowNormIn {
+  const float *ss;          // NULL: the operand is already normalised
+  int ss_ld, parts;         // parts <= kNormPartsMax sums per row
+  float dim, eps;           // H and the RMSNorm epsilon
+};
+
 // Decode-step projection (B <= 32 rows), see k_decode.hip.  f16 operands.
 struct DecGemvArgs {
   const void *W;            // [N, K] f16
@@ -234,6 +255,8 @@ struct DecGemvArgs {
   float *arg_v;             // [M, ceil(N / 64)]
   int *arg_i;
   int *num_flag;            // status word (kFlagFixRange, kFlagNonFinite)
+  RowNormOut nout;          // batched FixAdd residual projections: the next norm's operand
+  RowNormIn nin;            // batched projections and the LM head: operand u without 1/rms
 };
 
 // Decode-step attention, see k_decode.hip.
@@ -327,8 +350,13 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a);     // f16 operan
 bool decode_fast_supported(int head_dim, int group, int hidden, int q_dim, int inter);
 int dec_gemv_splits(int N, int K, int M, int target_groups);
 int dec_attn_splits(int batch, int n_kv_heads, int ctx, int target_groups);
+// with nout.w set, also u = f16(x * w) and each row's sum of x^2 (nout.ss[b * ss_ld])
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
-                            long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1);
+                            long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1,
+                            const RowNormOut &nout);
+// the column blocks a batched FixAdd projection of N outputs hands its norm
+// sums over (0: it cannot, and a norm kernel runs instead)
+int dec_norm_parts(int M, int N, int K);
 hipError_t launch_dec_norm(hipStream_t s, const long long *x_fix, int64_t rep_stride, int B, int H,
                            const float *w, float eps, void *u);
 // also advances pos_dev[b] for every row b

@@ -159,6 +159,8 @@ struct qw_model {
   float *arg_v = nullptr;            // [max_batch, ceil(V / 64)]
   int *arg_i = nullptr;
   float *att_m = nullptr, *att_l = nullptr, *att_o = nullptr;   // split-KV partials
+  float *norm_ss = nullptr;          // [max_batch, kNormPartsMax] row-norm hand-off sums
+  int *sync = nullptr;               // [kSyncCounters] last-arrival counters (zero between kernels)
   void *v_t = nullptr;               // prefill: V of the prompt transposed (f16 mode)
   float *splitk_ws = nullptr;        // prefill split-K slices, sized at creation
   size_t splitk_bytes = 0;
@@ -205,9 +207,15 @@ constexpr int kGemvTargetGroupsBatched = 256;
 // of ~1k keys beat 16 of ~512 (57.3 vs 60.5 us per launch, same box)
 constexpr int kAttnTargetGroups = 512;
 // Up to this many rows, a projection normalises its own operand (each
-// workgroup reads the whole residual rows); above it a norm kernel runs.
+// workgroup reads the whole residual rows); above it the residual
+// projections hand the norm's operand to the next projection (a norm kernel
+// where they cannot).
 constexpr int kFusedNormRows = 2;
 constexpr bool kHeadNormKernel = true;
+#ifndef QW_NORM_HANDOFF
+#define QW_NORM_HANDOFF 1
+#endif
+constexpr bool kNormHandOff = QW_NORM_HANDOFF;
 // Up to this context length (and two rows), attention and the o projection
 // are one kernel in which every workgroup reads its head's whole context;
 // past it the split-KV kernel and the o projection (measured: the merged
@@ -227,6 +235,8 @@ struct DecodeScratch {
   float *att_m = nullptr, *att_l = nullptr, *att_o = nullptr;   // [B][nq][16] (+ [hd])
   void *u = nullptr, *o = nullptr, *h = nullptr;   // f16 [B, H], [B, qd], [B, I]
   float *logits = nullptr;                         // [B, V], or NULL (argmax partials only)
+  float *norm_ss = nullptr;                        // [B, kNormPartsMax] row-norm hand-off sums
+  int *sync = nullptr;                             // [kSyncCounters] last-arrival counters, zero between kernels
 };
 
 // Which decode step the next decode call runs: 1 = attention merged with the
@@ -513,11 +523,37 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   // the residual is kXReps fixed-point replicas xs apart (value = their sum)
   const int64_t xs = (int64_t)B * H;
   const int64_t n_qkv = (int64_t)B * m->nqkv, n_gu = (int64_t)B * 2 * I;
+  // more than two rows: each residual projection hands the next RMSNorm its
+  // operand (u without 1/rms, sums of squares per column block), so no norm
+  // kernel runs; `parts` sums per row (1 after the embedding)
+  const int parts = fused_norm ? 0 : std::min(dec_norm_parts(B, H, m->qd), dec_norm_parts(B, H, I));
+  const bool hand = parts > 0 && kNormHandOff;
+  auto hand_out = [&](const float *w) {
+    RowNormOut r{};
+    if (!hand) return r;
+    r.w = w;
+    r.u = d.u;
+    r.ss = d.norm_ss;
+    r.ss_ld = kNormPartsMax;
+    r.counters = d.sync;
+    r.rep_stride = xs;
+    return r;
+  };
+  auto hand_in = [&](int n_parts) {
+    RowNormIn r{};
+    if (!hand) return r;
+    r.ss = d.norm_ss;
+    r.ss_ld = kNormPartsMax;
+    r.parts = n_parts;
+    r.dim = (float)H;
+    r.eps = c.rms_eps;
+    return r;
+  };
   hipError_t e = timed(m, s, F_EMBED, [&] {
     // the embedding goes to replica 0; the other replicas and the q/k/v
     // accumulator are cleared (attention clears the gate/up accumulator)
     return launch_dec_embed(s, ids, B, m->emb, m->emb_scale, H, V, d.x_fix, m->status, d.qkv_fix, n_qkv,
-                            d.x_fix + xs, (kXReps - 1) * xs);
+                            d.x_fix + xs, (kXReps - 1) * xs, hand_out(m->L[0].in_norm));
   });
   if (e != hipSuccess) return e;
   // operand of a projection that follows an RMSNorm
@@ -535,7 +571,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     }
   };
   auto norm = [&](const float *w) -> hipError_t {
-    if (fused_norm) return hipSuccess;
+    if (fused_norm || hand) return hipSuccess;
     return timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, w, c.rms_eps, d.u); });
   };
   for (int l = 0; l < c.n_layers; ++l) {
@@ -546,6 +582,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     const int gemv_target = fused_norm ? kGemvTargetGroups : kGemvTargetGroupsBatched;
     DecGemvArgs g = dec_args(m->status, Lw.w_qkv, B, m->nqkv, H, Lw.s_qkv, gemv_target);
     normed(g, Lw.in_norm);
+    g.nin = hand_in(l == 0 ? 1 : parts);
     g.out_fix = d.qkv_fix;
     g.ldo = m->nqkv;
     e = timed(m, s, F_GEMM_QKV, [&] { return launch_dec_gemv(s, g); });
@@ -623,6 +660,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       g.ldo = H;
       g.clear = d.qkv_fix;
       g.clear_n = n_qkv;
+      g.nout = hand_out(Lw.post_norm);
       e = timed(m, s, F_GEMM_O, [&] { return launch_dec_gemv(s, g); });
       if (e != hipSuccess) return e;
     }
@@ -654,6 +692,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     g = dec_args(m->status, Lw.w_gu, B, 2 * I, H, Lw.s_gu, fused_norm ? kGemvTargetGroups / 2 : kGemvTargetGroups);
     normed(g, Lw.post_norm);
     g.role_gate_up = 1;
+    g.nin = hand_in(parts);
     g.out_fix = d.gu_fix;
     if (!fused_norm) {
       // many rows: full K per workgroup, SwiGLU in the epilogue, f16 h out
@@ -682,13 +721,19 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     }
     g.out_fix = xr;
     g.ldo = H;
+    g.nout = hand_out(l + 1 < c.n_layers ? m->L[l + 1].in_norm : m->final_norm);
     e = timed(m, s, F_GEMM_DOWN, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
   }
   // the LM head has thousands of workgroups: the final row is normalised once
   // by a kernel of its own rather than in every workgroup's prologue
   DecGemvArgs g = dec_args(m->status, m->head, B, V, H, m->head_scale);
-  if (kHeadNormKernel || !fused_norm) {
+  if (hand) {
+    g.act_mode = 0;
+    g.act = d.u;
+    g.lda = H;
+    g.nin = hand_in(parts);
+  } else if (kHeadNormKernel || !fused_norm) {
     e = timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, m->final_norm, c.rms_eps, d.u); });
     if (e != hipSuccess) return e;
     g.act_mode = 0;
@@ -726,6 +771,8 @@ DecodeScratch model_scratch(const qw_model *m) {
   d.o = m->o;
   d.h = m->h;
   d.logits = m->logits;
+  d.norm_ss = m->norm_ss;
+  d.sync = m->sync;
   return d;
 }
 
@@ -1034,6 +1081,9 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
     CREATE_TRY(m->alloc((void **)&m->att_m, ns * 4));
     CREATE_TRY(m->alloc((void **)&m->att_l, ns * 4));
     CREATE_TRY(m->alloc((void **)&m->att_o, ns * c.head_dim * 4));
+    CREATE_TRY(m->alloc((void **)&m->norm_ss, nb * kNormPartsMax * 4));
+    CREATE_TRY(m->alloc((void **)&m->sync, kSyncCounters * 4));
+    CREATE_TRY(hipMemsetAsync(m->sync, 0, kSyncCounters * 4, s));
   }
   CREATE_TRY(m->alloc((void **)&m->next_stage, (size_t)c.max_batch * 4));
   CREATE_TRY(m->alloc((void **)&m->seq_ids, (size_t)c.max_batch * c.max_seq * 4));
@@ -1383,8 +1433,11 @@ qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits,
   const qw_config &c = m->cfg;
   const int64_t B = m->batch, H = c.hidden, I = c.intermediate, V = c.vocab;
   const DecodeNeeds need = decode_needs(m, (int)B);
-  // carve the step's buffers out of this device's array, 256-byte aligned
+  // carve the step's buffers out of this device's array, 256-byte aligned;
+  // the last-arrival counters always sit at its start (zero at load, and
+  // every kernel that counts leaves them at zero)
   const int64_t sizes[] = {
+      kSyncCounters * 4,                                 // sync
       kXReps * B * H * 8, kXReps * B * H * 8,             // x_fix, x_fix2
       B * m->nqkv * 8,                                   // qkv_fix
       need.gu_fix ? B * 2 * I * 8 : 0,                   // gu_fix
@@ -1392,6 +1445,7 @@ qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits,
       B * c.n_heads * 16 * 4, B * c.n_heads * 16 * 4,     // att_m, att_l (at most 16 splits)
       B * c.n_heads * 16 * c.head_dim * 4,               // att_o
       B * H * 2, B * m->qd * 2, B * I * 2,               // u, o, h (f16)
+      B * kNormPartsMax * 4,                             // norm_ss
   };
   constexpr int kParts = sizeof(sizes) / sizeof(sizes[0]);
   int64_t off[kParts], total = 0;
@@ -1412,18 +1466,20 @@ qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits,
   qw_status st = reserve_step_blocks(m, m->stream, "qw_decode_step_noalloc");
   if (st != QW_OK) return st;
   DecodeScratch d;
-  d.x_fix = (long long *)(base + off[0]);
-  d.x_fix2 = (long long *)(base + off[1]);
-  d.qkv_fix = (long long *)(base + off[2]);
-  d.gu_fix = need.gu_fix ? (long long *)(base + off[3]) : nullptr;
-  d.arg_v = (float *)(base + off[4]);
-  d.arg_i = (int *)(base + off[5]);
-  d.att_m = (float *)(base + off[6]);
-  d.att_l = (float *)(base + off[7]);
-  d.att_o = (float *)(base + off[8]);
-  d.u = base + off[9];
-  d.o = base + off[10];
-  d.h = base + off[11];
+  d.sync = (int *)(base + off[0]);
+  d.x_fix = (long long *)(base + off[1]);
+  d.x_fix2 = (long long *)(base + off[2]);
+  d.qkv_fix = (long long *)(base + off[3]);
+  d.gu_fix = need.gu_fix ? (long long *)(base + off[4]) : nullptr;
+  d.arg_v = (float *)(base + off[5]);
+  d.arg_i = (int *)(base + off[6]);
+  d.att_m = (float *)(base + off[7]);
+  d.att_l = (float *)(base + off[8]);
+  d.att_o = (float *)(base + off[9]);
+  d.u = base + off[10];
+  d.o = base + off[11];
+  d.h = base + off[12];
+  d.norm_ss = (float *)(base + off[13]);
   d.logits = logits;                 // the caller's buffer, or none
   // launched one by one on the model's stream (nothing captured or
   // instantiated); kernel timing stays off (it would create events)
