@@ -142,3 +142,30 @@ def test_generic_decode_across_prefill_lengths(Q):
             err, _ = compare_row(om, ids[b], toks[b], logits[b], "bf16", f"P={P} row {b}")
             say(f"generic decode P={P} row {b}: max err {err:.2e}")
     m.close()
+
+
+# hidden 1536: 96 column blocks of the residual projections at up to 16 rows,
+# 48 above; the K splits of the o and down projections are several slices
+HANDOFF_SHAPE = S.ModelShape("hand", 2, 1536, 12, 2, 128, 1024, 1200)
+
+
+@pytest.mark.parametrize("B", [5, 24])
+def test_batched_decode_norm_handoff_is_deterministic(Q, B):
+    """More than two rows: the residual projections hand the next RMSNorm
+    ("LLM Speedrun: Architecture", "Normalization") its operand through a
+    count of the workgroups that have added their share; whichever arrives
+    last does it, so three runs (captured graph, eager, graph again) must
+    give identical bits, and the first and last rows match the oracle."""
+    from tests.helpers import with_random_norms
+    W = with_random_norms(S.make_weights(HANDOFF_SHAPE, 91), HANDOFF_SHAPE)
+    P, D = 40, 8
+    ids = np.random.default_rng(92).integers(0, HANDOFF_SHAPE.vocab, (B, P)).astype(np.int32)
+    m = make(Q, HANDOFF_SHAPE, W, B, P + D + 2)
+    runs = [gpu_generate(m, ids, D, graph=g) for g in (True, False, True)]
+    m.close()
+    for t, l in runs[1:]:
+        assert np.array_equal(t, runs[0][0]) and np.array_equal(l, runs[0][1])
+    om = O.OracleModel(HANDOFF_SHAPE, W)
+    for b in (0, B - 1):
+        err, _ = compare_row(om, ids[b], runs[0][0][b], runs[0][1][b], "bf16", f"B={B} row {b}")
+        say(f"B={B} row {b}: max |dlogit| {err:.3e}")
