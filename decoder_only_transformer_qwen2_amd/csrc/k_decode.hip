@@ -8,7 +8,7 @@
 //
 //  * Kernel boundaries are the only cheap device-wide synchronisation here,
 //    and a device-scope fence per workgroup is expensive, so no workgroup
-//    waits on another.  Projections split K over workgroups and add their
+//    waits on another (the norm hand-off counts arrivals, without a fence).  Projections split K over workgroups and add their
 //    partial sums with 64-bit integer atomics on a fixed-point copy of the
 //    value (32 fractional bits).  Integer addition is associative, so the
 //    result does not depend on arrival order (deterministic), and no fence is
@@ -24,9 +24,10 @@
 //    residual is two fixed-point replicas (value = their sum) so that the
 //    MLP's workgroups, which all add into every value of a row, spread their
 //    atomics; it ping-pongs between two buffers around the MLP.
-//  * More than two rows: a norm kernel, the projections (gate/up without a K
-//    split, SwiGLU in its epilogue), split-KV attention on the matrix cores
-//    (dec_attn_mfma_kernel) and a merge kernel.
+//  * More than two rows: the projections (gate/up without a K split, SwiGLU
+//    in its epilogue), split-KV attention on the matrix cores
+//    (dec_attn_mfma_kernel) and a merge kernel; the residual projections hand
+//    the next RMSNorm its operand (norm_tail), so no norm kernel runs.
 //  * Every load of a kernel's first phase is issued before any is consumed
 //    (clamped addresses and selects rather than per-lane branches).
 //  * Accumulators are cleared by an earlier kernel of the same step, so the
@@ -274,8 +275,9 @@ __global__ void __launch_bounds__(256) dec_embed_kernel(const int32_t *ids, cons
   clear_share(clr1, n1, b, gridDim.x);
 }
 
-// u[b] = f16(x[b] / sqrt(mean(x[b]^2) + eps) * w): used when the batch is too
-// large for the projections to normalise their own operand.
+// u[b] = f16(x[b] / sqrt(mean(x[b]^2) + eps) * w): before the LM head of one or
+// two rows, and for larger batches whose residual projections cannot hand the
+// norm on (more column blocks than kNormPartsMax).
 __global__ void __launch_bounds__(256) dec_norm_kernel(const long long *x_fix, int64_t rep_stride, int H,
                                                        const float *w, float eps, f16 *u) {
   const int b = blockIdx.x;

@@ -489,9 +489,10 @@ DecGemvArgs dec_args(int *status, const void *W, int M, int N, int K, float scal
 // with per-block argmax and the argmax reduction.  For batches of up to two
 // rows the norms are folded into the projection that follows them and the
 // MLP is one kernel (norm, gate/up, SwiGLU, down) that reads the residual
-// from one buffer and accumulates into the other; for larger batches a norm
-// kernel, the gate/up projection and the down projection (SwiGLU on its
-// operand) run separately on one residual buffer.
+// from one buffer and accumulates into the other; for larger batches the
+// gate/up projection (SwiGLU in its epilogue) and the down projection run
+// separately on one residual buffer, and each residual projection hands the
+// next RMSNorm its operand (u without 1/rms, per-row sums of squares).
 // Which per-step buffers a fast decode step of B rows uses.
 struct DecodeNeeds {
   bool fused_norm, fused_mlp, gu_fix;
