@@ -19,9 +19,9 @@
 // 32-column sub-tiles (see swz).  V^T comes from a transposed copy of the
 // prompt's V written once per layer (transpose_v_kernel), since transposing
 // inside the kernel took 2-byte LDS stores with 16-way bank conflicts.  Work
-// items are ordered heaviest (latest
-// query tile) first and mapped so that the g query heads of a KV head and
-// query tile run on the same XCD, where they share the K/V tiles in L2.
+// items are ordered heaviest (latest query tile) first and mapped so that the
+// g query heads of a KV head and query tile run on the same XCD, where they
+// share the K/V tiles in L2.
 #include "qw_internal.h"
 
 #include <math.h>
@@ -174,12 +174,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   wait_vmcnt<0>();
   stage_barrier();
 
-  // S^T - m of K tile in slot sl (accumulators start at -m)
+  // S^T of K tile in slot sl (accumulators start at zero: an inline constant
+  // of the first MFMA, no register moves)
   auto smma = [&](f32x4 (&sc)[4][2], int sl) {
 #pragma unroll
     for (int y = 0; y < 4; ++y)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) sc[y][t] = f32x4{-m[t], -m[t], -m[t], -m[t]};
+      for (int t = 0; t < 2; ++t) sc[y][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -193,7 +194,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
   f32x4 sc[4][2];
   smma(sc, 0);
 
-  for (int kb = 0; kb < n_kb; ++kb) {
+  // block kb: its scores in sc, block kb + 1's computed into sn; the loop
+  // below alternates the two register sets (no copy between blocks)
+  auto block = [&](int kb, f32x4 (&sc)[4][2], f32x4 (&sn)[4][2]) {
     if (kb > 0) {
       wait_vmcnt<0>();             // K of block kb + 1 and V^T of block kb (issued one step ago) are in
       stage_barrier();             // ... for every wave; block kb - 1 is finished by all
@@ -232,30 +235,26 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
       }
     }
     const bool first = kb == 0;
-    if (__builtin_amdgcn_ballot_w64(first || lm[0] > thr || lm[1] > thr) != 0) {
+    if (__builtin_amdgcn_ballot_w64(first || lm[0] > m[0] + thr || lm[1] > m[1] + thr) != 0) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         float cm = lm[t];
         cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
         cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-        const float delta = (first || cm > thr) ? cm : 0.f;
-        if (delta != 0.f) {
-          const float corr = first ? 0.f : exp2_raw(-delta * sl2);
+        if (first || cm > m[t] + thr) {
+          const float corr = first ? 0.f : exp2_raw((m[t] - cm) * sl2);
 #pragma unroll
           for (int d = 0; d < DT; ++d) o[d][t] *= corr;
           lsum[t] *= corr;
-#pragma unroll
-          for (int y = 0; y < 4; ++y)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[y][t][r] -= delta;
-          m[t] += delta;
+          m[t] = cm;
         }
       }
     }
+    // p = 2^((s - m) sl2), the reference folded into one fused multiply-add
+    const float msl[2] = {-m[0] * sl2, -m[1] * sl2};
 
     // one basic block: S^T of block kb + 1 (after the last iteration a
     // stale slot, never used), the probabilities of block kb, P.V
-    f32x4 sn[4][2];
     smma(sn, (kb + 1) % 3);
     f16x8 pb[2][2];
 #pragma unroll
@@ -264,8 +263,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pb[t][u][e] = (f16)exp2_raw(sc[2 * u][t][e] * sl2);
-          pb[t][u][e + 4] = (f16)exp2_raw(sc[2 * u + 1][t][e] * sl2);
+          pb[t][u][e] = (f16)exp2_raw(fmaf(sc[2 * u][t][e], sl2, msl[t]));
+          pb[t][u][e + 4] = (f16)exp2_raw(fmaf(sc[2 * u + 1][t][e], sl2, msl[t]));
         }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -279,10 +278,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
 #pragma unroll
       for (int t = 0; t < 2; ++t) lsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[t][u], lsum[t], 0, 0, 0);
     }
-#pragma unroll
-    for (int y = 0; y < 4; ++y)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) sc[y][t] = sn[y][t];
+  };
+  f32x4 sn[4][2];
+  for (int kb = 0; kb < n_kb; kb += 2) {
+    block(kb, sc, sn);
+    if (kb + 1 < n_kb) block(kb + 1, sn, sc);
   }
 
   f16 *O = (f16 *)a.o + (int64_t)r0 * qd + h * HD;
