@@ -447,6 +447,29 @@ hipError_t launch_convert_t(hipStream_t s, int src_kind, const void *src, int ro
   return hipGetLastError();
 }
 
+// Unit-tiled copy of an f16 weight matrix (layout in qw_internal.h): one
+// thread per 16 bytes of the destination, read as 16 bytes of one source row.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+__global__ void __launch_bounds__(256) tile_units_kernel(const f16 *W, int N, int K, f16 *Wt, int64_t n8) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;      // 16-byte piece c of Wt
+  if (c >= n8) return;
+  const int64_t tile = c >> 6;
+  const int l = (int)(c & 63), i = l & 15, g = l >> 4;
+  const int units = K >> 5;
+  const int row = (int)(tile / units) * 16 + i, k = (int)(tile % units) * 32 + 8 * g;
+  f16x8_t v = {};
+  if (row < N) v = *reinterpret_cast<const f16x8_t *>(W + (int64_t)row * K + k);
+  *reinterpret_cast<f16x8_t *>(Wt + c * 8) = v;
+}
+
+hipError_t launch_tile_units(hipStream_t s, const void *W, int N, int K, void *Wt) {
+  if (N <= 0 || K <= 0) return hipSuccess;
+  if (K % 32) return hipErrorInvalidValue;
+  const int64_t n8 = (int64_t)(N + kTileRows - 1) / kTileRows * kTileRows * K / 8;
+  tile_units_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>((const f16 *)W, N, K, (f16 *)Wt, n8);
+  return hipGetLastError();
+}
+
 // RoPE table: entry (pos, i) = (cos, sin) of pos * theta^(-2i/hd), evaluated in
 // double and rounded once to float ("Rotary Positional Embeddings RoPE").
 __global__ void __launch_bounds__(256) rope_table_kernel(float2 *table, int max_seq, int head_dim, double theta) {

@@ -227,7 +227,7 @@ __device__ __forceinline__ void norm_tail(const DecGemvArgs &a, int n0, int nblk
         q += split ? ld_coherent(p) : *p;
       }
       const float x = from_fix(q);
-      ((f16 *)a.nout.u)[(int64_t)b * a.N + n] = (f16)(x * a.nout.w[n]);
+      ((f16 *)a.nout.u)[a.nout.tiled ? tile_off(b, n, a.N) : (int64_t)b * a.N + n] = (f16)(x * a.nout.w[n]);
       sq = x * x;
     }
     s_buf[b * RB + nl] = sq;
@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(256) dec_embed_kernel(const int32_t *ids, cons
     x_fix[(int64_t)b * H + c] = q;
     if (nout.w) {
       const float x = from_fix(q);
-      ((f16 *)nout.u)[(int64_t)b * H + c] = (f16)(x * nout.w[c]);
+      ((f16 *)nout.u)[nout.tiled ? tile_off(b, c, H) : (int64_t)b * H + c] = (f16)(x * nout.w[c]);
       ss += x * x;
     }
   }
@@ -380,10 +380,12 @@ __device__ __forceinline__ float merge_splits(const float *pm, const float *pl, 
 }
 
 __global__ void __launch_bounds__(128) dec_merge_kernel(const float *pm, const float *pl, const float *po, int S, int nq,
-                                                        int hd, f16 *o) {
+                                                        int hd, f16 *o, int tiled) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   if (d >= hd) return;
-  o[(int64_t)b * nq * hd + (int64_t)h * hd + d] = (f16)merge_splits(pm, pl, po, ((int64_t)b * nq + h) * S, S, hd, d);
+  const int qd = nq * hd;
+  o[tiled ? tile_off(b, h * hd + d, qd) : (int64_t)b * qd + (int64_t)h * hd + d] =
+      (f16)merge_splits(pm, pl, po, ((int64_t)b * nq + h) * S, S, hd, d);
 }
 
 // ---------------------------------------------------------------- projections
@@ -712,6 +714,11 @@ hipError_t launch_gemv_nb(hipStream_t s, const DecGemvArgs &a, dim3 grid) {
 // of its outputs: q/k/v sums are stored, residual rows read-modify-written,
 // and no atomics are needed.  With one, the slices add fixed-point values
 // atomically (deterministic, as above).
+// In the decode step both operands are unit-tiled (qw_internal.h): a wave's
+// 16-byte loads of one unit then read one contiguous 1 KB tile, where the
+// row-major layout gave 16 separate 64-byte pieces per load instruction, 3 KB
+// or more apart (weights) or re-read from L2 (activations).  Measured with
+// the loads alone at the 32-row gate/up shape: 22.8 -> 15.0 us per launch.
 template <int RT, int NB, int MAXU, DecOut OM, bool ATOMIC, int NW = 4>
 __global__ void __launch_bounds__(64 * NW) dec_rows_kernel(DecGemvArgs a) {
   constexpr int RB = 16 * RT, BT = 16 * NB, NT = 64 * NW;
@@ -737,12 +744,19 @@ __global__ void __launch_bounds__(64 * NW) dec_rows_kernel(DecGemvArgs a) {
 
   // lane (i, g): weight row n0 + 16 r + i and batch row 16 nb + i, k offset 8 g
   // of each unit; rows past N or M are clamped and their results never stored
+  // unit-tiled operands: a unit's 16 x 32 tile is one 1 KB piece (lane l
+  // reads bytes 16 l ..), tiles of a row block 512 elements apart
   const f16 *wp[RT];
   const f16 *xp[NB];
+  const int wstr = a.w_tiled ? 512 : 32, xstr = a.act_tiled ? 512 : 32;     // elements per unit
 #pragma unroll
-  for (int r = 0; r < RT; ++r) wp[r] = (const f16 *)a.W + (int64_t)min(n0 + 16 * r + i, a.N - 1) * a.K + 8 * g;
+  for (int r = 0; r < RT; ++r)
+    wp[r] = (const f16 *)a.W + (a.w_tiled ? (int64_t)(nblk * RT + r) * units * 512 + 8 * lane
+                                          : (int64_t)min(n0 + 16 * r + i, a.N - 1) * a.K + 8 * g);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) xp[nb] = (const f16 *)a.act + (int64_t)min(16 * nb + i, a.M - 1) * a.lda + 8 * g;
+  for (int nb = 0; nb < NB; ++nb)
+    xp[nb] = (const f16 *)a.act + (a.act_tiled ? (int64_t)nb * units * 512 + 8 * lane
+                                               : (int64_t)min(16 * nb + i, a.M - 1) * a.lda + 8 * g);
 
   f32x4 acc[RT][NB];
 #pragma unroll
@@ -755,11 +769,10 @@ __global__ void __launch_bounds__(64 * NW) dec_rows_kernel(DecGemvArgs a) {
 #pragma unroll
     for (int t = 0; t < MAXU; ++t) {
       if (ub + t < u1) {        // uniform (scalar) condition: no load past the share
-        const int k = 32 * (ub + t);
 #pragma unroll
-        for (int r = 0; r < RT; ++r) w[t][r] = load8(wp[r] + k);
+        for (int r = 0; r < RT; ++r) w[t][r] = load8(wp[r] + (int64_t)wstr * (ub + t));
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) x[t][nb] = load8(xp[nb] + k);
+        for (int nb = 0; nb < NB; ++nb) x[t][nb] = load8(xp[nb] + (int64_t)xstr * (ub + t));
       }
     }
     // keep every load of the batch ahead of the first multiply (the
@@ -817,7 +830,7 @@ __global__ void __launch_bounds__(64 * NW) dec_rows_kernel(DecGemvArgs a) {
       const int f = nblk * (RB / 2) + fl;
       if (b >= a.M || f >= a.N / 2) continue;
       const float gt = total(2 * GU_BLOCK * p + j, b), up = total(2 * GU_BLOCK * p + GU_BLOCK + j, b);
-      h[(int64_t)b * a.ldh + f] = (f16)(silu_f(gt) * up);
+      h[a.act_tiled ? tile_off(b, f, a.ldh) : (int64_t)b * a.ldh + f] = (f16)(silu_f(gt) * up);
     }
   } else {
     // logits (optional copy) and this block's (max, lowest index) per batch row
@@ -1352,7 +1365,7 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
         const int h = j * G + h_lo + t;
         if (S == 1) {
           const float inv = 1.0f / l[t];
-          f16 *out = (f16 *)a.o + (int64_t)b * qd + h * HD + d0;
+          f16 *out = (f16 *)a.o + (a.o_tiled ? tile_off(b, h * HD + d0, qd) : (int64_t)b * qd + h * HD + d0);
 #pragma unroll
           for (int e = 0; e < 8; ++e) out[e] = (f16)(o[t][e] * inv);
         } else {
@@ -1396,7 +1409,7 @@ __global__ void __launch_bounds__(256) dec_attn_kernel(DecAttnArgs a) {
       }
       const int h = j * G + hh;
       if (S == 1) {
-        ((f16 *)a.o)[(int64_t)b * qd + h * HD + d] = (f16)(O / L);
+        ((f16 *)a.o)[a.o_tiled ? tile_off(b, h * HD + d, qd) : (int64_t)b * qd + h * HD + d] = (f16)(O / L);
       } else {
         const int64_t st = ((int64_t)b * nq + h) * S + split;
         if (d == 0) {
@@ -1630,7 +1643,7 @@ __global__ void __launch_bounds__(256) dec_attn_mfma_kernel(DecAttnArgs a) {
     }
     const int h = j * G + hh;
     if (S == 1) {
-      ((f16 *)a.o)[(int64_t)b * qd + h * HD + d] = (f16)(O / L);
+      ((f16 *)a.o)[a.o_tiled ? tile_off(b, h * HD + d, qd) : (int64_t)b * qd + h * HD + d] = (f16)(O / L);
     } else {
       const int64_t st = ((int64_t)b * nq + h) * S + split;
       if (d == 0) {
@@ -2309,6 +2322,7 @@ int dec_attn_splits(int batch, int n_kv_heads, int ctx, int target_groups) {
 hipError_t launch_dec_embed(hipStream_t s, const int32_t *ids, int B, const void *emb, float emb_scale, int H, int V,
                             long long *x_fix, int *bad, long long *clr0, int64_t n0, long long *clr1, int64_t n1,
                             const RowNormOut &nout) {
+  if (nout.w && nout.tiled && H % 32) return hipErrorInvalidValue;
   QW_LAUNCH((dec_embed_kernel), dim3(B), dim3(256), 0, s, ids, (const f16 *)emb, emb_scale, H, V, x_fix, bad, clr0, n0,
             clr1, n1, nout);
   return hipGetLastError();
@@ -2324,9 +2338,9 @@ int dec_norm_parts(int M, int N, int K) {
 
 
 hipError_t launch_dec_merge(hipStream_t s, const float *pm, const float *pl, const float *po, int S, int B, int nq,
-                            int hd, void *o) {
-  if (S < 1 || S > MERGE_MAX_S || hd > 128) return hipErrorInvalidValue;
-  QW_LAUNCH((dec_merge_kernel), dim3(nq, B), dim3(128), 0, s, pm, pl, po, S, nq, hd, (f16 *)o);
+                            int hd, void *o, bool tiled) {
+  if (S < 1 || S > MERGE_MAX_S || hd > 128 || (tiled && (nq * hd) % 32)) return hipErrorInvalidValue;
+  QW_LAUNCH((dec_merge_kernel), dim3(nq, B), dim3(128), 0, s, pm, pl, po, S, nq, hd, (f16 *)o, (int)tiled);
   return hipGetLastError();
 }
 
@@ -2355,7 +2369,11 @@ hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &in) {
                    !(rows_path || a.logits_mode)))
     return hipErrorInvalidValue;
   if (a.nout.w && (!rows_path || a.swiglu_out || dec_norm_parts(a.M, a.N, a.K) == 0 || !a.nout.counters ||
-                   !a.nout.u || !a.nout.ss || a.nout.ss_ld < dec_norm_parts(a.M, a.N, a.K)))
+                   !a.nout.u || !a.nout.ss || a.nout.ss_ld < dec_norm_parts(a.M, a.N, a.K) ||
+                   (a.nout.tiled && a.N % 32)))
+    return hipErrorInvalidValue;
+  // unit-tiled weights and operands only in the batched kernels
+  if (((a.w_tiled || a.act_tiled) && !rows_path) || (a.act_tiled && a.swiglu_out && a.ldh % 32))
     return hipErrorInvalidValue;
   const int units = a.K / 32;
   int splits = (a.logits_mode || a.swiglu_out) ? 1 : (a.splits < 1 ? 1 : a.splits);
@@ -2377,6 +2395,7 @@ hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &in) {
 
 hipError_t launch_dec_attention(hipStream_t s, const DecAttnArgs &a) {
   const int g = a.n_heads / a.n_kv_heads;
+  if (a.o_tiled && (a.n_heads * a.head_dim) % 32) return hipErrorInvalidValue;
   dim3 grid(a.splits, a.n_kv_heads, a.batch);
   switch (a.head_dim) {
     case 32: return launch_attn_hd<32>(s, a, grid, g);

@@ -200,6 +200,18 @@ struct AttnArgs {
   float softmax_scale;
 };
 
+// Unit-tiled layout of the batched decode step's f16 matrices (more than two
+// rows): a [rows, K] matrix as 1 KB tiles of 16 rows x 32 k, tile (R, U) =
+// rows 16R .. 16R + 15, k 32U .. 32U + 31, tiles of a row block consecutive
+// in U; inside a tile, element (i, k) at 128 ((k % 32) / 8) + 8 i + k % 8, the
+// lane order of the MFMA operand (lane i + 16 g holds row i, k 8g .. 8g + 7),
+// so one wave-wide 16-byte load reads one tile.  Rows are padded to a multiple
+// of kTileRows for weights and of 16 for activations.
+constexpr int kTileRows = 64;
+__device__ __host__ __forceinline__ int64_t tile_off(int row, int k, int K) {
+  return ((int64_t)(row >> 4) * (K >> 5) + (k >> 5)) * 512 + ((k & 31) >> 3) * 128 + (row & 15) * 8 + (k & 7);
+}
+
 // RMSNorm hand-off between the batched decode projections (more than two
 // rows), see k_decode.hip.  The projection that finishes a block of residual
 // columns writes the next projection's operand without the row scale,
@@ -214,6 +226,7 @@ struct RowNormOut {
   int ss_ld;
   int *counters;            // one per column block, zero between launches
   int64_t rep_stride;       // residual replicas of out_fix (value = their sum)
+  int tiled;                // u in the unit-tiled layout
 };
 struct RowNormIn {
   const float *ss;          // NULL: the operand is already normalised
@@ -257,6 +270,8 @@ struct DecGemvArgs {
   int *num_flag;            // status word (kFlagFixRange, kFlagNonFinite)
   RowNormOut nout;          // batched FixAdd residual projections: the next norm's operand
   RowNormIn nin;            // batched projections and the LM head: operand u without 1/rms
+  int w_tiled;              // batched projections: W in the unit-tiled layout (rows padded to kTileRows)
+  int act_tiled;            // batched projections: f16 operand (and a SwiGLU projection's h) unit-tiled
 };
 
 // Decode-step attention, see k_decode.hip.
@@ -275,6 +290,7 @@ struct DecAttnArgs {
   float softmax_scale;
   long long *clear;                  // side job: zero clear[0 .. clear_n)
   int64_t clear_n;
+  int o_tiled;                       // splits == 1: o in the unit-tiled layout
 };
 
 // Decode-step attention merged with the o projection, for one or two rows and
@@ -368,7 +384,10 @@ hipError_t launch_dec_mlp(hipStream_t s, const DecMlpArgs &a);
 // the merged split-KV attention output o [B, nq*hd] as f16, formed once for
 // batches of more than two rows
 hipError_t launch_dec_merge(hipStream_t s, const float *pm, const float *pl, const float *po, int S, int B, int nq,
-                            int hd, void *o);
+                            int hd, void *o, bool tiled = false);
+// Wt = W [N, K] f16 in the unit-tiled layout, rows padded with zeros to a
+// multiple of kTileRows (Wt holds round_up(N, kTileRows) * K elements)
+hipError_t launch_tile_units(hipStream_t s, const void *W, int N, int K, void *Wt);
 hipError_t launch_dec_attn_o(hipStream_t s, const DecAttnOArgs &a);
 // also sets kFlagNonFinite in *flag when a row holds an inf or NaN logit, and
 // adds pos_add to pos_dev[r] for every row r (when pos_dev is non-NULL)

@@ -79,6 +79,9 @@ struct LayerBuf {
   void *w_gu = nullptr;     // [2I, H], GU_BLOCK-interleaved
   void *w_down = nullptr;   // [H, I]
   void *w_down_t = nullptr; // [I, H] copy read by the fused decode MLP (f16 mode)
+  // unit-tiled copies read by the batched decode projections (models that can
+  // decode more than two rows): w_qkv, w_o, w_gu, w_down
+  void *tl_qkv = nullptr, *tl_o = nullptr, *tl_gu = nullptr, *tl_down = nullptr;
   float *in_norm = nullptr, *post_norm = nullptr;
   float s_qkv = 1.f, s_o = 1.f, s_gu = 1.f, s_down = 1.f;
 };
@@ -216,6 +219,11 @@ constexpr bool kHeadNormKernel = true;
 #define QW_NORM_HANDOFF 1
 #endif
 constexpr bool kNormHandOff = QW_NORM_HANDOFF;
+#ifndef QW_TILED_DECODE
+#define QW_TILED_DECODE 1
+#endif
+// more than two rows: projections read unit-tiled weights and operands
+constexpr bool kTiledDecode = QW_TILED_DECODE;
 // Up to this context length (and two rows), attention and the o projection
 // are one kernel in which every workgroup reads its head's whole context;
 // past it the split-KV kernel and the o projection (measured: the merged
@@ -529,7 +537,12 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   // kernel runs; `parts` sums per row (1 after the embedding)
   const int parts = fused_norm ? 0 : std::min(dec_norm_parts(B, H, m->qd), dec_norm_parts(B, H, I));
   const bool hand = parts > 0 && kNormHandOff;
-  auto hand_out = [&](const float *w) {
+  // with the hand-off, the projections' weights and f16 operands (u, o, h)
+  // are unit-tiled (the producers of u, o and h write that layout)
+  const bool tiled = hand && m->L[0].tl_qkv != nullptr;
+  // (the final norm's operand, read only by the LM head's row-wise staging,
+  // keeps the row layout)
+  auto hand_out = [&](const float *w, bool row_layout = false) {
     RowNormOut r{};
     if (!hand) return r;
     r.w = w;
@@ -538,7 +551,14 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     r.ss_ld = kNormPartsMax;
     r.counters = d.sync;
     r.rep_stride = xs;
+    r.tiled = tiled && !row_layout;
     return r;
+  };
+  auto use_tiled = [&](DecGemvArgs &g, const void *w_tl) {
+    if (!tiled) return;
+    g.W = w_tl;
+    g.w_tiled = 1;
+    g.act_tiled = 1;
   };
   auto hand_in = [&](int n_parts) {
     RowNormIn r{};
@@ -584,6 +604,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     DecGemvArgs g = dec_args(m->status, Lw.w_qkv, B, m->nqkv, H, Lw.s_qkv, gemv_target);
     normed(g, Lw.in_norm);
     g.nin = hand_in(l == 0 ? 1 : parts);
+    use_tiled(g, Lw.tl_qkv);
     g.out_fix = d.qkv_fix;
     g.ldo = m->nqkv;
     e = timed(m, s, F_GEMM_QKV, [&] { return launch_dec_gemv(s, g); });
@@ -633,13 +654,14 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       da.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
       da.clear = fused_mlp ? xo : gu_clear;
       da.clear_n = fused_mlp ? kXReps * xs : n_gu;
+      da.o_tiled = tiled;
       e = timed(m, s, F_ATTENTION, [&] { return launch_dec_attention(s, da); });
       if (e != hipSuccess) return e;
       g = dec_args(m->status, Lw.w_o, B, H, m->qd, Lw.s_o, gemv_target);
       if (S > 1 && !fused_norm) {
         // many rows: merge once, then an f16 operand
         e = timed(m, s, F_ATTN_MERGE, [&] {
-          return launch_dec_merge(s, d.att_m, d.att_l, d.att_o, S, B, c.n_heads, c.head_dim, d.o);
+          return launch_dec_merge(s, d.att_m, d.att_l, d.att_o, S, B, c.n_heads, c.head_dim, d.o, tiled);
         });
         if (e != hipSuccess) return e;
         g.act_mode = 0;
@@ -662,6 +684,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       g.clear = d.qkv_fix;
       g.clear_n = n_qkv;
       g.nout = hand_out(Lw.post_norm);
+      use_tiled(g, Lw.tl_o);
       e = timed(m, s, F_GEMM_O, [&] { return launch_dec_gemv(s, g); });
       if (e != hipSuccess) return e;
     }
@@ -694,6 +717,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     normed(g, Lw.post_norm);
     g.role_gate_up = 1;
     g.nin = hand_in(parts);
+    use_tiled(g, Lw.tl_gu);
     g.out_fix = d.gu_fix;
     if (!fused_norm) {
       // many rows: full K per workgroup, SwiGLU in the epilogue, f16 h out
@@ -722,7 +746,8 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     }
     g.out_fix = xr;
     g.ldo = H;
-    g.nout = hand_out(l + 1 < c.n_layers ? m->L[l + 1].in_norm : m->final_norm);
+    g.nout = l + 1 < c.n_layers ? hand_out(m->L[l + 1].in_norm) : hand_out(m->final_norm, true);
+    use_tiled(g, Lw.tl_down);
     e = timed(m, s, F_GEMM_DOWN, [&] { return launch_dec_gemv(s, g); });
     if (e != hipSuccess) return e;
   }
@@ -734,6 +759,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     g.act = d.u;
     g.lda = H;
     g.nin = hand_in(parts);
+    // the LM head's operand (and its own weights) keep the row layout
   } else if (kHeadNormKernel || !fused_norm) {
     e = timed(m, s, F_RMSNORM, [&] { return launch_dec_norm(s, xr, xs, B, H, m->final_norm, c.rms_eps, d.u); });
     if (e != hipSuccess) return e;
@@ -977,6 +1003,13 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
                    decode_fast_supported(c.head_dim, c.n_heads / c.n_kv_heads, H, m->qd, I);
   // the fused decode MLP (batches of up to two rows) reads W_down transposed
   const bool with_down_t = m->fast_decode && dec_mlp_supported(H, I);
+  // the batched decode projections (more than two rows) read unit-tiled copies
+  const bool with_tiled = m->fast_decode && c.max_batch > kFusedNormRows && kTiledDecode;
+  auto tiled_copy = [&](void **dst, const void *W, int N, int K) -> hipError_t {
+    hipError_t e = m->alloc(dst, (size_t)(N + kTileRows - 1) / kTileRows * kTileRows * K * 2);
+    if (e != hipSuccess) return e;
+    return launch_tile_units(s, W, N, K, *dst);
+  };
   const size_t es = m->esz;
   for (int l = 0; l < c.n_layers; ++l) {
     const qw_layer_weights &Lw = weights->layers[l];
@@ -1003,6 +1036,12 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
     if (with_down_t) {
       CREATE_TRY(m->alloc(&B.w_down_t, (size_t)I * H * es));
       CREATE_TRY(launch_convert_t(s, src_kind, Lw.down_w, H, I, B.w_down_t, sd));
+    }
+    if (with_tiled) {
+      CREATE_TRY(tiled_copy(&B.tl_qkv, B.w_qkv, m->nqkv, H));
+      CREATE_TRY(tiled_copy(&B.tl_o, B.w_o, H, m->qd));
+      CREATE_TRY(tiled_copy(&B.tl_gu, B.w_gu, 2 * I, H));
+      CREATE_TRY(tiled_copy(&B.tl_down, B.w_down, H, I));
     }
     CREATE_TRY(launch_convert(s, src_kind, Lw.input_norm, H, false, B.in_norm, 0, 1.f));
     CREATE_TRY(launch_convert(s, src_kind, Lw.post_norm, H, false, B.post_norm, 0, 1.f));
@@ -1051,7 +1090,9 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
   CREATE_TRY(hipMemsetAsync(m->v_cache, 0, cache_bytes, s));
   CREATE_TRY(m->alloc((void **)&m->rope, (size_t)c.max_seq * (c.head_dim / 2) * sizeof(float2)));
   CREATE_TRY(launch_rope_table(s, m->rope, c.max_seq, c.head_dim, (double)c.rope_theta));
-  const size_t R = (size_t)m->rows_cap;
+  // (at least 16 rows per 16-row block: the batched decode step's operands
+  // are unit-tiled, in blocks of 16 rows)
+  const size_t R = std::max<size_t>((size_t)m->rows_cap, (size_t)(c.max_batch + 15) / 16 * 16);
   CREATE_TRY(m->alloc((void **)&m->x, R * H * 4));
   CREATE_TRY(m->alloc(&m->u, R * H * es));
   CREATE_TRY(m->alloc((void **)&m->qkv, R * m->nqkv * 4));
@@ -1433,6 +1474,7 @@ qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits,
     return fail(QW_ERR_INVALID_ARG, "qw_decode_step_noalloc: sampling reads the logits: pass a logits buffer");
   const qw_config &c = m->cfg;
   const int64_t B = m->batch, H = c.hidden, I = c.intermediate, V = c.vocab;
+  const int64_t B16 = (B + 15) / 16 * 16;
   const DecodeNeeds need = decode_needs(m, (int)B);
   // carve the step's buffers out of this device's array, 256-byte aligned;
   // the last-arrival counters always sit at its start (zero at load, and
@@ -1445,7 +1487,7 @@ qw_status qw_decode_step_noalloc(qw_model *m, const int32_t *ids, float *logits,
       B * ((V + 63) / 64) * 4, B * ((V + 63) / 64) * 4,   // arg_v, arg_i
       B * c.n_heads * 16 * 4, B * c.n_heads * 16 * 4,     // att_m, att_l (at most 16 splits)
       B * c.n_heads * 16 * c.head_dim * 4,               // att_o
-      B * H * 2, B * m->qd * 2, B * I * 2,               // u, o, h (f16)
+      B16 * H * 2, B16 * m->qd * 2, B16 * I * 2,         // u, o, h (f16; unit-tiled in blocks of 16 rows)
       B * kNormPartsMax * 4,                             // norm_ss
   };
   constexpr int kParts = sizeof(sizes) / sizeof(sizes[0]);
