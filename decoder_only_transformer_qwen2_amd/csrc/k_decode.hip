@@ -412,6 +412,8 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
   const int row = nblk * 64 + wave * 16 + i;
   const bool row_ok = row < a.N;
   const f16 *W = (const f16 *)a.W + (int64_t)(row_ok ? row : 0) * a.K;
+  // unit-tiled weights: the wave's 16 rows are row block 4 nblk + wave
+  const f16 *Wtl = (const f16 *)a.W + (int64_t)(nblk * 4 + wave) * (a.K >> 5) * 512 + 8 * lane;
   const int k0 = split * a.units_per_split * 32;
   const int k1 = min(a.K, k0 + a.units_per_split * 32);
   const f16x8 zero = {};
@@ -433,7 +435,9 @@ __global__ void __launch_bounds__(256) dec_gemv_kernel(DecGemvArgs a) {
     // are never stored
     const int nu = min(8, (k1 - kc) >> 5);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) w[t] = load8(W + kc + 32 * min(t, nu - 1) + 8 * g);
+    for (int t = 0; t < 8; ++t)
+      w[t] = a.w_tiled ? load8(Wtl + (int64_t)((kc >> 5) + min(t, nu - 1)) * 512)
+                       : load8(W + kc + 32 * min(t, nu - 1) + 8 * g);
   };
   // with the norm in the prologue the residual rows are loaded first (the
   // norm then runs while the weights arrive)
@@ -1741,11 +1745,15 @@ dec_mlp32_kernel(DecMlpArgs a) {
   const f16 *Wt = (const f16 *)a.w_gu + (int64_t)(2 * f0 + 16 * tau + i) * H;
   const int ku = H / 64;
   const int kw0 = kh * ku * 32;
+  // unit-tiled copy: the wave's 16 rows are row block 2 f0 / 16 + tau
+  const f16 *Wtl = a.w_gu_tiled ? (const f16 *)a.w_gu_tiled + ((int64_t)(2 * f0 / 16 + tau) * (H >> 5) + (kw0 >> 5)) * 512 + 8 * lane
+                                : nullptr;
   f16x8 wt[KU];
   // units past ku load a clamped (in-range) address and are never multiplied:
   // a condition around the load would become a branch per load
 #pragma unroll
-  for (int t = 0; t < KU; ++t) wt[t] = load8(Wt + kw0 + 32 * min(t, ku - 1) + 8 * g);
+  for (int t = 0; t < KU; ++t)
+    wt[t] = Wtl ? load8(Wtl + (int64_t)min(t, ku - 1) * 512) : load8(Wt + kw0 + 32 * min(t, ku - 1) + 8 * g);
   const int CB = H / 8;
   const int rg = tid / CB, cb = tid % CB;
   const bool d_ok = rg < RG;
@@ -1903,9 +1911,13 @@ dec_mlp16_kernel(DecMlpArgs a) {
   const f16 *Wt = (const f16 *)a.w_gu + (int64_t)(2 * f0 + 16 * tau + i) * H;
   const int ku = H / 64;
   const int kw0 = kh * ku * 32;
+  // unit-tiled copy: the wave's 16 rows are row block 2 f0 / 16 + tau
+  const f16 *Wtl = a.w_gu_tiled ? (const f16 *)a.w_gu_tiled + ((int64_t)(2 * f0 / 16 + tau) * (H >> 5) + (kw0 >> 5)) * 512 + 8 * lane
+                                : nullptr;
   f16x8 wt[KU];
 #pragma unroll
-  for (int t = 0; t < KU; ++t) wt[t] = load8(Wt + kw0 + 32 * min(t, ku - 1) + 8 * g);
+  for (int t = 0; t < KU; ++t)
+    wt[t] = Wtl ? load8(Wtl + (int64_t)min(t, ku - 1) * 512) : load8(Wt + kw0 + 32 * min(t, ku - 1) + 8 * g);
   __builtin_amdgcn_sched_barrier(0);
 
   // the norm (the weights stay in flight)
@@ -2372,9 +2384,8 @@ hipError_t launch_dec_gemv(hipStream_t s, const DecGemvArgs &in) {
                    !a.nout.u || !a.nout.ss || a.nout.ss_ld < dec_norm_parts(a.M, a.N, a.K) ||
                    (a.nout.tiled && a.N % 32)))
     return hipErrorInvalidValue;
-  // unit-tiled weights and operands only in the batched kernels
-  if (((a.w_tiled || a.act_tiled) && !rows_path) || (a.act_tiled && a.swiglu_out && a.ldh % 32))
-    return hipErrorInvalidValue;
+  // tiled operands only in the batched kernels (tiled weights: every kernel)
+  if ((a.act_tiled && !rows_path) || (a.act_tiled && a.swiglu_out && a.ldh % 32)) return hipErrorInvalidValue;
   const int units = a.K / 32;
   int splits = (a.logits_mode || a.swiglu_out) ? 1 : (a.splits < 1 ? 1 : a.splits);
   a.units_per_split = (units + splits - 1) / splits;

@@ -270,7 +270,7 @@ struct DecGemvArgs {
   int *num_flag;            // status word (kFlagFixRange, kFlagNonFinite)
   RowNormOut nout;          // batched FixAdd residual projections: the next norm's operand
   RowNormIn nin;            // batched projections and the LM head: operand u without 1/rms
-  int w_tiled;              // batched projections: W in the unit-tiled layout (rows padded to kTileRows)
+  int w_tiled;              // W in the unit-tiled layout (rows padded to kTileRows)
   int act_tiled;            // batched projections: f16 operand (and a SwiGLU projection's h) unit-tiled
 };
 
@@ -333,6 +333,7 @@ struct DecMlpArgs {
   float gu_scale;
   const void *w_down_t;              // [I, H] f16, W_down transposed
   float down_scale;
+  const void *w_gu_tiled;            // w_gu unit-tiled (read instead of w_gu when set)
   int M, H, I;
   long long *clear;                  // side job: zero clear[0 .. clear_n) (may be NULL)
   int64_t clear_n;

@@ -116,6 +116,7 @@ struct qw_model {
   void *emb = nullptr;
   float emb_scale = 1.f;
   void *head = nullptr;
+  void *head_tl = nullptr;           // head unit-tiled (decode LM head), rows padded to kTileRows
   float head_scale = 1.f;
   float *final_norm = nullptr;
   void *k_cache = nullptr, *v_cache = nullptr;
@@ -554,11 +555,13 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
     r.tiled = tiled && !row_layout;
     return r;
   };
+  // every decode projection reads the unit-tiled weight copy; the operand is
+  // tiled too in the batched step with the hand-off
   auto use_tiled = [&](DecGemvArgs &g, const void *w_tl) {
-    if (!tiled) return;
+    if (!w_tl) return;
     g.W = w_tl;
     g.w_tiled = 1;
-    g.act_tiled = 1;
+    g.act_tiled = tiled;
   };
   auto hand_in = [&](int n_parts) {
     RowNormIn r{};
@@ -698,6 +701,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       ma.w_gu = Lw.w_gu;
       ma.gu_scale = Lw.s_gu;
       ma.w_down_t = Lw.w_down_t;
+      ma.w_gu_tiled = Lw.tl_gu;
       ma.down_scale = Lw.s_down;
       ma.M = B;
       ma.H = H;
@@ -754,6 +758,10 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   // the LM head has thousands of workgroups: the final row is normalised once
   // by a kernel of its own rather than in every workgroup's prologue
   DecGemvArgs g = dec_args(m->status, m->head, B, V, H, m->head_scale);
+  if (m->head_tl) {
+    g.W = m->head_tl;
+    g.w_tiled = 1;
+  }
   if (hand) {
     g.act_mode = 0;
     g.act = d.u;
@@ -1003,8 +1011,9 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
                    decode_fast_supported(c.head_dim, c.n_heads / c.n_kv_heads, H, m->qd, I);
   // the fused decode MLP (batches of up to two rows) reads W_down transposed
   const bool with_down_t = m->fast_decode && dec_mlp_supported(H, I);
-  // the batched decode projections (more than two rows) read unit-tiled copies
-  const bool with_tiled = m->fast_decode && c.max_batch > kFusedNormRows && kTiledDecode;
+  // the decode projections read unit-tiled copies (one 1 KB tile per MFMA
+  // operand); prefill reads the row-major ones
+  const bool with_tiled = m->fast_decode && kTiledDecode;
   auto tiled_copy = [&](void **dst, const void *W, int N, int K) -> hipError_t {
     hipError_t e = m->alloc(dst, (size_t)(N + kTileRows - 1) / kTileRows * kTileRows * K * 2);
     if (e != hipSuccess) return e;
@@ -1064,6 +1073,7 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
       CREATE_TRY(launch_convert(s, src_kind, weights->lm_head, (int64_t)V * H, dst_f16, m->head, 0, sh));
       m->head_scale = 1.f / sh;
     }
+    if (with_tiled) CREATE_TRY(tiled_copy(&m->head_tl, m->head, V, H));
     CREATE_TRY(m->alloc((void **)&m->final_norm, (size_t)H * 4));
     CREATE_TRY(launch_convert(s, src_kind, weights->final_norm, H, false, m->final_norm, 0, 1.f));
   }
