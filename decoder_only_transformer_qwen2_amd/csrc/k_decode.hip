@@ -2062,9 +2062,12 @@ __global__ void __launch_bounds__(256) dec_attn_o_kernel(DecAttnOArgs a) {
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int row = r0 + 16 * tt + i;
+    // unit-tiled copy: row block min(row / 16, last), unit (h hd) / 32 + s
+    const int rblk = min((r0 >> 4) + tt, (H - 1) >> 4);
 #pragma unroll
     for (int s2 = 0; s2 < HD / 32; ++s2)
-      wf[tt][s2] = load8((const f16 *)a.w_o + (int64_t)min(row, H - 1) * qd + h * HD + 32 * s2 + 8 * g);  // rows >= H: never stored
+      wf[tt][s2] = a.w_o_tl ? load8((const f16 *)a.w_o_tl + ((int64_t)rblk * (qd >> 5) + ((h * HD) >> 5) + s2) * 512 + 8 * lane)
+                            : load8((const f16 *)a.w_o + (int64_t)min(row, H - 1) * qd + h * HD + 32 * s2 + 8 * g);  // rows >= H: never stored
   }
   // cached keys 0 .. pos - 1: first batch before the prologue
   f16 *Kc = (f16 *)a.k_cache;

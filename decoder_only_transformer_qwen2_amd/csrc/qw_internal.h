@@ -305,6 +305,7 @@ struct DecAttnOArgs {
   const int *pos_dev;                // pos_dev[b]: position of row b's new token
   float softmax_scale;
   const void *w_o;                   // [H, nq*hd] f16
+  const void *w_o_tl;                // w_o unit-tiled (read instead of w_o when set)
   float o_scale;
   int H;
   long long *x_out;                  // [batch, H] fixed-point residual (atomic adds)

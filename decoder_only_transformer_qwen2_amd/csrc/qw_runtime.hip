@@ -627,6 +627,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
       ao.pos_dev = m->pos_dev;
       ao.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
       ao.w_o = Lw.w_o;
+      ao.w_o_tl = Lw.tl_o;
       ao.o_scale = Lw.s_o;
       ao.H = H;
       ao.x_out = xr;
