@@ -285,7 +285,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
     if (kb + 1 < n_kb) block(kb + 1, sn, sc);
   }
 
-  f16 *O = (f16 *)a.o + (int64_t)r0 * qd + h * HD;
+  // o rows, row-major or unit-tiled (the o projection's operand): a lane's 4
+  // dims are consecutive within one 8-dim chunk either way
+  f16 *O = (f16 *)a.o;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int q = q0 + 16 * t + i;
@@ -296,7 +298,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) a
       f16x4 v;
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = (f16)(o[d][t][r] * inv);
-      *reinterpret_cast<f16x4 *>(O + (int64_t)q * qd + 16 * d + 4 * g) = v;
+      const int row = r0 + q, col = h * HD + 16 * d + 4 * g;
+      *reinterpret_cast<f16x4 *>(O + (a.o_tiled ? tile_off(row, col, qd) : (int64_t)row * qd + col)) = v;
     }
   }
 }

@@ -50,10 +50,12 @@ hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int ro
 
 // ---------------------------------------------------------------- rmsnorm
 // One wave per row; fp32 statistics; the product is rounded once to T.
+// tiled (f16 mode): out in the unit-tiled layout (a GEMM operand; each
+// thread's 4 consecutive values lie in one 8-value chunk)
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ x, int rows, int row_stride,
                                                       int hidden, const float *__restrict__ w, float eps,
-                                                      T *__restrict__ out) {
+                                                      T *__restrict__ out, int tiled) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -67,24 +69,27 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ 
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)hidden + eps);
   const float4 *w4 = reinterpret_cast<const float4 *>(w);
-  T *o = out + (int64_t)r * hidden;
   for (int c = lane; c < n4; c += 64) {
     float4 v = xr[c], g = w4[c];
-    o[4 * c + 0] = from_f32<T>(v.x * inv * g.x);
-    o[4 * c + 1] = from_f32<T>(v.y * inv * g.y);
-    o[4 * c + 2] = from_f32<T>(v.z * inv * g.z);
-    o[4 * c + 3] = from_f32<T>(v.w * inv * g.w);
+    T *o = out + (tiled ? tile_off(r, 4 * c, hidden) : (int64_t)r * hidden + 4 * c);
+    o[0] = from_f32<T>(v.x * inv * g.x);
+    o[1] = from_f32<T>(v.y * inv * g.y);
+    o[2] = from_f32<T>(v.z * inv * g.z);
+    o[3] = from_f32<T>(v.w * inv * g.w);
   }
 }
 
 hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows, int row_stride, int hidden,
-                          const float *w, float eps, void *out) {
+                          const float *w, float eps, void *out, bool tiled) {
   if (rows <= 0) return hipSuccess;
+  if (tiled && (!f16_mode || hidden % 32)) return hipErrorInvalidValue;
   dim3 grid((rows + 3) / 4);
   if (f16_mode)
-    QW_LAUNCH((rmsnorm_kernel<f16>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (f16 *)out);
+    QW_LAUNCH((rmsnorm_kernel<f16>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (f16 *)out,
+              (int)tiled);
   else
-    QW_LAUNCH((rmsnorm_kernel<float>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (float *)out);
+    QW_LAUNCH((rmsnorm_kernel<float>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (float *)out,
+              0);
   return hipGetLastError();
 }
 

@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(GemmArgs a) {
           const int row = m0 + wm * 64 + x * 16 + 4 * g + r;
           if (row < a.M && f < a.N / 2) {
             const float gt = acc[x][2 * p][r] * a.scale, up = acc[x][2 * p + 1][r] * a.scale;
-            out[(int64_t)row * a.ldo + f] = (f16)(silu_f(gt) * up);
+            out[a.h_tiled ? tile_off(row, f, a.ldo) : (int64_t)row * a.ldo + f] = (f16)(silu_f(gt) * up);
           }
         }
       }
@@ -230,7 +230,13 @@ __device__ __forceinline__ void qkv_rope_store(const QkvRopeArgs &q, int row, in
   }
 }
 
-template <Epi EPI, int TBM, int TBN, int WVM, int WVN, int NS, bool FP = false>
+// TL: A and W unit-tiled (qw_internal.h; a.W is then the tiled weight copy):
+// a DMA instruction reads one 1 KB tile (16 rows x 32 k) and lands it in the
+// same order, which is also the MFMA operand order, so fragments are read
+// back as 1 KB contiguous per wave (no swizzle needed).  Row-major operands
+// take 16 pieces of 64 B per instruction, 2.5x the cost of contiguous reads
+// even from L2 (measured).
+template <Epi EPI, int TBM, int TBN, int WVM, int WVN, int NS, bool FP = false, bool TL = false>
 __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   constexpr int NWV = WVM * WVN;                  // waves
   constexpr int XT = TBM / WVM / 16, YT = TBN / WVN / 16;   // MFMA tiles per wave
@@ -262,24 +268,39 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
   const int kt0 = blockIdx.z * kt_per;
   const int KT = max(0, min(KT_all, kt0 + kt_per) - kt0);
   const f16 *srcA[QA], *srcB[QB];
+  if constexpr (TL) {
+    // row block (clamped to the last one; rows past M or N are never stored)
 #pragma unroll
-  for (int q = 0; q < QA; ++q) {
-    const int row = 16 * (QA * wave + q) + (lane >> 2);
-    const int c = (lane & 3) ^ lds_swz(row);
-    srcA[q] = A + (int64_t)min(m0 + row, a.M - 1) * a.lda + (int64_t)kt0 * LK + 8 * c;
-  }
+    for (int q = 0; q < QA; ++q) {
+      const int rb = min(m0 / 16 + QA * wave + q, (a.M - 1) / 16);
+      srcA[q] = A + ((int64_t)rb * (a.K / LK) + kt0) * 512 + 8 * lane;
+    }
 #pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    const int row = 16 * (QB * wave + q) + (lane >> 2);
-    const int c = (lane & 3) ^ lds_swz(row);
-    srcB[q] = W + (int64_t)min(n0 + row, a.N - 1) * a.K + (int64_t)kt0 * LK + 8 * c;
+    for (int q = 0; q < QB; ++q) {
+      const int rb = min(n0 / 16 + QB * wave + q, (a.N - 1) / 16);
+      srcB[q] = W + ((int64_t)rb * (a.K / LK) + kt0) * 512 + 8 * lane;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      const int row = 16 * (QA * wave + q) + (lane >> 2);
+      const int c = (lane & 3) ^ lds_swz(row);
+      srcA[q] = A + (int64_t)min(m0 + row, a.M - 1) * a.lda + (int64_t)kt0 * LK + 8 * c;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int row = 16 * (QB * wave + q) + (lane >> 2);
+      const int c = (lane & 3) ^ lds_swz(row);
+      srcB[q] = W + (int64_t)min(n0 + row, a.N - 1) * a.K + (int64_t)kt0 * LK + 8 * c;
+    }
   }
+  constexpr int KSTEP = TL ? 512 : LK;            // elements between consecutive K stages of a source
   auto issue = [&](int kt) {
     const int st = kt % NS;
 #pragma unroll
-    for (int q = 0; q < QA; ++q) dma16(srcA[q] + kt * LK, &sA[st][64 * (QA * wave + q)]);
+    for (int q = 0; q < QA; ++q) dma16(srcA[q] + kt * KSTEP, &sA[st][64 * (QA * wave + q)]);
 #pragma unroll
-    for (int q = 0; q < QB; ++q) dma16(srcB[q] + kt * LK, &sB[st][64 * (QB * wave + q)]);
+    for (int q = 0; q < QB; ++q) dma16(srcB[q] + kt * KSTEP, &sB[st][64 * (QB * wave + q)]);
   };
   constexpr int PER_STAGE = QA + QB;              // vmcnt per stage and wave
 
@@ -309,12 +330,12 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
 #pragma unroll
     for (int x = 0; x < XT; ++x) {
       const int row = wm * (TBM / WVM) + x * 16 + i;
-      fa[x] = sA[st][row * 4 + (g ^ lds_swz(row))];
+      fa[x] = TL ? sA[st][(row >> 4) * 64 + lane] : sA[st][row * 4 + (g ^ lds_swz(row))];
     }
 #pragma unroll
     for (int y = 0; y < YT; ++y) {
       const int row = wn * (TBN / WVN) + y * 16 + i;
-      fb[y] = sB[st][row * 4 + (g ^ lds_swz(row))];
+      fb[y] = TL ? sB[st][(row >> 4) * 64 + lane] : sB[st][row * 4 + (g ^ lds_swz(row))];
     }
   };
   auto mma = [&](const f16x8 (&fa)[XT], const f16x8 (&fb)[YT]) {
@@ -457,7 +478,8 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
         const int lr = e / V8, v = e % V8;
         const int row = m0 + lr, f = n0 / 2 + 8 * v;
         if (row < a.M && f < a.N / 2)
-          *reinterpret_cast<f16x8 *>(out + (int64_t)row * a.ldo + f) = *reinterpret_cast<const f16x8 *>(&sh[lr * HS + 8 * v]);
+          *reinterpret_cast<f16x8 *>(out + (a.h_tiled ? tile_off(row, f, a.ldo) : (int64_t)row * a.ldo + f)) =
+              *reinterpret_cast<const f16x8 *>(&sh[lr * HS + 8 * v]);
       }
     } else {
 #pragma unroll
@@ -470,7 +492,7 @@ __global__ void __launch_bounds__(64 * WVM * WVN) gemm_lds_kernel(GemmArgs a) {
           const int row = rw0 + x * 16 + 4 * g + r;
           if (row < a.M && f < a.N / 2) {
             const float gt = acc[x][2 * p][r] * a.scale, up = acc[x][2 * p + 1][r] * a.scale;
-            out[(int64_t)row * a.ldo + f] = (f16)(silu_f(gt) * up);
+            out[a.h_tiled ? tile_off(row, f, a.ldo) : (int64_t)row * a.ldo + f] = (f16)(silu_f(gt) * up);
           }
         }
       }
@@ -525,7 +547,8 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs a, int S) {
       gt += a.ws[z * slice + (int64_t)row * a.N + cg];
       up += a.ws[z * slice + (int64_t)row * a.N + cg + GU_BLOCK];
     }
-    ((f16 *)a.act_out)[(int64_t)row * a.ldo + f] = (f16)(silu_f(gt * a.scale) * (up * a.scale));
+    ((f16 *)a.act_out)[a.h_tiled ? tile_off(row, f, a.ldo) : (int64_t)row * a.ldo + f] =
+        (f16)(silu_f(gt * a.scale) * (up * a.scale));
   } else if constexpr (EPI == Epi::QkvRope) {
     // one thread per (row, column pair) of the unpermuted layout: pair p is
     // dims d and d + hd/2 of head slot p / (hd/2) (q heads, then k, then v)
@@ -611,6 +634,10 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
   // QkvRope runs split only: the multiply writes raw slices (any epilogue's
   // kernel does), and the reduction applies bias + RoPE + the writes
   if (a.epi == Epi::QkvRope && S < 2) return hipErrorInvalidValue;
+  // unit-tiled A and W only on the LDS-pipeline kernels (K % 32 == 0); h
+  // written tiled only by a SwiGLU epilogue with N / 2 % 32 == 0
+  if ((a.tiled && !(kLdsPipeline && a.K % LK == 0)) || (a.h_tiled && (a.epi != Epi::SwiGLU || (a.N / 2) % 32)))
+    return hipErrorInvalidValue;
   const Epi ke = a.epi == Epi::QkvRope ? Epi::StoreF32 : a.epi;
   const int tiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
   dim3 grid(8 * ((tiles + 7) / 8), 1, S);
@@ -621,15 +648,33 @@ hipError_t launch_gemm_mfma(hipStream_t s, const GemmArgs &a) {
     // stage's MFMAs: gate/up of an 8x2048 prefill 25.5 -> 24.3 ms (three
     // stages with the same pipelining: 26.1 ms)
     switch (ke) {
-      case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, kBigStages, true>), dim3(g2), dim3(512), 0, s, a); break;
-      case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, kBigStages, true>), dim3(g2), dim3(512), 0, s, a); break;
-      case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 256, 256, 2, 4, kBigStages, true>), dim3(g2), dim3(512), 0, s, a); break;
+      case Epi::StoreF32:
+        if (a.tiled) QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, kBigStages, true, true>), dim3(g2), dim3(512), 0, s, a);
+        else QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 256, 256, 2, 4, kBigStages, true>), dim3(g2), dim3(512), 0, s, a);
+        break;
+      case Epi::ResidAdd:
+        if (a.tiled) QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, kBigStages, true, true>), dim3(g2), dim3(512), 0, s, a);
+        else QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 256, 256, 2, 4, kBigStages, true>), dim3(g2), dim3(512), 0, s, a);
+        break;
+      case Epi::SwiGLU:
+        if (a.tiled) QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 256, 256, 2, 4, kBigStages, true, true>), dim3(g2), dim3(512), 0, s, a);
+        else QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 256, 256, 2, 4, kBigStages, true>), dim3(g2), dim3(512), 0, s, a);
+        break;
     }
   } else if (kLdsPipeline && a.K % LK == 0) {
     switch (ke) {
-      case Epi::StoreF32: QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a); break;
-      case Epi::ResidAdd: QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a); break;
-      case Epi::SwiGLU: QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a); break;
+      case Epi::StoreF32:
+        if (a.tiled) QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 128, 128, 2, 2, 4, false, true>), dim3(grid), dim3(256), 0, s, a);
+        else QW_LAUNCH((gemm_lds_kernel<Epi::StoreF32, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a);
+        break;
+      case Epi::ResidAdd:
+        if (a.tiled) QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 128, 128, 2, 2, 4, false, true>), dim3(grid), dim3(256), 0, s, a);
+        else QW_LAUNCH((gemm_lds_kernel<Epi::ResidAdd, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a);
+        break;
+      case Epi::SwiGLU:
+        if (a.tiled) QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 128, 128, 2, 2, 4, false, true>), dim3(grid), dim3(256), 0, s, a);
+        else QW_LAUNCH((gemm_lds_kernel<Epi::SwiGLU, 128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, s, a);
+        break;
     }
   } else switch (ke) {
     case Epi::StoreF32: QW_LAUNCH((gemm_mfma_kernel<Epi::StoreF32>), dim3(grid), dim3(256), 0, s, a); break;

@@ -170,6 +170,8 @@ struct GemmArgs {
   int splits = 1;       // MFMA path: K slices (> 1 needs ws)
   float *ws = nullptr;  // [splits, M, N] fp32 slice tiles
   QkvRopeArgs qr;       // QkvRope
+  int tiled = 0;        // A and W unit-tiled (W = the tiled weight copy; A rows padded to 16)
+  int h_tiled = 0;      // SwiGLU: h written unit-tiled (the down projection's A)
 };
 
 struct RopeCacheArgs {
@@ -194,6 +196,7 @@ struct AttnArgs {
   int n_tiles;
   const void *v_t;            // prefill (f16): V of the prompt transposed, [B][nkv][hd][round_up(P, 64)]
   void *o;                    // [T, nq*hd]
+  int o_tiled = 0;            // prefill (f16): o unit-tiled (the o projection's operand)
   int T, rows_per_seq, n_heads, n_kv_heads, head_dim;
   int pos0;
   const int *pos0_dev;        // pos0_dev[b] for sequence b
@@ -350,7 +353,7 @@ hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int ro
                         int64_t ids_stride, const void *emb, float emb_scale, int hidden, int vocab, float *x,
                         int *bad_id_flag);
 hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows, int row_stride,
-                          int hidden, const float *w, float eps, void *out);
+                          int hidden, const float *w, float eps, void *out, bool tiled = false);
 hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a);
 hipError_t launch_attention_generic(hipStream_t s, bool f16_mode, const AttnArgs &a);
 bool attn_prefill_supported(int head_dim);

@@ -79,8 +79,8 @@ struct LayerBuf {
   void *w_gu = nullptr;     // [2I, H], GU_BLOCK-interleaved
   void *w_down = nullptr;   // [H, I]
   void *w_down_t = nullptr; // [I, H] copy read by the fused decode MLP (f16 mode)
-  // unit-tiled copies read by the batched decode projections (models that can
-  // decode more than two rows): w_qkv, w_o, w_gu, w_down
+  // unit-tiled copies of w_qkv, w_o, w_gu, w_down (f16 models whose widths
+  // are multiples of 32), read by the prefill GEMMs and the decode projections
   void *tl_qkv = nullptr, *tl_o = nullptr, *tl_gu = nullptr, *tl_down = nullptr;
   float *in_norm = nullptr, *post_norm = nullptr;
   float s_qkv = 1.f, s_o = 1.f, s_gu = 1.f, s_down = 1.f;
@@ -116,7 +116,7 @@ struct qw_model {
   void *emb = nullptr;
   float emb_scale = 1.f;
   void *head = nullptr;
-  void *head_tl = nullptr;           // head unit-tiled (decode LM head), rows padded to kTileRows
+  void *head_tl = nullptr;           // head unit-tiled (every LM head), rows padded to kTileRows
   float head_scale = 1.f;
   float *final_norm = nullptr;
   void *k_cache = nullptr, *v_cache = nullptr;
@@ -225,6 +225,12 @@ constexpr bool kNormHandOff = QW_NORM_HANDOFF;
 #endif
 // more than two rows: projections read unit-tiled weights and operands
 constexpr bool kTiledDecode = QW_TILED_DECODE;
+#ifndef QW_TILED_PREFILL
+#define QW_TILED_PREFILL 1
+#endif
+// prefill and the LM head over row batches: the MFMA GEMMs read unit-tiled
+// weights and operands (A and W stages land as whole 1 KB tiles)
+constexpr bool kTiledPrefill = QW_TILED_PREFILL;
 // Up to this context length (and two rows), attention and the o projection
 // are one kernel in which every workgroup reads its head's whole context;
 // past it the split-KV kernel and the o projection (measured: the merged
@@ -285,10 +291,18 @@ hipError_t timed(qw_model *m, hipStream_t s, Family fam, F &&launch) {
   return e;
 }
 
+// W_tl: the unit-tiled copy of W, with A unit-tiled too (NULL: both
+// row-major); h_tiled: a SwiGLU projection writes h unit-tiled
 hipError_t gemm(qw_model *m, hipStream_t s, Family fam, const void *A, int M, int K, int lda, const void *W, int N,
-                float scale, Epi epi, float *out_f32, void *act_out, int ldo, const QkvRopeArgs *qr = nullptr) {
+                float scale, Epi epi, float *out_f32, void *act_out, int ldo, const QkvRopeArgs *qr = nullptr,
+                const void *W_tl = nullptr, bool h_tiled = false) {
   GemmArgs a;
   if (qr) a.qr = *qr;
+  if (W_tl) {
+    W = W_tl;
+    a.tiled = 1;
+  }
+  a.h_tiled = h_tiled;
   a.A = A;
   a.W = W;
   a.M = M;
@@ -310,6 +324,7 @@ hipError_t gemm(qw_model *m, hipStream_t s, Family fam, const void *A, int M, in
     }
     return timed(m, s, fam, [&] { return launch_gemm_mfma(s, a); });
   }
+  if (a.tiled || a.h_tiled) return hipErrorInvalidValue;     // tiled operands only on the MFMA kernels
   return timed(m, s, fam, [&] { return launch_gemm_generic(s, m->f16, a); });
 }
 
@@ -344,10 +359,16 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
   probe.N = m->nqkv;
   probe.qr.head_dim = c.head_dim;
   const bool fuse_rope = m->f16 && !pos_dev && pos0 == 0 && gemm_mfma_supported(probe);
+  // the GEMM operands u, o and h unit-tiled, with the tiled weight copies,
+  // where every producer writes that layout (the prefill attention among them)
+  const bool tiled = kTiledPrefill && m->f16 && !pos_dev && pos0 == 0 && attn_prefill_supported(c.head_dim) &&
+                     m->L[0].tl_qkv && H % 32 == 0 && m->qd % 32 == 0 && I % 64 == 0;
+  auto tl = [&](const void *w) -> const void * { return tiled ? w : nullptr; };
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerBuf &Lw = m->L[l];
     hipError_t e;
-    e = timed(m, s, F_RMSNORM, [&] { return launch_rmsnorm(s, m->f16, m->x, T, H, H, Lw.in_norm, c.rms_eps, m->u); });
+    e = timed(m, s, F_RMSNORM,
+              [&] { return launch_rmsnorm(s, m->f16, m->x, T, H, H, Lw.in_norm, c.rms_eps, m->u, tiled); });
     if (e != hipSuccess) return e;
     char *kc = (char *)m->k_cache + (int64_t)l * m->cache_layer_elems * m->esz;
     char *vc = (char *)m->v_cache + (int64_t)l * m->cache_layer_elems * m->esz;
@@ -364,10 +385,12 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
       qr.n_heads = c.n_heads;
       qr.n_kv_heads = c.n_kv_heads;
       qr.head_dim = c.head_dim;
-      e = gemm(m, s, F_GEMM_QKV, m->u, T, H, H, Lw.w_qkv, m->nqkv, Lw.s_qkv, Epi::QkvRope, nullptr, nullptr, 0, &qr);
+      e = gemm(m, s, F_GEMM_QKV, m->u, T, H, H, Lw.w_qkv, m->nqkv, Lw.s_qkv, Epi::QkvRope, nullptr, nullptr, 0, &qr,
+               tl(Lw.tl_qkv));
       if (e != hipSuccess) return e;
     } else {
-    e = gemm(m, s, F_GEMM_QKV, m->u, T, H, H, Lw.w_qkv, m->nqkv, Lw.s_qkv, Epi::StoreF32, m->qkv, nullptr, m->nqkv);
+    e = gemm(m, s, F_GEMM_QKV, m->u, T, H, H, Lw.w_qkv, m->nqkv, Lw.s_qkv, Epi::StoreF32, m->qkv, nullptr, m->nqkv,
+             nullptr, tl(Lw.tl_qkv));
     if (e != hipSuccess) return e;
     RopeCacheArgs ra;
     ra.qkv = m->qkv;
@@ -410,6 +433,7 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
     aa.pos0_dev = pos_dev;
     aa.softmax_scale = 1.0f / sqrtf((float)c.head_dim);
     aa.v_t = m->v_t;
+    aa.o_tiled = tiled;
     if (m->f16 && !pos_dev && pos0 == 0 && attn_prefill_supported(c.head_dim)) {
       const int B = rag ? rag->rows.n : T / rows_per_seq;
       const int max_len = rag ? rag->max_len : rows_per_seq;
@@ -423,13 +447,17 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
       e = timed(m, s, F_ATTENTION, [&] { return launch_attention_generic(s, m->f16, aa); });
 
     if (e != hipSuccess) return e;
-    e = gemm(m, s, F_GEMM_O, m->o, T, m->qd, m->qd, Lw.w_o, H, Lw.s_o, Epi::ResidAdd, m->x, nullptr, H);
+    e = gemm(m, s, F_GEMM_O, m->o, T, m->qd, m->qd, Lw.w_o, H, Lw.s_o, Epi::ResidAdd, m->x, nullptr, H, nullptr,
+             tl(Lw.tl_o));
     if (e != hipSuccess) return e;
-    e = timed(m, s, F_RMSNORM, [&] { return launch_rmsnorm(s, m->f16, m->x, T, H, H, Lw.post_norm, c.rms_eps, m->u); });
+    e = timed(m, s, F_RMSNORM,
+              [&] { return launch_rmsnorm(s, m->f16, m->x, T, H, H, Lw.post_norm, c.rms_eps, m->u, tiled); });
     if (e != hipSuccess) return e;
-    e = gemm(m, s, F_GEMM_GATE_UP, m->u, T, H, H, Lw.w_gu, 2 * I, Lw.s_gu, Epi::SwiGLU, nullptr, m->h, I);
+    e = gemm(m, s, F_GEMM_GATE_UP, m->u, T, H, H, Lw.w_gu, 2 * I, Lw.s_gu, Epi::SwiGLU, nullptr, m->h, I, nullptr,
+             tl(Lw.tl_gu), tiled);
     if (e != hipSuccess) return e;
-    e = gemm(m, s, F_GEMM_DOWN, m->h, T, I, I, Lw.w_down, H, Lw.s_down, Epi::ResidAdd, m->x, nullptr, H);
+    e = gemm(m, s, F_GEMM_DOWN, m->h, T, I, I, Lw.w_down, H, Lw.s_down, Epi::ResidAdd, m->x, nullptr, H, nullptr,
+             tl(Lw.tl_down));
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -441,12 +469,16 @@ hipError_t run_head(qw_model *m, hipStream_t s, const float *x_rows, int rows, i
                     const float *arg_logits, int arg_rows, int64_t arg_stride, int32_t *next, int *pos_dev,
                     int pos_add) {
   const qw_config &c = m->cfg;
+  // the normed rows unit-tiled for the tiled head copy; not for one row
+  // (measured: 1.5B head 0.130 -> 0.148 ms tiled at one row, 0.152 -> 0.145
+  // at eight)
+  const bool tiled = kTiledPrefill && m->head_tl != nullptr && rows > 1;
   hipError_t e = timed(m, s, F_RMSNORM, [&] {
-    return launch_rmsnorm(s, m->f16, x_rows, rows, stride, c.hidden, m->final_norm, c.rms_eps, m->u);
+    return launch_rmsnorm(s, m->f16, x_rows, rows, stride, c.hidden, m->final_norm, c.rms_eps, m->u, tiled);
   });
   if (e != hipSuccess) return e;
   e = gemm(m, s, F_LM_HEAD, m->u, rows, c.hidden, c.hidden, m->head, c.vocab, m->head_scale, Epi::StoreF32, logits,
-           nullptr, c.vocab);
+           nullptr, c.vocab, nullptr, tiled ? m->head_tl : nullptr);
   if (e != hipSuccess) return e;
   return timed(m, s, F_ARGMAX,
                [&] { return launch_argmax(s, arg_logits, arg_rows, c.vocab, arg_stride, next, pos_dev, pos_add, m->status); });
@@ -540,7 +572,7 @@ hipError_t decode_fast(qw_model *m, hipStream_t s, const int32_t *ids, int32_t *
   const bool hand = parts > 0 && kNormHandOff;
   // with the hand-off, the projections' weights and f16 operands (u, o, h)
   // are unit-tiled (the producers of u, o and h write that layout)
-  const bool tiled = hand && m->L[0].tl_qkv != nullptr;
+  const bool tiled = kTiledDecode && hand && m->L[0].tl_qkv != nullptr;
   // (the final norm's operand, read only by the LM head's row-wise staging,
   // keeps the row layout)
   auto hand_out = [&](const float *w, bool row_layout = false) {
@@ -1012,9 +1044,9 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
                    decode_fast_supported(c.head_dim, c.n_heads / c.n_kv_heads, H, m->qd, I);
   // the fused decode MLP (batches of up to two rows) reads W_down transposed
   const bool with_down_t = m->fast_decode && dec_mlp_supported(H, I);
-  // the decode projections read unit-tiled copies (one 1 KB tile per MFMA
-  // operand); prefill reads the row-major ones
-  const bool with_tiled = m->fast_decode && kTiledDecode;
+  // the projections read unit-tiled copies (one 1 KB tile per MFMA
+  // operand), prefill and decode alike
+  const bool with_tiled = m->f16 && (kTiledDecode || kTiledPrefill) && H % 32 == 0 && m->qd % 32 == 0 && I % 32 == 0;
   auto tiled_copy = [&](void **dst, const void *W, int N, int K) -> hipError_t {
     hipError_t e = m->alloc(dst, (size_t)(N + kTileRows - 1) / kTileRows * kTileRows * K * 2);
     if (e != hipSuccess) return e;
@@ -1101,9 +1133,8 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
   CREATE_TRY(hipMemsetAsync(m->v_cache, 0, cache_bytes, s));
   CREATE_TRY(m->alloc((void **)&m->rope, (size_t)c.max_seq * (c.head_dim / 2) * sizeof(float2)));
   CREATE_TRY(launch_rope_table(s, m->rope, c.max_seq, c.head_dim, (double)c.rope_theta));
-  // (at least 16 rows per 16-row block: the batched decode step's operands
-  // are unit-tiled, in blocks of 16 rows)
-  const size_t R = std::max<size_t>((size_t)m->rows_cap, (size_t)(c.max_batch + 15) / 16 * 16);
+  // (whole 16-row blocks: unit-tiled operands are stored in blocks of 16 rows)
+  const size_t R = (std::max<size_t>((size_t)m->rows_cap, (size_t)c.max_batch) + 15) / 16 * 16;
   CREATE_TRY(m->alloc((void **)&m->x, R * H * 4));
   CREATE_TRY(m->alloc(&m->u, R * H * es));
   CREATE_TRY(m->alloc((void **)&m->qkv, R * m->nqkv * 4));
