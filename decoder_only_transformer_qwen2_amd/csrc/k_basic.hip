@@ -48,14 +48,14 @@ hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int ro
   return hipGetLastError();
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
 // ---------------------------------------------------------------- rmsnorm
 // One wave per row; fp32 statistics; the product is rounded once to T.
-// tiled (f16 mode): out in the unit-tiled layout (a GEMM operand; each
-// thread's 4 consecutive values lie in one 8-value chunk)
 template <typename T>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ x, int rows, int row_stride,
                                                       int hidden, const float *__restrict__ w, float eps,
-                                                      T *__restrict__ out, int tiled) {
+                                                      T *__restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -69,27 +69,102 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ 
   ss = wave_sum(ss);
   const float inv = 1.0f / sqrtf(ss / (float)hidden + eps);
   const float4 *w4 = reinterpret_cast<const float4 *>(w);
+  T *o = out + (int64_t)r * hidden;
   for (int c = lane; c < n4; c += 64) {
     float4 v = xr[c], g = w4[c];
-    T *o = out + (tiled ? tile_off(r, 4 * c, hidden) : (int64_t)r * hidden + 4 * c);
-    o[0] = from_f32<T>(v.x * inv * g.x);
-    o[1] = from_f32<T>(v.y * inv * g.y);
-    o[2] = from_f32<T>(v.z * inv * g.z);
-    o[3] = from_f32<T>(v.w * inv * g.w);
+    o[4 * c + 0] = from_f32<T>(v.x * inv * g.x);
+    o[4 * c + 1] = from_f32<T>(v.y * inv * g.y);
+    o[4 * c + 2] = from_f32<T>(v.z * inv * g.z);
+    o[4 * c + 3] = from_f32<T>(v.w * inv * g.w);
+  }
+}
+
+// The same norm with f16 output in the unit-tiled layout (a GEMM operand).
+// One workgroup of 16 waves per 16-row block, so a block's tiles are written
+// from one XCD's L2 (four-row workgroups put each tile's rows on four XCDs,
+// and their partial-line writes cost 60% more time).  Lane (i, g) of wave w
+// takes row i and values 8g .. 8g + 7 of the 32-value units w, w + 16, ...
+// (at most U of them), held in registers between the two passes: every load
+// is issued at once, and each store of a wave is one whole 1 KB tile.  The
+// row's sum of squares is added over the lanes of the row, then over the 16
+// waves in a fixed order.
+template <int U>
+__global__ void __launch_bounds__(1024) rmsnorm_tiled_kernel(const float *__restrict__ x, int rows, int row_stride,
+                                                             int hidden, const float *__restrict__ w, float eps,
+                                                             f16 *__restrict__ out) {
+  __shared__ float s_ss[16][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int r = blockIdx.x * 16 + i;
+  const bool live = r < rows;
+  const float *xr = x + (int64_t)(live ? r : rows - 1) * row_stride + 8 * g;
+  const int units = hidden >> 5;
+  float4 a[U], b[U];
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int t = wave + 16 * j;
+    if (t < units) {
+      a[j] = *reinterpret_cast<const float4 *>(xr + 32 * t);
+      b[j] = *reinterpret_cast<const float4 *>(xr + 32 * t + 4);
+    } else {
+      a[j] = b[j] = float4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < U; ++j)
+    ss += a[j].x * a[j].x + a[j].y * a[j].y + a[j].z * a[j].z + a[j].w * a[j].w + b[j].x * b[j].x +
+          b[j].y * b[j].y + b[j].z * b[j].z + b[j].w * b[j].w;
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  if (g == 0) s_ss[wave][i] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) tot += s_ss[v][i];
+  const float inv = 1.0f / sqrtf(tot / (float)hidden + eps);
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int t = wave + 16 * j;
+    if (t >= units) break;
+    const float4 wa = *reinterpret_cast<const float4 *>(w + 32 * t + 8 * g);
+    const float4 wb = *reinterpret_cast<const float4 *>(w + 32 * t + 8 * g + 4);
+    f16x8_t v;
+    v[0] = (f16)(a[j].x * inv * wa.x);
+    v[1] = (f16)(a[j].y * inv * wa.y);
+    v[2] = (f16)(a[j].z * inv * wa.z);
+    v[3] = (f16)(a[j].w * inv * wa.w);
+    v[4] = (f16)(b[j].x * inv * wb.x);
+    v[5] = (f16)(b[j].y * inv * wb.y);
+    v[6] = (f16)(b[j].z * inv * wb.z);
+    v[7] = (f16)(b[j].w * inv * wb.w);
+    if (live) *reinterpret_cast<f16x8_t *>(out + tile_off(r, 32 * t + 8 * g, hidden)) = v;
   }
 }
 
 hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows, int row_stride, int hidden,
                           const float *w, float eps, void *out, bool tiled) {
   if (rows <= 0) return hipSuccess;
-  if (tiled && (!f16_mode || hidden % 32)) return hipErrorInvalidValue;
+  if (tiled && (!f16_mode || hidden % 32 || hidden > kRmsTiledMaxHidden)) return hipErrorInvalidValue;
+  if (tiled) {
+    // units of 32 values per wave (16 waves)
+    const int per_wave = (hidden / 32 + 15) / 16;
+    const dim3 grid((rows + 15) / 16);
+    if (per_wave <= 2)
+      QW_LAUNCH(rmsnorm_tiled_kernel<2>, grid, dim3(1024), 0, s, x, rows, row_stride, hidden, w, eps, (f16 *)out);
+    else if (per_wave <= 4)
+      QW_LAUNCH(rmsnorm_tiled_kernel<4>, grid, dim3(1024), 0, s, x, rows, row_stride, hidden, w, eps, (f16 *)out);
+    else if (per_wave <= 8)
+      QW_LAUNCH(rmsnorm_tiled_kernel<8>, grid, dim3(1024), 0, s, x, rows, row_stride, hidden, w, eps, (f16 *)out);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   dim3 grid((rows + 3) / 4);
   if (f16_mode)
-    QW_LAUNCH((rmsnorm_kernel<f16>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (f16 *)out,
-              (int)tiled);
+    QW_LAUNCH((rmsnorm_kernel<f16>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (f16 *)out);
   else
-    QW_LAUNCH((rmsnorm_kernel<float>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (float *)out,
-              0);
+    QW_LAUNCH((rmsnorm_kernel<float>), dim3(grid), dim3(256), 0, s, x, rows, row_stride, hidden, w, eps, (float *)out);
   return hipGetLastError();
 }
 
@@ -454,7 +529,6 @@ hipError_t launch_convert_t(hipStream_t s, int src_kind, const void *src, int ro
 
 // Unit-tiled copy of an f16 weight matrix (layout in qw_internal.h): one
 // thread per 16 bytes of the destination, read as 16 bytes of one source row.
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 __global__ void __launch_bounds__(256) tile_units_kernel(const f16 *W, int N, int K, f16 *Wt, int64_t n8) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;      // 16-byte piece c of Wt
   if (c >= n8) return;

@@ -352,6 +352,8 @@ bool dec_mlp_supported(int hidden, int inter);
 hipError_t launch_embed(hipStream_t s, bool f16_mode, const int32_t *ids, int rows, int rows_per_seq,
                         int64_t ids_stride, const void *emb, float emb_scale, int hidden, int vocab, float *x,
                         int *bad_id_flag);
+// tiled: f16 out in the unit-tiled layout (hidden % 32 == 0, at most kRmsTiledMaxHidden)
+constexpr int kRmsTiledMaxHidden = 4096;
 hipError_t launch_rmsnorm(hipStream_t s, bool f16_mode, const float *x, int rows, int row_stride,
                           int hidden, const float *w, float eps, void *out, bool tiled = false);
 hipError_t launch_rope_cache(hipStream_t s, bool f16_mode, const RopeCacheArgs &a);

@@ -362,7 +362,8 @@ hipError_t run_layers(qw_model *m, hipStream_t s, int T, int rows_per_seq, int p
   // the GEMM operands u, o and h unit-tiled, with the tiled weight copies,
   // where every producer writes that layout (the prefill attention among them)
   const bool tiled = kTiledPrefill && m->f16 && !pos_dev && pos0 == 0 && attn_prefill_supported(c.head_dim) &&
-                     m->L[0].tl_qkv && H % 32 == 0 && m->qd % 32 == 0 && I % 64 == 0;
+                     m->L[0].tl_qkv && H % 32 == 0 && H <= kRmsTiledMaxHidden && m->qd % 32 == 0 &&
+                     I % 64 == 0;
   auto tl = [&](const void *w) -> const void * { return tiled ? w : nullptr; };
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerBuf &Lw = m->L[l];
@@ -472,7 +473,7 @@ hipError_t run_head(qw_model *m, hipStream_t s, const float *x_rows, int rows, i
   // the normed rows unit-tiled for the tiled head copy; not for one row
   // (measured: 1.5B head 0.130 -> 0.148 ms tiled at one row, 0.152 -> 0.145
   // at eight)
-  const bool tiled = kTiledPrefill && m->head_tl != nullptr && rows > 1;
+  const bool tiled = kTiledPrefill && m->head_tl != nullptr && rows > 1 && c.hidden <= kRmsTiledMaxHidden;
   hipError_t e = timed(m, s, F_RMSNORM, [&] {
     return launch_rmsnorm(s, m->f16, x_rows, rows, stride, c.hidden, m->final_norm, c.rms_eps, m->u, tiled);
   });
