@@ -374,7 +374,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is "
-              "described in DESIGN.md but not built", file=sys.stderr)
+              "a design only, not built", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -31,7 +31,7 @@ Sources, cited by page title and section:
        (prefill populates the KV cache, decode feeds one token at a time) and
        section 1.1 (compare logits, not only tokens).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * RoPE angle pos * theta**(-2i/hd) is evaluated in float64 (the harness
     listing evaluates it in float32; exact evaluation is the plain reading of
     the formula).
@@ -180,8 +180,8 @@ def greedy_token(logits: np.ndarray) -> int:
 
 # ---------------------------------------------------------------- sampling
 # "augur" lists temperature, top-k and top-p sampling as not yet built; the
-# pages give no formulas for them, so the plain reading is taken (listed in
-# the design doc): keep the top_k largest logits (ties: lower index first), weight
+# pages give no formulas for them, so the plain reading is taken: keep the
+# top_k largest logits (ties: lower index first), weight
 # them by exp((l - l_max) / temperature), keep the shortest prefix of that
 # order whose weight reaches top_p of the total, and pick by the inverse
 # cumulative distribution of one uniform draw u in [0, 1).
