@@ -203,8 +203,9 @@ struct AttnArgs {
   float softmax_scale;
 };
 
-// Unit-tiled layout of the batched decode step's f16 matrices (more than two
-// rows): a [rows, K] matrix as 1 KB tiles of 16 rows x 32 k, tile (R, U) =
+// Unit-tiled layout of f16 GEMM operands (the weight copies, and u, o and h
+// of prefill and of the batched decode step): a [rows, K] matrix as 1 KB
+// tiles of 16 rows x 32 k, tile (R, U) =
 // rows 16R .. 16R + 15, k 32U .. 32U + 31, tiles of a row block consecutive
 // in U; inside a tile, element (i, k) at 128 ((k % 32) / 8) + 8 i + k % 8, the
 // lane order of the MFMA operand (lane i + 16 g holds row i, k 8g .. 8g + 7),
