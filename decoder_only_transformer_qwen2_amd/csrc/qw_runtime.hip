@@ -1046,8 +1046,9 @@ static qw_status create_model(const qw_config *cfg, const qw_weights *weights, v
   // the fused decode MLP (batches of up to two rows) reads W_down transposed
   const bool with_down_t = m->fast_decode && dec_mlp_supported(H, I);
   // the projections read unit-tiled copies (one 1 KB tile per MFMA
-  // operand), prefill and decode alike
-  const bool with_tiled = m->f16 && (kTiledDecode || kTiledPrefill) && H % 32 == 0 && m->qd % 32 == 0 && I % 32 == 0;
+  // operand), prefill and decode alike: made where one of them reads them
+  const bool with_tiled = m->f16 && H % 32 == 0 && m->qd % 32 == 0 && I % 32 == 0 &&
+                          ((kTiledDecode && m->fast_decode) || (kTiledPrefill && H <= kRmsTiledMaxHidden));
   auto tiled_copy = [&](void **dst, const void *W, int N, int K) -> hipError_t {
     hipError_t e = m->alloc(dst, (size_t)(N + kTileRows - 1) / kTileRows * kTileRows * K * 2);
     if (e != hipSuccess) return e;

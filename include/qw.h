@@ -118,8 +118,9 @@ typedef struct qw_model qw_model;
 /* Build a model on the current HIP device.
  * Reads every weight once to make the library's own packed copies (fused QKV
  * with fp32 bias, row-interleaved gate/up, fp16 or fp32 compute copies; in
- * fp16 mode also a second copy of every projection and of the LM head in the
- * GEMMs' tiled operand order, so about twice the weight bytes), so the
+ * fp16 mode also, wherever the prefill or decode kernels read it (always
+ * for hidden <= 4096), a second copy of every projection and of the LM head
+ * in the kernels' tiled operand order: about twice the weight bytes), so the
  * caller's weight buffers may be freed after this returns.  Allocates the
  * KV cache (2 * n_layers * max_batch * nkv * max_seq * hd elements of the
  * compute type), a RoPE cos/sin table for max_seq positions, and workspace for
